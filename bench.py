@@ -1,0 +1,296 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the fused exponent-coded KV attention on one MI355X.
+
+Workload: a Qwen3-8B-shaped decode step at 8192-token context - 36 layers, batch 16, 32 query /
+8 KV heads, head_dim 128, 16-token pages; per sequence 511 compressed pages plus the 16-token BF16
+tail page (the page that completes in this step).  Seeded synthetic KV: per-channel scale 2^u,
+u ~ U[-5, 5], 5% of blocks with a forced out-of-window element; queries ~ N(0, 1).
+
+One step = the whole hot path once: fused decode attention for all 36 layers (each layer reads
+its own buffers, so no layer is served from cache), then page completion - the tail page of every
+(layer, sequence, KV head, K|V) is encoded into the slot pool - then those runs are freed again so
+every step sees the same pool state.
+
+Printed (one JSON line): effective BF16-equivalent KV GB/s of the whole step (value), ms per step,
+the roofline of the attention kernel (algorithmic bytes per launch / its average duration from
+HIP events on the launch stream), the uncompressed BF16 baseline kernel timed in the same run,
+and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attention µs/step + effective KV GB/s (fraction of HBM peak) at 8K ctx"
+HBM_PEAK_GBPS = 8000.0
+
+B, HQ, HKV, LAYERS, CTX = 16, 32, 8, 36, 8192
+N_COMP = 511
+TAIL = 16
+U_MAX = 5.0
+FORCED = 0.05
+SEED = 2
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--layers", type=int, default=LAYERS,
+                    help="layers per step (the workload has 36; fewer is for quick checks only)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: the path has no multi-GPU form in this build "
+              "(see DESIGN.md for how it would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from decode_attention_kvz_amd import kvz, paged, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kvz.kvz_device_check(0)
+    n_layers = args.layers
+    scale = 1.0 / math.sqrt(128.0)
+
+    # ---------------- setup: every layer's compressed pages, tails, baseline store ----------
+    n_phys = B * N_COMP
+    arena_bytes = n_layers * n_phys * HKV * 2 * 4096 + n_layers * B * HKV * 2 * 4096 + (16 << 20)
+    arena = paged.SlotArena(arena_bytes, device=dev)
+    layers = []
+    rng = np.random.default_rng(SEED)
+    t_setup = time.time()
+    for layer in range(n_layers):
+        pages = synth.kv_pages(B, N_COMP + 1, HKV, seed=SEED, layer=layer, u_max=U_MAX,
+                               forced_frac=FORCED, device=dev)
+        perm = rng.permutation(n_phys)
+        block_table = perm.reshape(B, N_COMP).astype(np.int32)
+        meta = paged.new_meta_table(n_phys, HKV, device=dev)
+        page_ids = [(b, p) for b in range(B) for p in range(N_COMP)]
+        items = paged.page_items(pages, page_ids, meta, block_table.reshape(-1))
+        d_items = paged.encode(arena, items)
+        tail = pages[:, N_COMP].contiguous()
+        store = None
+        if not args.no_baseline:
+            inv = torch.as_tensor(np.argsort(block_table.reshape(-1)), device=dev)
+            nat = pages[:, :N_COMP].reshape(n_phys, 2, HKV, 16, 128)[inv]
+            store = paged.pack_bf16_pages(nat)
+            del nat
+        q = synth.queries(B, HQ, seed=SEED * 1000 + layer, device=dev)
+        torch.cuda.synchronize()
+        del d_items, pages
+        layers.append(dict(meta=meta, block_table=torch.from_numpy(block_table).to(dev),
+                           tail=tail, q=q, store=store,
+                           out=torch.empty((B, HQ, 128), dtype=torch.float32, device=dev)))
+        if layer % 6 == 5 or layer == n_layers - 1:
+            log(f"setup: {layer + 1}/{n_layers} layers encoded ({time.time() - t_setup:.1f}s)")
+    seq_lens = torch.full((B,), CTX, dtype=torch.int32, device=dev)
+    n_comp = torch.full((B,), N_COMP, dtype=torch.int32, device=dev)
+    ws = paged.workspace(B, HQ, HKV, N_COMP, args.splits, device=dev)
+    ws_b = paged.workspace(B, HQ, HKV, N_COMP, args.splits, device=dev)
+
+    # page completion: the tail page of every (layer, sequence, KV head, K|V) this step
+    comp_meta = paged.new_meta_table(n_layers * B, HKV, device=dev)
+    src, dst, kinds = [], [], []
+    for layer, L in enumerate(layers):
+        t = L["tail"]
+        for b in range(B):
+            for h in range(HKV):
+                for kind in range(2):
+                    src.append(t.data_ptr() + (((b * 2 + kind) * HKV + h) * 2048) * 2)
+                    dst.append(comp_meta.data_ptr() + (((layer * B + b) * HKV + h) * 2 + kind) * 8)
+                    kinds.append(kind)
+    n_comp_items = len(src)
+    comp_items = torch.from_numpy(kvz.encode_items(src, dst, 128, kinds)).to(dev)
+    comp_ptrs = torch.from_numpy(np.asarray(dst, dtype=np.int64)).to(dev)
+
+    # algorithmic bytes of one attention launch (per layer): every group record + metadata +
+    # block table + tail + q + out
+    stats = arena.stats()
+    rec_bytes = stats["live_granules"] * 256 / n_layers
+    raw_frac = stats["live_raw_blocks"] / (stats["live_runs"] * 4)
+    bf16_kv_layer = B * CTX * HKV * 128 * 2 * 2
+    alg_bytes = (rec_bytes + B * N_COMP * HKV * 16 + B * N_COMP * 4 + B * 2 * HKV * 16 * 128 * 2
+                 + B * HQ * 128 * 2 + B * HQ * 128 * 4)
+    log(f"setup done in {time.time() - t_setup:.1f}s: raw block fraction {raw_frac:.3f}, "
+        f"records {rec_bytes / 1e6:.1f} MB/layer vs BF16 {B * N_COMP * HKV * 4096 * 2 / 1e6:.1f} MB")
+
+    stream = torch.cuda.current_stream()
+
+    def attention(L, fused=True):
+        if fused:
+            kvz.kvz_decode_attention(L["q"], L["out"], arena.arena, L["meta"], L["block_table"],
+                                     seq_lens, n_comp, L["tail"], scale, ws, args.splits)
+        else:
+            kvz.kvz_bf16_decode_attention(L["q"], L["out"], L["store"], L["block_table"], seq_lens,
+                                          n_comp, L["tail"], scale, ws_b, HKV, args.splits)
+
+    def step(events=None):
+        for i, L in enumerate(layers):
+            if events is not None:
+                events[i][0].record(stream)
+            attention(L)
+            if events is not None:
+                events[i][1].record(stream)
+        kvz.kvz_encode_pages(arena.pool, comp_items, n_comp_items)
+        kvz.kvz_slot_free(arena.pool, comp_ptrs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # whole steps, no events inside
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    # the attention kernel alone: HIP events around each launch on the launch stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in layers]
+    attn_ms = []
+    for _ in range(args.steps):
+        step(ev)
+        torch.cuda.synchronize()
+        attn_ms.append([e[0].elapsed_time(e[1]) for e in ev])
+    attn_ms = np.asarray(attn_ms)
+    us_layer = float(np.median(attn_ms)) * 1e3
+    us_layer_mean = float(np.mean(attn_ms)) * 1e3
+    achieved = alg_bytes / (us_layer_mean * 1e-6) / 1e9
+    # encode + free of the completed pages, alone
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        kvz.kvz_encode_pages(arena.pool, comp_items, n_comp_items)
+        kvz.kvz_slot_free(arena.pool, comp_ptrs)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    enc_us = e0.elapsed_time(e1) * 1e3 / args.steps
+    log(f"fused: {ms_step:.3f} ms/step, attention {us_layer:.1f} us/layer (median), "
+        f"{achieved:.0f} GB/s algorithmic; encode+free {enc_us:.1f} us/step")
+
+    baseline = None
+    if not args.no_baseline:
+        for _ in range(args.warmup):
+            for L in layers:
+                attention(L, fused=False)
+        torch.cuda.synchronize()
+        evb = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in layers]
+        b_ms = []
+        for _ in range(args.steps):
+            for i, L in enumerate(layers):
+                evb[i][0].record(stream)
+                attention(L, fused=False)
+                evb[i][1].record(stream)
+            torch.cuda.synchronize()
+            b_ms.append([e[0].elapsed_time(e[1]) for e in evb])
+        b_ms = np.asarray(b_ms)
+        b_alg = (B * N_COMP * HKV * 4096 * 2 + B * N_COMP * 4 + B * 2 * HKV * 16 * 128 * 2
+                 + B * HQ * 128 * 2 + B * HQ * 128 * 4)
+        b_us = float(np.median(b_ms)) * 1e3
+        b_mean = float(np.mean(b_ms)) * 1e3
+        baseline = {"us_per_layer": round(b_us, 2), "us_per_step_attention": round(b_mean * n_layers, 1),
+                    "achieved_GBps": round(b_alg / (b_mean * 1e-6) / 1e9, 1),
+                    "hbm_frac": round(b_alg / (b_mean * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+        log(f"bf16 baseline: {b_us:.1f} us/layer, {baseline['achieved_GBps']} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(layers, n_phys, scale)
+
+    value = bf16_kv_layer * n_layers / (ms_step * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; per-channel scale 2^U[-5,5], 5% forced-raw blocks)",
+        "config": {"workload": "qwen3-8b-shaped decode step at 8192-token context",
+                   "layers": n_layers, "batch": B, "q_heads": HQ, "kv_heads": HKV,
+                   "head_dim": 128, "page_tokens": 16, "context": CTX,
+                   "compressed_pages": N_COMP, "tail_tokens": TAIL, "splits": args.splits or "auto",
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "attention_us_per_layer": round(us_layer, 2),
+        "attention_us_per_step": round(us_layer_mean * n_layers, 1),
+        "encode_free_us_per_step": round(enc_us, 1),
+        "effective_attention_GBps": round(bf16_kv_layer / (us_layer_mean * 1e-6) / 1e9, 1),
+        "raw_block_fraction": round(raw_frac, 4),
+        "record_bytes_per_layer": int(rec_bytes),
+        "bf16_kv_bytes_per_layer": int(bf16_kv_layer),
+        "baseline_bf16": baseline,
+        "speedup_vs_bf16_kernel": (round(baseline["us_per_layer"] / us_layer, 4) if baseline else None),
+    }
+    print(json.dumps(line), flush=True)
+    arena.close()
+
+
+def cpu_baseline(layers, n_phys, scale):
+    """The oracle on a bounded sample: decode + fp64 attention of one sequence (all KV heads,
+    8192 tokens) of layer 0, inputs encoded by the oracle itself outside the timed region."""
+    import torch
+    from decode_attention_kvz_amd import synth
+    from oracle import attention
+    from oracle.cache import OracleCache
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:   # pragma: no cover
+        threadpool_limits = None
+
+    # regenerate sequence 0 of layer 0 (the same seeded pages) on the host side
+    pages = synth.kv_pages(B, N_COMP + 1, HKV, seed=SEED, layer=0, u_max=U_MAX, forced_frac=FORCED,
+                           device="cuda")
+    nat = synth.bits(pages[0])                      # [512, 2, Hkv, 16, 128]
+    del pages
+    q = synth.bits(layers[0]["q"])
+    t0 = time.time()
+    oc = OracleCache((N_COMP * HKV * 2 + 16) * 4096)
+    flat = nat[:N_COMP].transpose(0, 2, 1, 3, 4).reshape(-1, 16, 128)
+    metas = oc.encode(flat, [i % 2 for i in range(flat.shape[0])])
+    meta_table = [[[metas[(p * HKV + h) * 2 + k] for k in range(2)] for h in range(HKV)]
+                  for p in range(N_COMP)]
+    log(f"cpu baseline: oracle encode of the sample took {time.time() - t0:.1f}s (untimed)")
+    block_table = np.arange(N_COMP, dtype=np.int64).reshape(1, N_COMP)
+    tail = nat[N_COMP][None]
+    qs = q[:1]
+    import contextlib
+    limit = threadpool_limits(limits=1) if threadpool_limits is not None else contextlib.nullcontext()
+    with limit:
+        t0 = time.perf_counter()
+        attention.decode_attention(qs, oc.arena, meta_table, block_table, [CTX], [N_COMP], tail,
+                                   scale)
+        dt = time.perf_counter() - t0
+    bytes_eff = CTX * HKV * 128 * 2 * 2
+    log(f"cpu baseline: {dt:.1f}s for one sequence ({bytes_eff / dt / 1e9:.4f} GB/s)")
+    return {"value": round(bytes_eff / dt / 1e9, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "layer 0, sequence 0: 511 compressed pages + 16-token tail, 8 KV heads, 32 "
+                      "query heads (1/576 of a step's attention), decode + fp64 attention, "
+                      "1 thread"}
+
+
+if __name__ == "__main__":
+    main()

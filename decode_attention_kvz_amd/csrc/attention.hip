@@ -1,0 +1,535 @@
+// Paged split-K GQA decode attention over exponent-coded BF16 pages (fused restore), and the
+// same kernel over uncompressed BF16 pages (the baseline).
+//
+// Follows "GAAC: Lossless KV Compression for Bandwidth-Efficient LLM Inference on Personal
+// Devices", section "Attention with On-the-Fly Decompression": compressed tiles and their
+// metadata are read, BF16 is rebuilt only for the working tile and used at once for the scores
+// and the weighted sum of values, and compressed pages and the BF16 tail share one softmax.
+// The restore and the K/V operand layouts follow "ZipFusion: Fusing Lossless KV Decompression
+// with Attention for Efficient LLM Decoding", section "How it works".
+//
+// Work decomposition (one wave = one unit = (sequence b, KV head, split s)):
+//   * a unit walks a contiguous range of its sequence's pages (the tail page counts as the
+//     last page); per page it loads the four K and four V blocks of its KV head (16 bytes per
+//     lane per block: a compressed chunk is 12 bytes and the next 4 are ignored), restores them
+//     in registers, and runs
+//       S[16 tokens x 16 heads] = K_page(16x128) . Q^T   as 4 x v_mfma_f32_16x16x32_bf16,
+//       O[32 heads x 128]      += P(32x16) . V_page    as 4 x 2 x v_mfma_f32_32x32x16_bf16,
+//     with P split into bf16 hi + lo parts so that P is carried to ~2^-17 relative;
+//   * the query group (G <= 16 heads sharing the KV head) is the MFMA's head dimension;
+//   * online softmax in base 2 per head; rows of O are rescaled only when a head's max rises;
+//   * every unit writes (m, l, O) for its heads; attn_combine merges the splits.
+#include "kvz_internal.h"
+
+#include <math.h>
+
+namespace kvz {
+
+namespace {
+
+struct AttnParams {
+  const uint16_t* q;
+  const uint8_t* kv;            // pool arena (compressed) or BF16 pages (baseline)
+  const uint4* meta;            // [phys][Hkv] : {K off, K tags, V off, V tags}; compressed only
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* n_comp;
+  const uint16_t* tail;
+  float* out;                   // [B][Hq][128]
+  float* ws_ml;                 // [units][G][2]
+  float* ws_o;                  // [units][G][128]
+  uint64_t arena_bytes;         // compressed only: groups must end 16 bytes before this
+  int B, Hq, Hkv, G, max_pages, S, n_phys;
+  float scale_log2;
+};
+
+struct KV8 {
+  uint4 k[4];
+  uint4 v[4];
+};
+
+__device__ __forceinline__ float lane_xor(float x, int m) { return __shfl_xor(x, m, 64); }
+
+// max over this lane and lane^16 (v_permlane16_swap: rows 0<->1 and 2<->3 exchange)
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// max over this lane and lane^32 (v_permlane32_swap: lanes 0-31 <-> 32-63)
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// value of lane+16 in rows 0 and 2 (rows 1 and 3 keep their own)
+__device__ __forceinline__ uint32_t from_next_row(uint32_t x) {
+  return __builtin_amdgcn_permlane16_swap(x, x, false, false)[1];
+}
+
+__device__ __forceinline__ uint4 load16(const uint8_t* p) {
+  uint4 r;
+  __builtin_memcpy(&r, __builtin_assume_aligned(p, 4), 16);
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over [base, base + bytes); loads beyond `bytes` return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t group_rsrc(const uint8_t* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
+// Bytes of a group with these four tags: 768 per compressed block, 1024 per raw block.
+__device__ __forceinline__ uint32_t group_bytes(uint32_t tags) {
+  return 4 * kCompBlockBytes + 256u * (uint32_t)__popc(tags & 0x80808080u);
+}
+
+__device__ __forceinline__ float readlane_f(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+__device__ __forceinline__ uint4 restore_if_coded(uint4 c, uint32_t tag) {
+  if (tag == KVZ_RAW_TAG) return c;
+  return restore_chunk(c.x, c.y, c.z, tag * 0x01010101u);
+}
+
+template <int GB>
+struct Softmax {
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  f32x16 o[4];
+
+  __device__ Softmax() {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = f32x16{};
+  }
+
+  // sacc: scores of this lane (tokens 4*(lane/16)+r, head lane%16), already valid-masked and
+  // scaled by sm_scale*log2(e).  vop: the four V chunks of the page in operand order.
+  __device__ __forceinline__ void page(const float (&sv)[4], const uint4 (&vop)[4], int lane) {
+    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mx = max_xor16(mx);
+    mx = max_xor32(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    float pr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pr[r] = __builtin_amdgcn_exp2f(sv[r] - m_use);
+    l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+    m_run = m_new;
+    if (__ballot(alpha != 1.0f)) rescale(alpha, lane);
+
+    // P as the row operand of the 32x32x16 product: lane holds head lane%32 and tokens
+    // 8*(lane/32)+0..7; this lane has tokens 4*(lane/16)+0..3 of head lane%16, lane+16 has
+    // the next four.  hi = bf16(p), lo = bf16(p - hi), both rounded to nearest even.
+    uint32_t hi[2], lo[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const __bf16 h0 = (__bf16)pr[2 * m], h1 = (__bf16)pr[2 * m + 1];
+      const float r0 = pr[2 * m] - (float)h0, r1 = pr[2 * m + 1] - (float)h1;
+      const __bf16 l0 = (__bf16)r0, l1 = (__bf16)r1;
+      hi[m] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+      lo[m] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+    }
+    uint4 a_hi, a_lo;
+    a_hi.x = hi[0];
+    a_hi.y = hi[1];
+    a_hi.z = from_next_row(hi[0]);
+    a_hi.w = from_next_row(hi[1]);
+    a_lo.x = lo[0];
+    a_lo.y = lo[1];
+    a_lo.z = from_next_row(lo[0]);
+    a_lo.w = from_next_row(lo[1]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a_hi), as_bf16x8(vop[j]), o[j], 0, 0, 0);
+      o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a_lo), as_bf16x8(vop[j]), o[j], 0, 0, 0);
+    }
+  }
+
+  // O tile register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4 (a query head of the group).
+  __device__ __forceinline__ void rescale(float alpha, int lane) {
+    constexpr int NR = GB <= 8 ? 4 : 8;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int row_lo = 8 * (r / 4) + (r % 4);
+      const float a_lo = readlane_f(alpha, row_lo);
+      float a = a_lo;
+      if constexpr (GB > 4) {
+        const float a_hi = readlane_f(alpha, row_lo + 4);
+        a = lane < 32 ? a_lo : a_hi;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j][r] *= a;
+    }
+  }
+};
+
+constexpr int kBatch = 4;   // pages whose loads are in flight together per wave
+
+template <int GB, bool COMP>
+__global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
+  const int lane = threadIdx.x & 63;
+  const int unit = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (unit >= p.B * p.Hkv * p.S) return;
+  const int s = unit % p.S;
+  const int bh = unit / p.S;
+  const int kvh = bh % p.Hkv;
+  const int b = bh / p.Hkv;
+
+  int n_comp = p.n_comp[b];
+  n_comp = n_comp < 0 ? 0 : (n_comp > p.max_pages ? p.max_pages : n_comp);
+  int n_tail = 0;
+  if (p.tail) {
+    n_tail = p.seq_lens[b] - 16 * n_comp;
+    n_tail = n_tail < 0 ? 0 : (n_tail > 16 ? 16 : n_tail);
+  }
+  const int total = n_comp + (n_tail > 0 ? 1 : 0);
+  const int p0 = (int)(((int64_t)s * total) / p.S);
+  const int p1 = (int)(((int64_t)(s + 1) * total) / p.S);
+
+  // Q as the column operand of the 16x16x32 product: head lane%16, dims 32j + 8*(lane/16) + i.
+  const int head = lane & 15;
+  uint4 qop[4];
+  if (head < p.G) {
+    const uint16_t* qrow = p.q + ((size_t)b * p.Hq + (size_t)kvh * p.G + head) * KVZ_HEAD_DIM + 8 * (lane >> 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qop[j] = *reinterpret_cast<const uint4*>(qrow + 32 * j);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qop[j] = make_uint4(0, 0, 0, 0);
+  }
+
+  Softmax<GB> sm;
+  // per-lane byte offsets of a chunk inside a compressed / raw block (loop invariant), so that
+  // every page load is "uniform block base (SGPRs) + this offset"
+  const uint32_t lane12 = kCompChunkBytes * lane;
+  const uint32_t lane16 = kRawChunkBytes * lane;
+  const int pc_end = p1 < n_comp ? p1 : n_comp;
+  for (int cbase = p0; cbase < pc_end; cbase += 64) {
+    const int cnt = (pc_end - cbase) < 64 ? (pc_end - cbase) : 64;
+    // lane i describes page cbase + i: its physical page, its two metadata records, and
+    // whether the page can be read at all (a page that cannot is skipped)
+    int phys_l = 0;
+    bool ok_l = false;
+    if (lane < cnt) {
+      phys_l = p.block_table[(size_t)b * p.max_pages + cbase + lane];
+      ok_l = phys_l >= 0 && phys_l < p.n_phys;
+      if (!ok_l) phys_l = 0;
+    }
+    uint4 meta_l = make_uint4(0, 0, 0, 0);
+    if constexpr (COMP) {
+      if (ok_l) {
+        meta_l = p.meta[(size_t)phys_l * p.Hkv + kvh];
+        const uint64_t kend = (uint64_t)meta_l.x * KVZ_GRANULE_BYTES + group_bytes(meta_l.y);
+        const uint64_t vend = (uint64_t)meta_l.z * KVZ_GRANULE_BYTES + group_bytes(meta_l.w);
+        ok_l = meta_l.x != KVZ_OFF_NONE && meta_l.z != KVZ_OFF_NONE && kend <= p.arena_bytes &&
+               vend <= p.arena_bytes;
+        if (!ok_l) meta_l = make_uint4(0, 0, 0, 0);   // loads then stay at the arena start
+      }
+    }
+    const uint64_t ok_mask = __ballot(ok_l);
+
+    // Page i of the chunk: one buffer resource per group (base = the group's first block,
+    // size = the group's bytes, so the 4-byte over-read of a compressed block's last chunk is
+    // clipped by the hardware), block j at a uniform soffset, each lane at its chunk offset.
+    auto load_page = [&](int i, KV8& r) {
+      __amdgpu_buffer_rsrc_t kr, vr;
+      uint32_t kt, vt;
+      if constexpr (COMP) {
+        const uint32_t koff = (uint32_t)__builtin_amdgcn_readlane((int)meta_l.x, i);
+        const uint32_t voff = (uint32_t)__builtin_amdgcn_readlane((int)meta_l.z, i);
+        kt = (uint32_t)__builtin_amdgcn_readlane((int)meta_l.y, i);
+        vt = (uint32_t)__builtin_amdgcn_readlane((int)meta_l.w, i);
+        kr = group_rsrc(p.kv + (size_t)koff * KVZ_GRANULE_BYTES, group_bytes(kt));
+        vr = group_rsrc(p.kv + (size_t)voff * KVZ_GRANULE_BYTES, group_bytes(vt));
+      } else {
+        const int phys = __builtin_amdgcn_readlane(phys_l, i);
+        const uint8_t* kb = p.kv + ((size_t)phys * 2 * p.Hkv + kvh) * 4096;
+        kr = group_rsrc(kb, 4096);
+        vr = group_rsrc(kb + (size_t)p.Hkv * 4096, 4096);
+        kt = vt = 0xFFFFFFFFu;
+      }
+      uint32_t ks = 0, vs = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool kraw = ((kt >> (8 * j)) & 0xFFu) == KVZ_RAW_TAG;
+        r.k[j] = bload16(kr, kraw ? lane16 : lane12, ks);
+        ks += kraw ? kRawBlockBytes : kCompBlockBytes;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool vraw = ((vt >> (8 * j)) & 0xFFu) == KVZ_RAW_TAG;
+        r.v[j] = bload16(vr, vraw ? lane16 : lane12, vs);
+        vs += vraw ? kRawBlockBytes : kCompBlockBytes;
+      }
+    };
+    auto process = [&](const KV8& buf, int i) {
+      if (!((ok_mask >> i) & 1ull)) return;
+      uint32_t kt = 0xFFFFFFFFu, vt = 0xFFFFFFFFu;
+      if constexpr (COMP) {
+        kt = (uint32_t)__builtin_amdgcn_readlane((int)meta_l.y, i);
+        vt = (uint32_t)__builtin_amdgcn_readlane((int)meta_l.w, i);
+      }
+      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint4 kop = restore_if_coded(buf.k[j], (kt >> (8 * j)) & 0xFFu);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kop), as_bf16x8(qop[j]), sacc, 0, 0, 0);
+      }
+      float sv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sv[r] = sacc[r] * p.scale_log2;
+      uint4 vop[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vop[j] = restore_if_coded(buf.v[j], (vt >> (8 * j)) & 0xFFu);
+      sm.page(sv, vop, lane);
+    };
+
+    // Pages are read in batches of kBatch: the loads of a whole batch are issued together, then
+    // its pages are computed in order, each waiting only for its own loads.  The last batch
+    // re-reads the chunk's last page in place of missing ones (an L2 hit, never computed).
+    const int last = cnt - 1;
+    for (int i0 = 0; i0 < cnt; i0 += kBatch) {
+      KV8 buf[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) load_page(i0 + k < last ? i0 + k : last, buf[k]);
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k)
+        if (i0 + k <= last) process(buf[k], i0 + k);
+    }
+  }
+
+  // The BF16 tail page (natural layout [16][128]), masked to its n_tail tokens.
+  if (n_tail > 0 && p0 <= n_comp && n_comp < p1) {
+    const uint16_t* kt = p.tail + (((size_t)b * 2 + 0) * p.Hkv + kvh) * 2048;
+    const uint16_t* vt = p.tail + (((size_t)b * 2 + 1) * p.Hkv + kvh) * 2048;
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 kop = *reinterpret_cast<const uint4*>(kt + (lane & 15) * 128 + 32 * j + 8 * (lane >> 4));
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kop), as_bf16x8(qop[j]), sacc, 0, 0, 0);
+    }
+    float sv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tok = 4 * (lane >> 4) + r;
+      sv[r] = tok < n_tail ? sacc[r] * p.scale_log2 : -INFINITY;
+    }
+    uint4 vop[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t w[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int t0 = 8 * (lane >> 5) + 2 * m;
+        const uint32_t a = t0 < n_tail ? vt[t0 * 128 + 32 * j + (lane & 31)] : 0u;
+        const uint32_t c = t0 + 1 < n_tail ? vt[(t0 + 1) * 128 + 32 * j + (lane & 31)] : 0u;
+        w[m] = a | (c << 16);
+      }
+      vop[j] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    sm.page(sv, vop, lane);
+  }
+
+  float l_tot = sm.l_run + lane_xor(sm.l_run, 16);
+  l_tot += lane_xor(l_tot, 32);          // lane h (h < 16) now holds l of head h
+  constexpr int NR = GB <= 8 ? 4 : 8;
+  const bool empty_seq = p.seq_lens[b] <= 0;
+  float* out_bh = p.out + ((size_t)b * p.Hq + (size_t)kvh * p.G) * KVZ_HEAD_DIM;
+
+  if (p.S == 1) {
+    // the only split: normalize in place
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int row = 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+      const float l_row = __shfl(l_tot, row & 15, 64);
+      if (row < p.G) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          out_bh[(size_t)row * KVZ_HEAD_DIM + 32 * j + (lane & 31)] = empty_seq ? 0.f : sm.o[j][r] / l_row;
+      }
+    }
+    return;
+  }
+
+  // partial results of this unit: (m, l) per head and the unnormalized O rows
+  if (lane < p.G) {
+    p.ws_ml[((size_t)unit * p.G + lane) * 2 + 0] = sm.m_run;
+    p.ws_ml[((size_t)unit * p.G + lane) * 2 + 1] = l_tot;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int row = 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+      if (row < p.G) p.ws_o[((size_t)unit * p.G + row) * KVZ_HEAD_DIM + 32 * j + (lane & 31)] = sm.o[j][r];
+    }
+  }
+
+}
+
+// Merge the S splits of every (sequence, query head): M = max m_s, L = sum l_s 2^(m_s - M),
+// out = sum O_s 2^(m_s - M) / L.  A sequence of length 0 gives zeros.  A separate launch:
+// ordering the splits' partial writes before these reads needs no per-wave fence (a fence at
+// device scope writes back and invalidates the whole L2 of the issuing chiplet).
+__global__ __launch_bounds__(128) void attn_combine_kernel(const float* ws_ml, const float* ws_o,
+                                                           float* out, const int32_t* seq_lens,
+                                                           int Hq, int Hkv, int G, int S) {
+  const int bh = blockIdx.x;
+  const int b = bh / Hq, h = bh % Hq;
+  const int kvh = h / G, g = h % G;
+  const int d = threadIdx.x;
+  const size_t unit0 = ((size_t)b * Hkv + kvh) * S;
+  float M = -INFINITY;
+  for (int sp = 0; sp < S; ++sp) M = fmaxf(M, ws_ml[((unit0 + sp) * G + g) * 2]);
+  float L = 0.f, acc = 0.f;
+  for (int sp = 0; sp < S; ++sp) {
+    const size_t ug = (unit0 + sp) * G + g;
+    const float m = ws_ml[ug * 2];
+    const float w = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - M);
+    L += w * ws_ml[ug * 2 + 1];
+    acc += w * ws_o[ug * KVZ_HEAD_DIM + d];
+  }
+  out[(size_t)bh * KVZ_HEAD_DIM + d] = seq_lens[b] <= 0 ? 0.f : acc / L;
+}
+
+int choose_splits(int B, int Hkv, int max_pages) {
+  const int units = (B * Hkv) > 0 ? B * Hkv : 1;
+  int S = (2048 + units - 1) / units;
+  const int by_pages = (max_pages + 1 + 7) / 8;   // at least ~8 pages per split
+  if (S > by_pages) S = by_pages;
+  return S < 1 ? 1 : S;
+}
+
+uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+// workspace = [m, l: units*G*2 f32][O: units*G*128 f32], 256-B aligned parts
+void workspace_layout(int B, int Hq, int Hkv, int S, uint64_t* ml_bytes, uint64_t* total) {
+  const uint64_t units = (uint64_t)B * Hkv * S;
+  const uint64_t G = Hkv > 0 ? (uint64_t)(Hq / Hkv) : 0;
+  *ml_bytes = align256(units * G * 2 * sizeof(float));
+  *total = *ml_bytes + align256(units * G * KVZ_HEAD_DIM * sizeof(float));
+}
+
+struct CommonArgs {
+  const uint16_t* q;
+  float* out;
+  uint64_t arena_bytes;
+  int32_t n_phys_pages;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* n_comp_pages;
+  const uint16_t* tail;
+  int32_t batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages, splits;
+  float sm_scale;
+  void* workspace;
+  uint64_t workspace_bytes;
+};
+
+template <bool COMP>
+int launch_attention(const CommonArgs& a, const uint8_t* kv, const kvz_group_meta* meta,
+                     hipStream_t s) {
+  if (a.head_dim != KVZ_HEAD_DIM || a.page_size != KVZ_PAGE_TOKENS)
+    return set_error(KVZ_EUNSUPPORTED, "only head_dim 128 and 16-token pages are supported");
+  if (a.batch < 0 || a.num_q_heads <= 0 || a.num_kv_heads <= 0 || a.max_pages < 0)
+    return set_error(KVZ_EINVAL, "bad sizes");
+  if (a.num_q_heads % a.num_kv_heads != 0)
+    return set_error(KVZ_EINVAL, "num_q_heads must be a multiple of num_kv_heads");
+  const int G = a.num_q_heads / a.num_kv_heads;
+  if (G > 16) return set_error(KVZ_EUNSUPPORTED, "query group larger than 16");
+  if (a.batch == 0) return KVZ_OK;
+  if (!a.q || !a.out || !a.seq_lens || !a.n_comp_pages || !a.workspace)
+    return set_error(KVZ_EINVAL, "null pointer argument");
+  if (a.max_pages > 0 && (!kv || !a.block_table || (COMP && !meta)))
+    return set_error(KVZ_EINVAL, "null page pointer argument");
+  if (a.n_phys_pages < 0) return set_error(KVZ_EINVAL, "n_phys_pages < 0");
+  if (COMP && a.max_pages > 0 && a.arena_bytes < 4096)
+    return set_error(KVZ_EINVAL, "arena smaller than 4096 bytes");
+  if ((((uintptr_t)a.q) | ((uintptr_t)a.tail)) & 15u)
+    return set_error(KVZ_EINVAL, "q and tail must be 16-byte aligned");
+  if (COMP && (((uintptr_t)meta) & 15u)) return set_error(KVZ_EINVAL, "meta must be 16-byte aligned");
+  if (((uintptr_t)a.workspace) & 255u) return set_error(KVZ_EINVAL, "workspace must be 256-byte aligned");
+  if (a.splits < 0 || a.splits > 65535) return set_error(KVZ_EINVAL, "splits out of range");
+  const int S = a.splits ? a.splits : choose_splits(a.batch, a.num_kv_heads, a.max_pages);
+  uint64_t ml_bytes, need;
+  workspace_layout(a.batch, a.num_q_heads, a.num_kv_heads, S, &ml_bytes, &need);
+  if (a.workspace_bytes < need) return set_error(KVZ_EINVAL, "workspace too small");
+  const uint64_t units = (uint64_t)a.batch * a.num_kv_heads * S;
+  if (units > 0x7FFFFFFFull) return set_error(KVZ_EINVAL, "too many units");
+
+  AttnParams p;
+  p.q = a.q;
+  p.kv = kv;
+  p.meta = reinterpret_cast<const uint4*>(meta);
+  p.block_table = a.block_table;
+  p.seq_lens = a.seq_lens;
+  p.n_comp = a.n_comp_pages;
+  p.tail = a.tail;
+  p.out = a.out;
+  p.ws_ml = reinterpret_cast<float*>(a.workspace);
+  p.ws_o = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(a.workspace) + ml_bytes);
+  p.arena_bytes = a.arena_bytes;
+  p.n_phys = a.n_phys_pages;
+  p.B = a.batch;
+  p.Hq = a.num_q_heads;
+  p.Hkv = a.num_kv_heads;
+  p.G = G;
+  p.max_pages = a.max_pages;
+  p.S = S;
+  p.scale_log2 = a.sm_scale * 1.4426950408889634f;
+
+  const dim3 grid((unsigned)((units + 3) / 4));
+  if (G <= 4)
+    hipLaunchKernelGGL((attn_split_kernel<4, COMP>), grid, dim3(256), 0, s, p);
+  else if (G <= 8)
+    hipLaunchKernelGGL((attn_split_kernel<8, COMP>), grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((attn_split_kernel<16, COMP>), grid, dim3(256), 0, s, p);
+  int rc = check_hip(hipGetLastError(), "attention launch");
+  if (rc != KVZ_OK || S == 1) return rc;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.batch * a.num_q_heads)), dim3(128), 0, s,
+                     p.ws_ml, p.ws_o, a.out, a.seq_lens, p.Hq, p.Hkv, G, S);
+  return check_hip(hipGetLastError(), "combine launch");
+}
+
+}  // namespace
+}  // namespace kvz
+
+using namespace kvz;
+
+extern "C" int kvz_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t max_pages, int32_t splits, uint64_t* bytes) {
+  if (!bytes) return set_error(KVZ_EINVAL, "bytes is null");
+  if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_pages < 0 || splits < 0)
+    return set_error(KVZ_EINVAL, "bad sizes");
+  const int S = splits ? splits : choose_splits(batch, num_kv_heads, max_pages);
+  uint64_t ml, total;
+  workspace_layout(batch, num_q_heads, num_kv_heads, S, &ml, &total);
+  *bytes = total < 256 ? 256 : total;
+  return KVZ_OK;
+}
+
+extern "C" int kvz_decode_attention(const kvz_attn_args* a, hipStream_t s) {
+  if (!a) return set_error(KVZ_EINVAL, "args is null");
+  CommonArgs c{a->q, a->out, a->arena_bytes, a->n_phys_pages, a->block_table, a->seq_lens,
+               a->n_comp_pages, a->tail, a->batch, a->num_q_heads, a->num_kv_heads, a->head_dim,
+               a->page_size, a->max_pages, a->splits, a->sm_scale, a->workspace,
+               a->workspace_bytes};
+  return launch_attention<true>(c, a->arena, a->meta, s);
+}
+
+extern "C" int kvz_bf16_decode_attention(const kvz_bf16_attn_args* a, hipStream_t s) {
+  if (!a) return set_error(KVZ_EINVAL, "args is null");
+  CommonArgs c{a->q, a->out, 0, a->n_phys_pages, a->block_table, a->seq_lens,
+               a->n_comp_pages, a->tail, a->batch, a->num_q_heads, a->num_kv_heads, a->head_dim,
+               a->page_size, a->max_pages, a->splits, a->sm_scale, a->workspace,
+               a->workspace_bytes};
+  return launch_attention<false>(c, a->pages, nullptr, s);
+}

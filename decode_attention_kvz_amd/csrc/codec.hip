@@ -1,0 +1,229 @@
+// Page-completion encoder, block decoder and the baseline's BF16 page layout.
+//
+// Follows "ZipFusion: Fusing Lossless KV Decompression with Attention for Efficient LLM
+// Decoding", section "How it works": four 512-value blocks per K or V page (step 1), base b =
+// minimum exponent rounded down to even and the [b, b+15] eligibility test (step 2), low byte
+// plus a 4-bit sign/offset code (step 3), exact integer restore (step 4), K/V chunk orders that
+// put each lane's eight MFMA values together, and 8-byte group metadata.  The encoder runs at
+// page completion, once per page ("GAAC: ...", section "Block-Wise Compression Scheduling").
+//
+// kvz_encode_pages = classify (one wave per item) -> allocate (pool.hip, one workgroup, item
+// order) -> pack (one wave per item).  The item's metadata slot carries the tags from classify
+// to allocate and the offset from allocate to pack, so the encoder needs no scratch memory.
+#include "kvz_internal.h"
+
+namespace kvz {
+
+int launch_alloc_for_items(kvz_pool* p, const kvz_encode_item* d_items, int n, hipStream_t s);
+
+namespace {
+
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, d, 64));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, d, 64));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t exp_of(uint32_t w) { return (w >> 7) & 0xFFu; }
+
+// The 8 values of chunk c of block j of a natural page (row stride `stride` elements), packed
+// as 4 dwords (value 2m in the low half of dword m).  K: token c%16, dims 32j+8(c/16)+0..7;
+// V: dim 32j+c%32, tokens 8(c/32)+0..7.
+__device__ __forceinline__ uint4 load_chunk(const uint16_t* src, uint32_t stride, uint32_t kind,
+                                            int j, int c, bool aligned) {
+  uint16_t v[8];
+  if (kind == KVZ_KIND_K) {
+    const uint16_t* p = src + (size_t)(c & 15) * stride + 32 * j + 8 * (c >> 4);
+    if (aligned) {
+      return *reinterpret_cast<const uint4*>(p);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = p[i];
+  } else {
+    const uint16_t* p = src + (size_t)(8 * (c >> 5)) * stride + 32 * j + (c & 31);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = p[(size_t)i * stride];
+  }
+  uint4 r;
+  r.x = (uint32_t)v[0] | ((uint32_t)v[1] << 16);
+  r.y = (uint32_t)v[2] | ((uint32_t)v[3] << 16);
+  r.z = (uint32_t)v[4] | ((uint32_t)v[5] << 16);
+  r.w = (uint32_t)v[6] | ((uint32_t)v[7] << 16);
+  return r;
+}
+
+__device__ __forceinline__ void chunk_exp_range(uint4 w, uint32_t& lo, uint32_t& hi) {
+  const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const uint32_t e0 = exp_of(d[m] & 0xFFFFu), e1 = exp_of(d[m] >> 16);
+    lo = min(lo, min(e0, e1));
+    hi = max(hi, max(e0, e1));
+  }
+}
+
+// Step 2: tags of the four blocks of each item (b/2, or 0xFF when out of window).
+__global__ __launch_bounds__(256) void classify_kernel(const kvz_encode_item* items, int n,
+                                                       uint32_t flags) {
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= n) return;
+  const kvz_encode_item it = items[item];
+  const bool aligned = ((((uintptr_t)it.src) & 15u) == 0) && ((it.src_stride & 7u) == 0);
+  uint32_t tags = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // membership only matters here, so read the block in K chunk order for both kinds
+    const uint4 w = load_chunk(it.src, it.src_stride, KVZ_KIND_K, j, lane, aligned);
+    uint32_t lo = 255u, hi = 0u;
+    chunk_exp_range(w, lo, hi);
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    const uint32_t b = lo & 0xFEu;
+    uint32_t tag = (hi <= b + 15u) ? (b >> 1) : KVZ_RAW_TAG;
+    if (flags & KVZ_ENC_FORCE_RAW) tag = KVZ_RAW_TAG;
+    tags |= tag << (8 * j);
+  }
+  if (lane == 0) {
+    *reinterpret_cast<uint32_t*>(it.dst->tag) = tags;
+    it.dst->off = KVZ_OFF_NONE;
+  }
+}
+
+// Step 3: write the four blocks of each placed item at off*256 + prefix sizes.
+__global__ __launch_bounds__(256) void pack_kernel(const kvz_encode_item* items, int n,
+                                                   uint8_t* arena) {
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= n) return;
+  const kvz_encode_item it = items[item];
+  const uint32_t off = it.dst->off;
+  if (off == KVZ_OFF_NONE) return;
+  const uint32_t tags = *reinterpret_cast<const uint32_t*>(it.dst->tag);
+  const bool aligned = ((((uintptr_t)it.src) & 15u) == 0) && ((it.src_stride & 7u) == 0);
+  uint8_t* blk = arena + (size_t)off * KVZ_GRANULE_BYTES;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t tag = (tags >> (8 * j)) & 0xFFu;
+    const uint4 w = load_chunk(it.src, it.src_stride, it.kind, j, lane, aligned);
+    if (tag == KVZ_RAW_TAG) {
+      *reinterpret_cast<uint4*>(blk + kRawChunkBytes * lane) = w;
+    } else {
+      const uint3 c = compress_chunk(w, tag * 0x01010101u);
+      uint32_t* d = reinterpret_cast<uint32_t*>(blk + kCompChunkBytes * lane);
+      d[0] = c.x;
+      d[1] = c.y;
+      d[2] = c.z;
+    }
+    blk += block_bytes(tag);
+  }
+}
+
+// Step 4: natural-order BF16 [16 tokens][32 dims] of each referenced block.
+__global__ __launch_bounds__(256) void decode_block_kernel(const uint8_t* arena,
+                                                           uint64_t arena_bytes,
+                                                           const kvz_block_ref* refs, int n,
+                                                           uint16_t* out) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= n) return;
+  const kvz_block_ref ref = refs[r];
+  const uint32_t off = ref.meta->off;
+  const uint32_t tags = *reinterpret_cast<const uint32_t*>(ref.meta->tag);
+  uint16_t* o = out + (size_t)r * 512;
+  uint64_t start = (uint64_t)off * KVZ_GRANULE_BYTES;
+  if (ref.block <= 3)
+    for (uint32_t k = 0; k < ref.block; ++k) start += block_bytes((tags >> (8 * k)) & 0xFFu);
+  const uint32_t tag = ref.block <= 3 ? (tags >> (8 * ref.block)) & 0xFFu : 0u;
+  if (off == KVZ_OFF_NONE || ref.block > 3 || start + block_bytes(tag) > arena_bytes) {
+    for (int t = lane; t < 512; t += 64) o[t] = 0;
+    return;
+  }
+  const uint8_t* blk = arena + start;
+  uint4 w;
+  if (tag == KVZ_RAW_TAG) {
+    w = *reinterpret_cast<const uint4*>(blk + kRawChunkBytes * lane);
+  } else {
+    const uint32_t* s = reinterpret_cast<const uint32_t*>(blk + kCompChunkBytes * lane);
+    w = restore_chunk(s[0], s[1], s[2], tag * 0x01010101u);
+  }
+  const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+  if (ref.kind == KVZ_KIND_K) {
+    // token lane%16, dims 8*(lane/16)+i: one 16-byte row piece
+    *reinterpret_cast<uint4*>(o + (lane & 15) * 32 + 8 * (lane >> 4)) = w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint16_t v = (uint16_t)((d[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+      o[(8 * (lane >> 5) + i) * 32 + (lane & 31)] = v;
+    }
+  }
+}
+
+// Baseline page layout: every block as 64 raw chunks in the same chunk order.
+__global__ __launch_bounds__(256) void bf16_pack_kernel(const uint16_t* src, uint8_t* dst,
+                                                        int64_t n_groups, int hkv) {
+  const int lane = threadIdx.x & 63;
+  const int64_t gb = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // (group, block)
+  if (gb >= n_groups * 4) return;
+  const int64_t g = gb >> 2;
+  const int j = (int)(gb & 3);
+  const uint32_t kind = (uint32_t)((g / hkv) & 1);   // groups are [page][K|V][kv head]
+  const uint16_t* s = src + g * 2048;
+  const uint4 w = load_chunk(s, 128, kind, j, lane, true);
+  *reinterpret_cast<uint4*>(dst + g * 4096 + j * 1024 + kRawChunkBytes * lane) = w;
+}
+
+}  // namespace
+}  // namespace kvz
+
+using namespace kvz;
+
+extern "C" int kvz_encode_pages(kvz_pool* p, const kvz_encode_item* d_items, int32_t n,
+                                uint32_t flags, hipStream_t s) {
+  if (!p) return set_error(KVZ_EINVAL, "pool handle is null");
+  if (n < 0) return set_error(KVZ_EINVAL, "n < 0");
+  if (n == 0) return KVZ_OK;
+  if (!d_items) return set_error(KVZ_EINVAL, "items pointer is null");
+  if (flags & ~KVZ_ENC_FORCE_RAW) return set_error(KVZ_EINVAL, "unknown encode flag");
+  const int grid = (n + 3) / 4;
+  hipLaunchKernelGGL(classify_kernel, dim3(grid), dim3(256), 0, s, d_items, (int)n, flags);
+  int rc = check_hip(hipGetLastError(), "classify launch");
+  if (rc != KVZ_OK) return rc;
+  rc = launch_alloc_for_items(p, d_items, n, s);
+  if (rc != KVZ_OK) return rc;
+  hipLaunchKernelGGL(pack_kernel, dim3(grid), dim3(256), 0, s, d_items, (int)n, (uint8_t*)p->arena);
+  return check_hip(hipGetLastError(), "pack launch");
+}
+
+extern "C" int kvz_decode_block(const void* d_arena, uint64_t arena_bytes,
+                                const kvz_block_ref* d_refs, int32_t n, uint16_t* d_out,
+                                hipStream_t s) {
+  if (n < 0) return set_error(KVZ_EINVAL, "n < 0");
+  if (n == 0) return KVZ_OK;
+  if (!d_arena || !d_refs || !d_out) return set_error(KVZ_EINVAL, "null pointer argument");
+  if (((uintptr_t)d_out) & 15u) return set_error(KVZ_EINVAL, "out must be 16-byte aligned");
+  hipLaunchKernelGGL(decode_block_kernel, dim3((n + 3) / 4), dim3(256), 0, s,
+                     (const uint8_t*)d_arena, arena_bytes, d_refs, (int)n, d_out);
+  return check_hip(hipGetLastError(), "decode_block launch");
+}
+
+extern "C" int kvz_bf16_pack_pages(const uint16_t* d_src, uint8_t* d_dst, int64_t n_pages,
+                                   int32_t num_kv_heads, hipStream_t s) {
+  if (n_pages < 0 || num_kv_heads <= 0) return set_error(KVZ_EINVAL, "bad sizes");
+  if (n_pages == 0) return KVZ_OK;
+  if (!d_src || !d_dst) return set_error(KVZ_EINVAL, "null pointer argument");
+  if ((((uintptr_t)d_src) | ((uintptr_t)d_dst)) & 15u)
+    return set_error(KVZ_EINVAL, "src and dst must be 16-byte aligned");
+  const int64_t n_groups = n_pages * 2 * num_kv_heads;
+  const int64_t grid = n_groups;   // 4 (group, block) pairs per workgroup
+  if (grid > 0x7FFFFFFF) return set_error(KVZ_EINVAL, "too many pages for one call");
+  hipLaunchKernelGGL(bf16_pack_kernel, dim3((unsigned)grid), dim3(256), 0, s, d_src, d_dst,
+                     n_groups, (int)num_kv_heads);
+  return check_hip(hipGetLastError(), "bf16 pack launch");
+}

@@ -1,0 +1,257 @@
+"""Thin Python binding of libkvz.so (ctypes).
+
+Argument marshalling only: every step of the path runs in the HIP library.  Functions carry the
+C names; tensors are passed as device pointers (torch supplies device memory and the current
+HIP stream).  If libkvz.so has not been built this module raises at import time - there is no
+fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvz.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with decode_attention_kvz_amd/build.py "
+                      "(or __graft_entry__.build()) before using the binding")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+KVZ_OK = 0
+KVZ_EINVAL = -1
+KVZ_EUNSUPPORTED = -2
+KVZ_EHIP = -4
+KVZ_ESTATE = -5
+KVZ_RAW_TAG = 0xFF
+KVZ_OFF_NONE = 0xFFFFFFFF
+KVZ_KIND_K = 0
+KVZ_KIND_V = 1
+KVZ_ENC_FORCE_RAW = 1
+GRANULE = 256
+
+EXPORTED = [
+    "kvz_version", "kvz_last_error", "kvz_device_check", "kvz_pool_state_bytes", "kvz_pool_init",
+    "kvz_pool_destroy", "kvz_slot_alloc", "kvz_slot_free", "kvz_encode_pages", "kvz_decode_block",
+    "kvz_attn_workspace_bytes", "kvz_decode_attention", "kvz_bf16_pack_pages",
+    "kvz_bf16_decode_attention", "kvz_pool_stats",
+]
+
+
+class KvzError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"kvz error {code}: {msg}")
+        self.code = code
+
+
+class PoolStats(ctypes.Structure):
+    _fields_ = [("capacity_granules", ctypes.c_uint64), ("frontier_granules", ctypes.c_uint64),
+                ("free_runs", ctypes.c_uint64 * 5), ("live_runs", ctypes.c_uint64),
+                ("live_granules", ctypes.c_uint64), ("live_raw_blocks", ctypes.c_uint64),
+                ("enospc", ctypes.c_uint64), ("bad_frees", ctypes.c_uint64)]
+
+
+class AttnArgs(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("out", ctypes.c_void_p), ("arena", ctypes.c_void_p),
+                ("arena_bytes", ctypes.c_uint64), ("meta", ctypes.c_void_p),
+                ("n_phys_pages", ctypes.c_int32), ("block_table", ctypes.c_void_p),
+                ("seq_lens", ctypes.c_void_p), ("n_comp_pages", ctypes.c_void_p),
+                ("tail", ctypes.c_void_p), ("batch", ctypes.c_int32),
+                ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("max_pages", ctypes.c_int32), ("splits", ctypes.c_int32),
+                ("sm_scale", ctypes.c_float), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_uint64)]
+
+
+class Bf16AttnArgs(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("out", ctypes.c_void_p), ("pages", ctypes.c_void_p),
+                ("n_phys_pages", ctypes.c_int32), ("block_table", ctypes.c_void_p),
+                ("seq_lens", ctypes.c_void_p),
+                ("n_comp_pages", ctypes.c_void_p), ("tail", ctypes.c_void_p),
+                ("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("max_pages", ctypes.c_int32),
+                ("splits", ctypes.c_int32), ("sm_scale", ctypes.c_float),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64)]
+
+
+# kvz_encode_item / kvz_block_ref as numpy record layouts (device arrays are built from these)
+ENCODE_ITEM_DTYPE = np.dtype([("src", "<u8"), ("dst", "<u8"), ("src_stride", "<u4"),
+                              ("kind", "<u4")])
+BLOCK_REF_DTYPE = np.dtype([("meta", "<u8"), ("block", "<u4"), ("kind", "<u4")])
+
+_vp = ctypes.c_void_p
+_sig = {
+    "kvz_version": ([], ctypes.c_int),
+    "kvz_last_error": ([], ctypes.c_char_p),
+    "kvz_device_check": ([ctypes.c_int], ctypes.c_int),
+    "kvz_pool_state_bytes": ([ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64)], ctypes.c_int),
+    "kvz_pool_init": ([ctypes.POINTER(_vp), _vp, ctypes.c_uint64, _vp, ctypes.c_uint64, _vp],
+                      ctypes.c_int),
+    "kvz_pool_destroy": ([_vp], ctypes.c_int),
+    "kvz_slot_alloc": ([_vp, _vp, _vp, ctypes.c_int32, _vp], ctypes.c_int),
+    "kvz_slot_free": ([_vp, _vp, ctypes.c_int32, _vp], ctypes.c_int),
+    "kvz_encode_pages": ([_vp, _vp, ctypes.c_int32, ctypes.c_uint32, _vp], ctypes.c_int),
+    "kvz_decode_block": ([_vp, ctypes.c_uint64, _vp, ctypes.c_int32, _vp, _vp], ctypes.c_int),
+    "kvz_attn_workspace_bytes": ([ctypes.c_int32] * 5 + [ctypes.POINTER(ctypes.c_uint64)],
+                                 ctypes.c_int),
+    "kvz_decode_attention": ([ctypes.POINTER(AttnArgs), _vp], ctypes.c_int),
+    "kvz_bf16_pack_pages": ([_vp, _vp, ctypes.c_int64, ctypes.c_int32, _vp], ctypes.c_int),
+    "kvz_bf16_decode_attention": ([ctypes.POINTER(Bf16AttnArgs), _vp], ctypes.c_int),
+    "kvz_pool_stats": ([_vp, ctypes.POINTER(PoolStats), _vp], ctypes.c_int),
+}
+for _name, (_args, _ret) in _sig.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = _ret
+
+
+def _check(rc):
+    if rc != KVZ_OK:
+        raise KvzError(rc, _lib.kvz_last_error().decode(errors="replace"))
+
+
+def _ptr(t):
+    """Device pointer of a tensor (None -> NULL)."""
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+# ---------------------------------------------------------------------------------------------
+def kvz_version() -> int:
+    return _lib.kvz_version()
+
+
+def kvz_last_error() -> str:
+    return _lib.kvz_last_error().decode(errors="replace")
+
+
+def kvz_device_check(device: int = 0) -> None:
+    _check(_lib.kvz_device_check(device))
+
+
+def kvz_pool_state_bytes(arena_bytes: int) -> int:
+    out = ctypes.c_uint64()
+    _check(_lib.kvz_pool_state_bytes(arena_bytes, ctypes.byref(out)))
+    return out.value
+
+
+def kvz_pool_init(arena, state, stream=None):
+    """arena, state: uint8 device tensors.  Returns the opaque pool handle."""
+    h = ctypes.c_void_p()
+    _check(_lib.kvz_pool_init(ctypes.byref(h), _ptr(arena), arena.numel() * arena.element_size(),
+                              _ptr(state), state.numel() * state.element_size(), _stream(stream)))
+    return h
+
+
+def kvz_pool_destroy(pool) -> None:
+    _check(_lib.kvz_pool_destroy(pool))
+
+
+def kvz_slot_alloc(pool, tags, off, stream=None) -> None:
+    """tags: uint8 [n, 4] device; off: int32/uint32 [n] device (receives offsets)."""
+    n = tags.shape[0]
+    _check(_lib.kvz_slot_alloc(pool, _ptr(tags), _ptr(off), n, _stream(stream)))
+
+
+def kvz_slot_free(pool, meta_ptrs, stream=None) -> None:
+    """meta_ptrs: int64 [n] device tensor of device pointers to kvz_group_meta."""
+    _check(_lib.kvz_slot_free(pool, _ptr(meta_ptrs), meta_ptrs.shape[0], _stream(stream)))
+
+
+def kvz_encode_pages(pool, items, n: int, flags: int = 0, stream=None) -> None:
+    """items: device tensor holding n kvz_encode_item records (ENCODE_ITEM_DTYPE)."""
+    _check(_lib.kvz_encode_pages(pool, _ptr(items), n, flags, _stream(stream)))
+
+
+def kvz_decode_block(arena, refs, n: int, out, stream=None) -> None:
+    """refs: device tensor of n kvz_block_ref records; out: int16/uint16 [n, 16, 32] device."""
+    _check(_lib.kvz_decode_block(_ptr(arena), arena.numel() * arena.element_size(), _ptr(refs),
+                                 n, _ptr(out), _stream(stream)))
+
+
+def kvz_attn_workspace_bytes(batch, num_q_heads, num_kv_heads, max_pages, splits=0) -> int:
+    out = ctypes.c_uint64()
+    _check(_lib.kvz_attn_workspace_bytes(batch, num_q_heads, num_kv_heads, max_pages, splits,
+                                         ctypes.byref(out)))
+    return out.value
+
+
+def kvz_decode_attention(q, out, arena, meta, block_table, seq_lens, n_comp_pages, tail,
+                         sm_scale: float, workspace, splits: int = 0, stream=None) -> None:
+    """q [B,Hq,128] bf16; out [B,Hq,128] fp32; meta [n_phys,Hkv,2,8] uint8 (or any 8-byte
+    records); block_table [B,max_pages] int32; seq_lens, n_comp_pages [B] int32;
+    tail [B,2,Hkv,16,128] bf16 or None; workspace uint8 device tensor."""
+    bsz, hq, hd = q.shape
+    a = AttnArgs(q=q.data_ptr(), out=out.data_ptr(), arena=arena.data_ptr(),
+                 arena_bytes=arena.numel() * arena.element_size(), meta=meta.data_ptr(),
+                 n_phys_pages=meta.shape[0], block_table=block_table.data_ptr(), seq_lens=seq_lens.data_ptr(),
+                 n_comp_pages=n_comp_pages.data_ptr(),
+                 tail=None if tail is None else tail.data_ptr(), batch=bsz, num_q_heads=hq,
+                 num_kv_heads=meta.shape[1], head_dim=hd, page_size=16,
+                 max_pages=block_table.shape[1], splits=splits, sm_scale=sm_scale,
+                 workspace=workspace.data_ptr(),
+                 workspace_bytes=workspace.numel() * workspace.element_size())
+    _check(_lib.kvz_decode_attention(ctypes.byref(a), _stream(stream)))
+
+
+def kvz_bf16_pack_pages(src, dst, stream=None) -> None:
+    """src [n_pages,2,Hkv,16,128] bf16 natural pages -> dst [n_pages,2,Hkv,4,1024] uint8."""
+    _check(_lib.kvz_bf16_pack_pages(_ptr(src), _ptr(dst), src.shape[0], src.shape[2],
+                                    _stream(stream)))
+
+
+def kvz_bf16_decode_attention(q, out, pages, block_table, seq_lens, n_comp_pages, tail,
+                              sm_scale: float, workspace, num_kv_heads: int, splits: int = 0,
+                              stream=None) -> None:
+    bsz, hq, hd = q.shape
+    a = Bf16AttnArgs(q=q.data_ptr(), out=out.data_ptr(), pages=pages.data_ptr(),
+                     n_phys_pages=pages.shape[0], block_table=block_table.data_ptr(), seq_lens=seq_lens.data_ptr(),
+                     n_comp_pages=n_comp_pages.data_ptr(),
+                     tail=None if tail is None else tail.data_ptr(), batch=bsz, num_q_heads=hq,
+                     num_kv_heads=num_kv_heads, head_dim=hd, page_size=16,
+                     max_pages=block_table.shape[1], splits=splits, sm_scale=sm_scale,
+                     workspace=workspace.data_ptr(),
+                     workspace_bytes=workspace.numel() * workspace.element_size())
+    _check(_lib.kvz_bf16_decode_attention(ctypes.byref(a), _stream(stream)))
+
+
+def kvz_pool_stats(pool, stream=None) -> dict:
+    st = PoolStats()
+    _check(_lib.kvz_pool_stats(pool, ctypes.byref(st), _stream(stream)))
+    return {"capacity_granules": st.capacity_granules, "frontier_granules": st.frontier_granules,
+            "free_runs": list(st.free_runs), "live_runs": st.live_runs,
+            "live_granules": st.live_granules, "live_raw_blocks": st.live_raw_blocks,
+            "enospc": st.enospc, "bad_frees": st.bad_frees}
+
+
+# ---------------------------------------------------------------------------------------------
+# record builders (host side marshalling of the C structs)
+# ---------------------------------------------------------------------------------------------
+def encode_items(src_ptrs, dst_ptrs, src_stride, kinds) -> np.ndarray:
+    """kvz_encode_item records as a uint8 array (copy it to the device before the call)."""
+    n = len(src_ptrs)
+    rec = np.zeros(n, dtype=ENCODE_ITEM_DTYPE)
+    rec["src"] = np.asarray(src_ptrs, dtype=np.uint64)
+    rec["dst"] = np.asarray(dst_ptrs, dtype=np.uint64)
+    rec["src_stride"] = src_stride
+    rec["kind"] = np.asarray(kinds, dtype=np.uint32)
+    return rec.view(np.uint8)
+
+
+def block_refs(meta_ptrs, blocks, kinds) -> np.ndarray:
+    n = len(meta_ptrs)
+    rec = np.zeros(n, dtype=BLOCK_REF_DTYPE)
+    rec["meta"] = np.asarray(meta_ptrs, dtype=np.uint64)
+    rec["block"] = np.asarray(blocks, dtype=np.uint32)
+    rec["kind"] = np.asarray(kinds, dtype=np.uint32)
+    return rec.view(np.uint8)

@@ -1,0 +1,106 @@
+"""Host-side glue for a paged, exponent-coded KV cache built on the C-ABI.
+
+Owns device buffers (torch tensors): the slot arena and pool state shared by all layers, one
+8-byte-metadata table per layer, and the baseline's BF16 page store.  Every operation on the data
+is a library call; this module only lays out records and pointers.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import kvz
+
+PAGE = 16
+HEAD_DIM = 128
+GROUP_ELEMS = PAGE * HEAD_DIM
+
+
+class SlotArena:
+    """A pool arena plus its device state (one per device, shared by every layer)."""
+
+    def __init__(self, arena_bytes: int, device="cuda"):
+        arena_bytes = (int(arena_bytes) + 255) // 256 * 256
+        self.device = torch.device(device)
+        self.arena = torch.zeros(arena_bytes, dtype=torch.uint8, device=self.device)
+        self.state = torch.zeros(kvz.kvz_pool_state_bytes(arena_bytes), dtype=torch.uint8,
+                                 device=self.device)
+        self.pool = kvz.kvz_pool_init(self.arena, self.state)
+
+    def stats(self) -> dict:
+        return kvz.kvz_pool_stats(self.pool)
+
+    def close(self):
+        if self.pool is not None:
+            kvz.kvz_pool_destroy(self.pool)
+            self.pool = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def new_meta_table(n_phys: int, n_kv: int, device="cuda") -> torch.Tensor:
+    """[n_phys, Hkv, 2 (K,V), 8] uint8 metadata, every group marked 'not stored'."""
+    t = torch.zeros((n_phys, n_kv, 2, 8), dtype=torch.uint8, device=device)
+    t[..., :4] = 0xFF
+    return t
+
+
+def page_items(pages: torch.Tensor, page_ids, meta: torch.Tensor, phys_ids) -> np.ndarray:
+    """kvz_encode_item records for pages[s, p] (natural [n_seq, n_pages, 2, Hkv, 16, 128] bf16)
+    stored as physical page phys_ids[k] for (s, p) = page_ids[k].
+
+    Item order: page_ids order, then KV head, then K before V."""
+    n_kv = pages.shape[3]
+    n_pages = pages.shape[1]
+    assert pages.is_contiguous() and meta.is_contiguous()
+    sp = np.asarray(page_ids, dtype=np.int64).reshape(-1, 2)
+    phys = np.asarray(phys_ids, dtype=np.int64).reshape(-1)
+    h = np.arange(n_kv, dtype=np.int64)
+    kind = np.arange(2, dtype=np.int64)
+    src_group = (((sp[:, 0:1, None] * n_pages + sp[:, 1:2, None]) * 2 + kind[None, None, :])
+                 * n_kv + h[None, :, None])                               # [n, Hkv, 2]
+    dst_group = (phys[:, None, None] * n_kv + h[None, :, None]) * 2 + kind[None, None, :]
+    src = pages.data_ptr() + src_group.reshape(-1) * (GROUP_ELEMS * 2)
+    dst = meta.data_ptr() + dst_group.reshape(-1) * 8
+    kinds = np.broadcast_to(kind[None, None, :], src_group.shape).reshape(-1)
+    return kvz.encode_items(src.astype(np.uint64), dst.astype(np.uint64), HEAD_DIM, kinds)
+
+
+def encode(arena: SlotArena, items: np.ndarray, flags: int = 0, stream=None) -> torch.Tensor:
+    """Copy the item records to the device and run kvz_encode_pages; returns the device copy
+    (keep it alive until the stream has consumed it)."""
+    d = torch.from_numpy(np.ascontiguousarray(items)).to(arena.device)
+    n = items.size // kvz.ENCODE_ITEM_DTYPE.itemsize
+    kvz.kvz_encode_pages(arena.pool, d, n, flags, stream)
+    return d
+
+
+def meta_pointers(meta: torch.Tensor, groups) -> torch.Tensor:
+    """Device int64 tensor of pointers to the metadata records with flat indices `groups`."""
+    g = np.asarray(groups, dtype=np.int64)
+    return torch.from_numpy(meta.data_ptr() + g * 8).to(meta.device)
+
+
+def meta_host(meta: torch.Tensor) -> np.ndarray:
+    """Metadata table as a host structured view: off uint32, tags uint8[4]."""
+    raw = meta.detach().cpu().contiguous().numpy().reshape(-1, 8)
+    return raw
+
+
+def pack_bf16_pages(pages_by_phys: torch.Tensor) -> torch.Tensor:
+    """Baseline page store [n_phys, 2, Hkv, 4, 1024] uint8 from natural pages
+    [n_phys, 2, Hkv, 16, 128] bf16 (kvz_bf16_pack_pages)."""
+    n, _, hkv = pages_by_phys.shape[:3]
+    dst = torch.empty((n, 2, hkv, 4, 1024), dtype=torch.uint8, device=pages_by_phys.device)
+    kvz.kvz_bf16_pack_pages(pages_by_phys.contiguous(), dst)
+    return dst
+
+
+def workspace(batch: int, num_q_heads: int, num_kv_heads: int, max_pages: int, splits: int = 0,
+              device="cuda") -> torch.Tensor:
+    nbytes = kvz.kvz_attn_workspace_bytes(batch, num_q_heads, num_kv_heads, max_pages, splits)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)

@@ -1,0 +1,235 @@
+/*
+ * kvz.h - lossless 12-bit exponent-coded BF16 KV pages and fused paged decode attention
+ *         for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow two pages:
+ *   [ZF]   "ZipFusion: Fusing Lossless KV Decompression with Attention for Efficient LLM
+ *          Decoding" - section "How it works" (block format, steps 1-4; K/V layouts and the
+ *          register restore; 8-byte group metadata; the memory manager).
+ *   [GAAC] "GAAC: Lossless KV Compression for Bandwidth-Efficient LLM Inference on Personal
+ *          Devices" - sections "Attention with On-the-Fly Decompression" (compressed blocks and
+ *          the BF16 tail share one softmax; no decompressed copy in device memory) and
+ *          "Block-Wise Compression Scheduling" (fill-then-finalize; fixed-capacity slots in two
+ *          storage classes; a block that does not fit keeps its BF16 form).
+ *
+ * Format (readings where the pages are silent are marked *):
+ *   - A page holds 16 tokens.  Per (layer, KV head) its K and its V are each one GROUP of four
+ *     BLOCKS; block j = tokens 0..15 x dims [32j, 32j+32)*, 512 BF16 values ([ZF] step 1).
+ *   - Block base b = minimum exponent rounded down to even; the block is compressed only if
+ *     every exponent lies in [b, b+15], otherwise it stays raw ([ZF] step 2).
+ *   - A block is 64 chunks of 8 values, in MFMA operand order*:
+ *       K chunk c: token c%16, dims 32j + 8*(c/16) + 0..7;
+ *       V chunk c: dim 32j + c%32, tokens 8*(c/32) + 0..7.
+ *     Compressed chunk (12 B)*: 8 low bytes (7 fraction bits + exponent LSB) of values 0..7,
+ *     then the code word C = X | rotl32(Y, 4) (LE), where byte k of X is s<<7 | d of value k
+ *     and byte k of Y the same for value k+4, d = (e - b) >> 1 ([ZF] step 3).  Restore:
+ *     high bytes of values 0..3 = (C & 0x87878787) + (b/2)*0x01010101, of values 4..7 =
+ *     (rotr32(C,4) & 0x87878787) + (b/2)*0x01010101 (no carry; [ZF] step 4 and the restore
+ *     paragraph).  Raw chunk (16 B)*: the 8 BF16 words, little-endian.
+ *     Compressed block = 768 B, raw block = 1024 B.
+ *   - Group metadata, 8 B ([ZF] metadata paragraph): bytes 0-3 the first block's offset in
+ *     256-byte granules from the arena base* (LE), bytes 4-7 the tag of blocks 0..3: b/2 for a
+ *     compressed block, 0xFF* for a raw one.  Blocks of a group are contiguous; block j starts
+ *     at off*256 + (sizes of blocks 0..j-1).
+ *   - Slots: 768-B and 1024-B slots ([GAAC] two storage classes); a group occupies one
+ *     contiguous run of 12 + n_raw granules.  See kvz_slot_alloc for the allocation rule.
+ *
+ * Conventions for every call:
+ *   - Pointers named d_* or documented as "device" point to device memory owned by the caller
+ *     (e.g. torch tensors).  The library never allocates or frees device memory; it owns only
+ *     the small host-side pool handle.
+ *   - Calls that take a hipStream_t enqueue work on that stream and return without waiting,
+ *     except kvz_pool_stats, which synchronizes the stream.
+ *   - Return value: KVZ_OK or a negative KVZ_E* code; kvz_last_error() gives text (per thread).
+ *     Nothing throws or aborts across this interface.  Conditions that only the device can see
+ *     (no room in the pool) are counted in the pool state and reported by kvz_pool_stats.
+ *   - A pool handle is not thread-safe; calls on one pool must be ordered on one stream.
+ */
+#ifndef KVZ_H
+#define KVZ_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVZ_VERSION 1
+
+enum {
+  KVZ_OK = 0,
+  KVZ_EINVAL = -1,       /* bad argument (null pointer, size out of range, misalignment)       */
+  KVZ_EUNSUPPORTED = -2, /* device is not gfx950, or head_dim != 128, page != 16, group > 16   */
+  KVZ_EHIP = -4,         /* a HIP runtime call or kernel launch failed                          */
+  KVZ_ESTATE = -5        /* the pool state does not carry the expected magic/version            */
+};
+
+#define KVZ_PAGE_TOKENS 16
+#define KVZ_HEAD_DIM 128
+#define KVZ_GRANULE_BYTES 256
+#define KVZ_RAW_TAG 0xFFu
+#define KVZ_OFF_NONE 0xFFFFFFFFu
+#define KVZ_KIND_K 0u
+#define KVZ_KIND_V 1u
+#define KVZ_ENC_FORCE_RAW 1u    /* kvz_encode_pages flag: store every block raw */
+
+/* 8-byte metadata of one 4-block K or V group ([ZF] metadata paragraph). */
+typedef struct {
+  uint32_t off;     /* first block, in 256-B granules from the arena base; KVZ_OFF_NONE = not stored */
+  uint8_t tag[4];   /* per block: b/2 in 0..127, or KVZ_RAW_TAG                                     */
+} kvz_group_meta;
+
+/* One completed page of one (layer, KV head, K|V) to encode. */
+typedef struct {
+  const uint16_t* src;   /* device: 16 rows of 128 BF16 values, natural order [token][dim]      */
+  kvz_group_meta* dst;   /* device: where the group's metadata is written                        */
+  uint32_t src_stride;   /* elements between consecutive tokens of src, >= 128, multiple of 8   */
+  uint32_t kind;         /* KVZ_KIND_K or KVZ_KIND_V (selects the chunk order)                  */
+} kvz_encode_item;
+
+/* One block to decode: block `block` (0..3) of the group described by *meta. */
+typedef struct {
+  const kvz_group_meta* meta;  /* device */
+  uint32_t block;
+  uint32_t kind;
+} kvz_block_ref;
+
+typedef struct kvz_pool kvz_pool;   /* opaque host handle */
+
+typedef struct {
+  uint64_t capacity_granules;  /* usable granules: arena_bytes/256 - 1 (one guard granule)    */
+  uint64_t frontier_granules;  /* granules handed out from the frontier so far                 */
+  uint64_t free_runs[5];       /* free runs kept per n_raw bin (run = 12 + n_raw granules)     */
+  uint64_t live_runs;          /* groups currently stored                                      */
+  uint64_t live_granules;
+  uint64_t live_raw_blocks;
+  uint64_t enospc;             /* groups that found no room (cumulative)                        */
+  uint64_t bad_frees;          /* frees dropped because a bin was full (double free)            */
+} kvz_pool_stats_t;
+
+/* Decode-attention arguments, fused compressed path.
+ * For every sequence b: tokens 0 .. 16*n_comp_pages[b]-1 are read from compressed groups
+ * through block_table and meta; tokens 16*n_comp_pages[b] .. seq_lens[b]-1 (0..16 of them)
+ * from the BF16 tail.  All tokens share one softmax ([GAAC] "Attention with On-the-Fly
+ * Decompression").  Query head h uses KV head h / (num_q_heads/num_kv_heads).
+ * out[b][h][:] = sum_t softmax_t(sm_scale * q[b][h].K[t]) V[t]; a sequence of length 0 gives
+ * zeros.  Values of seq_lens/n_comp_pages outside their documented ranges are clamped, and a
+ * page whose block-table entry is outside [0, n_phys_pages) or whose groups are not stored or
+ * do not lie inside the arena is skipped (the output for such a sequence is then unspecified,
+ * but no memory outside the buffers is read).  The kernel may read up to 16 bytes past the end
+ * of a group; a pool arena never holds a group in its last 256-byte granule. */
+typedef struct {
+  const uint16_t* q;            /* device [B][Hq][128] BF16                                      */
+  float* out;                   /* device [B][Hq][128] fp32                                      */
+  const uint8_t* arena;         /* device: pool arena base                                       */
+  uint64_t arena_bytes;
+  const kvz_group_meta* meta;   /* device [n_phys_pages][Hkv][2] (K then V) for this layer       */
+  int32_t n_phys_pages;
+  const int32_t* block_table;   /* device [B][max_pages]: physical page of logical page p        */
+  const int32_t* seq_lens;      /* device [B]                                                    */
+  const int32_t* n_comp_pages;  /* device [B]: compressed pages, 0 <= n <= max_pages             */
+  const uint16_t* tail;         /* device [B][2][Hkv][16][128] BF16, or NULL if no sequence has
+                                   tokens past its compressed pages                             */
+  int32_t batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages;
+  int32_t splits;               /* pieces of each sequence's pages (split-K); 0 = automatic     */
+  float sm_scale;
+  void* workspace;              /* device, >= kvz_attn_workspace_bytes(...), 256-B aligned; calls
+                                   that share a workspace must be ordered on one stream         */
+  uint64_t workspace_bytes;
+} kvz_attn_args;
+
+/* Uncompressed baseline.  pages: device [n_phys][2][Hkv][4][64 chunks][16 B]: every block in
+ * the raw chunk layout above (what kvz_bf16_pack_pages writes).  Other fields as above, with
+ * n_comp_pages counting full BF16 pages. */
+typedef struct {
+  const uint16_t* q;
+  float* out;
+  const uint8_t* pages;
+  int32_t n_phys_pages;         /* pages holds n_phys_pages pages; other block-table entries are
+                                   skipped                                                       */
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* n_comp_pages;
+  const uint16_t* tail;
+  int32_t batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages;
+  int32_t splits;
+  float sm_scale;
+  void* workspace;
+  uint64_t workspace_bytes;
+} kvz_bf16_attn_args;
+
+int kvz_version(void);
+const char* kvz_last_error(void);
+
+/* KVZ_OK if `device` is a gfx950 GPU, KVZ_EUNSUPPORTED otherwise. */
+int kvz_device_check(int device);
+
+/* Bytes of device state a pool over an arena of arena_bytes needs. */
+int kvz_pool_state_bytes(uint64_t arena_bytes, uint64_t* state_bytes);
+
+/* Create a pool over d_arena (>= 2 granules, 256-B aligned) with its state in d_state
+ * (>= kvz_pool_state_bytes, 256-B aligned).  Resets the state on stream s: every granule
+ * free, frontier 0, bins empty, counters 0.  *out receives the host handle. */
+int kvz_pool_init(kvz_pool** out, void* d_arena, uint64_t arena_bytes, void* d_state,
+                  uint64_t state_bytes, hipStream_t s);
+
+/* Frees the host handle only; the caller frees arena and state. */
+int kvz_pool_destroy(kvz_pool* p);
+
+/* Allocate one run per item, in item order ([GAAC] fixed-capacity slots; [ZF] contiguous
+ * group blocks).  d_tags: device [n][4] block tags; d_off: device [n] receives the run offset in
+ * granules or KVZ_OFF_NONE.  Rule: an item with k raw blocks pops the most recently freed run
+ * of its bin k if there is one; otherwise it asks the frontier, and the frontier requests of one
+ * call are served as a prefix: a request succeeds iff frontier + (sizes of this call's frontier
+ * requests up to and including it) <= capacity.  Deterministic: the same calls give the same
+ * offsets. */
+int kvz_slot_alloc(kvz_pool* p, const uint8_t* d_tags, uint32_t* d_off, int32_t n, hipStream_t s);
+
+/* Return the runs of n groups to their bins, in item order, and reset each *d_metas[i] to
+ * {KVZ_OFF_NONE, {0,0,0,0}} ([ZF] memory manager: space freed by one layer is reused by
+ * another).  d_metas: device array of n device pointers.  Groups with off == KVZ_OFF_NONE are
+ * skipped. */
+int kvz_slot_free(kvz_pool* p, kvz_group_meta* const* d_metas, int32_t n, hipStream_t s);
+
+/* Page-completion encoder ([GAAC] fill-then-finalize; [ZF] steps 1-3): for each item, tag its
+ * four blocks, allocate a run (same rule and order as kvz_slot_alloc), write the blocks into
+ * the arena and the 8-byte metadata to item.dst.  If the pool has no room, dst->off is
+ * KVZ_OFF_NONE and nothing is written: the caller keeps that page in BF16.  flags:
+ * KVZ_ENC_FORCE_RAW stores every block raw.  d_items: device [n]. */
+int kvz_encode_pages(kvz_pool* p, const kvz_encode_item* d_items, int32_t n, uint32_t flags,
+                     hipStream_t s);
+
+/* Rebuild n blocks to natural order: d_out device [n][16 tokens][32 dims] BF16 ([ZF] step 4).
+ * A block of a group that is not stored, or that does not lie inside the arena_bytes of
+ * d_arena, decodes to zeros. */
+int kvz_decode_block(const void* d_arena, uint64_t arena_bytes, const kvz_block_ref* d_refs,
+                     int32_t n, uint16_t* d_out, hipStream_t s);
+
+/* Workspace bytes kvz_decode_attention / kvz_bf16_decode_attention need for these sizes
+ * (splits = 0: the automatic choice for max_pages). */
+int kvz_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t max_pages, int32_t splits, uint64_t* bytes);
+
+/* Fused paged split-K GQA decode attention over compressed pages plus the BF16 tail: blocks
+ * are restored bit-exactly in registers, never written back.  With one split per sequence the
+ * attention kernel writes out directly; otherwise a second small kernel merges the splits'
+ * partial softmax states from the workspace. */
+int kvz_decode_attention(const kvz_attn_args* a, hipStream_t s);
+
+/* Lay out n_pages natural BF16 pages (device [n_pages][2][Hkv][16][128]) as the baseline's
+ * pages (device [n_pages][2][Hkv][4][64][16 B], the raw chunk layout). */
+int kvz_bf16_pack_pages(const uint16_t* d_src, uint8_t* d_dst, int64_t n_pages,
+                        int32_t num_kv_heads, hipStream_t s);
+
+/* Uncompressed baseline: the same attention over BF16 pages laid out by kvz_bf16_pack_pages. */
+int kvz_bf16_decode_attention(const kvz_bf16_attn_args* a, hipStream_t s);
+
+/* Copy the pool counters to *host_out; synchronizes stream s. */
+int kvz_pool_stats(kvz_pool* p, kvz_pool_stats_t* host_out, hipStream_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVZ_H */

@@ -1,0 +1,156 @@
+"""GPU parity of the fused compressed decode attention and the BF16 baseline against the oracle.
+
+Tolerance (stated for the method): per output row, max_d |o - r| / max_d |r| <= 2e-3, and
+non-finite positions equal.  Storage-mode invariance is bitwise.
+"""
+import numpy as np
+import pytest
+import torch
+
+from decode_attention_kvz_amd import kvz, paged, synth
+
+from gpu_util import (announce, build_layer, check_rows, oracle_attention_rows, run_bf16,
+                      run_fused, sm_scale)
+
+pytestmark = pytest.mark.gpu
+
+
+def _layer(pages, seq_lens, n_comp, seed, arena_bytes=None, flags=0):
+    if arena_bytes is None:
+        arena_bytes = int(pages.numel() * 2 * 1.05) + (1 << 20)
+    arena = paged.SlotArena(arena_bytes)
+    return arena, build_layer(arena, pages, seq_lens, n_comp, seed=seed, flags=flags)
+
+
+@pytest.mark.parametrize("forced_exp,forced_frac", [(12.0, 0.10), (-16.0, 0.10), (0.0, 0.0)])
+def test_tiny_config_matches_oracle(forced_exp, forced_frac):
+    """1 sequence, 8 query / 2 KV heads, 256 tokens (16 compressed pages), seed 0."""
+    announce(f"tiny attention forced=({forced_exp},{forced_frac})")
+    pages = synth.kv_pages(1, 17, 2, seed=0, forced_frac=forced_frac, forced_exp=forced_exp,
+                           device="cuda")
+    q = synth.queries(1, 8, seed=0, device="cuda")
+    arena, layer = _layer(pages, [256], [16], seed=0)
+    got = run_fused(layer, arena, q, sm_scale()).cpu().numpy()
+    ref = oracle_attention_rows(layer, q, sm_scale(), [0])[0]
+    worst = check_rows(got[0], ref, what="fused")
+    announce(f"  max row rel err {worst:.2e}")
+
+
+def test_ragged_tails_and_empty_sequences():
+    """Sequences with 0..16 tail tokens, with no compressed pages, and of length 0."""
+    announce("ragged tails")
+    seq_lens = [16 * 5 + 0, 16 * 3 + 1, 16 * 7 + 15, 5, 0, 16 * 2 + 16, 16 * 9 + 8, 16]
+    n_comp = [5, 3, 7, 0, 0, 2, 9, 0]
+    pages = synth.kv_pages(len(seq_lens), 10, 2, seed=7, forced_frac=0.1, forced_exp=-16.0,
+                           device="cuda")
+    q = synth.queries(len(seq_lens), 8, seed=7, device="cuda")
+    arena, layer = _layer(pages, seq_lens, n_comp, seed=7)
+    got = run_fused(layer, arena, q, sm_scale()).cpu().numpy()
+    ref = oracle_attention_rows(layer, q, sm_scale(), range(len(seq_lens)))
+    for b in range(len(seq_lens)):
+        check_rows(got[b], ref[b], what=f"seq {b}")
+    assert not got[4].any(), "a sequence of length 0 gives zeros"
+    base = run_bf16(layer, q, sm_scale()).cpu().numpy()
+    for b in range(len(seq_lens)):
+        check_rows(base[b], ref[b], what=f"baseline seq {b}")
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (32, 8), (24, 4), (64, 4), (48, 3)])
+def test_query_group_sizes(hq, hkv):
+    announce(f"group sizes hq={hq} hkv={hkv}")
+    bsz = 3
+    pages = synth.kv_pages(bsz, 6, hkv, seed=11, forced_frac=0.05, forced_exp=-16.0,
+                           device="cuda")
+    q = synth.queries(bsz, hq, seed=11, device="cuda")
+    seq_lens, n_comp = [16 * 5 + 3, 16 * 2, 16 * 4 + 11], [5, 2, 4]
+    arena, layer = _layer(pages, seq_lens, n_comp, seed=11)
+    got = run_fused(layer, arena, q, sm_scale()).cpu().numpy()
+    ref = oracle_attention_rows(layer, q, sm_scale(), range(bsz))
+    for b in range(bsz):
+        check_rows(got[b], ref[b], what=f"seq {b}")
+
+
+def test_storage_mode_invariance_is_bitwise():
+    """The same KV stored compressed or all-raw gives bit-identical outputs (lossless)."""
+    announce("storage-mode invariance")
+    pages = synth.kv_pages(4, 21, 8, seed=12, forced_frac=0.05, device="cuda")
+    q = synth.queries(4, 32, seed=12, device="cuda")
+    seq_lens, n_comp = [16 * 20 + 7, 16 * 13, 16 * 20 + 16, 16 * 1 + 2], [20, 13, 20, 1]
+    arena_a, la = _layer(pages, seq_lens, n_comp, seed=12)
+    arena_b, lb = _layer(pages, seq_lens, n_comp, seed=12, flags=kvz.KVZ_ENC_FORCE_RAW)
+    for splits in (0, 3):
+        oa = run_fused(la, arena_a, q, sm_scale(), splits)
+        ob = run_fused(lb, arena_b, q, sm_scale(), splits)
+        assert torch.equal(oa, ob)
+    st_a, st_b = arena_a.stats(), arena_b.stats()
+    assert st_a["live_raw_blocks"] < st_b["live_raw_blocks"] == st_b["live_runs"] * 4
+
+
+def test_split_count_changes_output_only_by_rounding():
+    announce("split invariance")
+    pages = synth.kv_pages(2, 41, 8, seed=13, forced_frac=0.05, forced_exp=-16.0, device="cuda")
+    q = synth.queries(2, 32, seed=13, device="cuda")
+    seq_lens, n_comp = [16 * 40 + 9, 16 * 33], [40, 33]
+    arena, layer = _layer(pages, seq_lens, n_comp, seed=13)
+    outs = [run_fused(layer, arena, q, sm_scale(), s).cpu().numpy() for s in (1, 2, 5, 17, 0)]
+    for o in outs[1:]:
+        for b in range(2):
+            check_rows(o[b], outs[0][b], tol=1e-5, what="splits")
+    ref = oracle_attention_rows(layer, q, sm_scale(), range(2))
+    for b in range(2):
+        check_rows(outs[-1][b], ref[b], what=f"seq {b}")
+
+
+def test_non_finite_values_propagate_like_the_oracle():
+    """NaN and Inf in K and V (stress values): the positions of non-finite outputs equal the
+    oracle's."""
+    announce("non-finite propagation")
+    pages = synth.kv_pages(4, 9, 2, seed=14, forced_frac=0.0, device="cuda")
+    bits = pages.view(torch.int16)
+    bits[0, 2, 1, 0, 3, 17] = 0x7FC0          # NaN in V: one output dim of head group 0
+    bits[1, 4, 0, 1, 5, 3] = 0x7F80           # +Inf in K: scores of head group 1 go non-finite
+    bits[2, 8, 1, 0, 2, 40] = -128            # -Inf (0xFF80) in V on the tail page
+    q = synth.queries(4, 8, seed=14, device="cuda")
+    seq_lens, n_comp = [16 * 8 + 4, 16 * 8 + 4, 16 * 8 + 4, 16 * 8], [8, 8, 8, 8]
+    arena, layer = _layer(pages, seq_lens, n_comp, seed=14)
+    got = run_fused(layer, arena, q, sm_scale()).cpu().numpy()
+    ref = oracle_attention_rows(layer, q, sm_scale(), range(4))
+    for b in range(4):
+        check_rows(got[b], ref[b], what=f"seq {b}")
+    assert not np.isfinite(got[0]).all() and not np.isfinite(got[2]).all()
+
+
+def _full_size_sampled(bsz, n_pages_total, n_comp_pages, tail_tokens, hq, hkv, u_max, forced,
+                       seed, samples):
+    pages = synth.kv_pages(bsz, n_pages_total, hkv, seed=seed, u_max=u_max, forced_frac=forced,
+                           device="cuda")
+    q = synth.queries(bsz, hq, seed=seed, device="cuda")
+    seq_lens = [16 * n_comp_pages + tail_tokens] * bsz
+    arena, layer = _layer(pages, seq_lens, [n_comp_pages] * bsz, seed=seed)
+    got = run_fused(layer, arena, q, sm_scale()).cpu().numpy()
+    base = run_bf16(layer, q, sm_scale()).cpu().numpy()
+    ref = oracle_attention_rows(layer, q, sm_scale(), samples)
+    for b in samples:
+        check_rows(got[b], ref[b], what=f"fused seq {b}")
+        check_rows(base[b], ref[b], what=f"baseline seq {b}")
+    return arena
+
+
+def test_llama_shape_layer_sampled():
+    """Batch 32, 32 query / 8 KV heads, 2048 tokens, all pages compressed, 5% forced: one
+    layer at full shape with the automatic split count, checked on sampled sequences."""
+    announce("llama-shaped layer")
+    _full_size_sampled(32, 128, 128, 0, 32, 8, 3.0, 0.05, 1, [0, 17, 31])
+
+
+def test_qwen_shape_8k_layer_sampled():
+    """Batch 16, 32 query / 8 KV heads, 8192 tokens: 511 compressed pages plus a 16-token
+    BF16 tail, u~U[-5,5], 5% forced: one layer at full shape, sampled sequences."""
+    announce("qwen-shaped 8k layer")
+    _full_size_sampled(16, 512, 511, 16, 32, 8, 5.0, 0.05, 2, [0, 15])
+
+
+def test_long_context_layer_sampled():
+    """Batch 1, 32 query / 8 KV heads, 131072 tokens, split-K across the chip."""
+    announce("131k-token layer")
+    _full_size_sampled(1, 8192, 8192, 0, 32, 8, 3.0, 0.10, 4, [0])
