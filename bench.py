@@ -55,6 +55,9 @@ def main():
                     help="layers per step (the workload has 36; fewer is for quick checks only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-baseline", action="store_true")
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="for hardware-counter runs: one layer of fused and baseline attention "
+                         "(3 launches each) and a 1 GiB device copy as a traffic reference")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: the path has no multi-GPU form in this build "
@@ -67,6 +70,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     kvz.kvz_device_check(0)
+    if args.pmc_probe:
+        pmc_probe(args, dev)
+        return
     n_layers = args.layers
     scale = 1.0 / math.sqrt(128.0)
 
@@ -132,8 +138,6 @@ def main():
     log(f"setup done in {time.time() - t_setup:.1f}s: raw block fraction {raw_frac:.3f}, "
         f"records {rec_bytes / 1e6:.1f} MB/layer vs BF16 {B * N_COMP * HKV * 4096 * 2 / 1e6:.1f} MB")
 
-    stream = torch.cuda.current_stream()
-
     def attention(L, fused=True):
         if fused:
             kvz.kvz_decode_attention(L["q"], L["out"], arena.arena, L["meta"], L["block_table"],
@@ -142,64 +146,73 @@ def main():
             kvz.kvz_bf16_decode_attention(L["q"], L["out"], L["store"], L["block_table"], seq_lens,
                                           n_comp, L["tail"], scale, ws_b, HKV, args.splits)
 
-    def step(events=None):
-        for i, L in enumerate(layers):
-            if events is not None:
-                events[i][0].record(stream)
-            attention(L)
-            if events is not None:
-                events[i][1].record(stream)
+    def attention_all(fused=True):
+        for L in layers:
+            attention(L, fused)
+
+    def complete_pages():
         kvz.kvz_encode_pages(arena.pool, comp_items, n_comp_items)
         kvz.kvz_slot_free(arena.pool, comp_ptrs)
 
+    # Eager warm-up, then the step is captured as HIP graphs (36 attention calls; page
+    # completion) so that host launch overhead cannot starve the GPU between layers.
     for _ in range(args.warmup):
-        step()
+        attention_all()
+        complete_pages()
     torch.cuda.synchronize()
-    # whole steps, no events inside
+    eager_out = layers[-1]["out"].clone()
+    g_attn, g_comp = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_attn):
+        attention_all()
+    with torch.cuda.graph(g_comp):
+        complete_pages()
+    g_base = None
+    if not args.no_baseline:
+        attention_all(fused=False)
+        torch.cuda.synchronize()
+        g_base = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_base):
+            attention_all(fused=False)
+    for _ in range(args.warmup):
+        g_attn.replay()
+        g_comp.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(layers[-1]["out"], eager_out), "graph replay differs from the eager call"
+
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        """Mean ms per call from HIP events on the launch stream around `reps` calls."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def whole_step():
+        g_attn.replay()
+        g_comp.replay()
+
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        whole_step()
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    # the attention kernel alone: HIP events around each launch on the launch stream
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in layers]
-    attn_ms = []
-    for _ in range(args.steps):
-        step(ev)
-        torch.cuda.synchronize()
-        attn_ms.append([e[0].elapsed_time(e[1]) for e in ev])
-    attn_ms = np.asarray(attn_ms)
+    # the attention call alone (attention kernel + split merge), per layer, per step
+    attn_ms = np.asarray([timed(g_attn.replay, 1) / n_layers for _ in range(args.steps)])
     us_layer = float(np.median(attn_ms)) * 1e3
     us_layer_mean = float(np.mean(attn_ms)) * 1e3
     achieved = alg_bytes / (us_layer_mean * 1e-6) / 1e9
-    # encode + free of the completed pages, alone
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        kvz.kvz_encode_pages(arena.pool, comp_items, n_comp_items)
-        kvz.kvz_slot_free(arena.pool, comp_ptrs)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    enc_us = e0.elapsed_time(e1) * 1e3 / args.steps
+    enc_us = timed(g_comp.replay, args.steps) * 1e3
     log(f"fused: {ms_step:.3f} ms/step, attention {us_layer:.1f} us/layer (median), "
         f"{achieved:.0f} GB/s algorithmic; encode+free {enc_us:.1f} us/step")
 
     baseline = None
-    if not args.no_baseline:
-        for _ in range(args.warmup):
-            for L in layers:
-                attention(L, fused=False)
-        torch.cuda.synchronize()
-        evb = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in layers]
-        b_ms = []
-        for _ in range(args.steps):
-            for i, L in enumerate(layers):
-                evb[i][0].record(stream)
-                attention(L, fused=False)
-                evb[i][1].record(stream)
-            torch.cuda.synchronize()
-            b_ms.append([e[0].elapsed_time(e[1]) for e in evb])
-        b_ms = np.asarray(b_ms)
+    if g_base is not None:
+        b_ms = np.asarray([timed(g_base.replay, 1) / n_layers for _ in range(args.steps)])
         b_alg = (B * N_COMP * HKV * 4096 * 2 + B * N_COMP * 4 + B * 2 * HKV * 16 * 128 * 2
                  + B * HQ * 128 * 2 + B * HQ * 128 * 4)
         b_us = float(np.median(b_ms)) * 1e3
@@ -249,9 +262,51 @@ def main():
     arena.close()
 
 
+def pmc_probe(args, dev):
+    """Launches for a counter run: a 1 GiB device-to-device copy (reads and writes exactly
+    1 GiB; the reference that scales FETCH_SIZE / WRITE_SIZE), then 3 fused and 3 baseline
+    attention launches on layer 0 of the workload."""
+    import torch
+    from decode_attention_kvz_amd import kvz, paged, synth
+    src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    n_phys = B * N_COMP
+    pages = synth.kv_pages(B, N_COMP + 1, HKV, seed=SEED, layer=0, u_max=U_MAX, forced_frac=FORCED,
+                           device=dev)
+    arena = paged.SlotArena(n_phys * HKV * 2 * 4096 + (16 << 20), device=dev)
+    block_table = np.random.default_rng(SEED).permutation(n_phys).reshape(B, N_COMP).astype(np.int32)
+    meta = paged.new_meta_table(n_phys, HKV, device=dev)
+    items = paged.page_items(pages, [(b, p) for b in range(B) for p in range(N_COMP)], meta,
+                             block_table.reshape(-1))
+    d_items = paged.encode(arena, items)
+    inv = torch.as_tensor(np.argsort(block_table.reshape(-1)), device=dev)
+    store = paged.pack_bf16_pages(pages[:, :N_COMP].reshape(n_phys, 2, HKV, 16, 128)[inv])
+    tail = pages[:, N_COMP].contiguous()
+    q = synth.queries(B, HQ, seed=SEED * 1000, device=dev)
+    out = torch.empty((B, HQ, 128), dtype=torch.float32, device=dev)
+    bt = torch.from_numpy(block_table).to(dev)
+    seq_lens = torch.full((B,), CTX, dtype=torch.int32, device=dev)
+    n_comp = torch.full((B,), N_COMP, dtype=torch.int32, device=dev)
+    ws = paged.workspace(B, HQ, HKV, N_COMP, args.splits, device=dev)
+    torch.cuda.synchronize()
+    del d_items
+    for _ in range(3):
+        kvz.kvz_decode_attention(q, out, arena.arena, meta, bt, seq_lens, n_comp, tail,
+                                 1.0 / math.sqrt(128.0), ws, args.splits)
+    for _ in range(3):
+        kvz.kvz_bf16_decode_attention(q, out, store, bt, seq_lens, n_comp, tail,
+                                      1.0 / math.sqrt(128.0), ws, HKV, args.splits)
+    torch.cuda.synchronize()
+    st = arena.stats()
+    log(f"pmc probe done: {st['live_granules'] * 256} record bytes in the layer")
+    arena.close()
+
+
 def cpu_baseline(layers, n_phys, scale):
-    """The oracle on a bounded sample: decode + fp64 attention of one sequence (all KV heads,
-    8192 tokens) of layer 0, inputs encoded by the oracle itself outside the timed region."""
+    """The oracle on a bounded sample: decode + fp64 attention of layer 0 (all 16 sequences, all
+    KV heads, 8192 tokens each), inputs encoded by the oracle itself outside the timed region."""
     import torch
     from decode_attention_kvz_amd import synth
     from oracle import attention
@@ -261,35 +316,34 @@ def cpu_baseline(layers, n_phys, scale):
     except ImportError:   # pragma: no cover
         threadpool_limits = None
 
-    # regenerate sequence 0 of layer 0 (the same seeded pages) on the host side
+    # regenerate layer 0 (the same seeded pages) and hand the host copy to the oracle
     pages = synth.kv_pages(B, N_COMP + 1, HKV, seed=SEED, layer=0, u_max=U_MAX, forced_frac=FORCED,
                            device="cuda")
-    nat = synth.bits(pages[0])                      # [512, 2, Hkv, 16, 128]
+    nat = synth.bits(pages)                         # [B, 512, 2, Hkv, 16, 128]
     del pages
     q = synth.bits(layers[0]["q"])
     t0 = time.time()
-    oc = OracleCache((N_COMP * HKV * 2 + 16) * 4096)
-    flat = nat[:N_COMP].transpose(0, 2, 1, 3, 4).reshape(-1, 16, 128)
+    oc = OracleCache((B * N_COMP * HKV * 2 + 16) * 4096)
+    flat = nat[:, :N_COMP].transpose(0, 1, 3, 2, 4, 5).reshape(-1, 16, 128)   # (b, p, h, K/V)
     metas = oc.encode(flat, [i % 2 for i in range(flat.shape[0])])
-    meta_table = [[[metas[(p * HKV + h) * 2 + k] for k in range(2)] for h in range(HKV)]
-                  for p in range(N_COMP)]
+    meta_table = [[[metas[(pp * HKV + h) * 2 + k] for k in range(2)] for h in range(HKV)]
+                  for pp in range(B * N_COMP)]
     log(f"cpu baseline: oracle encode of the sample took {time.time() - t0:.1f}s (untimed)")
-    block_table = np.arange(N_COMP, dtype=np.int64).reshape(1, N_COMP)
-    tail = nat[N_COMP][None]
-    qs = q[:1]
+    block_table = np.arange(B * N_COMP, dtype=np.int64).reshape(B, N_COMP)
+    tail = nat[:, N_COMP]
     import contextlib
     limit = threadpool_limits(limits=1) if threadpool_limits is not None else contextlib.nullcontext()
     with limit:
         t0 = time.perf_counter()
-        attention.decode_attention(qs, oc.arena, meta_table, block_table, [CTX], [N_COMP], tail,
-                                   scale)
+        attention.decode_attention(q, oc.arena, meta_table, block_table, [CTX] * B, [N_COMP] * B,
+                                   tail, scale)
         dt = time.perf_counter() - t0
-    bytes_eff = CTX * HKV * 128 * 2 * 2
-    log(f"cpu baseline: {dt:.1f}s for one sequence ({bytes_eff / dt / 1e9:.4f} GB/s)")
+    bytes_eff = B * CTX * HKV * 128 * 2 * 2
+    log(f"cpu baseline: {dt:.1f}s for one layer ({bytes_eff / dt / 1e9:.4f} GB/s)")
     return {"value": round(bytes_eff / dt / 1e9, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "layer 0, sequence 0: 511 compressed pages + 16-token tail, 8 KV heads, 32 "
-                      "query heads (1/576 of a step's attention), decode + fp64 attention, "
-                      "1 thread"}
+            "sample": "layer 0 of the workload (16 sequences x 8192 tokens, 8 KV / 32 query heads; "
+                      "1/36 of a step's attention): oracle block decode + fp64 attention, "
+                      "1 thread, inputs encoded by the oracle beforehand (untimed)"}
 
 
 if __name__ == "__main__":

@@ -8,9 +8,9 @@
 // in one layer is reused by another).  A group with n_raw raw blocks takes 12 + n_raw granules
 // of 256 B (768-B and 1024-B slots).
 //
-// Both kernels run as ONE workgroup of 1024 threads that walks the items in chunks of 1024,
-// so the result depends only on item order: the i-th item of bin k pops the bin from the top,
-// frontier requests get prefix-summed offsets.
+// Both kernels run as ONE workgroup of 512 threads that walks the items in passes of 4096 (8
+// consecutive items per thread), so the result depends only on item order: the i-th item of
+// bin k pops the bin from the top, frontier requests get prefix-summed offsets.
 #include "kvz_internal.h"
 
 #include <algorithm>
@@ -19,73 +19,68 @@ namespace kvz {
 
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
+
+constexpr int kIpt = 8;   // items per thread per pass: the loads of 4096 items are in flight together
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const uint32_t lane = threadIdx.x & 63u;
   return lane == 0 ? 0ull : (~0ull >> (64u - lane));
 }
 
-// Exclusive prefix sum over the 1024 threads of the block; returns the block total in *total.
-__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_tmp, uint32_t* total) {
+// Block-wide exclusive scan of C columns in thread order (thread t's values come after those
+// of threads < t); excl[c] = sum over earlier threads, tot[c] = block total.
+template <int C>
+__device__ void block_scan_cols(const uint32_t (&v)[C], uint32_t (&excl)[C], uint32_t (&tot)[C],
+                                uint32_t (*s_wave)[8], uint32_t (*s_pre)[8], uint32_t* s_tot) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  uint32_t incl = v;
+  uint32_t incl[C];
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t o = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += o;
-  }
-  if (lane == 63) s_tmp[wave] = incl;
-  __syncthreads();
-  if (wave == 0) {
-    uint32_t w = lane < kWaves ? s_tmp[lane] : 0u;
-    uint32_t wi = w;
+  for (int c = 0; c < C; ++c) {
+    incl[c] = v[c];
 #pragma unroll
-    for (int d = 1; d < kWaves; d <<= 1) {
-      const uint32_t o = __shfl_up(wi, d, 64);
-      if (lane >= d) wi += o;
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t o = __shfl_up(incl[c], d, 64);
+      if (lane >= d) incl[c] += o;
     }
-    if (lane < kWaves) s_tmp[kWaves + lane] = wi - w;   // exclusive wave offsets
-    if (lane == kWaves - 1) s_tmp[2 * kWaves] = wi;
+    if (lane == 63) s_wave[wave][c] = incl[c];
   }
   __syncthreads();
-  const uint32_t r = s_tmp[kWaves + wave] + incl - v;
-  *total = s_tmp[2 * kWaves];
+  if ((int)threadIdx.x < C) {
+    uint32_t acc = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      s_pre[w][threadIdx.x] = acc;
+      acc += s_wave[w][threadIdx.x];
+    }
+    s_tot[threadIdx.x] = acc;
+  }
   __syncthreads();
-  return r;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    excl[c] = s_pre[wave][c] + incl[c] - v[c];
+    tot[c] = s_tot[c];
+  }
+  __syncthreads();
 }
 
-// Rank of this thread among the threads of the block whose key equals its key (key in
-// 0..kBins-1, or -1 for none), in thread order; counts[k] receives the block count of key k.
-__device__ uint32_t block_rank_by_key(int key, uint32_t (*s_cnt)[kBins], uint32_t* counts) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  uint32_t rank = 0;
+struct ScanShared {
+  uint32_t wave[kWaves][8];
+  uint32_t pre[kWaves][8];
+  uint32_t tot[8];
+};
+
+// Sum of v over the block (result valid in every thread).
+__device__ uint64_t block_sum(uint64_t v, uint64_t* s_red) {
 #pragma unroll
-  for (int k = 0; k < kBins; ++k) {
-    const uint64_t m = __ballot(key == k);
-    if (key == k) rank = __popcll(m & lanemask_lt());
-    if (lane == 0) s_cnt[wave][k] = __popcll(m);
-  }
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
   __syncthreads();
-  uint32_t before = 0;
-  for (int w = 0; w < kWaves; ++w) {
-#pragma unroll
-    for (int k = 0; k < kBins; ++k) {
-      const uint32_t c = s_cnt[w][k];
-      if (w < wave && key == k) before += c;
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < kBins; ++k) {
-    uint32_t c = 0;
-    for (int w = 0; w < kWaves; ++w) c += s_cnt[w][k];
-    counts[k] = c;
-  }
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = v;
   __syncthreads();
-  return before + rank;
+  uint64_t t = 0;
+  for (int w = 0; w < kWaves; ++w) t += s_red[w];
+  return t;
 }
 
 // Item accessors: tags in / offset out, either from plain arrays or from encode items' metadata.
@@ -108,146 +103,211 @@ struct EncodeItemAccess {
   __device__ void set_off(int i, uint32_t o) const { items[i].dst->off = o; }
 };
 
+// Allocation in item order.  A pass covers 4096 items; thread t owns items 8t..8t+7 of it, so
+// "earlier in item order" = earlier thread, or the same thread and a smaller index.
 template <class Access>
 __global__ __launch_bounds__(kThreads) void pool_alloc_kernel(PoolHdr* hdr, uint32_t* bins,
                                                               Access acc, int n) {
-  __shared__ uint32_t s_cnt[kWaves][kBins];
-  __shared__ uint32_t s_tmp[2 * kWaves + 1];
-  __shared__ uint32_t s_stat[4];   // successes, granules, raw blocks, failures of the chunk
+  __shared__ ScanShared sh;
+  __shared__ uint64_t s_red[kWaves];
+  __shared__ uint64_t s_cnt[kBins], s_base[kBins];   // bin state, uniform over the block
+  __shared__ uint32_t s_ktot[kBins];
   if (hdr->magic != kPoolMagic) return;   // host checked; never write through a bad state
 
   const uint64_t cap = hdr->capacity;
   const uint64_t f0 = hdr->frontier;
-  uint64_t cnt[kBins], base[kBins];
-#pragma unroll
-  for (int k = 0; k < kBins; ++k) {
-    cnt[k] = hdr->bin_cnt[k];
-    base[k] = hdr->bin_base[k];
+  if (threadIdx.x < kBins) {
+    s_cnt[threadIdx.x] = hdr->bin_cnt[threadIdx.x];
+    s_base[threadIdx.x] = hdr->bin_base[threadIdx.x];
   }
+  __syncthreads();
   uint64_t pending = 0;   // sizes of this call's frontier requests so far (granted or not)
-  uint64_t granted = 0;
-  uint64_t st_runs = 0, st_gran = 0, st_raw = 0, st_fail = 0;
+  uint64_t my_granted = 0, my_runs = 0, my_gran = 0, my_raw = 0, my_fail = 0;
 
-  for (int chunk = 0; chunk < n; chunk += kThreads) {
-    const int i = chunk + (int)threadIdx.x;
-    const bool valid = i < n;
-    uint32_t tags = valid ? acc.get_tags(i) : 0u;
-    const int k = valid ? (int)n_raw_of(tags) : -1;
-    uint32_t counts[kBins];
-    const uint32_t rank = block_rank_by_key(k, s_cnt, counts);
-
-    bool from_bin = false;
-    uint64_t off = KVZ_OFF_NONE;
-    if (valid && rank < cnt[k]) {
-      from_bin = true;
-      off = bins[base[k] + cnt[k] - 1 - rank];
-    }
-    const uint32_t z = (valid && !from_bin) ? run_granules((uint32_t)k) : 0u;
-    uint32_t ztot;
-    const uint32_t zpre = block_exclusive_scan(z, s_tmp, &ztot);
-    if (valid && !from_bin) {
-      const uint64_t start = f0 + pending + zpre;
-      off = (start + z <= cap) ? start : (uint64_t)KVZ_OFF_NONE;
-    }
-    if (threadIdx.x < 4) s_stat[threadIdx.x] = 0;
-    __syncthreads();
-    if (valid) {
-      acc.set_off(i, (uint32_t)off);
-      if (off != KVZ_OFF_NONE) {
-        atomicAdd(&s_stat[0], 1u);
-        atomicAdd(&s_stat[1], run_granules((uint32_t)k));
-        atomicAdd(&s_stat[2], (uint32_t)k);
-      } else {
-        atomicAdd(&s_stat[3], 1u);
+  for (int pass = 0; pass < n; pass += kThreads * kIpt) {
+    const int first = pass + (int)threadIdx.x * kIpt;
+    uint32_t tags[kIpt];
+#pragma unroll
+    for (int sub = 0; sub < kIpt; ++sub) tags[sub] = first + sub < n ? acc.get_tags(first + sub) : 0u;
+    // ranks among same-size items: local prefix, then across threads
+    int key[kIpt];
+    uint32_t lrank[kIpt];
+    uint32_t lcnt[kBins] = {0, 0, 0, 0, 0};
+#pragma unroll
+    for (int sub = 0; sub < kIpt; ++sub) {
+      key[sub] = first + sub < n ? (int)n_raw_of(tags[sub]) : -1;
+      lrank[sub] = 0;
+#pragma unroll
+      for (int k = 0; k < kBins; ++k) {
+        if (key[sub] == k) {
+          lrank[sub] = lcnt[k];
+          lcnt[k] += 1;
+        }
       }
     }
-    __syncthreads();
-    // frontier granules granted in this chunk = granules of successful frontier requests
-    uint32_t gz = (valid && !from_bin && off != KVZ_OFF_NONE) ? z : 0u;
-    uint32_t gtot;
-    (void)block_exclusive_scan(gz, s_tmp, &gtot);
-    granted += gtot;
-    pending += ztot;
+    uint32_t kbase[kBins], ktot[kBins];
+    block_scan_cols<kBins>(lcnt, kbase, ktot, sh.wave, sh.pre, sh.tot);
+    if (threadIdx.x == 0) {
 #pragma unroll
-    for (int kk = 0; kk < kBins; ++kk) cnt[kk] -= (counts[kk] < cnt[kk] ? counts[kk] : cnt[kk]);
-    st_runs += s_stat[0];
-    st_gran += s_stat[1];
-    st_raw += s_stat[2];
-    st_fail += s_stat[3];
+      for (int k = 0; k < kBins; ++k) s_ktot[k] = ktot[k];
+    }
+    // pop the bin while it lasts, else ask the frontier
+    uint64_t off[kIpt];
+    bool from_bin[kIpt];
+    uint32_t zoff[kIpt];
+    uint32_t lz[1] = {0};
+#pragma unroll
+    for (int sub = 0; sub < kIpt; ++sub) {
+      const int k = key[sub];
+      from_bin[sub] = false;
+      off[sub] = KVZ_OFF_NONE;
+      zoff[sub] = lz[0];
+      if (k >= 0) {
+        uint32_t kb = kbase[0];
+#pragma unroll
+        for (int j = 1; j < kBins; ++j) kb = (k == j) ? kbase[j] : kb;
+        const uint64_t rank = (uint64_t)kb + lrank[sub];
+        const uint64_t ck = s_cnt[k];
+        if (rank < ck) {
+          from_bin[sub] = true;
+          off[sub] = s_base[k] + ck - 1 - rank;   // bin slot, read below
+        } else {
+          lz[0] += run_granules((uint32_t)k);
+        }
+      }
+    }
+    uint32_t zbase[1], ztot[1];
+    block_scan_cols<1>(lz, zbase, ztot, sh.wave, sh.pre, sh.tot);
+#pragma unroll
+    for (int sub = 0; sub < kIpt; ++sub) {
+      const int k = key[sub];
+      if (k < 0) continue;
+      if (!from_bin[sub]) {
+        const uint32_t z = run_granules((uint32_t)k);
+        const uint64_t start = f0 + pending + zbase[0] + zoff[sub];
+        if (start + z <= cap) {
+          off[sub] = start;
+          my_granted += z;
+        }
+      }
+      if (from_bin[sub] || off[sub] != KVZ_OFF_NONE) {
+        my_runs += 1;
+        my_gran += run_granules((uint32_t)k);
+        my_raw += (uint32_t)k;
+      } else {
+        my_fail += 1;
+      }
+    }
+#pragma unroll
+    for (int sub = 0; sub < kIpt; ++sub)
+      if (from_bin[sub]) off[sub] = bins[off[sub]];
+#pragma unroll
+    for (int sub = 0; sub < kIpt; ++sub)
+      if (key[sub] >= 0) acc.set_off(first + sub, (uint32_t)off[sub]);
+    pending += ztot[0];
+    __syncthreads();
+    if (threadIdx.x < kBins) {
+      const uint64_t c = s_cnt[threadIdx.x], t = s_ktot[threadIdx.x];
+      s_cnt[threadIdx.x] = c - (t < c ? t : c);
+    }
     __syncthreads();
   }
+  const uint64_t granted = block_sum(my_granted, s_red);
+  const uint64_t runs = block_sum(my_runs, s_red);
+  const uint64_t gran = block_sum(my_gran, s_red);
+  const uint64_t raw = block_sum(my_raw, s_red);
+  const uint64_t fail = block_sum(my_fail, s_red);
+  if (threadIdx.x < kBins) hdr->bin_cnt[threadIdx.x] = s_cnt[threadIdx.x];
   if (threadIdx.x == 0) {
     hdr->frontier = f0 + granted;
-#pragma unroll
-    for (int k = 0; k < kBins; ++k) hdr->bin_cnt[k] = cnt[k];
-    hdr->live_runs += st_runs;
-    hdr->live_granules += st_gran;
-    hdr->live_raw_blocks += st_raw;
-    hdr->enospc += st_fail;
+    hdr->live_runs += runs;
+    hdr->live_granules += gran;
+    hdr->live_raw_blocks += raw;
+    hdr->enospc += fail;
   }
 }
 
+// Free in item order: item i pushes its run onto bin[n_raw] at position count + rank.
 __global__ __launch_bounds__(kThreads) void pool_free_kernel(PoolHdr* hdr, uint32_t* bins,
                                                              kvz_group_meta* const* metas, int n) {
-  __shared__ uint32_t s_cnt[kWaves][kBins];
-  __shared__ uint32_t s_stat[4];   // freed runs, granules, raw blocks, dropped
+  __shared__ ScanShared sh;
+  __shared__ uint64_t s_red[kWaves];
+  __shared__ uint64_t s_cnt[kBins], s_base[kBins], s_bcap[kBins];
+  __shared__ uint32_t s_ktot[kBins];
   if (hdr->magic != kPoolMagic) return;
-  uint64_t cnt[kBins], base[kBins], bcap[kBins];
-#pragma unroll
-  for (int k = 0; k < kBins; ++k) {
-    cnt[k] = hdr->bin_cnt[k];
-    base[k] = hdr->bin_base[k];
-    bcap[k] = hdr->bin_cap[k];
+  if (threadIdx.x < kBins) {
+    s_cnt[threadIdx.x] = hdr->bin_cnt[threadIdx.x];
+    s_base[threadIdx.x] = hdr->bin_base[threadIdx.x];
+    s_bcap[threadIdx.x] = hdr->bin_cap[threadIdx.x];
   }
-  uint64_t st_runs = 0, st_gran = 0, st_raw = 0, st_bad = 0;
-  for (int chunk = 0; chunk < n; chunk += kThreads) {
-    const int i = chunk + (int)threadIdx.x;
-    kvz_group_meta* m = i < n ? metas[i] : nullptr;
-    uint32_t off = KVZ_OFF_NONE, tags = 0;
-    if (m) {
-      off = m->off;
-      tags = *reinterpret_cast<const uint32_t*>(m->tag);
-    }
-    const bool valid = m && off != KVZ_OFF_NONE;
-    const int k = valid ? (int)n_raw_of(tags) : -1;
-    uint32_t counts[kBins];
-    const uint32_t rank = block_rank_by_key(k, s_cnt, counts);
-    if (threadIdx.x < 4) s_stat[threadIdx.x] = 0;
-    __syncthreads();
-    if (valid) {
-      const uint64_t slot = cnt[k] + rank;
-      if (slot < bcap[k]) {
-        bins[base[k] + slot] = off;
-        atomicAdd(&s_stat[0], 1u);
-        atomicAdd(&s_stat[1], run_granules((uint32_t)k));
-        atomicAdd(&s_stat[2], (uint32_t)k);
-      } else {
-        atomicAdd(&s_stat[3], 1u);
+  __syncthreads();
+  uint64_t my_runs = 0, my_gran = 0, my_raw = 0, my_bad = 0;
+  for (int pass = 0; pass < n; pass += kThreads * kIpt) {
+    const int first = pass + (int)threadIdx.x * kIpt;
+    kvz_group_meta* m[kIpt];
+#pragma unroll
+    for (int sub = 0; sub < kIpt; ++sub) m[sub] = first + sub < n ? metas[first + sub] : nullptr;
+    uint2 rec[kIpt];
+#pragma unroll
+    for (int sub = 0; sub < kIpt; ++sub)
+      rec[sub] = m[sub] ? *reinterpret_cast<const uint2*>(m[sub]) : make_uint2(KVZ_OFF_NONE, 0u);
+    int key[kIpt];
+    uint32_t lrank[kIpt];
+    uint32_t lcnt[kBins] = {0, 0, 0, 0, 0};
+#pragma unroll
+    for (int sub = 0; sub < kIpt; ++sub) {
+      key[sub] = (m[sub] && rec[sub].x != KVZ_OFF_NONE) ? (int)n_raw_of(rec[sub].y) : -1;
+      lrank[sub] = 0;
+#pragma unroll
+      for (int k = 0; k < kBins; ++k) {
+        if (key[sub] == k) {
+          lrank[sub] = lcnt[k];
+          lcnt[k] += 1;
+        }
       }
     }
-    if (m) {
-      m->off = KVZ_OFF_NONE;
-      *reinterpret_cast<uint32_t*>(m->tag) = 0u;
+    uint32_t kbase[kBins], ktot[kBins];
+    block_scan_cols<kBins>(lcnt, kbase, ktot, sh.wave, sh.pre, sh.tot);
+    if (threadIdx.x == 0) {
+#pragma unroll
+      for (int k = 0; k < kBins; ++k) s_ktot[k] = ktot[k];
+    }
+#pragma unroll
+    for (int sub = 0; sub < kIpt; ++sub) {
+      const int k = key[sub];
+      if (k >= 0) {
+        uint32_t kb = kbase[0];
+#pragma unroll
+        for (int j = 1; j < kBins; ++j) kb = (k == j) ? kbase[j] : kb;
+        const uint64_t slot = s_cnt[k] + kb + lrank[sub];
+        if (slot < s_bcap[k]) {
+          bins[s_base[k] + slot] = rec[sub].x;
+          my_runs += 1;
+          my_gran += run_granules((uint32_t)k);
+          my_raw += (uint32_t)k;
+        } else {
+          my_bad += 1;
+        }
+      }
+      if (m[sub]) *reinterpret_cast<uint2*>(m[sub]) = make_uint2(KVZ_OFF_NONE, 0u);
     }
     __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < kBins; ++kk) {
-      const uint64_t c = cnt[kk] + counts[kk];
-      cnt[kk] = c < bcap[kk] ? c : bcap[kk];
+    if (threadIdx.x < kBins) {
+      const uint64_t c = s_cnt[threadIdx.x] + s_ktot[threadIdx.x];
+      s_cnt[threadIdx.x] = c < s_bcap[threadIdx.x] ? c : s_bcap[threadIdx.x];
     }
-    st_runs += s_stat[0];
-    st_gran += s_stat[1];
-    st_raw += s_stat[2];
-    st_bad += s_stat[3];
     __syncthreads();
   }
+  const uint64_t runs = block_sum(my_runs, s_red);
+  const uint64_t gran = block_sum(my_gran, s_red);
+  const uint64_t raw = block_sum(my_raw, s_red);
+  const uint64_t bad = block_sum(my_bad, s_red);
+  if (threadIdx.x < kBins) hdr->bin_cnt[threadIdx.x] = s_cnt[threadIdx.x];
   if (threadIdx.x == 0) {
-#pragma unroll
-    for (int k = 0; k < kBins; ++k) hdr->bin_cnt[k] = cnt[k];
-    hdr->live_runs -= st_runs;
-    hdr->live_granules -= st_gran;
-    hdr->live_raw_blocks -= st_raw;
-    hdr->bad_frees += st_bad;
+    hdr->live_runs -= runs;
+    hdr->live_granules -= gran;
+    hdr->live_raw_blocks -= raw;
+    hdr->bad_frees += bad;
   }
 }
 
