@@ -176,8 +176,6 @@ struct Softmax {
   }
 };
 
-constexpr int kBatch = 2;   // pages whose loads are in flight together per wave
-
 template <int GB, bool COMP>
 __global__ __launch_bounds__(256, 3) void attn_split_kernel(AttnParams p) {
   const int lane = threadIdx.x & 63;
@@ -297,17 +295,21 @@ __global__ __launch_bounds__(256, 3) void attn_split_kernel(AttnParams p) {
       sm.page(sv, vop, lane);
     };
 
-    // Pages are read in batches of kBatch: the loads of a whole batch are issued together, then
-    // its pages are computed in order, each waiting only for its own loads.  The last batch
-    // re-reads the chunk's last page in place of missing ones (an L2 hit, never computed).
+    // Two one-page buffers in a ring: the loads of page i+1 are in flight while page i is
+    // computed.  The loop runs whole rounds of two (past the end a load re-reads the chunk's
+    // last page, an L2 hit that is never computed), so the wait before each compute covers
+    // exactly that page's eight loads.
     const int last = cnt - 1;
-    for (int i0 = 0; i0 < cnt; i0 += kBatch) {
-      KV8 buf[kBatch];
+    KV8 buf[2];
+    load_page(0, buf[0]);
+    const int rounds = (cnt + 1) / 2;
+    for (int r = 0; r < rounds; ++r) {
 #pragma unroll
-      for (int k = 0; k < kBatch; ++k) load_page(i0 + k < last ? i0 + k : last, buf[k]);
-#pragma unroll
-      for (int k = 0; k < kBatch; ++k)
-        if (i0 + k <= last) process(buf[k], i0 + k);
+      for (int k = 0; k < 2; ++k) {
+        const int i = 2 * r + k;
+        load_page(i + 1 < last ? i + 1 : last, buf[k ^ 1]);
+        if (i <= last) process(buf[k], i);
+      }
     }
   }
 
@@ -384,35 +386,86 @@ __global__ __launch_bounds__(256, 3) void attn_split_kernel(AttnParams p) {
 // out = sum O_s 2^(m_s - M) / L.  A sequence of length 0 gives zeros.  A separate launch:
 // ordering the splits' partial writes before these reads needs no per-wave fence (a fence at
 // device scope writes back and invalidates the whole L2 of the issuing chiplet).
-__global__ __launch_bounds__(128) void attn_combine_kernel(const float* ws_ml, const float* ws_o,
-                                                           float* out, const int32_t* seq_lens,
-                                                           int Hq, int Hkv, int G, int S) {
+// One workgroup of 256 threads per (sequence, query head), parallel over the splits.
+constexpr int kCombineThreads = 256;
+constexpr int kMaxSplits = 4096;
+
+__device__ __forceinline__ float block_reduce(float v, float* s_red, bool is_max) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const float o = __shfl_xor(v, d, 64);
+    v = is_max ? fmaxf(v, o) : v + o;
+  }
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = s_red[0];
+#pragma unroll
+  for (int w = 1; w < kCombineThreads / 64; ++w) r = is_max ? fmaxf(r, s_red[w]) : r + s_red[w];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(
+    const float* ws_ml, const float* ws_o, float* out, const int32_t* seq_lens, int Hq, int Hkv,
+    int G, int S) {
+  __shared__ float s_w[kMaxSplits];
+  __shared__ float s_red[kCombineThreads / 64];
+  __shared__ float s_part[kCombineThreads];
   const int bh = blockIdx.x;
   const int b = bh / Hq, h = bh % Hq;
   const int kvh = h / G, g = h % G;
-  const int d = threadIdx.x;
+  const int t = threadIdx.x;
   const size_t unit0 = ((size_t)b * Hkv + kvh) * S;
-  float M = -INFINITY;
-  for (int sp = 0; sp < S; ++sp) M = fmaxf(M, ws_ml[((unit0 + sp) * G + g) * 2]);
-  float L = 0.f, acc = 0.f;
-  for (int sp = 0; sp < S; ++sp) {
+  float m_loc = -INFINITY;
+  for (int sp = t; sp < S; sp += kCombineThreads) m_loc = fmaxf(m_loc, ws_ml[((unit0 + sp) * G + g) * 2]);
+  const float M = block_reduce(m_loc, s_red, true);
+  float l_loc = 0.f;
+  for (int sp = t; sp < S; sp += kCombineThreads) {
     const size_t ug = (unit0 + sp) * G + g;
     const float m = ws_ml[ug * 2];
     const float w = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - M);
-    L += w * ws_ml[ug * 2 + 1];
-    acc += w * ws_o[ug * KVZ_HEAD_DIM + d];
+    s_w[sp] = w;
+    l_loc += w * ws_ml[ug * 2 + 1];
   }
-  out[(size_t)bh * KVZ_HEAD_DIM + d] = seq_lens[b] <= 0 ? 0.f : acc / L;
+  const float L = block_reduce(l_loc, s_red, false);   // its barrier also publishes s_w
+  const int d = t & (KVZ_HEAD_DIM - 1);
+  float acc = 0.f;
+#pragma unroll 4
+  for (int sp = t >> 7; sp < S; sp += kCombineThreads / KVZ_HEAD_DIM)
+    acc += s_w[sp] * ws_o[((unit0 + sp) * G + g) * KVZ_HEAD_DIM + d];
+  s_part[t] = acc;
+  __syncthreads();
+  if (t < KVZ_HEAD_DIM) {
+    const float o = (s_part[t] + s_part[t + KVZ_HEAD_DIM]) / L;
+    out[(size_t)bh * KVZ_HEAD_DIM + d] = seq_lens[b] <= 0 ? 0.f : o;
+  }
 }
 
-// About 1024 waves in all (4 per CU) with at least ~16 pages each: measured fastest at the
-// 8K-context workload (more splits add combine work and contention, fewer leave CUs idle).
-int choose_splits(int B, int Hkv, int max_pages) {
-  const int units = (B * Hkv) > 0 ? B * Hkv : 1;
-  int S = (1024 + units - 1) / units;
-  const int by_pages = (max_pages + 1 + 15) / 16;
+// Split count: one workgroup (4 splits) per CU - the 2-page prefetch ring keeps enough bytes in
+// flight with 4 waves per CU, and measured as fast or faster than 2 workgroups per CU on every
+// workload shape - with at least 4 pages per split.  Workgroup counts that are not a multiple of
+// the CU count leave some CUs one workgroup more than others (measured 10-20% slower).
+int choose_splits(int B, int Hkv, int max_pages, int n_cu) {
+  const int64_t units = (int64_t)(B * Hkv > 0 ? B * Hkv : 1);
+  const int64_t pages = (int64_t)max_pages + 1;
+  int64_t S = (4 * (int64_t)n_cu + units - 1) / units;
+  const int64_t by_pages = (pages + 3) / 4;
   if (S > by_pages) S = by_pages;
-  return S < 1 ? 1 : S;
+  if (S > kMaxSplits) S = kMaxSplits;
+  return (int)(S < 1 ? 1 : S);
+}
+
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
@@ -463,8 +516,8 @@ int launch_attention(const CommonArgs& a, const uint8_t* kv, const kvz_group_met
     return set_error(KVZ_EINVAL, "q and tail must be 16-byte aligned");
   if (COMP && (((uintptr_t)meta) & 15u)) return set_error(KVZ_EINVAL, "meta must be 16-byte aligned");
   if (((uintptr_t)a.workspace) & 255u) return set_error(KVZ_EINVAL, "workspace must be 256-byte aligned");
-  if (a.splits < 0 || a.splits > 65535) return set_error(KVZ_EINVAL, "splits out of range");
-  const int S = a.splits ? a.splits : choose_splits(a.batch, a.num_kv_heads, a.max_pages);
+  if (a.splits < 0 || a.splits > kMaxSplits) return set_error(KVZ_EINVAL, "splits out of range");
+  const int S = a.splits ? a.splits : choose_splits(a.batch, a.num_kv_heads, a.max_pages, device_cus());
   uint64_t ml_bytes, need;
   workspace_layout(a.batch, a.num_q_heads, a.num_kv_heads, S, &ml_bytes, &need);
   if (a.workspace_bytes < need) return set_error(KVZ_EINVAL, "workspace too small");
@@ -501,7 +554,8 @@ int launch_attention(const CommonArgs& a, const uint8_t* kv, const kvz_group_met
     hipLaunchKernelGGL((attn_split_kernel<16, COMP>), grid, dim3(256), 0, s, p);
   int rc = check_hip(hipGetLastError(), "attention launch");
   if (rc != KVZ_OK || S == 1) return rc;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.batch * a.num_q_heads)), dim3(128), 0, s,
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.batch * a.num_q_heads)),
+                     dim3(kCombineThreads), 0, s,
                      p.ws_ml, p.ws_o, a.out, a.seq_lens, p.Hq, p.Hkv, G, S);
   return check_hip(hipGetLastError(), "combine launch");
 }
@@ -516,7 +570,8 @@ extern "C" int kvz_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int3
   if (!bytes) return set_error(KVZ_EINVAL, "bytes is null");
   if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_pages < 0 || splits < 0)
     return set_error(KVZ_EINVAL, "bad sizes");
-  const int S = splits ? splits : choose_splits(batch, num_kv_heads, max_pages);
+  if (splits > kMaxSplits) return set_error(KVZ_EINVAL, "splits out of range");
+  const int S = splits ? splits : choose_splits(batch, num_kv_heads, max_pages, device_cus());
   uint64_t ml, total;
   workspace_layout(batch, num_q_heads, num_kv_heads, S, &ml, &total);
   *bytes = total < 256 ? 256 : total;

@@ -132,7 +132,8 @@ typedef struct {
   const uint16_t* tail;         /* device [B][2][Hkv][16][128] BF16, or NULL if no sequence has
                                    tokens past its compressed pages                             */
   int32_t batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages;
-  int32_t splits;               /* pieces of each sequence's pages (split-K); 0 = automatic     */
+  int32_t splits;               /* pieces of each sequence's pages (split-K), 0..4096; 0 =
+                                   automatic (even over the device's CUs)                       */
   float sm_scale;
   void* workspace;              /* device, >= kvz_attn_workspace_bytes(...), 256-B aligned; calls
                                    that share a workspace must be ordered on one stream         */
