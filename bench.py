@@ -221,6 +221,8 @@ def main():
     attn_ms = np.asarray([timed(g_attn.replay, 1) / n_layers for _ in range(args.steps)])
     us_layer = float(np.median(attn_ms)) * 1e3
     us_layer_mean = float(np.mean(attn_ms)) * 1e3
+    # the same samples as 5 consecutive runs: median us/step of each, then their mean and sd
+    run_medians = [float(np.median(c)) * 1e3 * n_layers for c in np.array_split(attn_ms, 5) if len(c)]
     achieved = alg_bytes / (us_layer_mean * 1e-6) / 1e9
     enc_us = timed(g_comp.replay, args.steps) * 1e3
     log(f"fused: {ms_step:.3f} ms/step, attention {us_layer:.1f} us/layer (median), "
@@ -238,6 +240,7 @@ def main():
         del g_base
 
     traffic = committed_traffic()
+    read_peak = stream_read_peak(timed)
     variant = None if args.no_variant else compressible_variant(args, dev, seq_lens, n_comp, ws)
     del g_attn, g_comp
     cpu = None if args.no_cpu_baseline else cpu_baseline(layers)
@@ -263,10 +266,17 @@ def main():
                    "splits": args.splits or "auto", "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic},
+                     "traffic": traffic,
+                     "measured_read_peak": read_peak["GBps"],
+                     "frac_of_measured_read_peak": round(achieved / read_peak["GBps"], 4)},
         "cpu_baseline": cpu,
         "attention_us_per_layer": round(us_layer, 2),
         "attention_us_per_step": round(us_layer_mean * n_layers, 1),
+        "attention_us_per_step_runs": {"medians": [round(x, 1) for x in run_medians],
+                                       "mean": round(float(np.mean(run_medians)), 1),
+                                       "sd": round(float(np.std(run_medians, ddof=1)), 1)
+                                       if len(run_medians) > 1 else 0.0},
+        "stream_read_reference": read_peak,
         "algorithmic_bytes_per_launch": int(alg_bytes),
         "encode_free_us_per_step": round(enc_us, 1),
         "effective_attention_GBps": round(bf16_kv_layer / (us_layer_mean * 1e-6) / 1e9, 1),
@@ -279,6 +289,30 @@ def main():
     }
     print(json.dumps(line), flush=True)
     arena.close()
+
+
+def stream_read_peak(timed):
+    """Practical HBM read ceiling on this device: the library's streaming-read reference kernel
+    (16-byte non-temporal loads, as the page loads) over a 4 GiB buffer, best of a sweep of
+    workgroup counts."""
+    import torch
+    from decode_attention_kvz_amd import kvz
+    buf = torch.ones(1 << 32, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    best, best_wg, sweep = 0.0, 0, {}
+    for per_cu in (1, 2, 4, 8, 16):
+        wg = per_cu * n_cu
+        kvz.kvz_stream_read(buf, sink, wg)
+        ms = timed(lambda: kvz.kvz_stream_read(buf, sink, wg), 10)
+        gbps = buf.numel() / (ms * 1e-3) / 1e9
+        sweep[str(per_cu)] = round(gbps, 1)
+        if gbps > best:
+            best, best_wg = gbps, per_cu
+    del buf
+    log(f"stream read reference: {best:.0f} GB/s ({best_wg} workgroups per CU)")
+    return {"GBps": round(best, 1), "bytes": 1 << 32, "workgroups_per_cu": best_wg,
+            "sweep_GBps_by_workgroups_per_cu": sweep}
 
 
 def committed_traffic():

@@ -20,6 +20,19 @@ int check_hip(hipError_t e, const char* what) {
   return set_error(KVZ_EHIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 }  // namespace kvz
 
 using namespace kvz;

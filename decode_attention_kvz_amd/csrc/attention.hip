@@ -242,7 +242,9 @@ __global__ __launch_bounds__(256, 3) void attn_split_kernel(AttnParams p) {
     // Page i of the chunk: one buffer resource per group (base = the group's first block,
     // size = the group's bytes, so the 4-byte over-read of a compressed block's last chunk is
     // clipped by the hardware), block j at a uniform soffset, each lane at its chunk offset.
-    auto load_page = [&](int i, KV8& r) {
+    // A load that only keeps the loop's shape (`real` false) gets a zero-size resource: the
+    // hardware returns zeros without touching memory.
+    auto load_page = [&](int i, KV8& r, bool real) {
       __amdgpu_buffer_rsrc_t kr, vr;
       uint32_t kt, vt;
       if constexpr (COMP) {
@@ -250,13 +252,13 @@ __global__ __launch_bounds__(256, 3) void attn_split_kernel(AttnParams p) {
         const uint32_t voff = (uint32_t)__builtin_amdgcn_readlane((int)meta_l.z, i);
         kt = (uint32_t)__builtin_amdgcn_readlane((int)meta_l.y, i);
         vt = (uint32_t)__builtin_amdgcn_readlane((int)meta_l.w, i);
-        kr = group_rsrc(p.kv + (size_t)koff * KVZ_GRANULE_BYTES, group_bytes(kt));
-        vr = group_rsrc(p.kv + (size_t)voff * KVZ_GRANULE_BYTES, group_bytes(vt));
+        kr = group_rsrc(p.kv + (size_t)koff * KVZ_GRANULE_BYTES, real ? group_bytes(kt) : 0u);
+        vr = group_rsrc(p.kv + (size_t)voff * KVZ_GRANULE_BYTES, real ? group_bytes(vt) : 0u);
       } else {
         const int phys = __builtin_amdgcn_readlane(phys_l, i);
         const uint8_t* kb = p.kv + ((size_t)phys * 2 * p.Hkv + kvh) * 4096;
-        kr = group_rsrc(kb, 4096);
-        vr = group_rsrc(kb + (size_t)p.Hkv * 4096, 4096);
+        kr = group_rsrc(kb, real ? 4096u : 0u);
+        vr = group_rsrc(kb + (size_t)p.Hkv * 4096, real ? 4096u : 0u);
         kt = vt = 0xFFFFFFFFu;
       }
       uint32_t ks = 0, vs = 0;
@@ -296,18 +298,18 @@ __global__ __launch_bounds__(256, 3) void attn_split_kernel(AttnParams p) {
     };
 
     // Two one-page buffers in a ring: the loads of page i+1 are in flight while page i is
-    // computed.  The loop runs whole rounds of two (past the end a load re-reads the chunk's
-    // last page, an L2 hit that is never computed), so the wait before each compute covers
-    // exactly that page's eight loads.
+    // computed.  The loop runs whole rounds of two (a load past the chunk's end is issued with
+    // a zero-size resource and never computed), so the wait before each compute covers exactly
+    // that page's eight loads.
     const int last = cnt - 1;
     KV8 buf[2];
-    load_page(0, buf[0]);
+    load_page(0, buf[0], true);
     const int rounds = (cnt + 1) / 2;
     for (int r = 0; r < rounds; ++r) {
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const int i = 2 * r + k;
-        load_page(i + 1 < last ? i + 1 : last, buf[k ^ 1]);
+        load_page(i + 1 < last ? i + 1 : last, buf[k ^ 1], i + 1 <= last);
         if (i <= last) process(buf[k], i);
       }
     }
@@ -453,19 +455,6 @@ int choose_splits(int B, int Hkv, int max_pages, int n_cu) {
   if (S > by_pages) S = by_pages;
   if (S > kMaxSplits) S = kMaxSplits;
   return (int)(S < 1 ? 1 : S);
-}
-
-int device_cus() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
 }
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }

@@ -48,6 +48,8 @@ constexpr uint64_t kPoolHdrBytes = 256;
 // Per-thread error text behind kvz_last_error().
 int set_error(int code, const std::string& msg);
 int check_hip(hipError_t e, const char* what);
+// compute units of the current device (cached per device; 256 if the query fails)
+int device_cus();
 
 // ---------------------------------------------------------------------------------------------
 // Device helpers

@@ -229,6 +229,14 @@ int kvz_bf16_decode_attention(const kvz_bf16_attn_args* a, hipStream_t s);
 /* Copy the pool counters to *host_out; synchronizes stream s. */
 int kvz_pool_stats(kvz_pool* p, kvz_pool_stats_t* host_out, hipStream_t s);
 
+/* Measurement reference, not part of the path: read `bytes` of device memory d_buf once
+ * (16-byte non-temporal loads, the page loads' cache policy) with `workgroups` workgroups of
+ * 256 threads (0: four per compute unit).  d_sink: device, 4 bytes, written only when the
+ * XOR of everything read equals a fixed key (it exists so the loads cannot be removed).
+ * d_buf and bytes must be multiples of 16 (KVZ_EINVAL otherwise). */
+int kvz_stream_read(const void* d_buf, uint64_t bytes, uint32_t* d_sink, int32_t workgroups,
+                    hipStream_t s);
+
 #ifdef __cplusplus
 }
 #endif

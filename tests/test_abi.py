@@ -53,3 +53,8 @@ def test_host_side_argument_checks_without_a_gpu():
     assert kvz.kvz_attn_workspace_bytes(16, 32, 8, 512, 16) >= 16 * 8 * 16 * 4 * 130 * 4
     with pytest.raises(kvz.KvzError):
         kvz.kvz_attn_workspace_bytes(-1, 32, 8, 512, 0)
+    # the streaming-read reference rejects bad arguments before anything reaches the device
+    lib = kvz._lib
+    assert lib.kvz_stream_read(None, 16, None, 0, None) == kvz.KVZ_EINVAL
+    assert lib.kvz_stream_read(ctypes.c_void_p(256), 24, ctypes.c_void_p(256), 0, None) == kvz.KVZ_EINVAL
+    assert lib.kvz_stream_read(ctypes.c_void_p(256), 32, ctypes.c_void_p(256), -1, None) == kvz.KVZ_EINVAL
