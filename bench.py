@@ -74,10 +74,12 @@ def baseline_bytes_per_layer() -> float:
             + B * HQ * 128 * 2 + B * HQ * 128 * 4)
 
 
-def build_layers(arena, n_layers, u_max, seed, with_baseline, dev):
-    """Encode n_layers layers of the workload into `arena`; return per-layer device buffers."""
+def build_layers(arena, n_layers, u_max, seed, with_baseline, dev, encode_us=None):
+    """Encode n_layers layers of the workload into `arena` (the prompt's pages, in bulk); return
+    per-layer device buffers.  encode_us, if a list, receives each layer's kvz_encode_pages time
+    (HIP events around the call; item records already on the device)."""
     import torch
-    from decode_attention_kvz_amd import paged, synth
+    from decode_attention_kvz_amd import kvz, paged, synth
     rng = np.random.default_rng(seed)
     layers = []
     t0 = time.time()
@@ -88,7 +90,11 @@ def build_layers(arena, n_layers, u_max, seed, with_baseline, dev):
         meta = paged.new_meta_table(N_PHYS, HKV, device=dev)
         items = paged.page_items(pages, [(b, p) for b in range(B) for p in range(N_COMP)], meta,
                                  block_table.reshape(-1))
-        d_items = paged.encode(arena, items)
+        d_items = torch.from_numpy(np.ascontiguousarray(items)).to(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        kvz.kvz_encode_pages(arena.pool, d_items, N_PHYS * HKV * 2, 0)
+        e1.record()
         store = None
         if with_baseline:
             inv = torch.as_tensor(np.argsort(block_table.reshape(-1)), device=dev)
@@ -98,6 +104,8 @@ def build_layers(arena, n_layers, u_max, seed, with_baseline, dev):
                            q=synth.queries(B, HQ, seed=seed * 1000 + layer, device=dev),
                            out=torch.empty((B, HQ, 128), dtype=torch.float32, device=dev)))
         torch.cuda.synchronize()
+        if encode_us is not None:
+            encode_us.append(e0.elapsed_time(e1) * 1e3)
         del d_items, pages
         if layer % 6 == 5 or layer == n_layers - 1:
             log(f"setup: {layer + 1}/{n_layers} layers encoded (u_max {u_max}, "
@@ -138,7 +146,8 @@ def main():
 
     # ---------------- setup --------------------------------------------------------------
     arena = paged.SlotArena(n_layers * (N_PHYS + B) * HKV * 2 * 4096 + (16 << 20), device=dev)
-    layers = build_layers(arena, n_layers, U_MAX, SEED, not args.no_baseline, dev)
+    enc_layer_us = []
+    layers = build_layers(arena, n_layers, U_MAX, SEED, not args.no_baseline, dev, enc_layer_us)
     seq_lens = torch.full((B,), CTX, dtype=torch.int32, device=dev)
     n_comp = torch.full((B,), N_COMP, dtype=torch.int32, device=dev)
     ws = paged.workspace(B, HQ, HKV, N_COMP, args.splits, device=dev)
@@ -239,6 +248,9 @@ def main():
         log(f"bf16 baseline: {b_us:.1f} us/layer, {b_gbps:.0f} GB/s")
         del g_base
 
+    for L in layers:
+        L.pop("store", None)          # the baseline's stores are no longer needed
+    dfirst = decompress_first(args, arena, layers, seq_lens, n_comp, ws)
     traffic = committed_traffic()
     read_peak = stream_read_peak(timed)
     variant = None if args.no_variant else compressible_variant(args, dev, seq_lens, n_comp, ws)
@@ -285,6 +297,12 @@ def main():
         "bf16_kv_bytes_per_layer": int(bf16_kv_layer),
         "baseline_bf16": baseline,
         "speedup_vs_bf16_kernel": (round(baseline["us_per_layer"] / us_layer, 4) if baseline else None),
+        "decompress_first": dfirst,
+        "fused_speedup_vs_decompress_first": round(dfirst["us_per_layer"] / us_layer, 3),
+        "prefill_encode": {"groups_per_layer": N_PHYS * HKV * 2,
+                           "us_per_layer_median": round(float(np.median(enc_layer_us)), 1),
+                           "input_GBps": round(N_PHYS * HKV * 2 * 4096 /
+                                               (float(np.median(enc_layer_us)) * 1e-6) / 1e9, 1)},
         "compressible_variant": variant,
     }
     print(json.dumps(line), flush=True)
@@ -313,6 +331,56 @@ def stream_read_peak(timed):
     log(f"stream read reference: {best:.0f} GB/s ({best_wg} workgroups per CU)")
     return {"GBps": round(best, 1), "bytes": 1 << 32, "workgroups_per_cu": best_wg,
             "sweep_GBps_by_workgroups_per_cu": sweep}
+
+
+def graph_us_per_layer(run, n_layers, args):
+    """Warm up `run` (a pass over n_layers layers), capture it in a HIP graph and return the
+    median over replays of the event time per layer (us)."""
+    import torch
+    for _ in range(max(args.warmup, 1)):
+        run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(max(args.steps // 5, 3)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3 / n_layers)
+    del g
+    return float(np.median(ts))
+
+
+def decompress_first(args, arena, layers, seq_lens, n_comp, ws):
+    """The pipeline fused attention replaces: per layer, decompress every page of the layer into
+    one reused uncompressed store (kvz_decompress_pages), then the uncompressed attention over
+    it.  Also times the decompression alone."""
+    import torch
+    from decode_attention_kvz_amd import kvz, paged
+    scratch = torch.empty((N_PHYS, 2, HKV, 4, 1024), dtype=torch.uint8, device="cuda")
+
+    def both():
+        for L in layers:
+            paged.decompress_pages(arena, L["meta"], scratch)
+            kvz.kvz_bf16_decode_attention(L["q"], L["out"], scratch, L["block_table"], seq_lens,
+                                          n_comp, L["tail"], SCALE, ws, HKV, args.splits)
+
+    def decomp_only():
+        for L in layers:
+            paged.decompress_pages(arena, L["meta"], scratch)
+
+    n = len(layers)
+    total = graph_us_per_layer(both, n, args)
+    dec = graph_us_per_layer(decomp_only, n, args)
+    del scratch
+    log(f"decompress-first: {total:.1f} us/layer (decompress {dec:.1f})")
+    return {"us_per_layer": round(total, 2), "decompress_us_per_layer": round(dec, 2)}
 
 
 def committed_traffic():
@@ -349,24 +417,10 @@ def compressible_variant(args, dev, seq_lens, n_comp, ws):
                     kvz.kvz_bf16_decode_attention(L["q"], L["out"], L["store"], L["block_table"],
                                                   seq_lens, n_comp, L["tail"], SCALE, ws, HKV,
                                                   args.splits)
-        for _ in range(max(args.warmup, 1)):
-            run()
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            run()
-        g.replay()
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(max(args.steps // 5, 3)):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            g.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1) * 1e3 / VARIANT_LAYERS)
-        res[fused] = float(np.median(ts))
-        del g
+        res[fused] = graph_us_per_layer(run, VARIANT_LAYERS, args)
+    for L in layers:
+        del L["store"]
+    dfirst = decompress_first(args, arena, layers, seq_lens, n_comp, ws)
     arena.close()
     out = {"label": "same shape, u~U[-3,3] per-channel scale (compressible), 8 layers",
            "raw_block_fraction": round(st["live_raw_blocks"] / (st["live_runs"] * 4), 4),
@@ -374,6 +428,8 @@ def compressible_variant(args, dev, seq_lens, n_comp, ws):
            "fused_us_per_layer": round(res[True], 2),
            "fused_achieved_GBps": round(alg_bytes_per_layer(rec) / (res[True] * 1e-6) / 1e9, 1),
            "bf16_us_per_layer": round(res[False], 2),
+           "decompress_first": dfirst,
+           "fused_speedup_vs_decompress_first": round(dfirst["us_per_layer"] / res[True], 3),
            "speedup_vs_bf16_kernel": round(res[False] / res[True], 4)}
     log(f"compressible variant: fused {res[True]:.1f} us/layer vs bf16 {res[False]:.1f} "
         f"(raw fraction {out['raw_block_fraction']})")

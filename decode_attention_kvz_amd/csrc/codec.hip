@@ -7,6 +7,10 @@
 // put each lane's eight MFMA values together, and 8-byte group metadata.  The encoder runs at
 // page completion, once per page ("GAAC: ...", section "Block-Wise Compression Scheduling").
 //
+// kvz_decompress_pages rebuilds whole pages into the uncompressed layout: the decompress-first
+// pipeline that the fused attention is compared against ("GAAC: ...", section "Attention Time
+// Breakdown", Table 5, the decompress-first column).
+//
 // kvz_encode_pages = classify (one wave per item) -> allocate (pool.hip, one workgroup, item
 // order) -> pack (one wave per item).  The item's metadata slot carries the tags from classify
 // to allocate and the offset from allocate to pack, so the encoder needs no scratch memory.
@@ -179,6 +183,52 @@ __global__ __launch_bounds__(256) void bf16_pack_kernel(const uint16_t* src, uin
   *reinterpret_cast<uint4*>(dst + g * 4096 + j * 1024 + kRawChunkBytes * lane) = w;
 }
 
+// Decompress-first: every group of a page table rebuilt into the baseline's page layout
+// [page][K|V][kv head][4 blocks][64 chunks][16 B].  One wave per group; each lane loads its
+// chunk of the four blocks (16 bytes through a buffer resource sized to the group, so the
+// 12-byte compressed chunks need no tail handling) and writes 4 x 16 bytes.
+__global__ __launch_bounds__(256) void decompress_pages_kernel(const uint8_t* arena,
+                                                               uint64_t arena_bytes,
+                                                               const kvz_group_meta* meta,
+                                                               int64_t n_groups, int hkv,
+                                                               uint8_t* dst) {
+  const int lane = threadIdx.x & 63;
+  const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // output group index
+  if (g >= n_groups) return;
+  const int64_t page = g / (2 * hkv);
+  const int rem = (int)(g % (2 * hkv));
+  const int kind = rem / hkv, kvh = rem % hkv;
+  const kvz_group_meta m = meta[(page * hkv + kvh) * 2 + kind];
+  const uint32_t tags = *reinterpret_cast<const uint32_t*>(m.tag);
+  uint32_t bytes = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) bytes += block_bytes((tags >> (8 * j)) & 0xFFu);
+  const uint64_t start = (uint64_t)m.off * KVZ_GRANULE_BYTES;
+  uint4* out = reinterpret_cast<uint4*>(dst + g * 4096 + kRawChunkBytes * lane);
+  if (m.off == KVZ_OFF_NONE || start + bytes > arena_bytes) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j * 64] = make_uint4(0, 0, 0, 0);
+    return;
+  }
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(arena + start), 0, (int)bytes, 0x00020000);
+  uint4 c[4];
+  uint32_t so = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bool raw = ((tags >> (8 * j)) & 0xFFu) == KVZ_RAW_TAG;
+    c[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         r, (int)(raw ? kRawChunkBytes * lane : kCompChunkBytes * lane),
+                                         (int)so, 2));
+    so += raw ? kRawBlockBytes : kCompBlockBytes;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t tag = (tags >> (8 * j)) & 0xFFu;
+    out[j * 64] = tag == KVZ_RAW_TAG ? c[j] : restore_chunk(c[j].x, c[j].y, c[j].z, tag * 0x01010101u);
+  }
+}
+
 }  // namespace
 }  // namespace kvz
 
@@ -226,4 +276,20 @@ extern "C" int kvz_bf16_pack_pages(const uint16_t* d_src, uint8_t* d_dst, int64_
   hipLaunchKernelGGL(bf16_pack_kernel, dim3((unsigned)grid), dim3(256), 0, s, d_src, d_dst,
                      n_groups, (int)num_kv_heads);
   return check_hip(hipGetLastError(), "bf16 pack launch");
+}
+
+extern "C" int kvz_decompress_pages(const void* d_arena, uint64_t arena_bytes,
+                                    const kvz_group_meta* d_meta, int64_t n_pages,
+                                    int32_t num_kv_heads, uint8_t* d_dst, hipStream_t s) {
+  if (n_pages < 0 || num_kv_heads <= 0) return set_error(KVZ_EINVAL, "bad sizes");
+  if (n_pages == 0) return KVZ_OK;
+  if (!d_arena || !d_meta || !d_dst) return set_error(KVZ_EINVAL, "null pointer argument");
+  if ((((uintptr_t)d_meta) & 7u) || (((uintptr_t)d_dst) & 15u))
+    return set_error(KVZ_EINVAL, "meta must be 8-byte and dst 16-byte aligned");
+  const int64_t n_groups = n_pages * 2 * num_kv_heads;
+  const int64_t grid = (n_groups + 3) / 4;
+  if (grid > 0x7FFFFFFF) return set_error(KVZ_EINVAL, "too many pages for one call");
+  hipLaunchKernelGGL(decompress_pages_kernel, dim3((unsigned)grid), dim3(256), 0, s,
+                     (const uint8_t*)d_arena, arena_bytes, d_meta, n_groups, (int)num_kv_heads, d_dst);
+  return check_hip(hipGetLastError(), "decompress launch");
 }

@@ -37,7 +37,7 @@ EXPORTED = [
     "kvz_version", "kvz_last_error", "kvz_device_check", "kvz_pool_state_bytes", "kvz_pool_init",
     "kvz_pool_destroy", "kvz_slot_alloc", "kvz_slot_free", "kvz_encode_pages", "kvz_decode_block",
     "kvz_attn_workspace_bytes", "kvz_decode_attention", "kvz_bf16_pack_pages",
-    "kvz_bf16_decode_attention", "kvz_pool_stats", "kvz_stream_read",
+    "kvz_bf16_decode_attention", "kvz_pool_stats", "kvz_stream_read", "kvz_decompress_pages",
 ]
 
 
@@ -104,6 +104,8 @@ _sig = {
     "kvz_bf16_decode_attention": ([ctypes.POINTER(Bf16AttnArgs), _vp], ctypes.c_int),
     "kvz_pool_stats": ([_vp, ctypes.POINTER(PoolStats), _vp], ctypes.c_int),
     "kvz_stream_read": ([_vp, ctypes.c_uint64, _vp, ctypes.c_int32, _vp], ctypes.c_int),
+    "kvz_decompress_pages": ([_vp, ctypes.c_uint64, _vp, ctypes.c_int64, ctypes.c_int32, _vp, _vp],
+                             ctypes.c_int),
 }
 for _name, (_args, _ret) in _sig.items():
     _f = getattr(_lib, _name)
@@ -233,6 +235,15 @@ def kvz_pool_stats(pool, stream=None) -> dict:
             "free_runs": list(st.free_runs), "live_runs": st.live_runs,
             "live_granules": st.live_granules, "live_raw_blocks": st.live_raw_blocks,
             "enospc": st.enospc, "bad_frees": st.bad_frees}
+
+
+def kvz_decompress_pages(arena, meta, dst, stream=None) -> None:
+    """meta: [n_pages, Hkv, 2, 8] uint8; dst: n_pages * 2 * Hkv * 4096 bytes."""
+    n_pages, hkv = meta.shape[0], meta.shape[1]
+    if dst.numel() * dst.element_size() < n_pages * 2 * hkv * 4096:
+        raise ValueError("dst too small")
+    _check(_lib.kvz_decompress_pages(_ptr(arena), arena.numel() * arena.element_size(), _ptr(meta),
+                                     n_pages, hkv, _ptr(dst), _stream(stream)))
 
 
 def kvz_stream_read(buf, sink, workgroups: int = 0, stream=None) -> None:

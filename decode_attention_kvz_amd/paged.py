@@ -100,6 +100,16 @@ def pack_bf16_pages(pages_by_phys: torch.Tensor) -> torch.Tensor:
     return dst
 
 
+def decompress_pages(arena: "SlotArena", meta: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Decompress-first: every group of the meta table [n_phys, Hkv, 2, 8] rebuilt into the
+    baseline page store [n_phys, 2, Hkv, 4, 1024] uint8 (kvz_decompress_pages)."""
+    n, hkv = meta.shape[0], meta.shape[1]
+    if out is None:
+        out = torch.empty((n, 2, hkv, 4, 1024), dtype=torch.uint8, device=meta.device)
+    kvz.kvz_decompress_pages(arena.arena, meta, out)
+    return out
+
+
 def workspace(batch: int, num_q_heads: int, num_kv_heads: int, max_pages: int, splits: int = 0,
               device="cuda") -> torch.Tensor:
     nbytes = kvz.kvz_attn_workspace_bytes(batch, num_q_heads, num_kv_heads, max_pages, splits)

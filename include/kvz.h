@@ -207,6 +207,16 @@ int kvz_encode_pages(kvz_pool* p, const kvz_encode_item* d_items, int32_t n, uin
 int kvz_decode_block(const void* d_arena, uint64_t arena_bytes, const kvz_block_ref* d_refs,
                      int32_t n, uint16_t* d_out, hipStream_t s);
 
+/* Decompress-first: rebuild every group of n_pages physical pages (d_meta: device
+ * [n_pages][Hkv][2] (K then V), as for kvz_decode_attention) into the baseline's page layout,
+ * d_dst device [n_pages][2][Hkv][4][64][16 B] (byte-identical to kvz_bf16_pack_pages of the
+ * natural pages), for kvz_bf16_decode_attention.  The decompress-then-attend pipeline that
+ * fused attention replaces ([GAAC] section "Attention Time Breakdown", Table 5; [ZF] "What it
+ * claims").  A group that is not stored, or does not lie inside arena_bytes, becomes zeros.
+ * d_meta 8-byte and d_dst 16-byte aligned (KVZ_EINVAL otherwise). */
+int kvz_decompress_pages(const void* d_arena, uint64_t arena_bytes, const kvz_group_meta* d_meta,
+                         int64_t n_pages, int32_t num_kv_heads, uint8_t* d_dst, hipStream_t s);
+
 /* Workspace bytes kvz_decode_attention / kvz_bf16_decode_attention need for these sizes
  * (splits = 0: the automatic choice for max_pages). */
 int kvz_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
