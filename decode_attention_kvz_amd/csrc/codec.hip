@@ -101,14 +101,15 @@ __global__ __launch_bounds__(256) void classify_kernel(const kvz_encode_item* it
 
 // Step 3: write the four blocks of each placed item at off*256 + prefix sizes.
 __global__ __launch_bounds__(256) void pack_kernel(const kvz_encode_item* items, int n,
-                                                   uint8_t* arena) {
+                                                   uint8_t* arena, uint64_t capacity) {
   const int lane = threadIdx.x & 63;
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= n) return;
   const kvz_encode_item it = items[item];
   const uint32_t off = it.dst->off;
-  if (off == KVZ_OFF_NONE) return;
   const uint32_t tags = *reinterpret_cast<const uint32_t*>(it.dst->tag);
+  // an offset only comes from the allocator; the run must still lie inside the pool
+  if (off == KVZ_OFF_NONE || (uint64_t)off + run_granules(n_raw_of(tags)) > capacity) return;
   const bool aligned = ((((uintptr_t)it.src) & 15u) == 0) && ((it.src_stride & 7u) == 0);
   uint8_t* blk = arena + (size_t)off * KVZ_GRANULE_BYTES;
 #pragma unroll
@@ -247,7 +248,8 @@ extern "C" int kvz_encode_pages(kvz_pool* p, const kvz_encode_item* d_items, int
   if (rc != KVZ_OK) return rc;
   rc = launch_alloc_for_items(p, d_items, n, s);
   if (rc != KVZ_OK) return rc;
-  hipLaunchKernelGGL(pack_kernel, dim3(grid), dim3(256), 0, s, d_items, (int)n, (uint8_t*)p->arena);
+  hipLaunchKernelGGL(pack_kernel, dim3(grid), dim3(256), 0, s, d_items, (int)n, (uint8_t*)p->arena,
+                     p->capacity);
   return check_hip(hipGetLastError(), "pack launch");
 }
 

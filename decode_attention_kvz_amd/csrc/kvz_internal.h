@@ -110,4 +110,5 @@ struct kvz_pool {
   uint64_t state_bytes;
   uint64_t capacity;
   int device;
+  void* scratch;   // device: per-tile counts of the allocation / free passes (in the state buffer)
 };

@@ -8,9 +8,12 @@
 // in one layer is reused by another).  A group with n_raw raw blocks takes 12 + n_raw granules
 // of 256 B (768-B and 1024-B slots).
 //
-// Both kernels run as ONE workgroup of 512 threads that walks the items in passes of 4096 (8
-// consecutive items per thread), so the result depends only on item order: the i-th item of
-// bin k pops the bin from the top, frontier requests get prefix-summed offsets.
+// Allocation and free follow item order exactly (the i-th item of class k pops bin k from the
+// top, or pushes onto it; frontier requests get prefix-summed offsets), computed in parallel as
+// a three-pass scan over tiles of 4096 items: count the classes per tile, scan the tiles in one
+// workgroup, then assign (or push) per tile.  Calls of more than kMaxTiles tiles run as
+// consecutive chunks.  The per-tile counts and bases live in a fixed scratch area of the pool
+// state, so the pool needs no memory beyond the state the caller allocated.
 #include "kvz_internal.h"
 
 #include <algorithm>
@@ -22,7 +25,20 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 
-constexpr int kIpt = 8;   // items per thread per pass: the loads of 4096 items are in flight together
+constexpr int kIpt = 8;   // items per thread: the loads of a tile's 4096 items are in flight together
+constexpr int kTile = kThreads * kIpt;
+constexpr int kMaxTiles = 2 * kThreads;   // tiles per chunk: the scan pass takes 2 per thread
+constexpr int kChunkItems = kTile * kMaxTiles;
+
+// Scratch of the three passes (after the bins in the state buffer).
+struct PoolScratch {
+  uint32_t tile_cnt[kMaxTiles][kBins];    // items of each class in the tile
+  uint32_t tile_base[kMaxTiles][kBins];   // rank of the tile's first item of each class
+  uint64_t tile_fbase[kMaxTiles];         // frontier granules requested by earlier tiles
+  uint64_t snap_cnt[kBins];               // bin counts when the chunk started
+  uint64_t pend;                          // frontier + all requests of the call so far
+  uint64_t f_chunk;                       // `pend` when this chunk started
+};
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const uint32_t lane = threadIdx.x & 63u;
@@ -103,211 +119,304 @@ struct EncodeItemAccess {
   __device__ void set_off(int i, uint32_t o) const { items[i].dst->off = o; }
 };
 
-// Allocation in item order.  A pass covers 4096 items; thread t owns items 8t..8t+7 of it, so
-// "earlier in item order" = earlier thread, or the same thread and a smaller index.
-template <class Access>
-__global__ __launch_bounds__(kThreads) void pool_alloc_kernel(PoolHdr* hdr, uint32_t* bins,
-                                                              Access acc, int n) {
-  __shared__ ScanShared sh;
-  __shared__ uint64_t s_red[kWaves];
-  __shared__ uint64_t s_cnt[kBins], s_base[kBins];   // bin state, uniform over the block
-  __shared__ uint32_t s_ktot[kBins];
-  if (hdr->magic != kPoolMagic) return;   // host checked; never write through a bad state
-
-  const uint64_t cap = hdr->capacity;
-  const uint64_t f0 = hdr->frontier;
-  if (threadIdx.x < kBins) {
-    s_cnt[threadIdx.x] = hdr->bin_cnt[threadIdx.x];
-    s_base[threadIdx.x] = hdr->bin_base[threadIdx.x];
+// Free requests: a pointer to a group's metadata; a null pointer or an unstored group is no
+// request (class -1), but its metadata is still cleared.
+struct FreeAccess {
+  kvz_group_meta* const* metas;
+  __device__ int cls(int i) const {
+    const kvz_group_meta* m = metas[i];
+    if (!m) return -1;
+    const uint2 rec = *reinterpret_cast<const uint2*>(m);
+    return rec.x == KVZ_OFF_NONE ? -1 : (int)n_raw_of(rec.y);
   }
-  __syncthreads();
-  uint64_t pending = 0;   // sizes of this call's frontier requests so far (granted or not)
-  uint64_t my_granted = 0, my_runs = 0, my_gran = 0, my_raw = 0, my_fail = 0;
+};
 
-  for (int pass = 0; pass < n; pass += kThreads * kIpt) {
-    const int first = pass + (int)threadIdx.x * kIpt;
-    uint32_t tags[kIpt];
+template <class Access>
+__device__ __forceinline__ int alloc_cls(const Access& acc, int i) {
+  return (int)n_raw_of(acc.get_tags(i));
+}
+template <>
+__device__ __forceinline__ int alloc_cls<FreeAccess>(const FreeAccess& acc, int i) {
+  return acc.cls(i);
+}
+
+// Items of one tile (kTile consecutive items; thread t owns 8t..8t+7) by class, with each
+// item's rank among the same-class items of its thread.
+struct TileItems {
+  int key[kIpt];
+  uint32_t lrank[kIpt];
+  uint32_t lcnt[kBins];
+};
+
+template <class Access>
+__device__ __forceinline__ void tile_classes(const Access& acc, int i0, int n_end, TileItems& t) {
 #pragma unroll
-    for (int sub = 0; sub < kIpt; ++sub) tags[sub] = first + sub < n ? acc.get_tags(first + sub) : 0u;
-    // ranks among same-size items: local prefix, then across threads
-    int key[kIpt];
-    uint32_t lrank[kIpt];
-    uint32_t lcnt[kBins] = {0, 0, 0, 0, 0};
+  for (int k = 0; k < kBins; ++k) t.lcnt[k] = 0;
 #pragma unroll
-    for (int sub = 0; sub < kIpt; ++sub) {
-      key[sub] = first + sub < n ? (int)n_raw_of(tags[sub]) : -1;
-      lrank[sub] = 0;
+  for (int sub = 0; sub < kIpt; ++sub) t.key[sub] = i0 + sub < n_end ? alloc_cls(acc, i0 + sub) : -1;
+#pragma unroll
+  for (int sub = 0; sub < kIpt; ++sub) {
+    t.lrank[sub] = 0;
+#pragma unroll
+    for (int k = 0; k < kBins; ++k) {
+      if (t.key[sub] == k) {
+        t.lrank[sub] = t.lcnt[k];
+        t.lcnt[k] += 1;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t pick(const uint32_t (&v)[kBins], int k) {
+  uint32_t r = v[0];
+#pragma unroll
+  for (int j = 1; j < kBins; ++j) r = (k == j) ? v[j] : r;
+  return r;
+}
+
+// Pass 1 (one workgroup per tile): items of each class in the tile.
+template <class Access>
+__global__ __launch_bounds__(kThreads) void pool_count_kernel(const PoolHdr* hdr, PoolScratch* sc,
+                                                              Access acc, int first, int n_end) {
+  __shared__ ScanShared sh;
+  if (hdr->magic != kPoolMagic) return;   // host checked; never write through a bad state
+  const int tile = blockIdx.x;
+  TileItems t;
+  tile_classes(acc, first + tile * kTile + (int)threadIdx.x * kIpt, n_end, t);
+  uint32_t ex[kBins], tot[kBins];
+  block_scan_cols<kBins>(t.lcnt, ex, tot, sh.wave, sh.pre, sh.tot);
+  if (threadIdx.x < kBins) sc->tile_cnt[tile][threadIdx.x] = pick(tot, (int)threadIdx.x);
+}
+
+// Pass 2 (one workgroup): scan over the tiles (2 per thread).  Gives each tile the rank of its
+// first item of every class; for allocation, also the granules that earlier tiles request
+// from the frontier (an item of class k asks the frontier iff its rank >= the bin's count).
+// Updates the bin counts for the whole chunk and keeps the counts it started from.
+template <bool ALLOC>
+__global__ __launch_bounds__(kThreads) void pool_scan_kernel(PoolHdr* hdr, PoolScratch* sc,
+                                                             int n_tiles, int first_chunk) {
+  __shared__ ScanShared sh;
+  if (hdr->magic != kPoolMagic) return;
+  const int t0 = 2 * (int)threadIdx.x, t1 = t0 + 1;
+  uint64_t cnt[kBins];
+#pragma unroll
+  for (int k = 0; k < kBins; ++k) cnt[k] = hdr->bin_cnt[k];
+  const uint64_t pend = ALLOC ? (first_chunk ? hdr->frontier : sc->pend) : 0;
+  uint32_t c0[kBins], c1[kBins], v[kBins];
+#pragma unroll
+  for (int k = 0; k < kBins; ++k) {
+    c0[k] = t0 < n_tiles ? sc->tile_cnt[t0][k] : 0u;
+    c1[k] = t1 < n_tiles ? sc->tile_cnt[t1][k] : 0u;
+    v[k] = c0[k] + c1[k];
+  }
+  uint32_t b0[kBins], tot[kBins];
+  block_scan_cols<kBins>(v, b0, tot, sh.wave, sh.pre, sh.tot);   // its barriers order the reads above
+  uint32_t b1[kBins];
+#pragma unroll
+  for (int k = 0; k < kBins; ++k) b1[k] = b0[k] + c0[k];
+  if (t0 < n_tiles) {
+#pragma unroll
+    for (int k = 0; k < kBins; ++k) sc->tile_base[t0][k] = b0[k];
+  }
+  if (t1 < n_tiles) {
+#pragma unroll
+    for (int k = 0; k < kBins; ++k) sc->tile_base[t1][k] = b1[k];
+  }
+  if constexpr (ALLOC) {
+    auto frontier_granules = [&](const uint32_t (&base)[kBins], const uint32_t (&c)[kBins]) {
+      uint32_t g = 0;
 #pragma unroll
       for (int k = 0; k < kBins; ++k) {
-        if (key[sub] == k) {
-          lrank[sub] = lcnt[k];
-          lcnt[k] += 1;
-        }
+        const uint64_t lo = base[k] > cnt[k] ? base[k] : cnt[k];
+        const uint64_t hi = (uint64_t)base[k] + c[k];
+        if (hi > lo) g += (uint32_t)(hi - lo) * run_granules((uint32_t)k);
       }
-    }
-    uint32_t kbase[kBins], ktot[kBins];
-    block_scan_cols<kBins>(lcnt, kbase, ktot, sh.wave, sh.pre, sh.tot);
+      return g;
+    };
+    const uint32_t f0 = t0 < n_tiles ? frontier_granules(b0, c0) : 0u;
+    const uint32_t f1 = t1 < n_tiles ? frontier_granules(b1, c1) : 0u;
+    uint32_t fv[1] = {f0 + f1}, fex[1], ftot[1];
+    block_scan_cols<1>(fv, fex, ftot, sh.wave, sh.pre, sh.tot);
+    if (t0 < n_tiles) sc->tile_fbase[t0] = fex[0];
+    if (t1 < n_tiles) sc->tile_fbase[t1] = (uint64_t)fex[0] + f0;
     if (threadIdx.x == 0) {
-#pragma unroll
-      for (int k = 0; k < kBins; ++k) s_ktot[k] = ktot[k];
+      sc->f_chunk = pend;
+      sc->pend = pend + ftot[0];
     }
-    // pop the bin while it lasts, else ask the frontier
-    uint64_t off[kIpt];
-    bool from_bin[kIpt];
-    uint32_t zoff[kIpt];
-    uint32_t lz[1] = {0};
-#pragma unroll
-    for (int sub = 0; sub < kIpt; ++sub) {
-      const int k = key[sub];
-      from_bin[sub] = false;
-      off[sub] = KVZ_OFF_NONE;
-      zoff[sub] = lz[0];
-      if (k >= 0) {
-        uint32_t kb = kbase[0];
-#pragma unroll
-        for (int j = 1; j < kBins; ++j) kb = (k == j) ? kbase[j] : kb;
-        const uint64_t rank = (uint64_t)kb + lrank[sub];
-        const uint64_t ck = s_cnt[k];
-        if (rank < ck) {
-          from_bin[sub] = true;
-          off[sub] = s_base[k] + ck - 1 - rank;   // bin slot, read below
-        } else {
-          lz[0] += run_granules((uint32_t)k);
-        }
-      }
-    }
-    uint32_t zbase[1], ztot[1];
-    block_scan_cols<1>(lz, zbase, ztot, sh.wave, sh.pre, sh.tot);
-#pragma unroll
-    for (int sub = 0; sub < kIpt; ++sub) {
-      const int k = key[sub];
-      if (k < 0) continue;
-      if (!from_bin[sub]) {
-        const uint32_t z = run_granules((uint32_t)k);
-        const uint64_t start = f0 + pending + zbase[0] + zoff[sub];
-        if (start + z <= cap) {
-          off[sub] = start;
-          my_granted += z;
-        }
-      }
-      if (from_bin[sub] || off[sub] != KVZ_OFF_NONE) {
-        my_runs += 1;
-        my_gran += run_granules((uint32_t)k);
-        my_raw += (uint32_t)k;
-      } else {
-        my_fail += 1;
-      }
-    }
-#pragma unroll
-    for (int sub = 0; sub < kIpt; ++sub)
-      if (from_bin[sub]) off[sub] = bins[off[sub]];
-#pragma unroll
-    for (int sub = 0; sub < kIpt; ++sub)
-      if (key[sub] >= 0) acc.set_off(first + sub, (uint32_t)off[sub]);
-    pending += ztot[0];
-    __syncthreads();
-    if (threadIdx.x < kBins) {
-      const uint64_t c = s_cnt[threadIdx.x], t = s_ktot[threadIdx.x];
-      s_cnt[threadIdx.x] = c - (t < c ? t : c);
-    }
-    __syncthreads();
   }
+  if (threadIdx.x < kBins) {
+    const int k = (int)threadIdx.x;
+    const uint64_t tk = pick(tot, k);
+    sc->snap_cnt[k] = cnt[k];
+    if (ALLOC) {
+      hdr->bin_cnt[k] = cnt[k] - (tk < cnt[k] ? tk : cnt[k]);
+    } else {
+      const uint64_t c = cnt[k] + tk;
+      hdr->bin_cnt[k] = c < hdr->bin_cap[k] ? c : hdr->bin_cap[k];
+    }
+  }
+}
+
+__device__ __forceinline__ void add_u64(uint64_t* p, uint64_t v) {
+  if (v) atomicAdd(reinterpret_cast<unsigned long long*>(p), (unsigned long long)v);
+}
+
+// Pass 3 of allocation (one workgroup per tile): rank r of an item among its class: r < the
+// bin's count pops the bin from the top; otherwise the frontier request starts after every
+// earlier request of the call (granted or not) and is granted iff it ends within capacity.
+template <class Access>
+__global__ __launch_bounds__(kThreads) void pool_alloc_assign_kernel(PoolHdr* hdr,
+                                                                     const uint32_t* bins,
+                                                                     const PoolScratch* sc,
+                                                                     Access acc, int first,
+                                                                     int n_end) {
+  __shared__ ScanShared sh;
+  __shared__ uint64_t s_red[kWaves];
+  if (hdr->magic != kPoolMagic) return;
+  const int tile = blockIdx.x;
+  const int i0 = first + tile * kTile + (int)threadIdx.x * kIpt;
+  TileItems t;
+  tile_classes(acc, i0, n_end, t);
+  uint32_t kbase[kBins], ktot[kBins];
+  block_scan_cols<kBins>(t.lcnt, kbase, ktot, sh.wave, sh.pre, sh.tot);
+  const uint64_t cap = hdr->capacity;
+  uint64_t off[kIpt];
+  bool from_bin[kIpt];
+  uint32_t zoff[kIpt];
+  uint32_t lz[1] = {0};
+#pragma unroll
+  for (int sub = 0; sub < kIpt; ++sub) {
+    const int k = t.key[sub];
+    from_bin[sub] = false;
+    off[sub] = KVZ_OFF_NONE;
+    zoff[sub] = lz[0];
+    if (k >= 0) {
+      const uint64_t rank = (uint64_t)sc->tile_base[tile][k] + pick(kbase, k) + t.lrank[sub];
+      const uint64_t ck = sc->snap_cnt[k];
+      if (rank < ck) {
+        from_bin[sub] = true;
+        off[sub] = hdr->bin_base[k] + ck - 1 - rank;   // bin slot, read below
+      } else {
+        lz[0] += run_granules((uint32_t)k);
+      }
+    }
+  }
+  uint32_t zbase[1], ztot[1];
+  block_scan_cols<1>(lz, zbase, ztot, sh.wave, sh.pre, sh.tot);
+  const uint64_t fstart = sc->f_chunk + sc->tile_fbase[tile] + zbase[0];
+  uint64_t my_granted = 0, my_runs = 0, my_gran = 0, my_raw = 0, my_fail = 0;
+#pragma unroll
+  for (int sub = 0; sub < kIpt; ++sub) {
+    const int k = t.key[sub];
+    if (k < 0) continue;
+    const uint32_t z = run_granules((uint32_t)k);
+    if (!from_bin[sub]) {
+      const uint64_t start = fstart + zoff[sub];
+      if (start + z <= cap) {
+        off[sub] = start;
+        my_granted += z;
+      }
+    }
+    if (from_bin[sub] || off[sub] != KVZ_OFF_NONE) {
+      my_runs += 1;
+      my_gran += z;
+      my_raw += (uint32_t)k;
+    } else {
+      my_fail += 1;
+    }
+  }
+#pragma unroll
+  for (int sub = 0; sub < kIpt; ++sub)
+    if (from_bin[sub]) off[sub] = bins[off[sub]];
+#pragma unroll
+  for (int sub = 0; sub < kIpt; ++sub)
+    if (t.key[sub] >= 0) acc.set_off(i0 + sub, (uint32_t)off[sub]);
   const uint64_t granted = block_sum(my_granted, s_red);
   const uint64_t runs = block_sum(my_runs, s_red);
   const uint64_t gran = block_sum(my_gran, s_red);
   const uint64_t raw = block_sum(my_raw, s_red);
   const uint64_t fail = block_sum(my_fail, s_red);
-  if (threadIdx.x < kBins) hdr->bin_cnt[threadIdx.x] = s_cnt[threadIdx.x];
   if (threadIdx.x == 0) {
-    hdr->frontier = f0 + granted;
-    hdr->live_runs += runs;
-    hdr->live_granules += gran;
-    hdr->live_raw_blocks += raw;
-    hdr->enospc += fail;
+    add_u64(&hdr->frontier, granted);
+    add_u64(&hdr->live_runs, runs);
+    add_u64(&hdr->live_granules, gran);
+    add_u64(&hdr->live_raw_blocks, raw);
+    add_u64(&hdr->enospc, fail);
   }
 }
 
-// Free in item order: item i pushes its run onto bin[n_raw] at position count + rank.
-__global__ __launch_bounds__(kThreads) void pool_free_kernel(PoolHdr* hdr, uint32_t* bins,
-                                                             kvz_group_meta* const* metas, int n) {
+// Pass 3 of free (one workgroup per tile): the i-th freed run of class k in item order goes to
+// bin slot count + i (dropped and counted as a bad free if the bin is full).
+__global__ __launch_bounds__(kThreads) void pool_free_apply_kernel(PoolHdr* hdr, uint32_t* bins,
+                                                                   const PoolScratch* sc,
+                                                                   kvz_group_meta* const* metas,
+                                                                   int first, int n_end) {
   __shared__ ScanShared sh;
   __shared__ uint64_t s_red[kWaves];
-  __shared__ uint64_t s_cnt[kBins], s_base[kBins], s_bcap[kBins];
-  __shared__ uint32_t s_ktot[kBins];
   if (hdr->magic != kPoolMagic) return;
-  if (threadIdx.x < kBins) {
-    s_cnt[threadIdx.x] = hdr->bin_cnt[threadIdx.x];
-    s_base[threadIdx.x] = hdr->bin_base[threadIdx.x];
-    s_bcap[threadIdx.x] = hdr->bin_cap[threadIdx.x];
+  const int tile = blockIdx.x;
+  const int i0 = first + tile * kTile + (int)threadIdx.x * kIpt;
+  kvz_group_meta* m[kIpt];
+  uint2 rec[kIpt];
+#pragma unroll
+  for (int sub = 0; sub < kIpt; ++sub) m[sub] = i0 + sub < n_end ? metas[i0 + sub] : nullptr;
+#pragma unroll
+  for (int sub = 0; sub < kIpt; ++sub)
+    rec[sub] = m[sub] ? *reinterpret_cast<const uint2*>(m[sub]) : make_uint2(KVZ_OFF_NONE, 0u);
+  TileItems t;
+#pragma unroll
+  for (int k = 0; k < kBins; ++k) t.lcnt[k] = 0;
+#pragma unroll
+  for (int sub = 0; sub < kIpt; ++sub) {
+    t.key[sub] = rec[sub].x != KVZ_OFF_NONE ? (int)n_raw_of(rec[sub].y) : -1;
+    t.lrank[sub] = 0;
+#pragma unroll
+    for (int k = 0; k < kBins; ++k) {
+      if (t.key[sub] == k) {
+        t.lrank[sub] = t.lcnt[k];
+        t.lcnt[k] += 1;
+      }
+    }
   }
-  __syncthreads();
+  uint32_t kbase[kBins], ktot[kBins];
+  block_scan_cols<kBins>(t.lcnt, kbase, ktot, sh.wave, sh.pre, sh.tot);
   uint64_t my_runs = 0, my_gran = 0, my_raw = 0, my_bad = 0;
-  for (int pass = 0; pass < n; pass += kThreads * kIpt) {
-    const int first = pass + (int)threadIdx.x * kIpt;
-    kvz_group_meta* m[kIpt];
 #pragma unroll
-    for (int sub = 0; sub < kIpt; ++sub) m[sub] = first + sub < n ? metas[first + sub] : nullptr;
-    uint2 rec[kIpt];
-#pragma unroll
-    for (int sub = 0; sub < kIpt; ++sub)
-      rec[sub] = m[sub] ? *reinterpret_cast<const uint2*>(m[sub]) : make_uint2(KVZ_OFF_NONE, 0u);
-    int key[kIpt];
-    uint32_t lrank[kIpt];
-    uint32_t lcnt[kBins] = {0, 0, 0, 0, 0};
-#pragma unroll
-    for (int sub = 0; sub < kIpt; ++sub) {
-      key[sub] = (m[sub] && rec[sub].x != KVZ_OFF_NONE) ? (int)n_raw_of(rec[sub].y) : -1;
-      lrank[sub] = 0;
-#pragma unroll
-      for (int k = 0; k < kBins; ++k) {
-        if (key[sub] == k) {
-          lrank[sub] = lcnt[k];
-          lcnt[k] += 1;
-        }
+  for (int sub = 0; sub < kIpt; ++sub) {
+    const int k = t.key[sub];
+    if (k >= 0) {
+      const uint64_t slot = sc->snap_cnt[k] + sc->tile_base[tile][k] + pick(kbase, k) + t.lrank[sub];
+      if (slot < hdr->bin_cap[k]) {
+        bins[hdr->bin_base[k] + slot] = rec[sub].x;
+        my_runs += 1;
+        my_gran += run_granules((uint32_t)k);
+        my_raw += (uint32_t)k;
+      } else {
+        my_bad += 1;
       }
     }
-    uint32_t kbase[kBins], ktot[kBins];
-    block_scan_cols<kBins>(lcnt, kbase, ktot, sh.wave, sh.pre, sh.tot);
-    if (threadIdx.x == 0) {
-#pragma unroll
-      for (int k = 0; k < kBins; ++k) s_ktot[k] = ktot[k];
-    }
-#pragma unroll
-    for (int sub = 0; sub < kIpt; ++sub) {
-      const int k = key[sub];
-      if (k >= 0) {
-        uint32_t kb = kbase[0];
-#pragma unroll
-        for (int j = 1; j < kBins; ++j) kb = (k == j) ? kbase[j] : kb;
-        const uint64_t slot = s_cnt[k] + kb + lrank[sub];
-        if (slot < s_bcap[k]) {
-          bins[s_base[k] + slot] = rec[sub].x;
-          my_runs += 1;
-          my_gran += run_granules((uint32_t)k);
-          my_raw += (uint32_t)k;
-        } else {
-          my_bad += 1;
-        }
-      }
-      if (m[sub]) *reinterpret_cast<uint2*>(m[sub]) = make_uint2(KVZ_OFF_NONE, 0u);
-    }
-    __syncthreads();
-    if (threadIdx.x < kBins) {
-      const uint64_t c = s_cnt[threadIdx.x] + s_ktot[threadIdx.x];
-      s_cnt[threadIdx.x] = c < s_bcap[threadIdx.x] ? c : s_bcap[threadIdx.x];
-    }
-    __syncthreads();
   }
   const uint64_t runs = block_sum(my_runs, s_red);
   const uint64_t gran = block_sum(my_gran, s_red);
   const uint64_t raw = block_sum(my_raw, s_red);
   const uint64_t bad = block_sum(my_bad, s_red);
-  if (threadIdx.x < kBins) hdr->bin_cnt[threadIdx.x] = s_cnt[threadIdx.x];
   if (threadIdx.x == 0) {
-    hdr->live_runs -= runs;
-    hdr->live_granules -= gran;
-    hdr->live_raw_blocks -= raw;
-    hdr->bad_frees += bad;
+    add_u64(&hdr->live_runs, 0ull - runs);
+    add_u64(&hdr->live_granules, 0ull - gran);
+    add_u64(&hdr->live_raw_blocks, 0ull - raw);
+    add_u64(&hdr->bad_frees, bad);
+  }
+}
+
+// Pass 4 of free: clear every listed metadata record (after pass 3 has read them all, so a
+// record listed twice is seen the same way by every pass).
+__global__ __launch_bounds__(kThreads) void pool_clear_meta_kernel(kvz_group_meta* const* metas,
+                                                                   int first, int n_end) {
+  const int tile_first = first + (int)blockIdx.x * kTile;
+  const int tile_end = n_end - tile_first < kTile ? n_end : tile_first + kTile;
+  for (int k = tile_first + (int)threadIdx.x; k < tile_end; k += kThreads) {
+    kvz_group_meta* m = metas[k];
+    if (m) *reinterpret_cast<uint2*>(m) = make_uint2(KVZ_OFF_NONE, 0u);
   }
 }
 
@@ -318,6 +427,8 @@ __global__ void pool_init_kernel(PoolHdr* hdr, uint64_t capacity, PoolHdr tmpl) 
   }
 }
 
+uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
 void bin_layout(uint64_t capacity, uint64_t* cap, uint64_t* base, uint64_t* entries) {
   uint64_t at = 0;
   for (int k = 0; k < kBins; ++k) {
@@ -326,6 +437,26 @@ void bin_layout(uint64_t capacity, uint64_t* cap, uint64_t* base, uint64_t* entr
     at += cap[k];
   }
   *entries = at;
+}
+
+template <class Access>
+int run_alloc(kvz_pool* p, Access acc, int n, hipStream_t s) {
+  PoolHdr* hdr = (PoolHdr*)p->state;
+  const uint32_t* bins = (const uint32_t*)((uint8_t*)p->state + kPoolHdrBytes);
+  PoolScratch* sc = (PoolScratch*)p->scratch;
+  for (int first = 0; first < n; first += kChunkItems) {
+    const int n_end = n - first < kChunkItems ? n : first + kChunkItems;
+    const int tiles = (n_end - first + kTile - 1) / kTile;
+    hipLaunchKernelGGL(pool_count_kernel<Access>, dim3(tiles), dim3(kThreads), 0, s, hdr, sc, acc,
+                       first, n_end);
+    hipLaunchKernelGGL(pool_scan_kernel<true>, dim3(1), dim3(kThreads), 0, s, hdr, sc, tiles,
+                       first == 0 ? 1 : 0);
+    hipLaunchKernelGGL(pool_alloc_assign_kernel<Access>, dim3(tiles), dim3(kThreads), 0, s, hdr,
+                       bins, sc, acc, first, n_end);
+    const int rc = check_hip(hipGetLastError(), "slot alloc launch");
+    if (rc != KVZ_OK) return rc;
+  }
+  return KVZ_OK;
 }
 
 int check_pool(const kvz_pool* p) {
@@ -346,7 +477,7 @@ extern "C" int kvz_pool_state_bytes(uint64_t arena_bytes, uint64_t* state_bytes)
   if (capacity >= KVZ_OFF_NONE) return set_error(KVZ_EINVAL, "arena too large for 32-bit granule offsets");
   uint64_t cap[kBins], base[kBins], entries;
   bin_layout(capacity, cap, base, &entries);
-  *state_bytes = kPoolHdrBytes + 4 * entries;
+  *state_bytes = align256(kPoolHdrBytes + 4 * entries) + align256(sizeof(PoolScratch));
   return KVZ_OK;
 }
 
@@ -380,6 +511,7 @@ extern "C" int kvz_pool_init(kvz_pool** out, void* d_arena, uint64_t arena_bytes
   p->state_bytes = state_bytes;
   p->capacity = capacity;
   p->device = dev;
+  p->scratch = (uint8_t*)d_state + align256(kPoolHdrBytes + 4 * entries);
   *out = p;
   return KVZ_OK;
 }
@@ -396,11 +528,7 @@ extern "C" int kvz_slot_alloc(kvz_pool* p, const uint8_t* d_tags, uint32_t* d_of
   if (n < 0) return set_error(KVZ_EINVAL, "n < 0");
   if (n == 0) return KVZ_OK;
   if (!d_tags || !d_off) return set_error(KVZ_EINVAL, "null pointer argument");
-  PoolHdr* hdr = (PoolHdr*)p->state;
-  uint32_t* bins = (uint32_t*)((uint8_t*)p->state + kPoolHdrBytes);
-  hipLaunchKernelGGL(pool_alloc_kernel<TagArrayAccess>, dim3(1), dim3(kThreads), 0, s, hdr, bins,
-                     TagArrayAccess{d_tags, d_off}, (int)n);
-  return check_hip(hipGetLastError(), "slot alloc launch");
+  return run_alloc(p, TagArrayAccess{d_tags, d_off}, (int)n, s);
 }
 
 extern "C" int kvz_slot_free(kvz_pool* p, kvz_group_meta* const* d_metas, int32_t n, hipStream_t s) {
@@ -411,18 +539,29 @@ extern "C" int kvz_slot_free(kvz_pool* p, kvz_group_meta* const* d_metas, int32_
   if (!d_metas) return set_error(KVZ_EINVAL, "null pointer argument");
   PoolHdr* hdr = (PoolHdr*)p->state;
   uint32_t* bins = (uint32_t*)((uint8_t*)p->state + kPoolHdrBytes);
-  hipLaunchKernelGGL(pool_free_kernel, dim3(1), dim3(kThreads), 0, s, hdr, bins, d_metas, (int)n);
-  return check_hip(hipGetLastError(), "slot free launch");
+  PoolScratch* sc = (PoolScratch*)p->scratch;
+  const FreeAccess acc{d_metas};
+  for (int first = 0; first < n; first += kChunkItems) {
+    const int n_end = n - first < kChunkItems ? n : first + kChunkItems;
+    const int tiles = (n_end - first + kTile - 1) / kTile;
+    hipLaunchKernelGGL(pool_count_kernel<FreeAccess>, dim3(tiles), dim3(kThreads), 0, s, hdr, sc,
+                       acc, first, n_end);
+    hipLaunchKernelGGL(pool_scan_kernel<false>, dim3(1), dim3(kThreads), 0, s, hdr, sc, tiles,
+                       first == 0 ? 1 : 0);
+    hipLaunchKernelGGL(pool_free_apply_kernel, dim3(tiles), dim3(kThreads), 0, s, hdr, bins, sc,
+                       d_metas, first, n_end);
+    hipLaunchKernelGGL(pool_clear_meta_kernel, dim3(tiles), dim3(kThreads), 0, s, d_metas, first,
+                       n_end);
+    rc = check_hip(hipGetLastError(), "slot free launch");
+    if (rc != KVZ_OK) return rc;
+  }
+  return KVZ_OK;
 }
 
 namespace kvz {
 // Used by the encoder: the allocation step of kvz_encode_pages.
 int launch_alloc_for_items(kvz_pool* p, const kvz_encode_item* d_items, int n, hipStream_t s) {
-  PoolHdr* hdr = (PoolHdr*)p->state;
-  uint32_t* bins = (uint32_t*)((uint8_t*)p->state + kPoolHdrBytes);
-  hipLaunchKernelGGL(pool_alloc_kernel<EncodeItemAccess>, dim3(1), dim3(kThreads), 0, s, hdr, bins,
-                     EncodeItemAccess{d_items}, n);
-  return check_hip(hipGetLastError(), "encode alloc launch");
+  return run_alloc(p, EncodeItemAccess{d_items}, n, s);
 }
 }  // namespace kvz
 

@@ -313,3 +313,87 @@ def test_tiny_arena_reports_no_room_and_leaves_pages_unstored():
     assert placed.sum() == 4 and (~placed).sum() == 12
     st = arena.stats()
     assert st["enospc"] == 12 and st["live_runs"] == 4
+
+
+def _alloc_and_check(arena, model, tags):
+    d_tags = torch.from_numpy(np.ascontiguousarray(tags)).cuda()
+    d_off = torch.empty(tags.shape[0], dtype=torch.int32, device="cuda")
+    kvz.kvz_slot_alloc(arena.pool, d_tags, d_off)
+    got = d_off.cpu().numpy().view(np.uint32)
+    want = np.asarray(model.alloc(tags.tolist()), dtype=np.uint32)
+    np.testing.assert_array_equal(got, want)
+    return want
+
+
+def _free(arena, model, victims):
+    host = np.zeros((len(victims), 8), dtype=np.uint8)
+    offs = np.asarray([v[0] for v in victims], dtype=np.uint32)
+    host[:, :4] = offs.view(np.uint8).reshape(-1, 4)
+    host[:, 4:] = np.asarray([v[1] for v in victims], dtype=np.uint8)
+    meta = torch.from_numpy(host).cuda()
+    ptrs = torch.from_numpy(meta.data_ptr() + np.arange(len(victims), dtype=np.int64) * 8).cuda()
+    kvz.kvz_slot_free(arena.pool, ptrs)
+    model.free(victims)
+    cleared = meta.cpu().numpy()
+    assert (cleared[:, :4] == 0xFF).all() and (cleared[:, 4:] == 0).all()
+
+
+def _check_stats(arena, model):
+    st = arena.stats()
+    assert st["frontier_granules"] == model.frontier
+    assert st["free_runs"] == [len(model.bins[k]) for k in range(5)]
+    assert st["live_runs"] == model.live_runs
+    assert st["live_granules"] == model.live_granules
+    assert st["live_raw_blocks"] == model.raw_blocks
+    assert st["enospc"] == model.enospc
+
+
+def _random_tags(rng, n, p_raw):
+    tags = np.full((n, 4), 60, dtype=np.uint8)
+    tags[rng.random((n, 4)) < p_raw] = 0xFF
+    return tags
+
+
+def test_slot_pool_calls_spanning_many_tiles_match_model():
+    """Calls of several 4096-item tiles: frontier offsets, bin pops that run out part-way,
+    exhaustion in a later tile, and frees spanning tiles all equal the pool model."""
+    announce("slot pool: multi-tile calls")
+    rng = np.random.default_rng(61)
+    cap_target = 20000 * 14
+    arena = paged.SlotArena((cap_target + 1) * 256)
+    model = SlotPoolModel(arena.stats()["capacity_granules"])
+    tags = _random_tags(rng, 3 * 4096 + 777, 0.2)
+    offs = _alloc_and_check(arena, model, tags)
+    _check_stats(arena, model)
+    live = [(int(o), t.tolist()) for o, t in zip(offs, tags)]
+    order = rng.permutation(len(live))
+    victims = [live[i] for i in order[:6000]]
+    live = [live[i] for i in order[6000:]]
+    _free(arena, model, victims)
+    _check_stats(arena, model)
+    # pops of every class across tiles, some bins run dry, then the frontier runs out
+    tags2 = _random_tags(rng, 5 * 4096 + 100, 0.35)
+    offs2 = _alloc_and_check(arena, model, tags2)
+    _check_stats(arena, model)
+    assert model.enospc > 0 and (offs2 != OFF_NONE).sum() > 6000
+
+
+def test_slot_alloc_call_larger_than_one_chunk_matches_model():
+    """One call of 4 Mi + 5000 items (two chunks of the tiled allocator): bin state and the
+    frontier's request prefix carry from the first chunk into the second."""
+    announce("slot pool: call of more than one chunk")
+    rng = np.random.default_rng(62)
+    arena = paged.SlotArena(400_001 * 256)
+    model = SlotPoolModel(arena.stats()["capacity_granules"])
+    # fill bins 0 and 4
+    seed_tags = np.concatenate([_random_tags(rng, 3000, 0.0), np.full((500, 4), 0xFF, np.uint8)])
+    offs = _alloc_and_check(arena, model, seed_tags)
+    _free(arena, model, [(int(o), t.tolist()) for o, t in zip(offs, seed_tags)])
+    n = 4 * 1024 * 1024 + 5000
+    tags = np.full((n, 4), 60, dtype=np.uint8)
+    tags[rng.random(n) < 0.3, 0] = 0xFF             # classes 0 and 1 only ...
+    late = 4 * 1024 * 1024 + rng.choice(5000, 300, replace=False)
+    tags[late] = 0xFF                                # ... until the second chunk: class 4
+    _alloc_and_check(arena, model, tags)
+    _check_stats(arena, model)
+    assert len(model.bins[4]) == 200                 # 300 of the 500 class-4 runs popped late
