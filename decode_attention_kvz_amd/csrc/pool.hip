@@ -586,3 +586,27 @@ extern "C" int kvz_pool_stats(kvz_pool* p, kvz_pool_stats_t* host_out, hipStream
   host_out->bad_frees = h.bad_frees;
   return KVZ_OK;
 }
+
+extern "C" int kvz_pool_capacity(const kvz_pool_stats_t* st, int32_t num_layers,
+                                 int32_t num_kv_heads, kvz_capacity_t* out) {
+  if (!st || !out) return set_error(KVZ_EINVAL, "null pointer argument");
+  if (num_layers <= 0 || num_kv_heads <= 0) return set_error(KVZ_EINVAL, "bad sizes");
+  const uint64_t frontier_free =
+      st->capacity_granules > st->frontier_granules ? st->capacity_granules - st->frontier_granules : 0;
+  uint64_t binned = 0, min_bin = st->free_runs[0];
+  for (int k = 0; k < kBins; ++k) {
+    binned += st->free_runs[k] * (12u + (uint64_t)k);
+    min_bin = st->free_runs[k] < min_bin ? st->free_runs[k] : min_bin;
+  }
+  const uint64_t groups_per_page = 2ull * (uint64_t)num_kv_heads * (uint64_t)num_layers;
+  out->free_granules = frontier_free + binned;
+  out->guaranteed_groups = frontier_free / 16u + min_bin;
+  out->guaranteed_pages = out->guaranteed_groups / groups_per_page;
+  out->guaranteed_tokens = 16u * out->guaranteed_pages;
+  out->expected_group_granules =
+      st->live_runs ? 12.0 + 4.0 * (double)st->live_raw_blocks / (4.0 * (double)st->live_runs) : 16.0;
+  out->expected_pages = (uint64_t)((double)out->free_granules /
+                                   (out->expected_group_granules * (double)groups_per_page));
+  out->expected_tokens = 16u * out->expected_pages;
+  return KVZ_OK;
+}

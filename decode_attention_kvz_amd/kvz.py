@@ -38,6 +38,7 @@ EXPORTED = [
     "kvz_pool_destroy", "kvz_slot_alloc", "kvz_slot_free", "kvz_encode_pages", "kvz_decode_block",
     "kvz_attn_workspace_bytes", "kvz_decode_attention", "kvz_bf16_pack_pages",
     "kvz_bf16_decode_attention", "kvz_pool_stats", "kvz_stream_read", "kvz_decompress_pages",
+    "kvz_pool_capacity",
 ]
 
 
@@ -52,6 +53,13 @@ class PoolStats(ctypes.Structure):
                 ("free_runs", ctypes.c_uint64 * 5), ("live_runs", ctypes.c_uint64),
                 ("live_granules", ctypes.c_uint64), ("live_raw_blocks", ctypes.c_uint64),
                 ("enospc", ctypes.c_uint64), ("bad_frees", ctypes.c_uint64)]
+
+
+class Capacity(ctypes.Structure):
+    _fields_ = [("free_granules", ctypes.c_uint64), ("guaranteed_groups", ctypes.c_uint64),
+                ("guaranteed_pages", ctypes.c_uint64), ("guaranteed_tokens", ctypes.c_uint64),
+                ("expected_group_granules", ctypes.c_double), ("expected_pages", ctypes.c_uint64),
+                ("expected_tokens", ctypes.c_uint64)]
 
 
 class AttnArgs(ctypes.Structure):
@@ -104,6 +112,8 @@ _sig = {
     "kvz_bf16_decode_attention": ([ctypes.POINTER(Bf16AttnArgs), _vp], ctypes.c_int),
     "kvz_pool_stats": ([_vp, ctypes.POINTER(PoolStats), _vp], ctypes.c_int),
     "kvz_stream_read": ([_vp, ctypes.c_uint64, _vp, ctypes.c_int32, _vp], ctypes.c_int),
+    "kvz_pool_capacity": ([ctypes.POINTER(PoolStats), ctypes.c_int32, ctypes.c_int32,
+                           ctypes.POINTER(Capacity)], ctypes.c_int),
     "kvz_decompress_pages": ([_vp, ctypes.c_uint64, _vp, ctypes.c_int64, ctypes.c_int32, _vp, _vp],
                              ctypes.c_int),
 }
@@ -244,6 +254,19 @@ def kvz_decompress_pages(arena, meta, dst, stream=None) -> None:
         raise ValueError("dst too small")
     _check(_lib.kvz_decompress_pages(_ptr(arena), arena.numel() * arena.element_size(), _ptr(meta),
                                      n_pages, hkv, _ptr(dst), _stream(stream)))
+
+
+def kvz_pool_capacity(stats: dict, num_layers: int, num_kv_heads: int) -> dict:
+    """stats: a kvz_pool_stats result (dict); host arithmetic only."""
+    st = PoolStats()
+    for k in ("capacity_granules", "frontier_granules", "live_runs", "live_granules",
+              "live_raw_blocks", "enospc", "bad_frees"):
+        setattr(st, k, int(stats[k]))
+    for k in range(5):
+        st.free_runs[k] = int(stats["free_runs"][k])
+    cap = Capacity()
+    _check(_lib.kvz_pool_capacity(ctypes.byref(st), num_layers, num_kv_heads, ctypes.byref(cap)))
+    return {name: getattr(cap, name) for name, _ in Capacity._fields_}
 
 
 def kvz_stream_read(buf, sink, workgroups: int = 0, stream=None) -> None:

@@ -239,6 +239,30 @@ int kvz_bf16_decode_attention(const kvz_bf16_attn_args* a, hipStream_t s);
 /* Copy the pool counters to *host_out; synchronizes stream s. */
 int kvz_pool_stats(kvz_pool* p, kvz_pool_stats_t* host_out, hipStream_t s);
 
+/* Capacity left for KV writes, for a scheduler's admission decision ([ZF] "How it works": the
+ * memory manager tracks the space left as pages compress and reports it to the scheduler,
+ * which admits requests while reserving room for running generation).  Host arithmetic on a
+ * kvz_pool_stats result; no device call.  A page here is one 16-token page of every layer:
+ * 2 * num_kv_heads * num_layers groups.
+ *   guaranteed_*: what fits whatever the blocks' classes: a group never takes more than 16
+ *     granules from the frontier, and only a free run of its own n_raw can be reused, so
+ *     floor(unused frontier / 16) + min over bins of the free runs groups always fit.
+ *   expected_*: an estimate - all free granules divided by the mean run size of the live
+ *     groups (12 + 4 * live raw-block fraction; 16 with nothing live).
+ * KVZ_EINVAL for null pointers or num_layers / num_kv_heads <= 0. */
+typedef struct {
+  uint64_t free_granules;            /* unused frontier + every free run's granules             */
+  uint64_t guaranteed_groups;
+  uint64_t guaranteed_pages;
+  uint64_t guaranteed_tokens;        /* 16 * guaranteed_pages                                    */
+  double expected_group_granules;
+  uint64_t expected_pages;
+  uint64_t expected_tokens;          /* 16 * expected_pages                                      */
+} kvz_capacity_t;
+
+int kvz_pool_capacity(const kvz_pool_stats_t* stats, int32_t num_layers, int32_t num_kv_heads,
+                      kvz_capacity_t* out);
+
 /* Measurement reference, not part of the path: read `bytes` of device memory d_buf once
  * (16-byte non-temporal loads, the page loads' cache policy) with `workgroups` workgroups of
  * 256 threads (0: four per compute unit).  d_sink: device, 4 bytes, written only when the

@@ -58,3 +58,32 @@ def test_host_side_argument_checks_without_a_gpu():
     assert lib.kvz_stream_read(None, 16, None, 0, None) == kvz.KVZ_EINVAL
     assert lib.kvz_stream_read(ctypes.c_void_p(256), 24, ctypes.c_void_p(256), 0, None) == kvz.KVZ_EINVAL
     assert lib.kvz_stream_read(ctypes.c_void_p(256), 32, ctypes.c_void_p(256), -1, None) == kvz.KVZ_EINVAL
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="libkvz.so not built")
+def test_pool_capacity_hand_worked():
+    """Capacity report from pool counters (host arithmetic), against numbers worked by hand:
+    capacity 10000 granules, 3000 used from the frontier, free runs [10, 0, 5, 0, 2], 100 live
+    groups holding 40 raw blocks; 2 layers x 4 KV heads -> 16 groups per 16-token page.
+      free = 7000 + (10*12 + 5*14 + 2*16) = 7222 granules
+      guaranteed groups = 7000 // 16 + min(free runs) = 437 + 0 -> 27 pages, 432 tokens
+      expected run = 12 + 4 * 40 / 400 = 12.4 granules -> 7222 / (12.4 * 16) = 36.4 -> 36 pages"""
+    from decode_attention_kvz_amd import kvz
+    st = {"capacity_granules": 10000, "frontier_granules": 3000, "free_runs": [10, 0, 5, 0, 2],
+          "live_runs": 100, "live_granules": 1240, "live_raw_blocks": 40, "enospc": 0,
+          "bad_frees": 0}
+    c = kvz.kvz_pool_capacity(st, 2, 4)
+    assert c["free_granules"] == 7222
+    assert c["guaranteed_groups"] == 437 and c["guaranteed_pages"] == 27
+    assert c["guaranteed_tokens"] == 432
+    assert abs(c["expected_group_granules"] - 12.4) < 1e-12
+    assert c["expected_pages"] == 36 and c["expected_tokens"] == 576
+    # every bin non-empty: the smallest bin adds to the guarantee
+    st["free_runs"] = [10, 3, 5, 7, 2]
+    c = kvz.kvz_pool_capacity(st, 2, 4)
+    assert c["guaranteed_groups"] == 437 + 2
+    # nothing live: assume all-raw runs
+    st.update(live_runs=0, live_raw_blocks=0, live_granules=0)
+    assert kvz.kvz_pool_capacity(st, 1, 1)["expected_group_granules"] == 16.0
+    with pytest.raises(kvz.KvzError):
+        kvz.kvz_pool_capacity(st, 0, 4)

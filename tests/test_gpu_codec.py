@@ -397,3 +397,26 @@ def test_slot_alloc_call_larger_than_one_chunk_matches_model():
     _alloc_and_check(arena, model, tags)
     _check_stats(arena, model)
     assert len(model.bins[4]) == 200                 # 300 of the 500 class-4 runs popped late
+
+
+def test_guaranteed_capacity_always_fits():
+    """After churn that leaves free runs in several bins, as many all-raw groups as the capacity
+    report guarantees are all placed (the worst case for the frontier), and the report's free
+    granules match the pool model."""
+    announce("pool capacity guarantee")
+    rng = np.random.default_rng(63)
+    arena = paged.SlotArena(5001 * 256)
+    model = SlotPoolModel(arena.stats()["capacity_granules"])
+    tags = _random_tags(rng, 250, 0.3)
+    offs = _alloc_and_check(arena, model, tags)
+    _free(arena, model, [(int(o), t.tolist()) for o, t in zip(offs[:120], tags[:120])])
+    st = arena.stats()
+    cap = kvz.kvz_pool_capacity(st, 1, 1)
+    free_model = (model.capacity - model.frontier
+                  + sum(len(model.bins[k]) * (12 + k) for k in range(5)))
+    assert cap["free_granules"] == free_model
+    g = cap["guaranteed_groups"]
+    assert g > 100
+    raw = np.full((g, 4), 0xFF, dtype=np.uint8)
+    got = _alloc_and_check(arena, model, raw)
+    assert (got != OFF_NONE).all()
