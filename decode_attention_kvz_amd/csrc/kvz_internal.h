@@ -71,6 +71,32 @@ __device__ __forceinline__ uint32_t block_bytes(uint32_t tag) {
   return tag == KVZ_RAW_TAG ? kRawBlockBytes : kCompBlockBytes;
 }
 
+// The 8 values of chunk c of block j of a natural page (row stride `stride` elements), packed
+// as 4 dwords (value 2m in the low half of dword m).  K: token c%16, dims 32j+8(c/16)+0..7;
+// V: dim 32j+c%32, tokens 8(c/32)+0..7.
+__device__ __forceinline__ uint4 load_chunk(const uint16_t* src, uint32_t stride, uint32_t kind,
+                                            int j, int c, bool aligned) {
+  uint16_t v[8];
+  if (kind == KVZ_KIND_K) {
+    const uint16_t* p = src + (size_t)(c & 15) * stride + 32 * j + 8 * (c >> 4);
+    if (aligned) {
+      return *reinterpret_cast<const uint4*>(p);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = p[i];
+  } else {
+    const uint16_t* p = src + (size_t)(8 * (c >> 5)) * stride + 32 * j + (c & 31);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = p[(size_t)i * stride];
+  }
+  uint4 r;
+  r.x = (uint32_t)v[0] | ((uint32_t)v[1] << 16);
+  r.y = (uint32_t)v[2] | ((uint32_t)v[3] << 16);
+  r.z = (uint32_t)v[4] | ((uint32_t)v[5] << 16);
+  r.w = (uint32_t)v[6] | ((uint32_t)v[7] << 16);
+  return r;
+}
+
 // Rebuild 8 BF16 values (4 dwords, value 2m in the low half of dword m) from a compressed chunk:
 // lo0/lo1 = low bytes of values 0..3 / 4..7, code = code word, B = (b/2) * 0x01010101.
 __device__ __forceinline__ uint4 restore_chunk(uint32_t lo0, uint32_t lo1, uint32_t code,

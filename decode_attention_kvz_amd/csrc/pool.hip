@@ -110,8 +110,9 @@ struct TagArrayAccess {
   __device__ void set_off(int i, uint32_t o) const { off[i] = o; }
 };
 
-struct EncodeItemAccess {
-  const kvz_encode_item* items;
+template <class Item>
+struct ItemMetaAccess {
+  const Item* items;
   __device__ uint32_t get_tags(int i) const {
     const kvz_group_meta* m = items[i].dst;
     return *reinterpret_cast<const uint32_t*>(m->tag);
@@ -559,9 +560,12 @@ extern "C" int kvz_slot_free(kvz_pool* p, kvz_group_meta* const* d_metas, int32_
 }
 
 namespace kvz {
-// Used by the encoder: the allocation step of kvz_encode_pages.
+// Used by the encoders: the allocation step of kvz_encode_pages and kvz_gaac_encode_pages.
 int launch_alloc_for_items(kvz_pool* p, const kvz_encode_item* d_items, int n, hipStream_t s) {
-  return run_alloc(p, EncodeItemAccess{d_items}, n, s);
+  return run_alloc(p, ItemMetaAccess<kvz_encode_item>{d_items}, n, s);
+}
+int launch_alloc_for_gaac_items(kvz_pool* p, const kvz_gaac_item* d_items, int n, hipStream_t s) {
+  return run_alloc(p, ItemMetaAccess<kvz_gaac_item>{d_items}, n, s);
 }
 }  // namespace kvz
 

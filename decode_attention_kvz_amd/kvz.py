@@ -38,7 +38,7 @@ EXPORTED = [
     "kvz_pool_destroy", "kvz_slot_alloc", "kvz_slot_free", "kvz_encode_pages", "kvz_decode_block",
     "kvz_attn_workspace_bytes", "kvz_decode_attention", "kvz_bf16_pack_pages",
     "kvz_bf16_decode_attention", "kvz_pool_stats", "kvz_stream_read", "kvz_decompress_pages",
-    "kvz_pool_capacity",
+    "kvz_pool_capacity", "kvz_gaac_calibrate", "kvz_gaac_encode_pages", "kvz_gaac_decompress_pages",
 ]
 
 
@@ -91,6 +91,8 @@ class Bf16AttnArgs(ctypes.Structure):
 ENCODE_ITEM_DTYPE = np.dtype([("src", "<u8"), ("dst", "<u8"), ("src_stride", "<u4"),
                               ("kind", "<u4")])
 BLOCK_REF_DTYPE = np.dtype([("meta", "<u8"), ("block", "<u4"), ("kind", "<u4")])
+GAAC_ITEM_DTYPE = np.dtype([("src", "<u8"), ("dst", "<u8"), ("src_stride", "<u4"),
+                            ("kind", "<u4"), ("bases", "<u8")])
 
 _vp = ctypes.c_void_p
 _sig = {
@@ -112,6 +114,10 @@ _sig = {
     "kvz_bf16_decode_attention": ([ctypes.POINTER(Bf16AttnArgs), _vp], ctypes.c_int),
     "kvz_pool_stats": ([_vp, ctypes.POINTER(PoolStats), _vp], ctypes.c_int),
     "kvz_stream_read": ([_vp, ctypes.c_uint64, _vp, ctypes.c_int32, _vp], ctypes.c_int),
+    "kvz_gaac_calibrate": ([_vp, ctypes.c_int32, _vp, _vp, _vp], ctypes.c_int),
+    "kvz_gaac_encode_pages": ([_vp, _vp, ctypes.c_int32, ctypes.c_uint32, _vp], ctypes.c_int),
+    "kvz_gaac_decompress_pages": ([_vp, ctypes.c_uint64, _vp, _vp, ctypes.c_int64, ctypes.c_int32,
+                                   _vp, _vp], ctypes.c_int),
     "kvz_pool_capacity": ([ctypes.POINTER(PoolStats), ctypes.c_int32, ctypes.c_int32,
                            ctypes.POINTER(Capacity)], ctypes.c_int),
     "kvz_decompress_pages": ([_vp, ctypes.c_uint64, _vp, ctypes.c_int64, ctypes.c_int32, _vp, _vp],
@@ -269,6 +275,29 @@ def kvz_pool_capacity(stats: dict, num_layers: int, num_kv_heads: int) -> dict:
     return {name: getattr(cap, name) for name, _ in Capacity._fields_}
 
 
+def kvz_gaac_calibrate(items, n: int, hist, bases, stream=None) -> None:
+    """items: device kvz_encode_item records (pages of one (layer, K|V, KV head)); hist: device
+    >= 128*256 uint32 scratch; bases: device uint8 [2, 128] out (b3, b4)."""
+    if hist.numel() * hist.element_size() < 128 * 256 * 4 or bases.numel() < 256:
+        raise ValueError("hist or bases too small")
+    _check(_lib.kvz_gaac_calibrate(_ptr(items), n, _ptr(hist), _ptr(bases), _stream(stream)))
+
+
+def kvz_gaac_encode_pages(pool, items, n: int, flags: int = 0, stream=None) -> None:
+    """items: device tensor holding n kvz_gaac_item records (GAAC_ITEM_DTYPE)."""
+    _check(_lib.kvz_gaac_encode_pages(pool, _ptr(items), n, flags, _stream(stream)))
+
+
+def kvz_gaac_decompress_pages(arena, meta, bases, dst, stream=None) -> None:
+    """meta: [n_pages, Hkv, 2, 8] uint8; bases: [Hkv, 2, 2, 128] uint8; dst: n_pages*2*Hkv*4096 B."""
+    n_pages, hkv = meta.shape[0], meta.shape[1]
+    if dst.numel() * dst.element_size() < n_pages * 2 * hkv * 4096 or bases.numel() < hkv * 512:
+        raise ValueError("dst or bases too small")
+    _check(_lib.kvz_gaac_decompress_pages(_ptr(arena), arena.numel() * arena.element_size(),
+                                          _ptr(meta), _ptr(bases), n_pages, hkv, _ptr(dst),
+                                          _stream(stream)))
+
+
 def kvz_stream_read(buf, sink, workgroups: int = 0, stream=None) -> None:
     _check(_lib.kvz_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
                                 workgroups, _stream(stream)))
@@ -285,6 +314,18 @@ def encode_items(src_ptrs, dst_ptrs, src_stride, kinds) -> np.ndarray:
     rec["dst"] = np.asarray(dst_ptrs, dtype=np.uint64)
     rec["src_stride"] = src_stride
     rec["kind"] = np.asarray(kinds, dtype=np.uint32)
+    return rec.view(np.uint8)
+
+
+def gaac_items(src_ptrs, dst_ptrs, src_stride, kinds, bases_ptrs) -> np.ndarray:
+    """kvz_gaac_item records as a uint8 array (copy it to the device before the call)."""
+    n = len(src_ptrs)
+    rec = np.zeros(n, dtype=GAAC_ITEM_DTYPE)
+    rec["src"] = np.asarray(src_ptrs, dtype=np.uint64)
+    rec["dst"] = np.asarray(dst_ptrs, dtype=np.uint64)
+    rec["src_stride"] = src_stride
+    rec["kind"] = np.asarray(kinds, dtype=np.uint32)
+    rec["bases"] = np.asarray(bases_ptrs, dtype=np.uint64)
     return rec.view(np.uint8)
 
 

@@ -100,6 +100,57 @@ def pack_bf16_pages(pages_by_phys: torch.Tensor) -> torch.Tensor:
     return dst
 
 
+def gaac_page_items(pages: torch.Tensor, page_ids, meta: torch.Tensor, phys_ids,
+                    bases: torch.Tensor) -> np.ndarray:
+    """kvz_gaac_item records, in page_items order; bases: [Hkv, 2 (K,V), 2 (b3,b4), 128] uint8
+    of this layer (device)."""
+    rec = page_items(pages, page_ids, meta, phys_ids).view(kvz.ENCODE_ITEM_DTYPE)
+    n_kv = pages.shape[3]
+    assert bases.is_contiguous() and tuple(bases.shape) == (n_kv, 2, 2, HEAD_DIM)
+    n = rec.shape[0]
+    h = np.tile(np.repeat(np.arange(n_kv, dtype=np.int64), 2), n // (2 * n_kv))
+    kind = rec["kind"].astype(np.int64)
+    bases_ptr = bases.data_ptr() + (h * 2 + kind) * 256
+    return kvz.gaac_items(rec["src"], rec["dst"], HEAD_DIM, kind, bases_ptr.astype(np.uint64))
+
+
+def gaac_calibrate(pages: torch.Tensor, device="cuda") -> torch.Tensor:
+    """Bases [Hkv, 2, 2, 128] uint8 from calibration pages [n_seq, n_pages, 2, Hkv, 16, 128] bf16
+    (device): one kvz_gaac_calibrate call per (K|V, KV head)."""
+    n_kv = pages.shape[3]
+    assert pages.is_contiguous()
+    bases = torch.zeros((n_kv, 2, 2, HEAD_DIM), dtype=torch.uint8, device=device)
+    hist = torch.empty(128 * 256, dtype=torch.int32, device=device)
+    n_pg = pages.shape[0] * pages.shape[1]
+    keep = []
+    for h in range(n_kv):
+        for kind in range(2):
+            g = (np.arange(n_pg, dtype=np.int64) * 2 + kind) * n_kv + h
+            src = pages.data_ptr() + g * (GROUP_ELEMS * 2)
+            items = torch.from_numpy(kvz.encode_items(src.astype(np.uint64), np.zeros(n_pg, np.uint64),
+                                                      HEAD_DIM, np.full(n_pg, kind))).to(device)
+            keep.append(items)
+            kvz.kvz_gaac_calibrate(items, n_pg, hist, bases[h, kind])
+    torch.cuda.synchronize()
+    return bases
+
+
+def gaac_encode(arena: SlotArena, items: np.ndarray, flags: int = 0, stream=None) -> torch.Tensor:
+    d = torch.from_numpy(np.ascontiguousarray(items)).to(arena.device)
+    n = items.size // kvz.GAAC_ITEM_DTYPE.itemsize
+    kvz.kvz_gaac_encode_pages(arena.pool, d, n, flags, stream)
+    return d
+
+
+def gaac_decompress_pages(arena: SlotArena, meta: torch.Tensor, bases: torch.Tensor,
+                          out: torch.Tensor | None = None) -> torch.Tensor:
+    n, hkv = meta.shape[0], meta.shape[1]
+    if out is None:
+        out = torch.empty((n, 2, hkv, 4, 1024), dtype=torch.uint8, device=meta.device)
+    kvz.kvz_gaac_decompress_pages(arena.arena, meta, bases, out)
+    return out
+
+
 def decompress_pages(arena: "SlotArena", meta: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """Decompress-first: every group of the meta table [n_phys, Hkv, 2, 8] rebuilt into the
     baseline page store [n_phys, 2, Hkv, 4, 1024] uint8 (kvz_decompress_pages)."""

@@ -11,6 +11,8 @@ KV value model (per layer; sigma is per (K|V, KV head, dim) = channel):
   Optional stress values, each element independently: exact +-0 (1%), a subnormal with
   mantissa uniform in 1..127 and random sign (0.5%), exponent 255 with mantissa uniform in
   0..127 and random sign, i.e. +-Inf or NaN (0.1%).
+`sample` > 0 draws other values (z, signs, forced positions, stress) from the same per-channel
+sigma - another sample of the same layer, as calibration data of one model would be.
 Queries: q ~ N(0,1), rounded to BF16.
 """
 from __future__ import annotations
@@ -26,11 +28,13 @@ def _gen(seed: int, stream: int, device) -> torch.Generator:
 
 def kv_pages(n_seq: int, n_pages: int, n_kv: int, *, seed: int, layer: int = 0,
              u_max: float = 3.0, forced_frac: float = 0.10, forced_exp: float = 12.0,
-             stress: bool = False, device="cpu") -> torch.Tensor:
+             stress: bool = False, sample: int = 0, device="cpu") -> torch.Tensor:
     """BF16 KV pages [n_seq, n_pages, 2 (K,V), n_kv, 16, 128] (natural token-major order)."""
     g = _gen(seed, 2 * layer, device)
     shape = (n_seq, n_pages, 2, n_kv, 16, 128)
     u = torch.rand((2, n_kv, 128), generator=g, device=device) * (2 * u_max) - u_max
+    if sample:
+        g = _gen(seed, 2 * layer + 1 + 2_000_000 * int(sample), device)
     sigma = torch.exp2(u)                                            # [2, Hkv, 128]
     x = torch.randn(shape, generator=g, device=device)
     x.abs_().clamp_(2.0 ** -6, 8.0)

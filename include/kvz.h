@@ -88,6 +88,16 @@ typedef struct {
   uint32_t kind;         /* KVZ_KIND_K or KVZ_KIND_V (selects the chunk order)                  */
 } kvz_encode_item;
 
+/* One completed page of one (layer, KV head, K|V) to encode in the group-adaptive format
+ * (kvz_gaac_encode_pages): the fields of kvz_encode_item plus the tile's calibrated bases. */
+typedef struct {
+  const uint16_t* src;   /* device: 16 rows of 128 BF16 values, natural order [token][dim]      */
+  kvz_group_meta* dst;   /* device: where the tile's metadata is written                         */
+  uint32_t src_stride;   /* elements between consecutive tokens of src, >= 128, multiple of 8   */
+  uint32_t kind;         /* KVZ_KIND_K or KVZ_KIND_V                                             */
+  const uint8_t* bases;  /* device [2][128]: b3 then b4 of this (layer, K|V, KV head), per dim   */
+} kvz_gaac_item;
+
 /* One block to decode: block `block` (0..3) of the group described by *meta. */
 typedef struct {
   const kvz_group_meta* meta;  /* device */
@@ -216,6 +226,46 @@ int kvz_decode_block(const void* d_arena, uint64_t arena_bytes, const kvz_block_
  * d_meta 8-byte and d_dst 16-byte aligned (KVZ_EINVAL otherwise). */
 int kvz_decompress_pages(const void* d_arena, uint64_t arena_bytes, const kvz_group_meta* d_meta,
                          int64_t n_pages, int32_t num_kv_heads, uint8_t* d_dst, hipStream_t s);
+
+/* ---------------------------------------------------------------------------------------------
+ * Second format: the group-adaptive additive exponent code ([GAAC] "GAAC: Lossless KV
+ * Compression for Bandwidth-Efficient LLM Inference on Personal Devices", section "Lossless KV
+ * Compression"; appendix "Storage", Table 9).  A TILE is one page's K or V for one KV head
+ * (2048 values); its groups of eight are the chunks above.  Per dim, calibrated bases b3 and b4
+ * open windows of 8 and 16 exponents; a group takes the narrowest of: 3-bit offsets e - b3,
+ * 4-bit offsets e - b4, raw 8-bit exponents; sign and 7 fraction bits stay as one byte.
+ * Compressed record* (<= 3008 B, in a run of 12 granules): sign+fraction plane 2048 B (value i
+ * of group (block j, chunk c) at 512j+8c+i), code plane 768 B (lane c's 12 bytes at 2048+12c:
+ * block j's 24 low-code bits at +3j, value i at bits 3i..3i+2), mode plane 64 B (byte c: block
+ * j's mode at bits 2j..2j+1; 0 = 3-bit, 1 = 4-bit, 2 = raw), then the escape bytes, at most 128
+ * (lanes in order, blocks in order; 4-bit group: one byte, bit i = code bit 3 of value i; raw
+ * group: five bytes, value i's exponent bits 3..7 at bits 5i..5i+4, little-endian).  A tile
+ * whose escapes exceed 128 bytes is stored raw: 4096 B in the raw chunk layout (16 granules).
+ * Metadata: kvz_group_meta with tags 00 00 00 00 (compressed) or FF FF FF FF (raw), so the
+ * slot pool and the meta tables are shared with the first format.
+ * ------------------------------------------------------------------------------------------- */
+
+/* Calibrate one base set ([GAAC] "Lossless KV Compression": per head-channel pair, the
+ * contiguous exponent windows of length 8 and 16 that hold the most values; ties go to the
+ * smallest base*).  All n items are pages of the same (layer, K|V, KV head); only src and
+ * src_stride are read.  d_hist: device [128][256] uint32 scratch (overwritten).  d_bases:
+ * device [2][128] uint8 out (b3 then b4). */
+int kvz_gaac_calibrate(const kvz_encode_item* d_items, int32_t n, uint32_t* d_hist,
+                       uint8_t* d_bases, hipStream_t s);
+
+/* Encode completed pages in the group-adaptive format: classify the groups of each tile, fall
+ * back to raw when the escapes exceed 128 bytes (or with KVZ_ENC_FORCE_RAW), allocate a run of
+ * 12 or 16 granules (same pool, same rule and order as kvz_slot_alloc), write the record and
+ * the metadata.  Each item's dst must be distinct. */
+int kvz_gaac_encode_pages(kvz_pool* p, const kvz_gaac_item* d_items, int32_t n, uint32_t flags,
+                          hipStream_t s);
+
+/* Decompress-first for the group-adaptive format: like kvz_decompress_pages, with d_bases device
+ * [Hkv][2 (K,V)][2 (b3,b4)][128] uint8 for this layer. */
+int kvz_gaac_decompress_pages(const void* d_arena, uint64_t arena_bytes,
+                              const kvz_group_meta* d_meta, const uint8_t* d_bases,
+                              int64_t n_pages, int32_t num_kv_heads, uint8_t* d_dst,
+                              hipStream_t s);
 
 /* Workspace bytes kvz_decode_attention / kvz_bf16_decode_attention need for these sizes
  * (splits = 0: the automatic choice for max_pages). */

@@ -5,13 +5,15 @@ TEST INFRASTRUCTURE ONLY (see oracle/codec.py for who may import it).
 Follows "GAAC: ..." section "Block-Wise Compression Scheduling" (a completed page is encoded
 once; its compressed segments become the cache representation; the block table records where
 and how each block is stored) and the "How it works" metadata paragraph of "ZipFusion: ...".
-Composes oracle.codec (the format) and oracle.alloc (the slot pool model) in item order.
+Composes oracle.codec (the format) and oracle.alloc (the slot pool model) in item order;
+GaacOracleCache does the same with oracle.gaac, whose tiles take runs of 12 or 16 granules of
+the same pool.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from . import codec
+from . import codec, gaac
 from .alloc import SlotPoolModel, OFF_NONE
 
 
@@ -61,3 +63,30 @@ def metas_to_array(metas) -> np.ndarray:
     for n, (off, tags) in enumerate(metas):
         out[n] = np.frombuffer(codec.meta_bytes(off, tags), dtype=np.uint8)
     return out
+
+
+class GaacOracleCache(OracleCache):
+    """The same arena and pool model, filled with group-adaptive tiles."""
+
+    def encode_gaac(self, pages, kinds, bases, force_raw: bool = False):
+        """pages: uint16 [n, 16, 128]; kinds: n values; bases: n pairs (b3 [128], b4 [128]).
+        Returns metas: list of (off, tags) with tags 00x4 (compressed) or FFx4 (raw)."""
+        pages = np.asarray(pages, dtype=np.uint16).reshape(-1, codec.PAGE_TOKENS, codec.HEAD_DIM)
+        encoded = [gaac.encode_tile(pages[n], int(kinds[n]), bases[n][0], bases[n][1], force_raw)
+                   for n in range(pages.shape[0])]
+        offs = self.pool.alloc([gaac.tags_of(raw) for raw, _ in encoded])
+        metas = []
+        for (raw, rec), off in zip(encoded, offs):
+            if off != OFF_NONE:
+                at = off * codec.GRANULE_BYTES
+                self.arena[at:at + rec.size] = rec
+            metas.append((off, gaac.tags_of(raw)))
+        return metas
+
+    def gaac_page(self, meta, kind: int, b3, b4) -> np.ndarray:
+        off, tags = meta
+        assert off != OFF_NONE
+        raw = tags == gaac.TAGS_RAW
+        at = off * codec.GRANULE_BYTES
+        size = gaac.RAW_TILE_BYTES if raw else gaac.SLOT_BYTES
+        return gaac.decode_tile(self.arena[at:at + size], raw, kind, b3, b4)
