@@ -8,6 +8,10 @@
 // The restore and the K/V operand layouts follow "ZipFusion: Fusing Lossless KV Decompression
 // with Attention for Efficient LLM Decoding", section "How it works".
 //
+// Three page formats share the kernel: BF16 (the baseline), the exponent-coded 12-bit pages,
+// and the group-adaptive additive code ("GAAC: ...", section "Lossless KV Compression"), whose
+// tiles are rebuilt with calibrated per-dim bases.
+//
 // Work decomposition (one wave = one unit = (sequence b, KV head, split s)):
 //   * a unit walks a contiguous range of its sequence's pages (the tail page counts as the
 //     last page); per page it loads the four K and four V blocks of its KV head (16 bytes per
@@ -19,13 +23,17 @@
 //   * the query group (G <= 16 heads sharing the KV head) is the MFMA's head dimension;
 //   * online softmax in base 2 per head; rows of O are rescaled only when a head's max rises;
 //   * every unit writes (m, l, O) for its heads; attn_combine merges the splits.
-#include "kvz_internal.h"
+#include "gaac_internal.h"
 
 #include <math.h>
 
 namespace kvz {
 
 namespace {
+
+constexpr int kFmtBf16 = 0;   // uncompressed pages (baseline)
+constexpr int kFmtZf = 1;     // exponent-coded 12-bit pages
+constexpr int kFmtGaac = 2;   // group-adaptive additive code
 
 struct AttnParams {
   const uint16_t* q;
@@ -35,6 +43,7 @@ struct AttnParams {
   const int32_t* seq_lens;
   const int32_t* n_comp;
   const uint16_t* tail;
+  const uint8_t* bases;         // GAAC only: [Hkv][2 (K,V)][2 (b3,b4)][128]
   float* out;                   // [B][Hq][128]
   float* ws_ml;                 // [units][G][2]
   float* ws_o;                  // [units][G][128]
@@ -46,6 +55,28 @@ struct AttnParams {
 struct KV8 {
   uint4 k[4];
   uint4 v[4];
+};
+
+// One GAAC tile as loaded: four 16-byte chunks (raw tile: the BF16 chunks; compressed: the
+// lane's 8 sign+fraction bytes in the low half), the lane's 12 code bytes, the dword holding
+// its mode byte and one dword of the escape area.
+struct GaacTileLoad {
+  uint4 c[4];
+  uint32_t code[3];
+  uint32_t mode;
+  uint32_t esc;
+};
+struct GaacPage {
+  GaacTileLoad k, v;
+};
+
+template <int FMT>
+struct PageBufOf {
+  using type = KV8;
+};
+template <>
+struct PageBufOf<kFmtGaac> {
+  using type = GaacPage;
 };
 
 __device__ __forceinline__ float lane_xor(float x, int m) { return __shfl_xor(x, m, 64); }
@@ -176,8 +207,10 @@ struct Softmax {
   }
 };
 
-template <int GB, bool COMP>
-__global__ __launch_bounds__(256, 3) void attn_split_kernel(AttnParams p) {
+template <int GB, int FMT>
+__global__ __launch_bounds__(256, FMT == kFmtGaac ? 2 : 3) void attn_split_kernel(AttnParams p) {
+  constexpr bool COMP = FMT != kFmtBf16;
+  using PageBuf = typename PageBufOf<FMT>::type;
   const int lane = threadIdx.x & 63;
   const int unit = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (unit >= p.B * p.Hkv * p.S) return;
@@ -214,6 +247,27 @@ __global__ __launch_bounds__(256, 3) void attn_split_kernel(AttnParams p) {
   // every page load is "uniform block base (SGPRs) + this offset"
   const uint32_t lane12 = kCompChunkBytes * lane;
   const uint32_t lane16 = kRawChunkBytes * lane;
+
+  // GAAC: the calibrated bases of this lane's values, as bytes.  K chunk (block j) = dims
+  // 32j + 8*(lane/16) + 0..7: two dwords per base per block.  V chunk = dim 32j + lane%32 for
+  // all eight values: one byte per base per block (byte j of vb3 / vb4).
+  uint32_t kb3[4][2], kb4[4][2], vb3 = 0, vb4 = 0;
+  if constexpr (FMT == kFmtGaac) {
+    const uint8_t* kbase = p.bases + (size_t)(kvh * 2 + 0) * 256;
+    const uint8_t* vbase = p.bases + (size_t)(kvh * 2 + 1) * 256;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int dim = 32 * j + 8 * (lane >> 4);
+      const uint2 b3 = *reinterpret_cast<const uint2*>(kbase + dim);
+      const uint2 b4 = *reinterpret_cast<const uint2*>(kbase + 128 + dim);
+      kb3[j][0] = b3.x;
+      kb3[j][1] = b3.y;
+      kb4[j][0] = b4.x;
+      kb4[j][1] = b4.y;
+      vb3 |= (uint32_t)vbase[32 * j + (lane & 31)] << (8 * j);
+      vb4 |= (uint32_t)vbase[128 + 32 * j + (lane & 31)] << (8 * j);
+    }
+  }
   const int pc_end = p1 < n_comp ? p1 : n_comp;
   for (int cbase = p0; cbase < pc_end; cbase += 64) {
     const int cnt = (pc_end - cbase) < 64 ? (pc_end - cbase) : 64;
@@ -234,6 +288,9 @@ __global__ __launch_bounds__(256, 3) void attn_split_kernel(AttnParams p) {
         const uint64_t vend = (uint64_t)meta_l.z * KVZ_GRANULE_BYTES + group_bytes(meta_l.w);
         ok_l = meta_l.x != KVZ_OFF_NONE && meta_l.z != KVZ_OFF_NONE && kend <= p.arena_bytes &&
                vend <= p.arena_bytes;
+        if (FMT == kFmtGaac)   // a tile is either compressed (tags 0) or raw (tags all 0xFF)
+          ok_l = ok_l && (meta_l.y == 0u || meta_l.y == 0xFFFFFFFFu) &&
+                 (meta_l.w == 0u || meta_l.w == 0xFFFFFFFFu);
         if (!ok_l) meta_l = make_uint4(0, 0, 0, 0);   // loads then stay at the arena start
       }
     }
@@ -244,7 +301,34 @@ __global__ __launch_bounds__(256, 3) void attn_split_kernel(AttnParams p) {
     // clipped by the hardware), block j at a uniform soffset, each lane at its chunk offset.
     // A load that only keeps the loop's shape (`real` false) gets a zero-size resource: the
     // hardware returns zeros without touching memory.
-    auto load_page = [&](int i, KV8& r, bool real) {
+    auto load_gaac_tile = [&](uint32_t off, bool raw, bool real, GaacTileLoad& t) {
+      // the same seven loads for a raw and a compressed tile (so every wait is exact); a raw
+      // tile's code/mode/escape loads get a zero-size resource and touch no memory
+      const uint8_t* base = p.kv + (size_t)off * KVZ_GRANULE_BYTES;
+      const __amdgpu_buffer_rsrc_t r = group_rsrc(base, real ? (raw ? 4096u : kGaacSlotBytes) : 0u);
+      const __amdgpu_buffer_rsrc_t aux = group_rsrc(base, (real && !raw) ? kGaacSlotBytes : 0u);
+      const uint32_t voff = raw ? lane16 : 8u * lane;
+      const uint32_t step = raw ? kRawBlockBytes : 512u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) t.c[j] = bload16(r, voff, step * j);
+      typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+      const u32x3 cw = __builtin_amdgcn_raw_buffer_load_b96(aux, (int)(kGaacCodeOff + 12u * lane), 0, kStreamLoad);
+      t.code[0] = cw.x;
+      t.code[1] = cw.y;
+      t.code[2] = cw.z;
+      t.mode = __builtin_amdgcn_raw_buffer_load_b32(aux, (int)(kGaacModeOff + 4u * (lane >> 2)), 0, kStreamLoad);
+      t.esc = __builtin_amdgcn_raw_buffer_load_b32(aux, (int)(kGaacEscOff + 4u * (lane & 31)), 0, kStreamLoad);
+    };
+    auto load_page = [&](int i, PageBuf& r, bool real) {
+      if constexpr (FMT == kFmtGaac) {
+        const uint32_t koff = (uint32_t)__builtin_amdgcn_readlane((int)meta_l.x, i);
+        const uint32_t voff = (uint32_t)__builtin_amdgcn_readlane((int)meta_l.z, i);
+        const uint32_t kt = (uint32_t)__builtin_amdgcn_readlane((int)meta_l.y, i);
+        const uint32_t vt = (uint32_t)__builtin_amdgcn_readlane((int)meta_l.w, i);
+        load_gaac_tile(koff, kt != 0u, real, r.k);
+        load_gaac_tile(voff, vt != 0u, real, r.v);
+        return;
+      } else {
       __amdgpu_buffer_rsrc_t kr, vr;
       uint32_t kt, vt;
       if constexpr (COMP) {
@@ -274,26 +358,78 @@ __global__ __launch_bounds__(256, 3) void attn_split_kernel(AttnParams p) {
         r.v[j] = bload16(vr, vraw ? lane16 : lane12, vs);
         vs += vraw ? kRawBlockBytes : kCompBlockBytes;
       }
+      }
     };
-    auto process = [&](const KV8& buf, int i) {
+    // GAAC tile -> the four operand chunks.  Each lane finds its escape bytes by an exclusive
+    // scan of the lanes' escape counts; lanes 0..31 hold the 128-byte escape area as dwords and
+    // a lane fetches the two dwords covering its group's bytes (a group's five bytes never
+    // reach past the area, so the second dword is always one of those 32).
+    auto gaac_ops = [&](const GaacTileLoad& t, bool raw, bool is_k, uint4 (&ops)[4]) {
+      if (raw) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ops[j] = t.c[j];
+        return;
+      }
+      const uint32_t m8 = (t.mode >> (8 * (lane & 3))) & 0xFFu;
+      uint32_t len = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) len += gaac_escape_bytes((m8 >> (2 * j)) & 3u);
+      uint32_t pos = gaac_exclusive_scan(len, lane);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t mode = (m8 >> (2 * j)) & 3u;
+        uint32_t esc = 0, esc_hi = 0;
+        if (__ballot(mode != kGaacMode3)) {
+          const int q = (int)(pos >> 2);
+          const uint32_t d0 = (uint32_t)__shfl((int)t.esc, q, 64);
+          const uint32_t d1 = (uint32_t)__shfl((int)t.esc, q + 1, 64);
+          const uint32_t sh = 8u * (pos & 3u);
+          esc = __builtin_amdgcn_alignbit(d1, d0, sh);
+          esc_hi = (sh ? (d1 >> sh) : d1) & 0xFFu;
+          if (mode == kGaacMode4) esc &= 0xFFu;
+          pos += gaac_escape_bytes(mode);
+        }
+        uint32_t b3lo, b3hi, b4lo, b4hi;
+        if (is_k) {
+          b3lo = kb3[j][0];
+          b3hi = kb3[j][1];
+          b4lo = kb4[j][0];
+          b4hi = kb4[j][1];
+        } else {
+          b3lo = b3hi = ((vb3 >> (8 * j)) & 0xFFu) * 0x01010101u;
+          b4lo = b4hi = ((vb4 >> (8 * j)) & 0xFFu) * 0x01010101u;
+        }
+        ops[j] = gaac_restore_group(t.c[j].x, t.c[j].y, gaac_low24(t.code, j), mode, esc, esc_hi,
+                                    b3lo, b3hi, b4lo, b4hi);
+      }
+    };
+    auto process = [&](const PageBuf& buf, int i) {
       if (!((ok_mask >> i) & 1ull)) return;
       uint32_t kt = 0xFFFFFFFFu, vt = 0xFFFFFFFFu;
       if constexpr (COMP) {
         kt = (uint32_t)__builtin_amdgcn_readlane((int)meta_l.y, i);
         vt = (uint32_t)__builtin_amdgcn_readlane((int)meta_l.w, i);
       }
+      uint4 kops[4], vop[4];
+      if constexpr (FMT == kFmtGaac) {
+        gaac_ops(buf.k, kt != 0u, true, kops);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kops[j] = restore_if_coded(buf.k[j], (kt >> (8 * j)) & 0xFFu);
+      }
       f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint4 kop = restore_if_coded(buf.k[j], (kt >> (8 * j)) & 0xFFu);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kop), as_bf16x8(qop[j]), sacc, 0, 0, 0);
-      }
+      for (int j = 0; j < 4; ++j)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kops[j]), as_bf16x8(qop[j]), sacc, 0, 0, 0);
       float sv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) sv[r] = sacc[r] * p.scale_log2;
-      uint4 vop[4];
+      if constexpr (FMT == kFmtGaac) {
+        gaac_ops(buf.v, vt != 0u, false, vop);
+      } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) vop[j] = restore_if_coded(buf.v[j], (vt >> (8 * j)) & 0xFFu);
+        for (int j = 0; j < 4; ++j) vop[j] = restore_if_coded(buf.v[j], (vt >> (8 * j)) & 0xFFu);
+      }
       sm.page(sv, vop, lane);
     };
 
@@ -302,7 +438,7 @@ __global__ __launch_bounds__(256, 3) void attn_split_kernel(AttnParams p) {
     // a zero-size resource and never computed), so the wait before each compute covers exactly
     // that page's eight loads.
     const int last = cnt - 1;
-    KV8 buf[2];
+    PageBuf buf[2];
     load_page(0, buf[0], true);
     const int rounds = (cnt + 1) / 2;
     for (int r = 0; r < rounds; ++r) {
@@ -482,9 +618,10 @@ struct CommonArgs {
   uint64_t workspace_bytes;
 };
 
-template <bool COMP>
+template <int FMT>
 int launch_attention(const CommonArgs& a, const uint8_t* kv, const kvz_group_meta* meta,
-                     hipStream_t s) {
+                     const uint8_t* bases, hipStream_t s) {
+  constexpr bool COMP = FMT != kFmtBf16;
   if (a.head_dim != KVZ_HEAD_DIM || a.page_size != KVZ_PAGE_TOKENS)
     return set_error(KVZ_EUNSUPPORTED, "only head_dim 128 and 16-token pages are supported");
   if (a.batch < 0 || a.num_q_heads <= 0 || a.num_kv_heads <= 0 || a.max_pages < 0)
@@ -504,6 +641,8 @@ int launch_attention(const CommonArgs& a, const uint8_t* kv, const kvz_group_met
   if ((((uintptr_t)a.q) | ((uintptr_t)a.tail)) & 15u)
     return set_error(KVZ_EINVAL, "q and tail must be 16-byte aligned");
   if (COMP && (((uintptr_t)meta) & 15u)) return set_error(KVZ_EINVAL, "meta must be 16-byte aligned");
+  if (FMT == kFmtGaac && (!bases || (((uintptr_t)bases) & 7u)))
+    return set_error(KVZ_EINVAL, "bases must be a non-null 8-byte aligned pointer");
   if (((uintptr_t)a.workspace) & 255u) return set_error(KVZ_EINVAL, "workspace must be 256-byte aligned");
   if (a.splits < 0 || a.splits > kMaxSplits) return set_error(KVZ_EINVAL, "splits out of range");
   const int S = a.splits ? a.splits : choose_splits(a.batch, a.num_kv_heads, a.max_pages, device_cus());
@@ -521,6 +660,7 @@ int launch_attention(const CommonArgs& a, const uint8_t* kv, const kvz_group_met
   p.seq_lens = a.seq_lens;
   p.n_comp = a.n_comp_pages;
   p.tail = a.tail;
+  p.bases = bases;
   p.out = a.out;
   p.ws_ml = reinterpret_cast<float*>(a.workspace);
   p.ws_o = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(a.workspace) + ml_bytes);
@@ -536,11 +676,11 @@ int launch_attention(const CommonArgs& a, const uint8_t* kv, const kvz_group_met
 
   const dim3 grid((unsigned)((units + 3) / 4));
   if (G <= 4)
-    hipLaunchKernelGGL((attn_split_kernel<4, COMP>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((attn_split_kernel<4, FMT>), grid, dim3(256), 0, s, p);
   else if (G <= 8)
-    hipLaunchKernelGGL((attn_split_kernel<8, COMP>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((attn_split_kernel<8, FMT>), grid, dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL((attn_split_kernel<16, COMP>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((attn_split_kernel<16, FMT>), grid, dim3(256), 0, s, p);
   int rc = check_hip(hipGetLastError(), "attention launch");
   if (rc != KVZ_OK || S == 1) return rc;
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.batch * a.num_q_heads)),
@@ -573,7 +713,17 @@ extern "C" int kvz_decode_attention(const kvz_attn_args* a, hipStream_t s) {
                a->n_comp_pages, a->tail, a->batch, a->num_q_heads, a->num_kv_heads, a->head_dim,
                a->page_size, a->max_pages, a->splits, a->sm_scale, a->workspace,
                a->workspace_bytes};
-  return launch_attention<true>(c, a->arena, a->meta, s);
+  return launch_attention<kFmtZf>(c, a->arena, a->meta, nullptr, s);
+}
+
+extern "C" int kvz_gaac_decode_attention(const kvz_attn_args* a, const uint8_t* d_bases,
+                                         hipStream_t s) {
+  if (!a) return set_error(KVZ_EINVAL, "args is null");
+  CommonArgs c{a->q, a->out, a->arena_bytes, a->n_phys_pages, a->block_table, a->seq_lens,
+               a->n_comp_pages, a->tail, a->batch, a->num_q_heads, a->num_kv_heads, a->head_dim,
+               a->page_size, a->max_pages, a->splits, a->sm_scale, a->workspace,
+               a->workspace_bytes};
+  return launch_attention<kFmtGaac>(c, a->arena, a->meta, d_bases, s);
 }
 
 extern "C" int kvz_bf16_decode_attention(const kvz_bf16_attn_args* a, hipStream_t s) {
@@ -582,5 +732,5 @@ extern "C" int kvz_bf16_decode_attention(const kvz_bf16_attn_args* a, hipStream_
                a->n_comp_pages, a->tail, a->batch, a->num_q_heads, a->num_kv_heads, a->head_dim,
                a->page_size, a->max_pages, a->splits, a->sm_scale, a->workspace,
                a->workspace_bytes};
-  return launch_attention<false>(c, a->pages, nullptr, s);
+  return launch_attention<kFmtBf16>(c, a->pages, nullptr, nullptr, s);
 }

@@ -39,6 +39,7 @@ EXPORTED = [
     "kvz_attn_workspace_bytes", "kvz_decode_attention", "kvz_bf16_pack_pages",
     "kvz_bf16_decode_attention", "kvz_pool_stats", "kvz_stream_read", "kvz_decompress_pages",
     "kvz_pool_capacity", "kvz_gaac_calibrate", "kvz_gaac_encode_pages", "kvz_gaac_decompress_pages",
+    "kvz_gaac_decode_attention",
 ]
 
 
@@ -115,6 +116,7 @@ _sig = {
     "kvz_pool_stats": ([_vp, ctypes.POINTER(PoolStats), _vp], ctypes.c_int),
     "kvz_stream_read": ([_vp, ctypes.c_uint64, _vp, ctypes.c_int32, _vp], ctypes.c_int),
     "kvz_gaac_calibrate": ([_vp, ctypes.c_int32, _vp, _vp, _vp], ctypes.c_int),
+    "kvz_gaac_decode_attention": ([ctypes.POINTER(AttnArgs), _vp, _vp], ctypes.c_int),
     "kvz_gaac_encode_pages": ([_vp, _vp, ctypes.c_int32, ctypes.c_uint32, _vp], ctypes.c_int),
     "kvz_gaac_decompress_pages": ([_vp, ctypes.c_uint64, _vp, _vp, ctypes.c_int64, ctypes.c_int32,
                                    _vp, _vp], ctypes.c_int),
@@ -205,13 +207,10 @@ def kvz_attn_workspace_bytes(batch, num_q_heads, num_kv_heads, max_pages, splits
     return out.value
 
 
-def kvz_decode_attention(q, out, arena, meta, block_table, seq_lens, n_comp_pages, tail,
-                         sm_scale: float, workspace, splits: int = 0, stream=None) -> None:
-    """q [B,Hq,128] bf16; out [B,Hq,128] fp32; meta [n_phys,Hkv,2,8] uint8 (or any 8-byte
-    records); block_table [B,max_pages] int32; seq_lens, n_comp_pages [B] int32;
-    tail [B,2,Hkv,16,128] bf16 or None; workspace uint8 device tensor."""
+def _attn_args(q, out, arena, meta, block_table, seq_lens, n_comp_pages, tail, sm_scale,
+               workspace, splits):
     bsz, hq, hd = q.shape
-    a = AttnArgs(q=q.data_ptr(), out=out.data_ptr(), arena=arena.data_ptr(),
+    return AttnArgs(q=q.data_ptr(), out=out.data_ptr(), arena=arena.data_ptr(),
                  arena_bytes=arena.numel() * arena.element_size(), meta=meta.data_ptr(),
                  n_phys_pages=meta.shape[0], block_table=block_table.data_ptr(), seq_lens=seq_lens.data_ptr(),
                  n_comp_pages=n_comp_pages.data_ptr(),
@@ -220,7 +219,27 @@ def kvz_decode_attention(q, out, arena, meta, block_table, seq_lens, n_comp_page
                  max_pages=block_table.shape[1], splits=splits, sm_scale=sm_scale,
                  workspace=workspace.data_ptr(),
                  workspace_bytes=workspace.numel() * workspace.element_size())
+
+
+def kvz_decode_attention(q, out, arena, meta, block_table, seq_lens, n_comp_pages, tail,
+                         sm_scale: float, workspace, splits: int = 0, stream=None) -> None:
+    """q [B,Hq,128] bf16; out [B,Hq,128] fp32; meta [n_phys,Hkv,2,8] uint8 (or any 8-byte
+    records); block_table [B,max_pages] int32; seq_lens, n_comp_pages [B] int32;
+    tail [B,2,Hkv,16,128] bf16 or None; workspace uint8 device tensor."""
+    a = _attn_args(q, out, arena, meta, block_table, seq_lens, n_comp_pages, tail, sm_scale,
+                   workspace, splits)
     _check(_lib.kvz_decode_attention(ctypes.byref(a), _stream(stream)))
+
+
+def kvz_gaac_decode_attention(q, out, arena, meta, bases, block_table, seq_lens, n_comp_pages,
+                              tail, sm_scale: float, workspace, splits: int = 0,
+                              stream=None) -> None:
+    """As kvz_decode_attention over group-adaptive tiles; bases [Hkv,2,2,128] uint8 device."""
+    if bases.numel() < meta.shape[1] * 512:
+        raise ValueError("bases too small")
+    a = _attn_args(q, out, arena, meta, block_table, seq_lens, n_comp_pages, tail, sm_scale,
+                   workspace, splits)
+    _check(_lib.kvz_gaac_decode_attention(ctypes.byref(a), _ptr(bases), _stream(stream)))
 
 
 def kvz_bf16_pack_pages(src, dst, stream=None) -> None:

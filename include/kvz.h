@@ -267,6 +267,14 @@ int kvz_gaac_decompress_pages(const void* d_arena, uint64_t arena_bytes,
                               int64_t n_pages, int32_t num_kv_heads, uint8_t* d_dst,
                               hipStream_t s);
 
+/* Fused decode attention over pages in the group-adaptive format: the arguments of
+ * kvz_decode_attention (meta: tile metadata written by kvz_gaac_encode_pages), plus d_bases:
+ * device [Hkv][2 (K,V)][2 (b3,b4)][128] uint8, 8-byte aligned, the layer's calibrated bases.
+ * Tiles are rebuilt bit-exactly in registers (e = code + b_w) and used at once ([GAAC]
+ * "Attention with On-the-Fly Decompression").  A page whose tiles carry tags other than
+ * 00x4 / FFx4 is skipped.  Same output contract as kvz_decode_attention. */
+int kvz_gaac_decode_attention(const kvz_attn_args* a, const uint8_t* d_bases, hipStream_t s);
+
 /* Workspace bytes kvz_decode_attention / kvz_bf16_decode_attention need for these sizes
  * (splits = 0: the automatic choice for max_pages). */
 int kvz_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

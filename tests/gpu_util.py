@@ -32,9 +32,11 @@ class Layer:
 
 
 def build_layer(arena: paged.SlotArena, pages: torch.Tensor, seq_lens, n_comp, *, seed: int,
-                flags: int = 0, with_tail: bool = True) -> Layer:
+                flags: int = 0, with_tail: bool = True, gaac_bases=None) -> Layer:
     """Encode pages [b, p] for p < n_comp[b] into the arena (physical pages in a seeded random
-    order) and return the layer.  The tail of sequence b is pages[b, n_comp[b]]."""
+    order) and return the layer.  The tail of sequence b is pages[b, n_comp[b]].  With
+    gaac_bases ([Hkv, 2, 2, 128] uint8, device) the pages are encoded in the group-adaptive
+    format instead."""
     bsz, n_total, _, hkv = pages.shape[:4]
     seq_lens = np.asarray(seq_lens, dtype=np.int64)
     n_comp = np.asarray(n_comp, dtype=np.int64)
@@ -52,8 +54,12 @@ def build_layer(arena: paged.SlotArena, pages: torch.Tensor, seq_lens, n_comp, *
             phys_ids.append(perm[used])
             used += 1
     meta = paged.new_meta_table(max(n_phys, 1), hkv, device=pages.device)
-    items = paged.page_items(pages, page_ids, meta, phys_ids) if page_ids else None
-    d_items = paged.encode(arena, items, flags) if items is not None else None
+    if gaac_bases is None:
+        items = paged.page_items(pages, page_ids, meta, phys_ids) if page_ids else None
+        d_items = paged.encode(arena, items, flags) if items is not None else None
+    else:
+        items = paged.gaac_page_items(pages, page_ids, meta, phys_ids, gaac_bases) if page_ids else None
+        d_items = paged.gaac_encode(arena, items, flags) if items is not None else None
     tail = None
     if with_tail:
         idx = torch.as_tensor(np.minimum(n_comp, n_total - 1), device=pages.device)
@@ -74,6 +80,17 @@ def run_fused(layer: Layer, arena: paged.SlotArena, q: torch.Tensor, sm_scale: f
     ws = paged.workspace(bsz, hq, hkv, layer.block_table.shape[1], splits, device=q.device)
     kvz.kvz_decode_attention(q, out, arena.arena, layer.meta, layer.block_table, layer.seq_lens,
                              layer.n_comp, layer.tail, sm_scale, ws, splits)
+    return out
+
+
+def run_gaac(layer: Layer, arena: paged.SlotArena, bases: torch.Tensor, q: torch.Tensor,
+             sm_scale: float, splits: int = 0) -> torch.Tensor:
+    bsz, hq, _ = q.shape
+    hkv = layer.meta.shape[1]
+    out = torch.empty((bsz, hq, 128), dtype=torch.float32, device=q.device)
+    ws = paged.workspace(bsz, hq, hkv, layer.block_table.shape[1], splits, device=q.device)
+    kvz.kvz_gaac_decode_attention(q, out, arena.arena, layer.meta, bases, layer.block_table,
+                                  layer.seq_lens, layer.n_comp, layer.tail, sm_scale, ws, splits)
     return out
 
 

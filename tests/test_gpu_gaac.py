@@ -180,3 +180,77 @@ def test_full_size_qwen8k_layer_round_trip_and_ratio():
         assert off != OFF_NONE
         assert list(m[ph, h, kind, 4:]) == gaac.tags_of(raw)
         np.testing.assert_array_equal(arena_h[off * 256: off * 256 + rec.size], rec)
+
+
+# ---------------------------------------------------------------------------------------------
+# fused attention over group-adaptive tiles
+# ---------------------------------------------------------------------------------------------
+from gpu_util import check_rows, oracle_attention_rows, run_bf16, run_gaac, sm_scale  # noqa: E402
+
+
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (16, 2), (12, 4)])
+def test_gaac_attention_matches_oracle_and_baseline(hq, hkv):
+    """Ragged sequences (an empty one, a tail-only one, partial tails), some tiles raw: within
+    the tolerance of the fp64 oracle, and bit for bit the uncompressed kernel's output."""
+    announce(f"gaac attention hq={hq} hkv={hkv}")
+    bsz = 5
+    cal = synth.kv_pages(2, 8, hkv, seed=80, u_max=3.0, forced_frac=0.05, sample=1, device="cuda")
+    bases = paged.gaac_calibrate(cal)
+    pages = synth.kv_pages(bsz, 41, hkv, seed=80, u_max=3.0, forced_frac=0.05, device="cuda")
+    q = synth.queries(bsz, hq, seed=80, device="cuda")
+    seq_lens, n_comp = [16 * 40 + 7, 16 * 23 + 16, 0, 9, 16 * 40], [40, 23, 0, 0, 40]
+    arena = paged.SlotArena(bsz * 41 * hkv * 2 * 4096 + (1 << 20))
+    layer = build_layer(arena, pages, seq_lens, n_comp, seed=80, gaac_bases=bases)
+    tags = layer.meta.cpu().numpy()[..., 4:]
+    assert (tags == 0).all(axis=-1).any()
+    got = run_gaac(layer, arena, bases, q, sm_scale())
+    base = run_bf16(layer, q, sm_scale())
+    torch.cuda.synchronize()
+    assert torch.equal(got, base)
+    ref = oracle_attention_rows(layer, q, sm_scale(), range(bsz))
+    g = got.cpu().numpy()
+    for b in range(bsz):
+        if seq_lens[b] == 0:
+            assert (g[b] == 0).all()
+        else:
+            check_rows(g[b], ref[b], what=f"gaac seq {b}")
+
+
+def test_gaac_attention_raw_and_compressed_tiles_agree_bitwise():
+    """The same pages stored all raw (KVZ_ENC_FORCE_RAW) and compressed give identical output:
+    the restore is exact."""
+    announce("gaac attention storage-mode invariance")
+    cal = synth.kv_pages(1, 8, 8, seed=81, u_max=5.0, forced_frac=0.05, sample=1, device="cuda")
+    bases = paged.gaac_calibrate(cal)
+    pages = synth.kv_pages(3, 30, 8, seed=81, u_max=5.0, forced_frac=0.05, device="cuda")
+    q = synth.queries(3, 32, seed=81, device="cuda")
+    outs = []
+    for flags in (0, kvz.KVZ_ENC_FORCE_RAW):
+        arena = paged.SlotArena(3 * 30 * 8 * 2 * 4096 + (1 << 20))
+        layer = build_layer(arena, pages, [16 * 29 + 5] * 3, [29] * 3, seed=81, flags=flags,
+                            gaac_bases=bases)
+        outs.append(run_gaac(layer, arena, bases, q, sm_scale()).clone())
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+
+
+def test_gaac_attention_full_size_qwen8k_sampled():
+    """The 8K workload's shape (16 x 511 compressed pages + the 16-token tail, u~U[-5,5]): rows
+    of 3 sequences against the oracle, all rows bit for bit against the uncompressed kernel."""
+    announce("gaac attention full 8K")
+    bsz, n_comp, hkv, hq = 16, 511, 8, 32
+    cal = synth.kv_pages(4, 32, hkv, seed=2, u_max=5.0, forced_frac=0.05, sample=1, device="cuda")
+    bases = paged.gaac_calibrate(cal)
+    pages = synth.kv_pages(bsz, n_comp + 1, hkv, seed=2, u_max=5.0, forced_frac=0.05, device="cuda")
+    q = synth.queries(bsz, hq, seed=2, device="cuda")
+    arena = paged.SlotArena(bsz * n_comp * hkv * 2 * 4096 + (16 << 20))
+    layer = build_layer(arena, pages, [16 * n_comp + 16] * bsz, [n_comp] * bsz, seed=2,
+                        gaac_bases=bases)
+    got = run_gaac(layer, arena, bases, q, sm_scale())
+    base = run_bf16(layer, q, sm_scale())
+    torch.cuda.synchronize()
+    assert torch.equal(got, base)
+    ref = oracle_attention_rows(layer, q, sm_scale(), [0, 7, 15])
+    g = got.cpu().numpy()
+    for b in (0, 7, 15):
+        check_rows(g[b], ref[b], what=f"gaac 8K seq {b}")
