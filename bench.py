@@ -42,12 +42,13 @@ U_MAX = 5.0
 FORCED = 0.05
 SEED = 2
 VARIANT_LAYERS, VARIANT_U_MAX = 8, 3.0
+GAAC_LAYERS = 8
 N_PHYS = B * N_COMP
 SCALE = 1.0 / math.sqrt(128.0)
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_qwen8k_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "decode_attention_kvz_amd", "csrc", f)
-                  for f in ("attention.hip", "kvz_internal.h")]
+                  for f in ("attention.hip", "kvz_internal.h", "gaac_internal.h")]
 
 
 def log(msg):
@@ -124,6 +125,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-baseline", action="store_true")
     ap.add_argument("--no-variant", action="store_true")
+    ap.add_argument("--no-gaac", action="store_true")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="for hardware-counter runs: one layer of fused and baseline attention "
                          "(3 launches each) and a 1 GiB device copy as a traffic reference")
@@ -254,6 +256,7 @@ def main():
     traffic = committed_traffic()
     read_peak = stream_read_peak(timed)
     variant = None if args.no_variant else compressible_variant(args, dev, seq_lens, n_comp, ws)
+    gaac_leg = None if args.no_gaac else gaac_format(args, dev, seq_lens, n_comp, ws)
     del g_attn, g_comp
     cpu = None if args.no_cpu_baseline else cpu_baseline(layers)
 
@@ -304,6 +307,7 @@ def main():
                            "input_GBps": round(N_PHYS * HKV * 2 * 4096 /
                                                (float(np.median(enc_layer_us)) * 1e-6) / 1e9, 1)},
         "compressible_variant": variant,
+        "gaac_format": gaac_leg,
     }
     print(json.dumps(line), flush=True)
     arena.close()
@@ -331,6 +335,89 @@ def stream_read_peak(timed):
     log(f"stream read reference: {best:.0f} GB/s ({best_wg} workgroups per CU)")
     return {"GBps": round(best, 1), "bytes": 1 << 32, "workgroups_per_cu": best_wg,
             "sweep_GBps_by_workgroups_per_cu": sweep}
+
+
+def gaac_format(args, dev, seq_lens, n_comp, ws):
+    """The second page format (group-adaptive additive code) on the headline workload's shape
+    and data model (u~U[-5,5], 5% forced), 8 layers, each with bases calibrated on another
+    sample of the same layer: fused attention vs the uncompressed kernel and vs
+    decompress-first, and the storage ratio."""
+    import torch
+    from decode_attention_kvz_amd import kvz, paged, synth
+    arena = paged.SlotArena(GAAC_LAYERS * (N_PHYS + B) * HKV * 2 * 4096 + (16 << 20), device=dev)
+    rng = np.random.default_rng(SEED)
+    layers = []
+    for layer in range(GAAC_LAYERS):
+        cal = synth.kv_pages(4, 32, HKV, seed=SEED, layer=layer, u_max=U_MAX, forced_frac=FORCED,
+                             sample=1, device=dev)
+        bases = paged.gaac_calibrate(cal)
+        del cal
+        pages = synth.kv_pages(B, N_COMP + 1, HKV, seed=SEED, layer=layer, u_max=U_MAX,
+                               forced_frac=FORCED, device=dev)
+        block_table = rng.permutation(N_PHYS).reshape(B, N_COMP).astype(np.int32)
+        meta = paged.new_meta_table(N_PHYS, HKV, device=dev)
+        items = paged.gaac_page_items(pages, [(b, p) for b in range(B) for p in range(N_COMP)],
+                                      meta, block_table.reshape(-1), bases)
+        d_items = paged.gaac_encode(arena, items)
+        inv = torch.as_tensor(np.argsort(block_table.reshape(-1)), device=dev)
+        store = paged.pack_bf16_pages(pages[:, :N_COMP].reshape(N_PHYS, 2, HKV, 16, 128)[inv])
+        layers.append(dict(meta=meta, bases=bases, store=store,
+                           block_table=torch.from_numpy(block_table).to(dev),
+                           tail=pages[:, N_COMP].contiguous(),
+                           q=synth.queries(B, HQ, seed=SEED * 1000 + layer, device=dev),
+                           out=torch.empty((B, HQ, 128), dtype=torch.float32, device=dev)))
+        torch.cuda.synchronize()
+        del d_items, pages
+    st = arena.stats()
+    rec = st["live_granules"] * 256 / GAAC_LAYERS
+    raw_tiles = st["live_raw_blocks"] / 4 / st["live_runs"]
+    res = {}
+    for mode in ("gaac", "bf16"):
+        def run():
+            for L in layers:
+                if mode == "gaac":
+                    kvz.kvz_gaac_decode_attention(L["q"], L["out"], arena.arena, L["meta"], L["bases"],
+                                                  L["block_table"], seq_lens, n_comp, L["tail"],
+                                                  SCALE, ws, args.splits)
+                else:
+                    kvz.kvz_bf16_decode_attention(L["q"], L["out"], L["store"], L["block_table"],
+                                                  seq_lens, n_comp, L["tail"], SCALE, ws, HKV,
+                                                  args.splits)
+        res[mode] = graph_us_per_layer(run, GAAC_LAYERS, args)
+    # same split count -> the same arithmetic on the same values: bit-identical outputs
+    L = layers[-1]
+    same = [torch.empty_like(L["out"]) for _ in range(2)]
+    kvz.kvz_gaac_decode_attention(L["q"], same[0], arena.arena, L["meta"], L["bases"],
+                                  L["block_table"], seq_lens, n_comp, L["tail"], SCALE, ws, 16)
+    kvz.kvz_bf16_decode_attention(L["q"], same[1], L["store"], L["block_table"], seq_lens, n_comp,
+                                  L["tail"], SCALE, ws, HKV, 16)
+    torch.cuda.synchronize()
+    assert torch.equal(same[0], same[1]), "GAAC attention differs from the BF16 kernel"
+    for L in layers:
+        del L["store"]
+    scratch = torch.empty((N_PHYS, 2, HKV, 4, 1024), dtype=torch.uint8, device=dev)
+
+    def dfirst():
+        for L in layers:
+            paged.gaac_decompress_pages(arena, L["meta"], L["bases"], scratch)
+            kvz.kvz_bf16_decode_attention(L["q"], L["out"], scratch, L["block_table"], seq_lens,
+                                          n_comp, L["tail"], SCALE, ws, HKV, args.splits)
+    dfirst_us = graph_us_per_layer(dfirst, GAAC_LAYERS, args)
+    arena.close()
+    alg = alg_bytes_per_layer(rec) + HKV * 512      # + the layer's bases
+    out = {"label": "group-adaptive additive code (second format), headline shape and data model, "
+                    "8 layers, per-layer bases calibrated on another sample of the layer",
+           "record_bytes_per_layer": int(rec),
+           "storage_ratio_vs_bf16": round(N_PHYS * HKV * 2 * 4096 / rec, 4),
+           "raw_tile_fraction": round(raw_tiles, 4),
+           "fused_us_per_layer": round(res["gaac"], 2),
+           "fused_achieved_GBps": round(alg / (res["gaac"] * 1e-6) / 1e9, 1),
+           "bf16_us_per_layer": round(res["bf16"], 2),
+           "speedup_vs_bf16_kernel": round(res["bf16"] / res["gaac"], 4),
+           "decompress_first_us_per_layer": round(dfirst_us, 2)}
+    log(f"gaac format: fused {res['gaac']:.1f} us/layer vs bf16 {res['bf16']:.1f} "
+        f"(storage ratio {out['storage_ratio_vs_bf16']}, raw tiles {raw_tiles:.4f})")
+    return out
 
 
 def graph_us_per_layer(run, n_layers, args):

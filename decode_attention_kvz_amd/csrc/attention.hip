@@ -375,11 +375,24 @@ __global__ __launch_bounds__(256, FMT == kFmtGaac ? 2 : 3) void attn_split_kerne
 #pragma unroll
       for (int j = 0; j < 4; ++j) len += gaac_escape_bytes((m8 >> (2 * j)) & 3u);
       uint32_t pos = gaac_exclusive_scan(len, lane);
+      // no raw group in the wave: each lane has at most four escape bytes (one per 4-bit
+      // group), all inside the two dwords fetched here once for the tile
+      const bool any_raw = __ballot((m8 & 0xAAu) != 0u) != 0ull;
+      uint32_t win = 0;
+      if (!any_raw && __ballot(len != 0u)) {
+        const int q = (int)(pos >> 2);
+        const uint32_t d0 = (uint32_t)__shfl((int)t.esc, q, 64);
+        const uint32_t d1 = (uint32_t)__shfl((int)t.esc, q + 1, 64);
+        win = __builtin_amdgcn_alignbit(d1, d0, 8u * (pos & 3u));
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t mode = (m8 >> (2 * j)) & 3u;
         uint32_t esc = 0, esc_hi = 0;
-        if (__ballot(mode != kGaacMode3)) {
+        if (!any_raw) {
+          esc = win & 0xFFu;                      // this group's byte if it is a 4-bit group
+          if (mode == kGaacMode4) win >>= 8;
+        } else if (__ballot(mode != kGaacMode3)) {
           const int q = (int)(pos >> 2);
           const uint32_t d0 = (uint32_t)__shfl((int)t.esc, q, 64);
           const uint32_t d1 = (uint32_t)__shfl((int)t.esc, q + 1, 64);
@@ -583,10 +596,14 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(
 // flight with 4 waves per CU, and measured as fast or faster than 2 workgroups per CU on every
 // workload shape - with at least 4 pages per split.  Workgroup counts that are not a multiple of
 // the CU count leave some CUs one workgroup more than others (measured 10-20% slower).
-int choose_splits(int B, int Hkv, int max_pages, int n_cu) {
+// The group-adaptive tiles' restore has long dependent latencies (ballots, lane shuffles), so
+// that format runs two workgroups per CU (two waves per SIMD) to overlap them.
+constexpr int kGaacWavesPerCu = 8;
+
+int choose_splits(int B, int Hkv, int max_pages, int n_cu, int waves_per_cu = 4) {
   const int64_t units = (int64_t)(B * Hkv > 0 ? B * Hkv : 1);
   const int64_t pages = (int64_t)max_pages + 1;
-  int64_t S = (4 * (int64_t)n_cu + units - 1) / units;
+  int64_t S = ((int64_t)waves_per_cu * n_cu + units - 1) / units;
   const int64_t by_pages = (pages + 3) / 4;
   if (S > by_pages) S = by_pages;
   if (S > kMaxSplits) S = kMaxSplits;
@@ -645,7 +662,9 @@ int launch_attention(const CommonArgs& a, const uint8_t* kv, const kvz_group_met
     return set_error(KVZ_EINVAL, "bases must be a non-null 8-byte aligned pointer");
   if (((uintptr_t)a.workspace) & 255u) return set_error(KVZ_EINVAL, "workspace must be 256-byte aligned");
   if (a.splits < 0 || a.splits > kMaxSplits) return set_error(KVZ_EINVAL, "splits out of range");
-  const int S = a.splits ? a.splits : choose_splits(a.batch, a.num_kv_heads, a.max_pages, device_cus());
+  const int S = a.splits ? a.splits
+                         : choose_splits(a.batch, a.num_kv_heads, a.max_pages, device_cus(),
+                                         FMT == kFmtGaac ? kGaacWavesPerCu : 4);
   uint64_t ml_bytes, need;
   workspace_layout(a.batch, a.num_q_heads, a.num_kv_heads, S, &ml_bytes, &need);
   if (a.workspace_bytes < need) return set_error(KVZ_EINVAL, "workspace too small");
@@ -700,7 +719,9 @@ extern "C" int kvz_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int3
   if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_pages < 0 || splits < 0)
     return set_error(KVZ_EINVAL, "bad sizes");
   if (splits > kMaxSplits) return set_error(KVZ_EINVAL, "splits out of range");
-  const int S = splits ? splits : choose_splits(batch, num_kv_heads, max_pages, device_cus());
+  // sized for the format with the most splits, so one workspace serves every format
+  const int S = splits ? splits
+                       : choose_splits(batch, num_kv_heads, max_pages, device_cus(), kGaacWavesPerCu);
   uint64_t ml, total;
   workspace_layout(batch, num_q_heads, num_kv_heads, S, &ml, &total);
   *bytes = total < 256 ? 256 : total;

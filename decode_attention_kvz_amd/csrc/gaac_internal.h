@@ -23,15 +23,20 @@ __device__ __forceinline__ uint32_t gaac_escape_bytes(uint32_t mode) {
   return mode == kGaacMode4 ? 1u : (mode == kGaacModeRaw ? 5u : 0u);
 }
 
-// Exclusive prefix sum of v over the lanes of the wave (lane order).
+// Exclusive prefix sum over the lanes of the wave (lane order) of v < 32 (a lane's escape
+// bytes, at most 4 x 5): bit by bit, the lanes below this one with that bit set are counted
+// with a ballot and mbcnt - no cross-lane data movement.
 __device__ __forceinline__ uint32_t gaac_exclusive_scan(uint32_t v, int lane) {
-  uint32_t incl = v;
+  (void)lane;
+  uint32_t sum = 0;
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t o = (uint32_t)__shfl_up((int)incl, d, 64);
-    if (lane >= d) incl += o;
+  for (int bit = 0; bit < 5; ++bit) {
+    const uint64_t m = __ballot((v >> bit) & 1u);
+    const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    sum += below << bit;
   }
-  return incl - v;
+  return sum;
 }
 
 // Block j's 24 low-code bits from a lane's 12 code bytes (3 dwords, little-endian).
