@@ -87,3 +87,27 @@ def test_pool_capacity_hand_worked():
     assert kvz.kvz_pool_capacity(st, 1, 1)["expected_group_granules"] == 16.0
     with pytest.raises(kvz.KvzError):
         kvz.kvz_pool_capacity(st, 0, 4)
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="libkvz.so not built")
+def test_gaac_entry_points_reject_bad_arguments_on_the_host():
+    """The second format's calls validate their arguments before anything reaches a device."""
+    from decode_attention_kvz_amd import kvz
+    lib = kvz._lib
+    p = ctypes.c_void_p(256)
+    assert lib.kvz_gaac_calibrate(None, 1, p, p, None) == kvz.KVZ_EINVAL          # items null, n > 0
+    assert lib.kvz_gaac_calibrate(p, -1, p, p, None) == kvz.KVZ_EINVAL
+    assert lib.kvz_gaac_calibrate(p, 1, ctypes.c_void_p(258), p, None) == kvz.KVZ_EINVAL  # hist misaligned
+    assert lib.kvz_gaac_encode_pages(None, p, 1, 0, None) == kvz.KVZ_EINVAL       # no pool
+    assert lib.kvz_gaac_decompress_pages(p, 4096, p, p, -1, 8, p, None) == kvz.KVZ_EINVAL
+    assert lib.kvz_gaac_decompress_pages(p, 4096, p, p, 1, 0, p, None) == kvz.KVZ_EINVAL
+    assert lib.kvz_gaac_decompress_pages(p, 4096, ctypes.c_void_p(260), p, 1, 8, p, None) == kvz.KVZ_EINVAL
+    assert lib.kvz_gaac_decompress_pages(p, 4096, p, p, 0, 8, p, None) == kvz.KVZ_OK   # nothing to do
+    args = kvz.AttnArgs(q=256, out=256, arena=256, arena_bytes=1 << 20, meta=256, n_phys_pages=1,
+                        block_table=256, seq_lens=256, n_comp_pages=256, tail=None, batch=1,
+                        num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16, max_pages=1,
+                        splits=1, sm_scale=0.1, workspace=256, workspace_bytes=1 << 20)
+    assert lib.kvz_gaac_decode_attention(ctypes.byref(args), None, None) == kvz.KVZ_EINVAL   # no bases
+    assert lib.kvz_gaac_decode_attention(ctypes.byref(args), ctypes.c_void_p(260), None) == kvz.KVZ_EINVAL
+    args.head_dim = 64
+    assert lib.kvz_gaac_decode_attention(ctypes.byref(args), p, None) == kvz.KVZ_EUNSUPPORTED
