@@ -337,17 +337,14 @@ def stream_read_peak(timed):
             "sweep_GBps_by_workgroups_per_cu": sweep}
 
 
-def gaac_format(args, dev, seq_lens, n_comp, ws):
-    """The second page format (group-adaptive additive code) on the headline workload's shape
-    and data model (u~U[-5,5], 5% forced), 8 layers, each with bases calibrated on another
-    sample of the same layer: fused attention vs the uncompressed kernel and vs
-    decompress-first, and the storage ratio."""
+def build_gaac_layers(arena, n_layers, dev):
+    """Layers of the headline workload (u~U[-5,5], 5% forced) in the group-adaptive format, each
+    with bases calibrated on another sample of the same layer; plus the BF16 page store."""
     import torch
-    from decode_attention_kvz_amd import kvz, paged, synth
-    arena = paged.SlotArena(GAAC_LAYERS * (N_PHYS + B) * HKV * 2 * 4096 + (16 << 20), device=dev)
+    from decode_attention_kvz_amd import paged, synth
     rng = np.random.default_rng(SEED)
     layers = []
-    for layer in range(GAAC_LAYERS):
+    for layer in range(n_layers):
         cal = synth.kv_pages(4, 32, HKV, seed=SEED, layer=layer, u_max=U_MAX, forced_frac=FORCED,
                              sample=1, device=dev)
         bases = paged.gaac_calibrate(cal)
@@ -368,6 +365,18 @@ def gaac_format(args, dev, seq_lens, n_comp, ws):
                            out=torch.empty((B, HQ, 128), dtype=torch.float32, device=dev)))
         torch.cuda.synchronize()
         del d_items, pages
+    return layers
+
+
+def gaac_format(args, dev, seq_lens, n_comp, ws):
+    """The second page format (group-adaptive additive code) on the headline workload's shape
+    and data model (u~U[-5,5], 5% forced), 8 layers, each with bases calibrated on another
+    sample of the same layer: fused attention vs the uncompressed kernel and vs
+    decompress-first, and the storage ratio."""
+    import torch
+    from decode_attention_kvz_amd import kvz, paged
+    arena = paged.SlotArena(GAAC_LAYERS * (N_PHYS + B) * HKV * 2 * 4096 + (16 << 20), device=dev)
+    layers = build_gaac_layers(arena, GAAC_LAYERS, dev)
     st = arena.stats()
     rec = st["live_granules"] * 256 / GAAC_LAYERS
     raw_tiles = st["live_raw_blocks"] / 4 / st["live_runs"]
@@ -526,7 +535,8 @@ def compressible_variant(args, dev, seq_lens, n_comp, ws):
 def pmc_probe(args, dev):
     """Launches for a counter run: a 1 GiB device-to-device copy (reads and writes exactly
     1 GiB; the reference that scales FETCH_SIZE / WRITE_SIZE), then 3 fused and 3 baseline
-    attention calls on layer 0 of the workload."""
+    attention calls on layer 0 of the workload, then 3 calls over the same layer in the
+    group-adaptive format."""
     import torch
     from decode_attention_kvz_amd import kvz, paged
     src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
@@ -547,6 +557,15 @@ def pmc_probe(args, dev):
                                       n_comp, L["tail"], SCALE, ws, HKV, args.splits)
     torch.cuda.synchronize()
     st = arena.stats()
+    garena = paged.SlotArena((N_PHYS + B) * HKV * 2 * 4096 + (16 << 20), device=dev)
+    G = build_gaac_layers(garena, 1, dev)[0]
+    for _ in range(3):
+        kvz.kvz_gaac_decode_attention(G["q"], G["out"], garena.arena, G["meta"], G["bases"],
+                                      G["block_table"], seq_lens, n_comp, G["tail"], SCALE, ws,
+                                      args.splits)
+    torch.cuda.synchronize()
+    log(f"pmc probe: GAAC layer {garena.stats()['live_granules'] * 256} record bytes")
+    garena.close()
     log(f"pmc probe done: {st['live_granules'] * 256} record bytes in the layer, algorithmic "
         f"{alg_bytes_per_layer(st['live_granules'] * 256):.0f} bytes per call; kernel source "
         f"sha256 {kernel_source_sha()}")

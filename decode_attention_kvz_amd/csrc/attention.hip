@@ -211,6 +211,13 @@ template <int GB, int FMT>
 __global__ __launch_bounds__(256, FMT == kFmtGaac ? 2 : 3) void attn_split_kernel(AttnParams p) {
   constexpr bool COMP = FMT != kFmtBf16;
   using PageBuf = typename PageBufOf<FMT>::type;
+  // GAAC: a 16 KiB table from four packed 3-bit codes to four bytes, filled by the whole
+  // workgroup before any wave leaves (one LDS read replaces the bit-field spreading)
+  __shared__ uint32_t s_spread3[FMT == kFmtGaac ? 4096 : 1];
+  if constexpr (FMT == kFmtGaac) {
+    for (int x = threadIdx.x; x < 4096; x += 256) s_spread3[x] = gaac_spread3((uint32_t)x);
+    __syncthreads();
+  }
   const int lane = threadIdx.x & 63;
   const int unit = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (unit >= p.B * p.Hkv * p.S) return;
@@ -412,8 +419,10 @@ __global__ __launch_bounds__(256, FMT == kFmtGaac ? 2 : 3) void attn_split_kerne
           b3lo = b3hi = ((vb3 >> (8 * j)) & 0xFFu) * 0x01010101u;
           b4lo = b4hi = ((vb4 >> (8 * j)) & 0xFFu) * 0x01010101u;
         }
-        ops[j] = gaac_restore_group(t.c[j].x, t.c[j].y, gaac_low24(t.code, j), mode, esc, esc_hi,
-                                    b3lo, b3hi, b4lo, b4hi);
+        const uint32_t low24 = gaac_low24(t.code, j);
+        ops[j] = gaac_restore_group_spread(t.c[j].x, t.c[j].y, s_spread3[low24 & 0xFFFu],
+                                           s_spread3[low24 >> 12], mode, esc, esc_hi, b3lo, b3hi,
+                                           b4lo, b4hi, any_raw);
       }
     };
     auto process = [&](const PageBuf& buf, int i) {

@@ -95,4 +95,33 @@ __device__ __forceinline__ uint4 gaac_restore_group(uint32_t sm0, uint32_t sm1, 
   return r;
 }
 
+// The same rebuild from codes already spread to bytes (c0/c1: the low 3 code bits of values
+// 0..3 / 4..7, one per byte); the raw path only when `wave_has_raw` (wave-uniform).
+__device__ __forceinline__ uint4 gaac_restore_group_spread(uint32_t sm0, uint32_t sm1, uint32_t c0,
+                                                           uint32_t c1, uint32_t mode, uint32_t esc,
+                                                           uint32_t esc_hi, uint32_t b3lo,
+                                                           uint32_t b3hi, uint32_t b4lo,
+                                                           uint32_t b4hi, bool wave_has_raw) {
+  const uint32_t h4 = mode == kGaacMode4 ? esc : 0u;
+  c0 |= gaac_spread1(h4) << 3;
+  c1 |= gaac_spread1(h4 >> 4) << 3;
+  if (wave_has_raw && mode == kGaacModeRaw) {
+    c0 |= gaac_spread5(esc & 0xFFFFFu) << 3;
+    c1 |= gaac_spread5((esc >> 20) | (esc_hi << 12)) << 3;
+  }
+  const uint32_t base0 = mode == kGaacMode3 ? b3lo : (mode == kGaacMode4 ? b4lo : 0u);
+  const uint32_t base1 = mode == kGaacMode3 ? b3hi : (mode == kGaacMode4 ? b4hi : 0u);
+  const uint32_t e0 = c0 + base0, e1 = c1 + base1;
+  const uint32_t h0 = (sm0 & 0x80808080u) | ((e0 >> 1) & 0x7F7F7F7Fu);
+  const uint32_t l0 = (sm0 & 0x7F7F7F7Fu) | ((e0 << 7) & 0x80808080u);
+  const uint32_t h1 = (sm1 & 0x80808080u) | ((e1 >> 1) & 0x7F7F7F7Fu);
+  const uint32_t l1 = (sm1 & 0x7F7F7F7Fu) | ((e1 << 7) & 0x80808080u);
+  uint4 r;
+  r.x = __builtin_amdgcn_perm(h0, l0, 0x05010400u);
+  r.y = __builtin_amdgcn_perm(h0, l0, 0x07030602u);
+  r.z = __builtin_amdgcn_perm(h1, l1, 0x05010400u);
+  r.w = __builtin_amdgcn_perm(h1, l1, 0x07030602u);
+  return r;
+}
+
 }  // namespace kvz
