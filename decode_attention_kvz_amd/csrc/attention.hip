@@ -1,5 +1,6 @@
-// Paged split-K GQA decode attention over exponent-coded BF16 pages (fused restore), and the
-// same kernel over uncompressed BF16 pages (the baseline).
+// Paged split-K GQA decode attention over losslessly compressed BF16 pages (two formats, each
+// restored bit-exactly in registers), and the same kernel over uncompressed BF16 pages (the
+// baseline).
 //
 // Follows "GAAC: Lossless KV Compression for Bandwidth-Efficient LLM Inference on Personal
 // Devices", section "Attention with On-the-Fly Decompression": compressed tiles and their

@@ -275,8 +275,9 @@ int kvz_gaac_decompress_pages(const void* d_arena, uint64_t arena_bytes,
  * 00x4 / FFx4 is skipped.  Same output contract as kvz_decode_attention. */
 int kvz_gaac_decode_attention(const kvz_attn_args* a, const uint8_t* d_bases, hipStream_t s);
 
-/* Workspace bytes kvz_decode_attention / kvz_bf16_decode_attention need for these sizes
- * (splits = 0: the automatic choice for max_pages). */
+/* Workspace bytes the attention calls (kvz_decode_attention, kvz_gaac_decode_attention,
+ * kvz_bf16_decode_attention) need for these sizes.  splits = 0: enough for the automatic
+ * split count of every one of them (the group-adaptive format uses twice as many splits). */
 int kvz_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                              int32_t max_pages, int32_t splits, uint64_t* bytes);
 
