@@ -259,3 +259,27 @@ def test_gaac_attention_full_size_qwen8k_sampled():
     g = got.cpu().numpy()
     for b in (0, 7, 15):
         check_rows(g[b], ref[b], what=f"gaac 8K seq {b}")
+
+
+def test_gaac_attention_non_finite_values_propagate_like_the_oracle():
+    """NaN / Inf in K and V: out of both windows, so their groups go raw inside compressed tiles;
+    the non-finite output positions equal the oracle's."""
+    announce("gaac attention non-finite propagation")
+    cal = synth.kv_pages(2, 8, 2, seed=82, forced_frac=0.0, sample=1, device="cuda")
+    bases = paged.gaac_calibrate(cal)
+    pages = synth.kv_pages(4, 9, 2, seed=82, forced_frac=0.0, device="cuda")
+    bits = pages.view(torch.int16)
+    bits[0, 2, 1, 0, 3, 17] = 0x7FC0          # NaN in V: one output dim of head group 0
+    bits[1, 4, 0, 1, 5, 3] = 0x7F80           # +Inf in K: scores of head group 1 go non-finite
+    bits[2, 8, 1, 0, 2, 40] = -128            # -Inf (0xFF80) in V on the tail page
+    q = synth.queries(4, 8, seed=82, device="cuda")
+    seq_lens, n_comp = [16 * 8 + 4, 16 * 8 + 4, 16 * 8 + 4, 16 * 8], [8, 8, 8, 8]
+    arena = paged.SlotArena(4 * 9 * 2 * 2 * 4096 + (1 << 20))
+    layer = build_layer(arena, pages, seq_lens, n_comp, seed=82, gaac_bases=bases)
+    tags = layer.meta.cpu().numpy()[..., 4:]
+    assert (tags == 0).all()                  # every tile compressed (raw groups inside)
+    got = run_gaac(layer, arena, bases, q, sm_scale()).cpu().numpy()
+    ref = oracle_attention_rows(layer, q, sm_scale(), range(4))
+    for b in range(4):
+        check_rows(got[b], ref[b], what=f"gaac seq {b}")
+    assert not np.isfinite(got[0]).all() and not np.isfinite(got[2]).all()
