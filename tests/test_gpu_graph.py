@@ -86,3 +86,31 @@ def test_encode_and_free_graph_replays_follow_the_pool_model():
         assert st["live_runs"] == model.live_runs == n_items
         assert st["free_runs"] == [len(model.bins[k]) for k in range(5)]
         assert st["frontier_granules"] == model.frontier
+
+
+def test_gaac_attention_graph_replays_match_eager():
+    announce("graph replay: GAAC attention")
+    cal = synth.kv_pages(2, 8, 8, seed=33, forced_frac=0.05, sample=1, device="cuda")
+    bases = paged.gaac_calibrate(cal)
+    pages = synth.kv_pages(4, 33, 8, seed=33, forced_frac=0.05, device="cuda")
+    q = synth.queries(4, 32, seed=33, device="cuda")
+    seq_lens, n_comp = [16 * 32 + 9, 16 * 20, 16 * 32 + 16, 7], [32, 20, 32, 0]
+    arena = paged.SlotArena(int(pages.numel() * 2 * 1.05) + (1 << 20))
+    layer = build_layer(arena, pages, seq_lens, n_comp, seed=33, gaac_bases=bases)
+    ws = paged.workspace(4, 32, 8, layer.block_table.shape[1])
+    eager = torch.empty((4, 32, 128), dtype=torch.float32, device="cuda")
+    kvz.kvz_gaac_decode_attention(q, eager, arena.arena, layer.meta, bases, layer.block_table,
+                                  layer.seq_lens, layer.n_comp, layer.tail, 1 / math.sqrt(128), ws)
+    out = torch.zeros_like(eager)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        kvz.kvz_gaac_decode_attention(q, out, arena.arena, layer.meta, bases, layer.block_table,
+                                      layer.seq_lens, layer.n_comp, layer.tail, 1 / math.sqrt(128), ws)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        _ = (q.float() * 2).sum()          # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep}"
