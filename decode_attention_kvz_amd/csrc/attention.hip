@@ -208,8 +208,145 @@ struct Softmax {
   }
 };
 
+constexpr int kMaxSplits = 4096;
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// Balanced split-K.  The B*S splits of a KV head are shared by page count: sequence b is cut
+// into S_b = ceil(T_b / P) pieces of at most P pages, with P the smallest piece size for which
+// the S_b add up to at most B*S (searched between ceil(W / (B*S)) and ceil(W / (B*S - B)),
+// which always fits; W = the batch's pages per KV head; beyond 64 sequences the upper bound is
+// used).  A long sequence gets more pieces than a short one, so one long sequence no longer
+// sets the kernel time.  With equal lengths S_b = S and the pieces are exactly the uniform ones
+// (that case skips the search, at any batch size); with S = 1 every sequence keeps one piece.
+// Sequence b owns splits [base_b, base_b + S_b); the rest stay unused.  Computed by one whole
+// wave (every lane gets the result); the sequence's clamped n_comp and tail tokens come with it.
+struct SplitOf {
+  int b;       // sequence (-1: unused split)
+  int base;    // first split of the sequence
+  int sb;      // splits of the sequence
+  int total;   // its pages
+  int n_comp;  // its compressed pages, clamped to [0, max_pages]
+  int n_tail;  // its tail tokens, clamped to [0, 16] (0 without a tail buffer)
+};
+
+__device__ __forceinline__ void seq_counts(const int32_t* n_comp_v, const int32_t* seq_lens,
+                                           bool has_tail, int max_pages, int b, int& n, int& t) {
+  n = n_comp_v[b];
+  n = n < 0 ? 0 : (n > max_pages ? max_pages : n);
+  t = 0;
+  if (has_tail) {
+    t = seq_lens[b] - 16 * n;
+    t = t < 0 ? 0 : (t > 16 ? 16 : t);
+  }
+}
+
+__device__ __forceinline__ SplitOf split_of(const int32_t* n_comp_v, const int32_t* seq_lens,
+                                            bool has_tail, int max_pages, int B, int S, int k,
+                                            int want_b) {
+  const int lane = threadIdx.x & 63;
+  SplitOf r{-1, 0, 0, 0, 0, 0};
+  // pass 1: W, and whether every sequence has the same page count
+  int64_t W = 0;
+  bool uniform = true;
+  int t0 = -1;
+  int T_first = 0;                   // this lane's page count in the first 64 sequences
+  for (int c0 = 0; c0 < B; c0 += 64) {
+    const int b = c0 + lane;
+    int n = 0, t = 0;
+    if (b < B) seq_counts(n_comp_v, seq_lens, has_tail, max_pages, b, n, t);
+    int T = n + (t > 0 ? 1 : 0);
+    if (c0 == 0) T_first = T;
+    if (t0 < 0) t0 = __builtin_amdgcn_readfirstlane(T);
+    uniform = uniform && !__ballot(b < B && T != t0);
+    if (B <= 64 && (uniform || S == 1)) {   // S_b = S, base_b = b * S
+      const int bb = want_b >= 0 ? want_b : k / S;
+      if (bb >= B) return r;
+      r.b = bb;
+      r.base = bb * S;
+      r.sb = S;
+      r.total = __builtin_amdgcn_readlane(T, bb);
+      r.n_comp = __builtin_amdgcn_readlane(n, bb);
+      r.n_tail = __builtin_amdgcn_readlane(t, bb);
+      return r;
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) T += __shfl_xor(T, d, 64);
+    W += T;
+  }
+  if (uniform || S == 1) {               // more than 64 sequences: the same uniform pieces
+    const int bb = want_b >= 0 ? want_b : k / S;
+    if (bb >= B) return r;
+    int n, t;
+    seq_counts(n_comp_v, seq_lens, has_tail, max_pages, bb, n, t);
+    r.b = bb;
+    r.base = bb * S;
+    r.sb = S;
+    r.total = n + (t > 0 ? 1 : 0);
+    r.n_comp = n;
+    r.n_tail = t;
+    return r;
+  }
+  // the piece size: smallest P whose pieces fit the B*S splits
+  const int64_t BS = (int64_t)B * S;
+  int64_t P = 1;
+  if (S > 1 && W > 0) {
+    int64_t lo = (W + BS - 1) / BS;
+    int64_t hi = (W + (BS - B) - 1) / (BS - B);      // sum of ceil(T/hi) <= W/hi + B <= BS
+    if (B <= 64) {
+      while (lo < hi) {
+        const int64_t mid = (lo + hi) / 2;
+        int c = T_first > 0 ? (int)((T_first + mid - 1) / mid) : 1;
+        c = c > kMaxSplits ? kMaxSplits : c;
+        if (lane >= B) c = 0;
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d, 64);
+        if (c <= BS) hi = mid;
+        else lo = mid + 1;
+      }
+    }
+    P = hi;
+  }
+  // pass 2: prefix sums of S_b, find the owner
+  int base = 0;
+  for (int c0 = 0; c0 < B; c0 += 64) {
+    const int b = c0 + lane;
+    int n = 0, t = 0, T = 0, sb = 0;
+    if (b < B) {
+      seq_counts(n_comp_v, seq_lens, has_tail, max_pages, b, n, t);
+      T = n + (t > 0 ? 1 : 0);
+      sb = S == 1 ? 1 : (T > 0 ? (int)((T + P - 1) / P) : 1);
+      sb = sb > kMaxSplits ? kMaxSplits : sb;
+    }
+    const int incl = wave_incl_scan(sb) + base;
+    const int start = incl - sb;
+    const bool mine = b < B && (want_b >= 0 ? b == want_b : (k >= start && k < incl));
+    const uint64_t m = __ballot(mine);
+    if (m) {
+      const int src = __builtin_ctzll(m);
+      r.b = __builtin_amdgcn_readlane(b, src);
+      r.base = __builtin_amdgcn_readlane(start, src);
+      r.sb = __builtin_amdgcn_readlane(sb, src);
+      r.total = __builtin_amdgcn_readlane(T, src);
+      r.n_comp = __builtin_amdgcn_readlane(n, src);
+      r.n_tail = __builtin_amdgcn_readlane(t, src);
+      return r;
+    }
+    base = __builtin_amdgcn_readlane(incl, 63);
+  }
+  return r;
+}
+
 template <int GB, int FMT>
-__global__ __launch_bounds__(256, FMT == kFmtGaac ? 2 : 3) void attn_split_kernel(AttnParams p) {
+__global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
   constexpr bool COMP = FMT != kFmtBf16;
   using PageBuf = typename PageBufOf<FMT>::type;
   // GAAC: a 16 KiB table from four packed 3-bit codes to four bytes, filled by the whole
@@ -221,22 +358,21 @@ __global__ __launch_bounds__(256, FMT == kFmtGaac ? 2 : 3) void attn_split_kerne
   }
   const int lane = threadIdx.x & 63;
   const int unit = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (unit >= p.B * p.Hkv * p.S) return;
-  const int s = unit % p.S;
-  const int bh = unit / p.S;
-  const int kvh = bh % p.Hkv;
-  const int b = bh / p.Hkv;
-
-  int n_comp = p.n_comp[b];
-  n_comp = n_comp < 0 ? 0 : (n_comp > p.max_pages ? p.max_pages : n_comp);
-  int n_tail = 0;
-  if (p.tail) {
-    n_tail = p.seq_lens[b] - 16 * n_comp;
-    n_tail = n_tail < 0 ? 0 : (n_tail > 16 ? 16 : n_tail);
-  }
-  const int total = n_comp + (n_tail > 0 ? 1 : 0);
-  const int p0 = (int)(((int64_t)s * total) / p.S);
-  const int p1 = (int)(((int64_t)(s + 1) * total) / p.S);
+  // unit = kvh * U + k: a workgroup's four waves take four consecutive splits of one KV head
+  const int U = p.B * p.S;                 // splits per KV head
+  if (unit >= U * p.Hkv) return;
+  const int kvh = unit / U;
+  const int k = unit % U;
+  const SplitOf so = split_of(p.n_comp, p.seq_lens, p.tail != nullptr, p.max_pages, p.B, p.S, k,
+                              -1);
+  if (so.b < 0) return;                    // an unused split
+  const int b = so.b;
+  const int s = k - so.base;
+  const int n_comp = so.n_comp;
+  const int n_tail = so.n_tail;
+  const int total = so.total;
+  const int p0 = (int)(((int64_t)s * total) / so.sb);
+  const int p1 = (int)(((int64_t)(s + 1) * total) / so.sb);
 
   // Q as the column operand of the 16x16x32 product: head lane%16, dims 32j + 8*(lane/16) + i.
   const int head = lane & 15;
@@ -543,13 +679,13 @@ __global__ __launch_bounds__(256, FMT == kFmtGaac ? 2 : 3) void attn_split_kerne
 
 }
 
-// Merge the S splits of every (sequence, query head): M = max m_s, L = sum l_s 2^(m_s - M),
-// out = sum O_s 2^(m_s - M) / L.  A sequence of length 0 gives zeros.  A separate launch:
+// Merge the splits of every (sequence, query head): M = max m_s, L = sum l_s 2^(m_s - M),
+// out = sum O_s 2^(m_s - M) / L, over the sequence's S_b splits (split_of).  A sequence of
+// length 0 gives zeros.  A separate launch:
 // ordering the splits' partial writes before these reads needs no per-wave fence (a fence at
 // device scope writes back and invalidates the whole L2 of the issuing chiplet).
 // One workgroup of 256 threads per (sequence, query head), parallel over the splits.
 constexpr int kCombineThreads = 256;
-constexpr int kMaxSplits = 4096;
 
 __device__ __forceinline__ float block_reduce(float v, float* s_red, bool is_max) {
 #pragma unroll
@@ -567,8 +703,8 @@ __device__ __forceinline__ float block_reduce(float v, float* s_red, bool is_max
 }
 
 __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(
-    const float* ws_ml, const float* ws_o, float* out, const int32_t* seq_lens, int Hq, int Hkv,
-    int G, int S) {
+    const float* ws_ml, const float* ws_o, float* out, const int32_t* seq_lens,
+    const int32_t* n_comp_v, bool has_tail, int max_pages, int B, int Hq, int G, int S_avg) {
   __shared__ float s_w[kMaxSplits];
   __shared__ float s_red[kCombineThreads / 64];
   __shared__ float s_part[kCombineThreads];
@@ -576,13 +712,16 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(
   const int b = bh / Hq, h = bh % Hq;
   const int kvh = h / G, g = h % G;
   const int t = threadIdx.x;
-  const size_t unit0 = ((size_t)b * Hkv + kvh) * S;
+  const SplitOf so = split_of(n_comp_v, seq_lens, has_tail, max_pages, B, S_avg, 0, b);
+  const int S = so.sb;
+  // the partials of split base+sp of this KV head
+  auto unit_of = [&](int sp) { return (size_t)kvh * B * S_avg + so.base + sp; };
   float m_loc = -INFINITY;
-  for (int sp = t; sp < S; sp += kCombineThreads) m_loc = fmaxf(m_loc, ws_ml[((unit0 + sp) * G + g) * 2]);
+  for (int sp = t; sp < S; sp += kCombineThreads) m_loc = fmaxf(m_loc, ws_ml[(unit_of(sp) * G + g) * 2]);
   const float M = block_reduce(m_loc, s_red, true);
   float l_loc = 0.f;
   for (int sp = t; sp < S; sp += kCombineThreads) {
-    const size_t ug = (unit0 + sp) * G + g;
+    const size_t ug = unit_of(sp) * G + g;
     const float m = ws_ml[ug * 2];
     const float w = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - M);
     s_w[sp] = w;
@@ -593,7 +732,7 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(
   float acc = 0.f;
 #pragma unroll 4
   for (int sp = t >> 7; sp < S; sp += kCombineThreads / KVZ_HEAD_DIM)
-    acc += s_w[sp] * ws_o[((unit0 + sp) * G + g) * KVZ_HEAD_DIM + d];
+    acc += s_w[sp] * ws_o[(unit_of(sp) * G + g) * KVZ_HEAD_DIM + d];
   s_part[t] = acc;
   __syncthreads();
   if (t < KVZ_HEAD_DIM) {
@@ -714,7 +853,8 @@ int launch_attention(const CommonArgs& a, const uint8_t* kv, const kvz_group_met
   if (rc != KVZ_OK || S == 1) return rc;
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.batch * a.num_q_heads)),
                      dim3(kCombineThreads), 0, s,
-                     p.ws_ml, p.ws_o, a.out, a.seq_lens, p.Hq, p.Hkv, G, S);
+                     p.ws_ml, p.ws_o, a.out, a.seq_lens, a.n_comp_pages, a.tail != nullptr,
+                     p.max_pages, p.B, p.Hq, G, S);
   return check_hip(hipGetLastError(), "combine launch");
 }
 

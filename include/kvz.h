@@ -142,8 +142,11 @@ typedef struct {
   const uint16_t* tail;         /* device [B][2][Hkv][16][128] BF16, or NULL if no sequence has
                                    tokens past its compressed pages                             */
   int32_t batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages;
-  int32_t splits;               /* pieces of each sequence's pages (split-K), 0..4096; 0 =
-                                   automatic (even over the device's CUs)                       */
+  int32_t splits;               /* split-K: pieces per sequence on average, 0..4096; 0 =
+                                   automatic (even over the device's CUs).  With S > 1 a piece
+                                   holds at most ceil(W / (B*S)) pages (W = the batch's pages),
+                                   so longer sequences are cut into more pieces; equal lengths
+                                   give exactly S pieces each                                    */
   float sm_scale;
   void* workspace;              /* device, >= kvz_attn_workspace_bytes(...), 256-B aligned; calls
                                    that share a workspace must be ordered on one stream         */

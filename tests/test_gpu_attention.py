@@ -154,3 +154,56 @@ def test_long_context_layer_sampled():
     """Batch 1, 32 query / 8 KV heads, 131072 tokens, split-K across the chip."""
     announce("131k-token layer")
     _full_size_sampled(1, 8192, 8192, 0, 32, 8, 3.0, 0.10, 4, [0])
+
+
+@pytest.mark.parametrize("splits", [0, 3, 8])
+def test_ragged_batch_balanced_splits(splits):
+    """Lengths from one page to 40 pages and an empty sequence: long sequences are cut into more
+    splits than short ones.  Every row meets the tolerance against the oracle, and the fused
+    kernel equals the uncompressed one bit for bit at the same split count."""
+    announce(f"ragged batch splits={splits}")
+    n_comp = [40, 1, 0, 17, 33, 5]
+    seq_lens = [16 * 40 + 3, 16 * 1 + 16, 0, 16 * 17, 16 * 33 + 9, 16 * 5 + 1]
+    pages = synth.kv_pages(6, 41, 2, seed=16, forced_frac=0.05, forced_exp=-16.0, device="cuda")
+    q = synth.queries(6, 8, seed=16, device="cuda")
+    arena, layer = _layer(pages, seq_lens, n_comp, seed=16)
+    fused = run_fused(layer, arena, q, sm_scale(), splits)
+    base = run_bf16(layer, q, sm_scale(), splits)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, base)
+    ref = oracle_attention_rows(layer, q, sm_scale(), range(6))
+    got = fused.cpu().numpy()
+    for b in range(6):
+        if seq_lens[b] == 0:
+            assert (got[b] == 0).all()
+        else:
+            check_rows(got[b], ref[b], what=f"ragged seq {b}")
+
+
+@pytest.mark.parametrize("ragged", [True, False])
+def test_large_batch_split_map(ragged):
+    """72 sequences (more than one wave's worth): the split map scans the batch in two chunks.
+    Ragged lengths (some empty) and equal lengths, two splits per sequence on average."""
+    announce(f"72-sequence batch ragged={ragged}")
+    bsz = 72
+    if ragged:
+        n_comp = [(7 * i) % 11 for i in range(bsz)]
+        seq_lens = [16 * n + 5 * (i % 3) for i, n in enumerate(n_comp)]
+    else:
+        n_comp = [3] * bsz
+        seq_lens = [16 * 3 + 7] * bsz
+    pages = synth.kv_pages(bsz, 12, 2, seed=17, forced_frac=0.05, forced_exp=-16.0, device="cuda")
+    q = synth.queries(bsz, 4, seed=17, device="cuda")
+    arena, layer = _layer(pages, seq_lens, n_comp, seed=17)
+    fused = run_fused(layer, arena, q, sm_scale(), 2)
+    base = run_bf16(layer, q, sm_scale(), 2)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, base)
+    rows = [b for b in range(bsz) if seq_lens[b] > 0]
+    ref = oracle_attention_rows(layer, q, sm_scale(), rows)
+    got = fused.cpu().numpy()
+    for b in range(bsz):
+        if seq_lens[b] == 0:
+            assert (got[b] == 0).all()
+    for b in rows:
+        check_rows(got[b], ref[b], what=f"seq {b}")
