@@ -5,4 +5,4 @@ the CPU-baseline leg of bench.py; never by the HIP library or its binding, and i
 neither.  Every function is a plain, slow statement of what the pages define; see the module
 headers for the passages followed and the pins that check each part.
 """
-from . import codec, alloc, cache, attention  # noqa: F401
+from . import codec, alloc, cache, attention, gaac, fp8  # noqa: F401

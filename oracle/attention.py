@@ -36,6 +36,11 @@ def attention_fp64(q_bits, k_bits, v_bits, sm_scale: float) -> np.ndarray:
     q = codec.bf16_bits_to_f64(q_bits)
     k = codec.bf16_bits_to_f64(k_bits)
     v = codec.bf16_bits_to_f64(v_bits)
+    return attention_values_fp64(q, k, v, sm_scale)
+
+
+def attention_values_fp64(q, k, v, sm_scale: float) -> np.ndarray:
+    """The same definition on values: q [Hq, D], k/v [T, Hkv, D] float64.  Returns [Hq, D]."""
     hq, d = q.shape
     t, hkv, _ = k.shape
     out = np.zeros((hq, d), dtype=np.float64)

@@ -13,7 +13,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import codec, gaac
+from . import codec, fp8, gaac
 from .alloc import SlotPoolModel, OFF_NONE
 
 
@@ -90,3 +90,39 @@ class GaacOracleCache(OracleCache):
         at = off * codec.GRANULE_BYTES
         size = gaac.RAW_TILE_BYTES if raw else gaac.SLOT_BYTES
         return gaac.decode_tile(self.arena[at:at + size], raw, kind, b3, b4)
+
+
+class Fp8OracleCache:
+    """An arena of FP8 tiles: the same slot pool model over 128-byte granules (a compressed
+    E4M3 / E5M2 tile takes 15 / 13 granules, a raw tile 16; see oracle/fp8.py)."""
+
+    def __init__(self, arena_bytes: int, fk: int):
+        self.fk = fk
+        self.arena = np.zeros(int(arena_bytes), dtype=np.uint8)
+        self.pool = SlotPoolModel(max(int(arena_bytes) // fp8.GRANULE_BYTES - 1, 0))
+
+    def encode(self, pages, kinds, bases, force_raw: bool = False):
+        """pages: uint8 [n, 16, 128] FP8 tiles; kinds: n values; bases: n pairs (b3, b4).
+        Returns metas: list of (off, tags), off == OFF_NONE where the pool had no room."""
+        pages = np.asarray(pages, dtype=np.uint8).reshape(-1, fp8.TILE_TOKENS, fp8.HEAD_DIM)
+        encoded = [fp8.encode_tile(pages[n], int(kinds[n]), self.fk, bases[n][0], bases[n][1],
+                                   force_raw) for n in range(pages.shape[0])]
+        offs = self.pool.alloc([fp8.tags_of(raw, self.fk) for raw, _ in encoded])
+        metas = []
+        for (raw, rec), off in zip(encoded, offs):
+            if off != OFF_NONE:
+                at = off * fp8.GRANULE_BYTES
+                self.arena[at:at + rec.size] = rec
+            metas.append((off, fp8.tags_of(raw, self.fk)))
+        return metas
+
+    def free(self, metas):
+        self.pool.free(metas)
+
+    def page(self, meta, kind: int, b3, b4) -> np.ndarray:
+        off, tags = meta
+        assert off != OFF_NONE
+        raw = list(tags) == fp8.TAGS_RAW
+        at = off * fp8.GRANULE_BYTES
+        size = fp8.RAW_TILE_BYTES if raw else fp8.slot_bytes(self.fk)
+        return fp8.decode_tile(self.arena[at:at + size], raw, kind, self.fk, b3, b4)
