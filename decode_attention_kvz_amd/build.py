@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvz.so")
-SOURCES = ["api.hip", "pool.hip", "codec.hip", "attention.hip", "measure.hip", "gaac.hip"]
+SOURCES = ["api.hip", "pool.hip", "codec.hip", "attention.hip", "measure.hip", "gaac.hip", "fp8.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -24,7 +24,7 @@
 //   * the query group (G <= 16 heads sharing the KV head) is the MFMA's head dimension;
 //   * online softmax in base 2 per head; rows of O are rescaled only when a head's max rises;
 //   * every unit writes (m, l, O) for its heads; attn_combine merges the splits.
-#include "gaac_internal.h"
+#include "fp8_internal.h"
 
 #include <math.h>
 
@@ -35,6 +35,8 @@ namespace {
 constexpr int kFmtBf16 = 0;   // uncompressed pages (baseline)
 constexpr int kFmtZf = 1;     // exponent-coded 12-bit pages
 constexpr int kFmtGaac = 2;   // group-adaptive additive code
+constexpr int kFmtFp8 = 3;    // uncompressed FP8 pages (the FP8 baseline)
+constexpr int kFmtFp8c = 4;   // exponent-coded FP8 tiles
 
 struct AttnParams {
   const uint16_t* q;
@@ -43,14 +45,15 @@ struct AttnParams {
   const int32_t* block_table;
   const int32_t* seq_lens;
   const int32_t* n_comp;
-  const uint16_t* tail;
-  const uint8_t* bases;         // GAAC only: [Hkv][2 (K,V)][2 (b3,b4)][128]
+  const void* tail;             // BF16 or (FP8 formats) FP8 [B][2][Hkv][16][128]
+  const uint8_t* bases;         // GAAC / FP8 tiles: [Hkv][2 (K,V)][2 (b3,b4)][128]
   float* out;                   // [B][Hq][128]
   float* ws_ml;                 // [units][G][2]
   float* ws_o;                  // [units][G][128]
   uint64_t arena_bytes;         // compressed only: groups must end 16 bytes before this
   int B, Hq, Hkv, G, max_pages, S, n_phys;
-  float scale_log2;
+  float scale_log2;             // sm_scale (* k_scale for FP8) * log2(e)
+  float v_scale;                // FP8 formats: the output is multiplied by it
 };
 
 struct KV8 {
@@ -71,6 +74,21 @@ struct GaacPage {
   GaacTileLoad k, v;
 };
 
+// One FP8 tile as loaded: a = the lane's sign+fraction words (compressed) or blocks 0,1
+// (uncompressed), b = its 12 code bytes (+4 unused) or blocks 2,3, the dword holding its mode
+// byte and one dword of the escape area (compressed only).
+struct Fp8TileLoad {
+  uint4 a, b;
+  uint32_t mode;
+  uint32_t esc;
+};
+struct Fp8Page {
+  Fp8TileLoad k, v;
+};
+struct Fp8RawPage {
+  uint4 k[2], v[2];
+};
+
 template <int FMT>
 struct PageBufOf {
   using type = KV8;
@@ -78,6 +96,14 @@ struct PageBufOf {
 template <>
 struct PageBufOf<kFmtGaac> {
   using type = GaacPage;
+};
+template <>
+struct PageBufOf<kFmtFp8> {
+  using type = Fp8RawPage;
+};
+template <>
+struct PageBufOf<kFmtFp8c> {
+  using type = Fp8Page;
 };
 
 __device__ __forceinline__ float lane_xor(float x, int m) { return __shfl_xor(x, m, 64); }
@@ -345,14 +371,17 @@ __device__ __forceinline__ SplitOf split_of(const int32_t* n_comp_v, const int32
   return r;
 }
 
-template <int GB, int FMT>
+template <int GB, int FMT, int FK = 0>
 __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
-  constexpr bool COMP = FMT != kFmtBf16;
+  // COMP: pages are found through the pool metadata (exponent-coded, GAAC or FP8 tiles)
+  constexpr bool COMP = FMT == kFmtZf || FMT == kFmtGaac || FMT == kFmtFp8c;
+  constexpr bool IS_FP8 = FMT == kFmtFp8 || FMT == kFmtFp8c;
+  constexpr bool CODED = FMT == kFmtGaac || FMT == kFmtFp8c;   // group-adaptive modes
   using PageBuf = typename PageBufOf<FMT>::type;
-  // GAAC: a 16 KiB table from four packed 3-bit codes to four bytes, filled by the whole
-  // workgroup before any wave leaves (one LDS read replaces the bit-field spreading)
-  __shared__ uint32_t s_spread3[FMT == kFmtGaac ? 4096 : 1];
-  if constexpr (FMT == kFmtGaac) {
+  // group-adaptive tiles: a 16 KiB table from four packed 3-bit codes to four bytes, filled by
+  // the whole workgroup before any wave leaves (one LDS read replaces the bit-field spreading)
+  __shared__ uint32_t s_spread3[CODED ? 4096 : 1];
+  if constexpr (CODED) {
     for (int x = threadIdx.x; x < 4096; x += 256) s_spread3[x] = gaac_spread3((uint32_t)x);
     __syncthreads();
   }
@@ -396,7 +425,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
   // 32j + 8*(lane/16) + 0..7: two dwords per base per block.  V chunk = dim 32j + lane%32 for
   // all eight values: one byte per base per block (byte j of vb3 / vb4).
   uint32_t kb3[4][2], kb4[4][2], vb3 = 0, vb4 = 0;
-  if constexpr (FMT == kFmtGaac) {
+  if constexpr (CODED) {
     const uint8_t* kbase = p.bases + (size_t)(kvh * 2 + 0) * 256;
     const uint8_t* vbase = p.bases + (size_t)(kvh * 2 + 1) * 256;
 #pragma unroll
@@ -428,13 +457,23 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
     if constexpr (COMP) {
       if (ok_l) {
         meta_l = p.meta[(size_t)phys_l * p.Hkv + kvh];
-        const uint64_t kend = (uint64_t)meta_l.x * KVZ_GRANULE_BYTES + group_bytes(meta_l.y);
-        const uint64_t vend = (uint64_t)meta_l.z * KVZ_GRANULE_BYTES + group_bytes(meta_l.w);
+        uint64_t kend, vend;
+        if constexpr (FMT == kFmtFp8c) {
+          using F = Fp8Fmt<FK>;
+          kend = (uint64_t)meta_l.x * kFp8Granule + (meta_l.y == kFp8TagsRaw ? kFp8RawTile : F::kSlot);
+          vend = (uint64_t)meta_l.z * kFp8Granule + (meta_l.w == kFp8TagsRaw ? kFp8RawTile : F::kSlot);
+        } else {
+          kend = (uint64_t)meta_l.x * KVZ_GRANULE_BYTES + group_bytes(meta_l.y);
+          vend = (uint64_t)meta_l.z * KVZ_GRANULE_BYTES + group_bytes(meta_l.w);
+        }
         ok_l = meta_l.x != KVZ_OFF_NONE && meta_l.z != KVZ_OFF_NONE && kend <= p.arena_bytes &&
                vend <= p.arena_bytes;
         if (FMT == kFmtGaac)   // a tile is either compressed (tags 0) or raw (tags all 0xFF)
           ok_l = ok_l && (meta_l.y == 0u || meta_l.y == 0xFFFFFFFFu) &&
                  (meta_l.w == 0u || meta_l.w == 0xFFFFFFFFu);
+        if (FMT == kFmtFp8c)   // compressed tags of this FP8 format, or raw
+          ok_l = ok_l && (meta_l.y == Fp8Fmt<FK>::kTagsComp || meta_l.y == kFp8TagsRaw) &&
+                 (meta_l.w == Fp8Fmt<FK>::kTagsComp || meta_l.w == kFp8TagsRaw);
         if (!ok_l) meta_l = make_uint4(0, 0, 0, 0);   // loads then stay at the arena start
       }
     }
@@ -463,8 +502,41 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
       t.mode = __builtin_amdgcn_raw_buffer_load_b32(aux, (int)(kGaacModeOff + 4u * (lane >> 2)), 0, kStreamLoad);
       t.esc = __builtin_amdgcn_raw_buffer_load_b32(aux, (int)(kGaacEscOff + 4u * (lane & 31)), 0, kStreamLoad);
     };
+    // FP8 tile: the same four loads whether it is compressed or not - the lane's 16 bytes at
+    // 16c (sign+fraction words, E5M2 ignoring the last 4) or blocks 0,1; its 12 code bytes (+4
+    // ignored) or blocks 2,3; the dword holding its mode byte; one dword of the escape area.
+    // An uncompressed tile's last two loads get a zero-size resource and touch no memory.
+    auto load_fp8_tile = [&](uint32_t off, bool raw, bool real, Fp8TileLoad& t) {
+      using F = Fp8Fmt<FK>;
+      const uint8_t* base = p.kv + (size_t)off * kFp8Granule;
+      const __amdgpu_buffer_rsrc_t r = group_rsrc(base, real ? (raw ? kFp8RawTile : F::kSlot) : 0u);
+      const __amdgpu_buffer_rsrc_t aux = group_rsrc(base, (real && !raw) ? F::kSlot : 0u);
+      t.a = bload16(r, raw ? 16u * lane : F::kSmLane * lane, 0);
+      t.b = bload16(r, raw ? 1024u + 16u * lane : F::kCodeOff + 12u * lane, 0);
+      t.mode = __builtin_amdgcn_raw_buffer_load_b32(aux, (int)(F::kModeOff + 4u * (lane >> 2)), 0, kStreamLoad);
+      t.esc = __builtin_amdgcn_raw_buffer_load_b32(aux, (int)(F::kEscOff + 4u * (lane & 15)), 0, kStreamLoad);
+    };
     auto load_page = [&](int i, PageBuf& r, bool real) {
-      if constexpr (FMT == kFmtGaac) {
+      real = real && ((ok_mask >> i) & 1ull);   // a page that cannot be read is never touched
+      if constexpr (FMT == kFmtFp8c) {
+        const uint32_t koff = (uint32_t)__builtin_amdgcn_readlane((int)meta_l.x, i);
+        const uint32_t voff = (uint32_t)__builtin_amdgcn_readlane((int)meta_l.z, i);
+        const uint32_t kt = (uint32_t)__builtin_amdgcn_readlane((int)meta_l.y, i);
+        const uint32_t vt = (uint32_t)__builtin_amdgcn_readlane((int)meta_l.w, i);
+        load_fp8_tile(koff, kt == kFp8TagsRaw, real, r.k);
+        load_fp8_tile(voff, vt == kFp8TagsRaw, real, r.v);
+        return;
+      } else if constexpr (FMT == kFmtFp8) {
+        const int phys = __builtin_amdgcn_readlane(phys_l, i);
+        const uint8_t* kb = p.kv + ((size_t)phys * 2 * p.Hkv + kvh) * kFp8RawTile;
+        const __amdgpu_buffer_rsrc_t kr = group_rsrc(kb, real ? kFp8RawTile : 0u);
+        const __amdgpu_buffer_rsrc_t vr = group_rsrc(kb + (size_t)p.Hkv * kFp8RawTile, real ? kFp8RawTile : 0u);
+        r.k[0] = bload16(kr, 16u * lane, 0);
+        r.k[1] = bload16(kr, 1024u + 16u * lane, 0);
+        r.v[0] = bload16(vr, 16u * lane, 0);
+        r.v[1] = bload16(vr, 1024u + 16u * lane, 0);
+        return;
+      } else if constexpr (FMT == kFmtGaac) {
         const uint32_t koff = (uint32_t)__builtin_amdgcn_readlane((int)meta_l.x, i);
         const uint32_t voff = (uint32_t)__builtin_amdgcn_readlane((int)meta_l.z, i);
         const uint32_t kt = (uint32_t)__builtin_amdgcn_readlane((int)meta_l.y, i);
@@ -562,6 +634,62 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
                                            b4lo, b4hi, any_raw);
       }
     };
+    // FP8 tile -> the four operand chunks (BF16).  Uncompressed: each block's 8 bytes are
+    // converted.  Compressed: the lane's escape bytes (at most 8) start at an exclusive scan of
+    // the lanes' escape counts; lanes 0..15 hold the 64-byte escape area as dwords and three
+    // lane shuffles give every lane a 64-bit window from its first escape byte, consumed group
+    // by group.  Exponents are rebuilt per byte and placed above the fraction bits.
+    auto fp8_ops = [&](const Fp8TileLoad& t, bool raw, bool is_k, uint4 (&ops)[4]) {
+      if (raw) {
+        ops[0] = fp8x8_to_bf16<FK>(t.a.x, t.a.y);
+        ops[1] = fp8x8_to_bf16<FK>(t.a.z, t.a.w);
+        ops[2] = fp8x8_to_bf16<FK>(t.b.x, t.b.y);
+        ops[3] = fp8x8_to_bf16<FK>(t.b.z, t.b.w);
+        return;
+      }
+      const uint32_t m8 = (t.mode >> (8 * (lane & 3))) & 0xFFu;
+      uint32_t len = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) len += fp8_escape_bytes<FK>((m8 >> (2 * j)) & 3u);
+      const bool any_raw = FK == KVZ_FP8_E5M2 && __ballot((m8 & 0xAAu) != 0u) != 0ull;
+      uint32_t lo = 0, hi = 0;
+      if (__ballot(len != 0u)) {
+        const uint32_t pos = gaac_exclusive_scan(len, lane);
+        const int q = (int)(pos >> 2);
+        const uint32_t d0 = (uint32_t)__shfl((int)t.esc, q, 64);
+        const uint32_t d1 = (uint32_t)__shfl((int)t.esc, q + 1, 64);
+        const uint32_t d2 = (uint32_t)__shfl((int)t.esc, q + 2, 64);
+        const uint32_t sh = 8u * (pos & 3u);
+        lo = __builtin_amdgcn_alignbit(d1, d0, sh);
+        hi = __builtin_amdgcn_alignbit(d2, d1, sh);
+      }
+      const uint32_t w[4] = {t.a.x, t.a.y, t.a.z, t.a.w};
+      const uint32_t cw[3] = {t.b.x, t.b.y, t.b.z};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t mode = (m8 >> (2 * j)) & 3u;
+        const uint32_t esc = lo;
+        const uint32_t nb8 = 8u * fp8_escape_bytes<FK>(mode);
+        lo = __builtin_amdgcn_alignbit(hi, lo, nb8);
+        hi = nb8 ? hi >> nb8 : hi;
+        uint32_t b3lo, b3hi, b4lo, b4hi;
+        if (is_k) {
+          b3lo = kb3[j][0];
+          b3hi = kb3[j][1];
+          b4lo = kb4[j][0];
+          b4hi = kb4[j][1];
+        } else {
+          b3lo = b3hi = ((vb3 >> (8 * j)) & 0xFFu) * 0x01010101u;
+          b4lo = b4hi = ((vb4 >> (8 * j)) & 0xFFu) * 0x01010101u;
+        }
+        uint32_t X, Y;
+        fp8_sm_xy<FK>(w, j, X, Y);
+        const uint32_t low24 = gaac_low24(cw, j);
+        const uint2 f = fp8_restore_group<FK>(X, Y, s_spread3[low24 & 0xFFFu], s_spread3[low24 >> 12],
+                                              mode, esc, b3lo, b3hi, b4lo, b4hi, any_raw);
+        ops[j] = fp8x8_to_bf16<FK>(f.x, f.y);
+      }
+    };
     auto process = [&](const PageBuf& buf, int i) {
       if (!((ok_mask >> i) & 1ull)) return;
       uint32_t kt = 0xFFFFFFFFu, vt = 0xFFFFFFFFu;
@@ -572,6 +700,13 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
       uint4 kops[4], vop[4];
       if constexpr (FMT == kFmtGaac) {
         gaac_ops(buf.k, kt != 0u, true, kops);
+      } else if constexpr (FMT == kFmtFp8c) {
+        fp8_ops(buf.k, kt == kFp8TagsRaw, true, kops);
+      } else if constexpr (FMT == kFmtFp8) {
+        kops[0] = fp8x8_to_bf16<FK>(buf.k[0].x, buf.k[0].y);
+        kops[1] = fp8x8_to_bf16<FK>(buf.k[0].z, buf.k[0].w);
+        kops[2] = fp8x8_to_bf16<FK>(buf.k[1].x, buf.k[1].y);
+        kops[3] = fp8x8_to_bf16<FK>(buf.k[1].z, buf.k[1].w);
       } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j) kops[j] = restore_if_coded(buf.k[j], (kt >> (8 * j)) & 0xFFu);
@@ -585,6 +720,13 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
       for (int r = 0; r < 4; ++r) sv[r] = sacc[r] * p.scale_log2;
       if constexpr (FMT == kFmtGaac) {
         gaac_ops(buf.v, vt != 0u, false, vop);
+      } else if constexpr (FMT == kFmtFp8c) {
+        fp8_ops(buf.v, vt == kFp8TagsRaw, false, vop);
+      } else if constexpr (FMT == kFmtFp8) {
+        vop[0] = fp8x8_to_bf16<FK>(buf.v[0].x, buf.v[0].y);
+        vop[1] = fp8x8_to_bf16<FK>(buf.v[0].z, buf.v[0].w);
+        vop[2] = fp8x8_to_bf16<FK>(buf.v[1].x, buf.v[1].y);
+        vop[3] = fp8x8_to_bf16<FK>(buf.v[1].z, buf.v[1].w);
       } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j) vop[j] = restore_if_coded(buf.v[j], (vt >> (8 * j)) & 0xFFu);
@@ -610,15 +752,51 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
     }
   }
 
-  // The BF16 tail page (natural layout [16][128]), masked to its n_tail tokens.
+  // The tail page (natural layout [16][128], BF16 - or FP8 for the FP8 formats), masked to its
+  // n_tail tokens; masked V values are zeros, so they add nothing even where p is 0.
   if (n_tail > 0 && p0 <= n_comp && n_comp < p1) {
-    const uint16_t* kt = p.tail + (((size_t)b * 2 + 0) * p.Hkv + kvh) * 2048;
-    const uint16_t* vt = p.tail + (((size_t)b * 2 + 1) * p.Hkv + kvh) * 2048;
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    uint4 vop[4];
+    if constexpr (IS_FP8) {
+      const uint8_t* kt = static_cast<const uint8_t*>(p.tail) + (((size_t)b * 2 + 0) * p.Hkv + kvh) * 2048;
+      const uint8_t* vt = static_cast<const uint8_t*>(p.tail) + (((size_t)b * 2 + 1) * p.Hkv + kvh) * 2048;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint4 kop = *reinterpret_cast<const uint4*>(kt + (lane & 15) * 128 + 32 * j + 8 * (lane >> 4));
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kop), as_bf16x8(qop[j]), sacc, 0, 0, 0);
+      for (int j = 0; j < 4; ++j) {
+        const uint2 k8 = *reinterpret_cast<const uint2*>(kt + (lane & 15) * 128 + 32 * j + 8 * (lane >> 4));
+        const uint4 kop = fp8x8_to_bf16<FK>(k8.x, k8.y);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kop), as_bf16x8(qop[j]), sacc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t f[2] = {0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int t0 = 8 * (lane >> 5) + i;
+          const uint32_t x = t0 < n_tail ? vt[t0 * 128 + 32 * j + (lane & 31)] : 0u;
+          f[i >> 2] |= x << (8 * (i & 3));
+        }
+        vop[j] = fp8x8_to_bf16<FK>(f[0], f[1]);
+      }
+    } else {
+      const uint16_t* kt = static_cast<const uint16_t*>(p.tail) + (((size_t)b * 2 + 0) * p.Hkv + kvh) * 2048;
+      const uint16_t* vt = static_cast<const uint16_t*>(p.tail) + (((size_t)b * 2 + 1) * p.Hkv + kvh) * 2048;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint4 kop = *reinterpret_cast<const uint4*>(kt + (lane & 15) * 128 + 32 * j + 8 * (lane >> 4));
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kop), as_bf16x8(qop[j]), sacc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t w[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int t0 = 8 * (lane >> 5) + 2 * m;
+          const uint32_t a = t0 < n_tail ? vt[t0 * 128 + 32 * j + (lane & 31)] : 0u;
+          const uint32_t c = t0 + 1 < n_tail ? vt[(t0 + 1) * 128 + 32 * j + (lane & 31)] : 0u;
+          w[m] = a | (c << 16);
+        }
+        vop[j] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
     }
     float sv[4];
 #pragma unroll
@@ -626,20 +804,12 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
       const int tok = 4 * (lane >> 4) + r;
       sv[r] = tok < n_tail ? sacc[r] * p.scale_log2 : -INFINITY;
     }
-    uint4 vop[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t w[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int t0 = 8 * (lane >> 5) + 2 * m;
-        const uint32_t a = t0 < n_tail ? vt[t0 * 128 + 32 * j + (lane & 31)] : 0u;
-        const uint32_t c = t0 + 1 < n_tail ? vt[(t0 + 1) * 128 + 32 * j + (lane & 31)] : 0u;
-        w[m] = a | (c << 16);
-      }
-      vop[j] = make_uint4(w[0], w[1], w[2], w[3]);
-    }
     sm.page(sv, vop, lane);
+  }
+
+  if constexpr (IS_FP8) {   // the V dequantization scale, applied once to O
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sm.o[j] *= p.v_scale;
   }
 
   float l_tot = sm.l_run + lane_xor(sm.l_run, 16);
@@ -777,17 +947,19 @@ struct CommonArgs {
   const int32_t* block_table;
   const int32_t* seq_lens;
   const int32_t* n_comp_pages;
-  const uint16_t* tail;
+  const void* tail;
   int32_t batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages, splits;
   float sm_scale;
   void* workspace;
   uint64_t workspace_bytes;
+  float k_scale = 1.f, v_scale = 1.f;   // FP8 formats only
 };
 
-template <int FMT>
+template <int FMT, int FK = 0>
 int launch_attention(const CommonArgs& a, const uint8_t* kv, const kvz_group_meta* meta,
                      const uint8_t* bases, hipStream_t s) {
-  constexpr bool COMP = FMT != kFmtBf16;
+  constexpr bool COMP = FMT == kFmtZf || FMT == kFmtGaac || FMT == kFmtFp8c;
+  constexpr bool CODED = FMT == kFmtGaac || FMT == kFmtFp8c;
   if (a.head_dim != KVZ_HEAD_DIM || a.page_size != KVZ_PAGE_TOKENS)
     return set_error(KVZ_EUNSUPPORTED, "only head_dim 128 and 16-token pages are supported");
   if (a.batch < 0 || a.num_q_heads <= 0 || a.num_kv_heads <= 0 || a.max_pages < 0)
@@ -802,18 +974,20 @@ int launch_attention(const CommonArgs& a, const uint8_t* kv, const kvz_group_met
   if (a.max_pages > 0 && (!kv || !a.block_table || (COMP && !meta)))
     return set_error(KVZ_EINVAL, "null page pointer argument");
   if (a.n_phys_pages < 0) return set_error(KVZ_EINVAL, "n_phys_pages < 0");
-  if (COMP && a.max_pages > 0 && a.arena_bytes < 4096)
-    return set_error(KVZ_EINVAL, "arena smaller than 4096 bytes");
+  if (COMP && a.max_pages > 0 && a.arena_bytes < (FMT == kFmtFp8c ? 2048u : 4096u))
+    return set_error(KVZ_EINVAL, "arena smaller than one record");
   if ((((uintptr_t)a.q) | ((uintptr_t)a.tail)) & 15u)
     return set_error(KVZ_EINVAL, "q and tail must be 16-byte aligned");
+  if (FMT == kFmtFp8 && (((uintptr_t)kv) & 15u))
+    return set_error(KVZ_EINVAL, "pages must be 16-byte aligned");
   if (COMP && (((uintptr_t)meta) & 15u)) return set_error(KVZ_EINVAL, "meta must be 16-byte aligned");
-  if (FMT == kFmtGaac && (!bases || (((uintptr_t)bases) & 7u)))
+  if (CODED && (!bases || (((uintptr_t)bases) & 7u)))
     return set_error(KVZ_EINVAL, "bases must be a non-null 8-byte aligned pointer");
   if (((uintptr_t)a.workspace) & 255u) return set_error(KVZ_EINVAL, "workspace must be 256-byte aligned");
   if (a.splits < 0 || a.splits > kMaxSplits) return set_error(KVZ_EINVAL, "splits out of range");
   const int S = a.splits ? a.splits
                          : choose_splits(a.batch, a.num_kv_heads, a.max_pages, device_cus(),
-                                         FMT == kFmtGaac ? kGaacWavesPerCu : 4);
+                                         CODED ? kGaacWavesPerCu : 4);
   uint64_t ml_bytes, need;
   workspace_layout(a.batch, a.num_q_heads, a.num_kv_heads, S, &ml_bytes, &need);
   if (a.workspace_bytes < need) return set_error(KVZ_EINVAL, "workspace too small");
@@ -840,15 +1014,16 @@ int launch_attention(const CommonArgs& a, const uint8_t* kv, const kvz_group_met
   p.G = G;
   p.max_pages = a.max_pages;
   p.S = S;
-  p.scale_log2 = a.sm_scale * 1.4426950408889634f;
+  p.scale_log2 = a.sm_scale * a.k_scale * 1.4426950408889634f;
+  p.v_scale = a.v_scale;
 
   const dim3 grid((unsigned)((units + 3) / 4));
   if (G <= 4)
-    hipLaunchKernelGGL((attn_split_kernel<4, FMT>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((attn_split_kernel<4, FMT, FK>), grid, dim3(256), 0, s, p);
   else if (G <= 8)
-    hipLaunchKernelGGL((attn_split_kernel<8, FMT>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((attn_split_kernel<8, FMT, FK>), grid, dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL((attn_split_kernel<16, FMT>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((attn_split_kernel<16, FMT, FK>), grid, dim3(256), 0, s, p);
   int rc = check_hip(hipGetLastError(), "attention launch");
   if (rc != KVZ_OK || S == 1) return rc;
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.batch * a.num_q_heads)),
@@ -904,4 +1079,30 @@ extern "C" int kvz_bf16_decode_attention(const kvz_bf16_attn_args* a, hipStream_
                a->page_size, a->max_pages, a->splits, a->sm_scale, a->workspace,
                a->workspace_bytes};
   return launch_attention<kFmtBf16>(c, a->pages, nullptr, nullptr, s);
+}
+
+extern "C" int kvz_fp8_decode_attention(const kvz_fp8_attn_args* a, hipStream_t s) {
+  if (!a) return set_error(KVZ_EINVAL, "args is null");
+  CommonArgs c{a->q, a->out, a->arena_bytes, a->n_phys_pages, a->block_table, a->seq_lens,
+               a->n_comp_pages, a->tail, a->batch, a->num_q_heads, a->num_kv_heads, a->head_dim,
+               a->page_size, a->max_pages, a->splits, a->sm_scale, a->workspace,
+               a->workspace_bytes, a->k_scale, a->v_scale};
+  if (a->format == KVZ_FP8_E4M3)
+    return launch_attention<kFmtFp8c, KVZ_FP8_E4M3>(c, a->arena, a->meta, a->bases, s);
+  if (a->format == KVZ_FP8_E5M2)
+    return launch_attention<kFmtFp8c, KVZ_FP8_E5M2>(c, a->arena, a->meta, a->bases, s);
+  return set_error(KVZ_EINVAL, "unknown FP8 format");
+}
+
+extern "C" int kvz_fp8_raw_decode_attention(const kvz_fp8_attn_args* a, hipStream_t s) {
+  if (!a) return set_error(KVZ_EINVAL, "args is null");
+  CommonArgs c{a->q, a->out, 0, a->n_phys_pages, a->block_table, a->seq_lens,
+               a->n_comp_pages, a->tail, a->batch, a->num_q_heads, a->num_kv_heads, a->head_dim,
+               a->page_size, a->max_pages, a->splits, a->sm_scale, a->workspace,
+               a->workspace_bytes, a->k_scale, a->v_scale};
+  if (a->format == KVZ_FP8_E4M3)
+    return launch_attention<kFmtFp8, KVZ_FP8_E4M3>(c, a->pages, nullptr, nullptr, s);
+  if (a->format == KVZ_FP8_E5M2)
+    return launch_attention<kFmtFp8, KVZ_FP8_E5M2>(c, a->pages, nullptr, nullptr, s);
+  return set_error(KVZ_EINVAL, "unknown FP8 format");
 }

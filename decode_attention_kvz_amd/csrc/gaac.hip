@@ -317,6 +317,8 @@ extern "C" int kvz_gaac_calibrate(const kvz_encode_item* d_items, int32_t n, uin
 extern "C" int kvz_gaac_encode_pages(kvz_pool* p, const kvz_gaac_item* d_items, int32_t n,
                                      uint32_t flags, hipStream_t s) {
   if (!p) return set_error(KVZ_EINVAL, "pool handle is null");
+  if (p->granule_bytes != KVZ_GRANULE_BYTES)
+    return set_error(KVZ_EINVAL, "pool was made for FP8 tiles (kvz_fp8_pool_init)");
   if (n < 0) return set_error(KVZ_EINVAL, "n < 0");
   if (n == 0) return KVZ_OK;
   if (!d_items) return set_error(KVZ_EINVAL, "items pointer is null");

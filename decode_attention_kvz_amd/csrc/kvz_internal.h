@@ -137,4 +137,5 @@ struct kvz_pool {
   uint64_t capacity;
   int device;
   void* scratch;   // device: per-tile counts of the allocation / free passes (in the state buffer)
+  uint32_t granule_bytes;   // 256 (BF16 formats) or 128 (FP8 tiles, kvz_fp8_pool_init)
 };

@@ -471,10 +471,14 @@ int check_pool(const kvz_pool* p) {
 
 using namespace kvz;
 
-extern "C" int kvz_pool_state_bytes(uint64_t arena_bytes, uint64_t* state_bytes) {
+namespace kvz {
+namespace {
+
+// A pool over `granule`-byte granules: capacity = whole granules minus one kept as a guard.
+int pool_state_bytes_g(uint64_t arena_bytes, uint64_t granule, uint64_t* state_bytes) {
   if (!state_bytes) return set_error(KVZ_EINVAL, "state_bytes is null");
-  if (arena_bytes < 2 * KVZ_GRANULE_BYTES) return set_error(KVZ_EINVAL, "arena smaller than 2 granules");
-  const uint64_t capacity = arena_bytes / KVZ_GRANULE_BYTES - 1;
+  if (arena_bytes < 2 * granule) return set_error(KVZ_EINVAL, "arena smaller than 2 granules");
+  const uint64_t capacity = arena_bytes / granule - 1;
   if (capacity >= KVZ_OFF_NONE) return set_error(KVZ_EINVAL, "arena too large for 32-bit granule offsets");
   uint64_t cap[kBins], base[kBins], entries;
   bin_layout(capacity, cap, base, &entries);
@@ -482,19 +486,19 @@ extern "C" int kvz_pool_state_bytes(uint64_t arena_bytes, uint64_t* state_bytes)
   return KVZ_OK;
 }
 
-extern "C" int kvz_pool_init(kvz_pool** out, void* d_arena, uint64_t arena_bytes, void* d_state,
-                             uint64_t state_bytes, hipStream_t s) {
+int pool_init_g(kvz_pool** out, void* d_arena, uint64_t arena_bytes, void* d_state,
+                uint64_t state_bytes, uint32_t granule, hipStream_t s) {
   if (!out || !d_arena || !d_state) return set_error(KVZ_EINVAL, "null pointer argument");
   if (((uintptr_t)d_arena | (uintptr_t)d_state) & 255u)
     return set_error(KVZ_EINVAL, "arena and state must be 256-byte aligned");
   uint64_t need = 0;
-  int rc = kvz_pool_state_bytes(arena_bytes, &need);
+  int rc = pool_state_bytes_g(arena_bytes, granule, &need);
   if (rc != KVZ_OK) return rc;
   if (state_bytes < need) return set_error(KVZ_EINVAL, "state buffer too small");
   int dev = 0;
   rc = check_hip(hipGetDevice(&dev), "hipGetDevice");
   if (rc != KVZ_OK) return rc;
-  const uint64_t capacity = arena_bytes / KVZ_GRANULE_BYTES - 1;
+  const uint64_t capacity = arena_bytes / granule - 1;
   PoolHdr t = {};
   t.magic = kPoolMagic;
   t.version = kPoolVersion;
@@ -513,8 +517,30 @@ extern "C" int kvz_pool_init(kvz_pool** out, void* d_arena, uint64_t arena_bytes
   p->capacity = capacity;
   p->device = dev;
   p->scratch = (uint8_t*)d_state + align256(kPoolHdrBytes + 4 * entries);
+  p->granule_bytes = granule;
   *out = p;
   return KVZ_OK;
+}
+
+}  // namespace
+}  // namespace kvz
+
+extern "C" int kvz_pool_state_bytes(uint64_t arena_bytes, uint64_t* state_bytes) {
+  return pool_state_bytes_g(arena_bytes, KVZ_GRANULE_BYTES, state_bytes);
+}
+
+extern "C" int kvz_pool_init(kvz_pool** out, void* d_arena, uint64_t arena_bytes, void* d_state,
+                             uint64_t state_bytes, hipStream_t s) {
+  return pool_init_g(out, d_arena, arena_bytes, d_state, state_bytes, KVZ_GRANULE_BYTES, s);
+}
+
+extern "C" int kvz_fp8_pool_state_bytes(uint64_t arena_bytes, uint64_t* state_bytes) {
+  return pool_state_bytes_g(arena_bytes, KVZ_FP8_GRANULE_BYTES, state_bytes);
+}
+
+extern "C" int kvz_fp8_pool_init(kvz_pool** out, void* d_arena, uint64_t arena_bytes, void* d_state,
+                                 uint64_t state_bytes, hipStream_t s) {
+  return pool_init_g(out, d_arena, arena_bytes, d_state, state_bytes, KVZ_FP8_GRANULE_BYTES, s);
 }
 
 extern "C" int kvz_pool_destroy(kvz_pool* p) {
@@ -560,12 +586,16 @@ extern "C" int kvz_slot_free(kvz_pool* p, kvz_group_meta* const* d_metas, int32_
 }
 
 namespace kvz {
-// Used by the encoders: the allocation step of kvz_encode_pages and kvz_gaac_encode_pages.
+// Used by the encoders: the allocation step of kvz_encode_pages, kvz_gaac_encode_pages and
+// kvz_fp8_encode_pages.
 int launch_alloc_for_items(kvz_pool* p, const kvz_encode_item* d_items, int n, hipStream_t s) {
   return run_alloc(p, ItemMetaAccess<kvz_encode_item>{d_items}, n, s);
 }
 int launch_alloc_for_gaac_items(kvz_pool* p, const kvz_gaac_item* d_items, int n, hipStream_t s) {
   return run_alloc(p, ItemMetaAccess<kvz_gaac_item>{d_items}, n, s);
+}
+int launch_alloc_for_fp8_items(kvz_pool* p, const kvz_fp8_item* d_items, int n, hipStream_t s) {
+  return run_alloc(p, ItemMetaAccess<kvz_fp8_item>{d_items}, n, s);
 }
 }  // namespace kvz
 

@@ -32,6 +32,9 @@ KVZ_KIND_K = 0
 KVZ_KIND_V = 1
 KVZ_ENC_FORCE_RAW = 1
 GRANULE = 256
+KVZ_FP8_E4M3 = 0
+KVZ_FP8_E5M2 = 1
+FP8_GRANULE = 128
 
 EXPORTED = [
     "kvz_version", "kvz_last_error", "kvz_device_check", "kvz_pool_state_bytes", "kvz_pool_init",
@@ -39,7 +42,9 @@ EXPORTED = [
     "kvz_attn_workspace_bytes", "kvz_decode_attention", "kvz_bf16_pack_pages",
     "kvz_bf16_decode_attention", "kvz_pool_stats", "kvz_stream_read", "kvz_decompress_pages",
     "kvz_pool_capacity", "kvz_gaac_calibrate", "kvz_gaac_encode_pages", "kvz_gaac_decompress_pages",
-    "kvz_gaac_decode_attention",
+    "kvz_gaac_decode_attention", "kvz_fp8_pool_state_bytes", "kvz_fp8_pool_init",
+    "kvz_fp8_calibrate", "kvz_fp8_encode_pages", "kvz_fp8_decompress_pages", "kvz_fp8_pack_pages",
+    "kvz_fp8_decode_attention", "kvz_fp8_raw_decode_attention",
 ]
 
 
@@ -88,12 +93,28 @@ class Bf16AttnArgs(ctypes.Structure):
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64)]
 
 
+class Fp8AttnArgs(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("out", ctypes.c_void_p), ("arena", ctypes.c_void_p),
+                ("arena_bytes", ctypes.c_uint64), ("meta", ctypes.c_void_p),
+                ("bases", ctypes.c_void_p), ("pages", ctypes.c_void_p),
+                ("n_phys_pages", ctypes.c_int32), ("block_table", ctypes.c_void_p),
+                ("seq_lens", ctypes.c_void_p), ("n_comp_pages", ctypes.c_void_p),
+                ("tail", ctypes.c_void_p), ("batch", ctypes.c_int32),
+                ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("max_pages", ctypes.c_int32), ("splits", ctypes.c_int32),
+                ("format", ctypes.c_uint32), ("sm_scale", ctypes.c_float),
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64)]
+
+
 # kvz_encode_item / kvz_block_ref as numpy record layouts (device arrays are built from these)
 ENCODE_ITEM_DTYPE = np.dtype([("src", "<u8"), ("dst", "<u8"), ("src_stride", "<u4"),
                               ("kind", "<u4")])
 BLOCK_REF_DTYPE = np.dtype([("meta", "<u8"), ("block", "<u4"), ("kind", "<u4")])
 GAAC_ITEM_DTYPE = np.dtype([("src", "<u8"), ("dst", "<u8"), ("src_stride", "<u4"),
                             ("kind", "<u4"), ("bases", "<u8")])
+FP8_ITEM_DTYPE = GAAC_ITEM_DTYPE          # kvz_fp8_item: the same fields (src points to bytes)
 
 _vp = ctypes.c_void_p
 _sig = {
@@ -124,6 +145,17 @@ _sig = {
                            ctypes.POINTER(Capacity)], ctypes.c_int),
     "kvz_decompress_pages": ([_vp, ctypes.c_uint64, _vp, ctypes.c_int64, ctypes.c_int32, _vp, _vp],
                              ctypes.c_int),
+    "kvz_fp8_pool_state_bytes": ([ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64)], ctypes.c_int),
+    "kvz_fp8_pool_init": ([ctypes.POINTER(_vp), _vp, ctypes.c_uint64, _vp, ctypes.c_uint64, _vp],
+                          ctypes.c_int),
+    "kvz_fp8_calibrate": ([_vp, ctypes.c_int32, ctypes.c_uint32, _vp, _vp, _vp], ctypes.c_int),
+    "kvz_fp8_encode_pages": ([_vp, _vp, ctypes.c_int32, ctypes.c_uint32, ctypes.c_uint32, _vp],
+                             ctypes.c_int),
+    "kvz_fp8_decompress_pages": ([_vp, ctypes.c_uint64, _vp, _vp, ctypes.c_int64, ctypes.c_int32,
+                                  ctypes.c_uint32, _vp, _vp], ctypes.c_int),
+    "kvz_fp8_pack_pages": ([_vp, _vp, ctypes.c_int64, ctypes.c_int32, _vp], ctypes.c_int),
+    "kvz_fp8_decode_attention": ([ctypes.POINTER(Fp8AttnArgs), _vp], ctypes.c_int),
+    "kvz_fp8_raw_decode_attention": ([ctypes.POINTER(Fp8AttnArgs), _vp], ctypes.c_int),
 }
 for _name, (_args, _ret) in _sig.items():
     _f = getattr(_lib, _name)
@@ -315,6 +347,93 @@ def kvz_gaac_decompress_pages(arena, meta, bases, dst, stream=None) -> None:
     _check(_lib.kvz_gaac_decompress_pages(_ptr(arena), arena.numel() * arena.element_size(),
                                           _ptr(meta), _ptr(bases), n_pages, hkv, _ptr(dst),
                                           _stream(stream)))
+
+
+def kvz_fp8_pool_state_bytes(arena_bytes: int) -> int:
+    out = ctypes.c_uint64()
+    _check(_lib.kvz_fp8_pool_state_bytes(arena_bytes, ctypes.byref(out)))
+    return out.value
+
+
+def kvz_fp8_pool_init(arena, state, stream=None):
+    """A pool of FP8 tiles (128-byte granules).  arena, state: uint8 device tensors."""
+    h = ctypes.c_void_p()
+    _check(_lib.kvz_fp8_pool_init(ctypes.byref(h), _ptr(arena),
+                                  arena.numel() * arena.element_size(), _ptr(state),
+                                  state.numel() * state.element_size(), _stream(stream)))
+    return h
+
+
+def kvz_fp8_calibrate(items, n: int, fmt: int, hist, bases, stream=None) -> None:
+    """items: device kvz_fp8_item records (pages of one (layer, K|V, KV head)); hist: device
+    >= 128*32 uint32 scratch; bases: device uint8 [2, 128] out (b3, b4)."""
+    if hist.numel() * hist.element_size() < 128 * 32 * 4 or bases.numel() < 256:
+        raise ValueError("hist or bases too small")
+    _check(_lib.kvz_fp8_calibrate(_ptr(items), n, fmt, _ptr(hist), _ptr(bases), _stream(stream)))
+
+
+def kvz_fp8_encode_pages(pool, items, n: int, fmt: int, flags: int = 0, stream=None) -> None:
+    """items: device tensor holding n kvz_fp8_item records (FP8_ITEM_DTYPE)."""
+    _check(_lib.kvz_fp8_encode_pages(pool, _ptr(items), n, fmt, flags, _stream(stream)))
+
+
+def kvz_fp8_decompress_pages(arena, meta, bases, fmt: int, dst, stream=None) -> None:
+    """meta: [n_pages, Hkv, 2, 8] uint8; bases: [Hkv, 2, 2, 128] uint8; dst: n_pages*2*Hkv*2048 B."""
+    n_pages, hkv = meta.shape[0], meta.shape[1]
+    if dst.numel() * dst.element_size() < n_pages * 2 * hkv * 2048 or bases.numel() < hkv * 512:
+        raise ValueError("dst or bases too small")
+    _check(_lib.kvz_fp8_decompress_pages(_ptr(arena), arena.numel() * arena.element_size(),
+                                         _ptr(meta), _ptr(bases), n_pages, hkv, fmt, _ptr(dst),
+                                         _stream(stream)))
+
+
+def kvz_fp8_pack_pages(src, dst, stream=None) -> None:
+    """src [n_pages,2,Hkv,16,128] uint8 natural FP8 pages -> dst [n_pages,2,Hkv,2048] uint8."""
+    if dst.numel() * dst.element_size() < src.numel() * src.element_size():
+        raise ValueError("dst too small")
+    _check(_lib.kvz_fp8_pack_pages(_ptr(src), _ptr(dst), src.shape[0], src.shape[2],
+                                   _stream(stream)))
+
+
+def _fp8_args(q, out, fmt, block_table, seq_lens, n_comp_pages, tail, sm_scale, k_scale, v_scale,
+              workspace, splits, num_kv_heads, n_phys, arena=None, meta=None, bases=None,
+              pages=None):
+    bsz, hq, hd = q.shape
+    return Fp8AttnArgs(
+        q=q.data_ptr(), out=out.data_ptr(), arena=None if arena is None else arena.data_ptr(),
+        arena_bytes=0 if arena is None else arena.numel() * arena.element_size(),
+        meta=None if meta is None else meta.data_ptr(),
+        bases=None if bases is None else bases.data_ptr(),
+        pages=None if pages is None else pages.data_ptr(), n_phys_pages=n_phys,
+        block_table=block_table.data_ptr(), seq_lens=seq_lens.data_ptr(),
+        n_comp_pages=n_comp_pages.data_ptr(), tail=None if tail is None else tail.data_ptr(),
+        batch=bsz, num_q_heads=hq, num_kv_heads=num_kv_heads, head_dim=hd, page_size=16,
+        max_pages=block_table.shape[1], splits=splits, format=fmt, sm_scale=sm_scale,
+        k_scale=k_scale, v_scale=v_scale, workspace=workspace.data_ptr(),
+        workspace_bytes=workspace.numel() * workspace.element_size())
+
+
+def kvz_fp8_decode_attention(q, out, fmt: int, arena, meta, bases, block_table, seq_lens,
+                             n_comp_pages, tail, sm_scale: float, k_scale: float, v_scale: float,
+                             workspace, splits: int = 0, stream=None) -> None:
+    """Fused attention over FP8 tiles.  meta [n_phys,Hkv,2,8] uint8; bases [Hkv,2,2,128] uint8;
+    tail [B,2,Hkv,16,128] uint8 (FP8) or None."""
+    if bases.numel() < meta.shape[1] * 512:
+        raise ValueError("bases too small")
+    a = _fp8_args(q, out, fmt, block_table, seq_lens, n_comp_pages, tail, sm_scale, k_scale,
+                  v_scale, workspace, splits, meta.shape[1], meta.shape[0], arena=arena,
+                  meta=meta, bases=bases)
+    _check(_lib.kvz_fp8_decode_attention(ctypes.byref(a), _stream(stream)))
+
+
+def kvz_fp8_raw_decode_attention(q, out, fmt: int, pages, block_table, seq_lens, n_comp_pages,
+                                 tail, sm_scale: float, k_scale: float, v_scale: float,
+                                 workspace, num_kv_heads: int, splits: int = 0,
+                                 stream=None) -> None:
+    """The FP8 baseline: pages [n_phys,2,Hkv,2048] uint8 (kvz_fp8_pack_pages)."""
+    a = _fp8_args(q, out, fmt, block_table, seq_lens, n_comp_pages, tail, sm_scale, k_scale,
+                  v_scale, workspace, splits, num_kv_heads, pages.shape[0], pages=pages)
+    _check(_lib.kvz_fp8_raw_decode_attention(ctypes.byref(a), _stream(stream)))
 
 
 def kvz_stream_read(buf, sink, workgroups: int = 0, stream=None) -> None:

@@ -17,15 +17,18 @@ GROUP_ELEMS = PAGE * HEAD_DIM
 
 
 class SlotArena:
-    """A pool arena plus its device state (one per device, shared by every layer)."""
+    """A pool arena plus its device state (one per device, shared by every layer).  fp8=True
+    makes a pool of FP8 tiles (128-byte granules, kvz_fp8_pool_init)."""
 
-    def __init__(self, arena_bytes: int, device="cuda"):
+    def __init__(self, arena_bytes: int, device="cuda", fp8: bool = False):
         arena_bytes = (int(arena_bytes) + 255) // 256 * 256
         self.device = torch.device(device)
+        self.fp8 = fp8
+        self.granule = kvz.FP8_GRANULE if fp8 else kvz.GRANULE
         self.arena = torch.zeros(arena_bytes, dtype=torch.uint8, device=self.device)
-        self.state = torch.zeros(kvz.kvz_pool_state_bytes(arena_bytes), dtype=torch.uint8,
-                                 device=self.device)
-        self.pool = kvz.kvz_pool_init(self.arena, self.state)
+        state_bytes = (kvz.kvz_fp8_pool_state_bytes if fp8 else kvz.kvz_pool_state_bytes)(arena_bytes)
+        self.state = torch.zeros(state_bytes, dtype=torch.uint8, device=self.device)
+        self.pool = (kvz.kvz_fp8_pool_init if fp8 else kvz.kvz_pool_init)(self.arena, self.state)
 
     def stats(self) -> dict:
         return kvz.kvz_pool_stats(self.pool)
@@ -50,8 +53,9 @@ def new_meta_table(n_phys: int, n_kv: int, device="cuda") -> torch.Tensor:
 
 
 def page_items(pages: torch.Tensor, page_ids, meta: torch.Tensor, phys_ids) -> np.ndarray:
-    """kvz_encode_item records for pages[s, p] (natural [n_seq, n_pages, 2, Hkv, 16, 128] bf16)
-    stored as physical page phys_ids[k] for (s, p) = page_ids[k].
+    """kvz_encode_item records for pages[s, p] (natural [n_seq, n_pages, 2, Hkv, 16, 128] bf16,
+    or uint8 FP8 pages) stored as physical page phys_ids[k] for (s, p) = page_ids[k].  The row
+    stride is 128 elements (bytes for FP8).
 
     Item order: page_ids order, then KV head, then K before V."""
     n_kv = pages.shape[3]
@@ -64,7 +68,7 @@ def page_items(pages: torch.Tensor, page_ids, meta: torch.Tensor, phys_ids) -> n
     src_group = (((sp[:, 0:1, None] * n_pages + sp[:, 1:2, None]) * 2 + kind[None, None, :])
                  * n_kv + h[None, :, None])                               # [n, Hkv, 2]
     dst_group = (phys[:, None, None] * n_kv + h[None, :, None]) * 2 + kind[None, None, :]
-    src = pages.data_ptr() + src_group.reshape(-1) * (GROUP_ELEMS * 2)
+    src = pages.data_ptr() + src_group.reshape(-1) * (GROUP_ELEMS * pages.element_size())
     dst = meta.data_ptr() + dst_group.reshape(-1) * 8
     kinds = np.broadcast_to(kind[None, None, :], src_group.shape).reshape(-1)
     return kvz.encode_items(src.astype(np.uint64), dst.astype(np.uint64), HEAD_DIM, kinds)
@@ -165,3 +169,65 @@ def workspace(batch: int, num_q_heads: int, num_kv_heads: int, max_pages: int, s
               device="cuda") -> torch.Tensor:
     nbytes = kvz.kvz_attn_workspace_bytes(batch, num_q_heads, num_kv_heads, max_pages, splits)
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------------------------
+# FP8 tiles
+# ---------------------------------------------------------------------------------------------
+def fp8_page_items(pages: torch.Tensor, page_ids, meta: torch.Tensor, phys_ids,
+                   bases: torch.Tensor) -> np.ndarray:
+    """kvz_fp8_item records for uint8 FP8 pages [n_seq, n_pages, 2, Hkv, 16, 128], in
+    page_items order; bases [Hkv, 2, 2, 128] uint8 of this layer (device)."""
+    assert pages.dtype == torch.uint8
+    return gaac_page_items(pages, page_ids, meta, phys_ids, bases)
+
+
+def fp8_encode(arena: SlotArena, items: np.ndarray, fmt: int, flags: int = 0,
+               stream=None) -> torch.Tensor:
+    assert arena.fp8, "FP8 tiles need an FP8 pool"
+    d = torch.from_numpy(np.ascontiguousarray(items)).to(arena.device)
+    n = items.size // kvz.FP8_ITEM_DTYPE.itemsize
+    kvz.kvz_fp8_encode_pages(arena.pool, d, n, fmt, flags, stream)
+    return d
+
+
+def fp8_calibrate(pages: torch.Tensor, fmt: int, device="cuda") -> torch.Tensor:
+    """Bases [Hkv, 2, 2, 128] uint8 from FP8 calibration pages [n_seq, n_pages, 2, Hkv, 16, 128]
+    uint8 (device): one kvz_fp8_calibrate call per (K|V, KV head)."""
+    n_kv = pages.shape[3]
+    assert pages.is_contiguous() and pages.dtype == torch.uint8
+    bases = torch.zeros((n_kv, 2, 2, HEAD_DIM), dtype=torch.uint8, device=device)
+    hist = torch.empty(128 * 32, dtype=torch.int32, device=device)
+    n_pg = pages.shape[0] * pages.shape[1]
+    keep = []
+    for h in range(n_kv):
+        for kind in range(2):
+            g = (np.arange(n_pg, dtype=np.int64) * 2 + kind) * n_kv + h
+            src = pages.data_ptr() + g * GROUP_ELEMS
+            items = torch.from_numpy(kvz.gaac_items(src.astype(np.uint64), np.zeros(n_pg, np.uint64),
+                                                    HEAD_DIM, np.full(n_pg, kind),
+                                                    np.zeros(n_pg, np.uint64))).to(device)
+            keep.append(items)
+            kvz.kvz_fp8_calibrate(items, n_pg, fmt, hist, bases[h, kind])
+    torch.cuda.synchronize()
+    return bases
+
+
+def fp8_decompress_pages(arena: SlotArena, meta: torch.Tensor, bases: torch.Tensor, fmt: int,
+                         out: torch.Tensor | None = None) -> torch.Tensor:
+    """Every tile of the meta table [n_phys, Hkv, 2, 8] rebuilt into uncompressed FP8 pages
+    [n_phys, 2, Hkv, 2048] uint8 (kvz_fp8_decompress_pages)."""
+    n, hkv = meta.shape[0], meta.shape[1]
+    if out is None:
+        out = torch.empty((n, 2, hkv, 2048), dtype=torch.uint8, device=meta.device)
+    kvz.kvz_fp8_decompress_pages(arena.arena, meta, bases, fmt, out)
+    return out
+
+
+def pack_fp8_pages(pages_by_phys: torch.Tensor) -> torch.Tensor:
+    """Uncompressed FP8 pages [n_phys, 2, Hkv, 2048] uint8 (the FP8 chunk layout) from natural
+    FP8 pages [n_phys, 2, Hkv, 16, 128] uint8 (kvz_fp8_pack_pages)."""
+    n, _, hkv = pages_by_phys.shape[:3]
+    dst = torch.empty((n, 2, hkv, 2048), dtype=torch.uint8, device=pages_by_phys.device)
+    kvz.kvz_fp8_pack_pages(pages_by_phys.contiguous(), dst)
+    return dst

@@ -14,6 +14,7 @@ KV value model (per layer; sigma is per (K|V, KV head, dim) = channel):
 `sample` > 0 draws other values (z, signs, forced positions, stress) from the same per-channel
 sigma - another sample of the same layer, as calibration data of one model would be.
 Queries: q ~ N(0,1), rounded to BF16.
+FP8 pages (fp8_kv_pages): the same values converted to E4M3 or E5M2 by torch.
 """
 from __future__ import annotations
 
@@ -73,6 +74,39 @@ def kv_pages(n_seq: int, n_pages: int, n_kv: int, *, seed: int, layer: int = 0,
         w = torch.where(nonfin, sgn | 0x7F80 | mant, w)
         kv = (((w + 32768) & 0xFFFF) - 32768).to(torch.int16).view(torch.bfloat16)
     return kv
+
+
+FP8_DTYPES = {0: torch.float8_e4m3fn, 1: torch.float8_e5m2}   # KVZ_FP8_E4M3, KVZ_FP8_E5M2
+
+
+def fp8_kv_pages(n_seq: int, n_pages: int, n_kv: int, *, seed: int, fmt: int, layer: int = 0,
+                 u_max: float = 3.0, forced_frac: float = 0.05, forced_exp: float = 4.0,
+                 stress: bool = False, sample: int = 0, device="cpu") -> torch.Tensor:
+    """FP8 KV pages [n_seq, n_pages, 2, n_kv, 16, 128] as uint8 bytes: the BF16 value model
+    above (forced elements at +-sigma_c * 2**forced_exp, which stays inside E4M3's range for
+    u_max <= 3), converted to FP8 by torch (round to nearest even) - the initial FP8 conversion
+    of a KV cache.  Stress values, each element independently: +-0 (1%), a subnormal (exponent
+    field 0, nonzero fraction, 0.5%), an all-ones exponent field with any fraction and sign (NaN
+    in E4M3 only for fraction 7; Inf or NaN in E5M2) (0.1%)."""
+    kv = kv_pages(n_seq, n_pages, n_kv, seed=seed, layer=layer, u_max=u_max,
+                  forced_frac=forced_frac, forced_exp=forced_exp, stress=False, sample=sample,
+                  device=device)
+    x = kv.float().to(FP8_DTYPES[fmt]).view(torch.uint8)
+    del kv
+    if stress:
+        g = _gen(seed, 3_000_003 + 2 * layer + 7 * int(sample), device)
+        shape = x.shape
+        mw = 3 if fmt == 0 else 2
+        r = torch.rand(shape, generator=g, device=device)
+        sgn = (torch.rand(shape, generator=g, device=device) < 0.5).to(torch.int32) << 7
+        frac = torch.randint(0, 1 << mw, shape, generator=g, device=device, dtype=torch.int32)
+        w = x.to(torch.int32)
+        w = torch.where(r < 0.01, sgn, w)
+        w = torch.where((r >= 0.01) & (r < 0.015), sgn | torch.clamp(frac, min=1), w)
+        top = (0x78 if fmt == 0 else 0x7C)
+        w = torch.where((r >= 0.015) & (r < 0.016), sgn | top | frac, w)
+        x = w.to(torch.uint8)
+    return x.contiguous()
 
 
 def queries(batch: int, num_q_heads: int, *, seed: int, device="cpu") -> torch.Tensor:

@@ -278,6 +278,114 @@ int kvz_gaac_decompress_pages(const void* d_arena, uint64_t arena_bytes,
  * 00x4 / FFx4 is skipped.  Same output contract as kvz_decode_attention. */
 int kvz_gaac_decode_attention(const kvz_attn_args* a, const uint8_t* d_bases, hipStream_t s);
 
+/* ---------------------------------------------------------------------------------------------
+ * Third format: the same exponent code on FP8 KV ([GAAC] appendix "Relation to FP8 KV", Table 7:
+ * KV converted to FP8 - E4M3 or E5M2 - compresses further, losslessly, with the code of section
+ * "Lossless KV Compression").  FP8 values follow the OCP formats: E4M3 "fn" (bias 7, no
+ * infinities, S.1111.111 is NaN) and E5M2 (bias 15, IEEE-style Inf/NaN).  Reading*: sign and
+ * fraction are kept (4 bits in E4M3, 3 in E5M2); the exponent field (4 or 5 bits) takes the group
+ * modes of the second format - 3-bit offsets from b3, 4-bit offsets from b4, raw - with windows
+ * calibrated inside the field; a raw group's escape holds the exponent bits above the low three
+ * (1 byte in E4M3, 2 in E5M2: value i's bits at 2i..2i+1).  All-3-bit tiles are 7.25 / 6.25
+ * bits per value.
+ * Uncompressed FP8 tile* (2048 B, "FP8 chunk layout"): chunk c of block j (the MFMA operand
+ * chunks above, 8 values) at byte 1024*(j/2) + 16c + 8*(j%2).
+ * Compressed record*: sign+fraction plane (E4M3: 1024 B, lane c's 16 bytes at 16c, word j =
+ * X | rotl32(Y, 4); E5M2: 768 B, lane c's 12 bytes at 12c, words t = 0..2 = X | rotl32(Y, 3)
+ * of block t and block 3 in bits 5..6 of every byte: word 0 = fraction of values 0..3, word 1
+ * of values 4..7, word 2 bit 5 / bit 6 = sign of value k / k+4; X / Y = the bytes s<<7 | fraction
+ * of values 0..3 / 4..7), code plane (768 B as in the second format), mode plane (64 B), then
+ * at most 64 escape bytes.  A compressed record takes 1920 B (E4M3) / 1664 B (E5M2), i.e. 15 /
+ * 13 granules of 128 bytes; a tile whose escapes exceed 64 bytes is stored uncompressed (2048 B,
+ * 16 granules).  FP8 tiles live in a pool made by kvz_fp8_pool_init, whose granule is 128 bytes;
+ * the tile's tags give the pool its run class as in the first format (12 + number of 0xFF tag
+ * bytes granules): FF FF FF 00 (compressed E4M3), FF 00 00 00 (compressed E5M2), FF FF FF FF
+ * (uncompressed).  Metadata offsets count 128-byte granules.
+ * ------------------------------------------------------------------------------------------- */
+#define KVZ_FP8_E4M3 0u
+#define KVZ_FP8_E5M2 1u
+#define KVZ_FP8_GRANULE_BYTES 128
+
+/* One completed FP8 page of one (layer, KV head, K|V). */
+typedef struct {
+  const uint8_t* src;    /* device: 16 rows of 128 FP8 values, natural order [token][dim]       */
+  kvz_group_meta* dst;   /* device: where the tile's metadata is written                          */
+  uint32_t src_stride;   /* bytes between consecutive tokens of src, >= 128, multiple of 8       */
+  uint32_t kind;         /* KVZ_KIND_K or KVZ_KIND_V                                              */
+  const uint8_t* bases;  /* device [2][128]: b3 then b4 of this (layer, K|V, KV head), per dim    */
+} kvz_fp8_item;
+
+/* Attention over FP8 KV.  Scores use the K values times k_scale, the output the V values times
+ * v_scale (a per-layer dequantization scale each).  Fused path (kvz_fp8_decode_attention):
+ * arena/arena_bytes/meta/bases as for the second format (meta offsets in 128-byte granules;
+ * bases device [Hkv][2 (K,V)][2 (b3,b4)][128], 8-byte aligned); uncompressed path
+ * (kvz_fp8_raw_decode_attention): pages device [n_phys][2][Hkv][2048] in the FP8 chunk layout
+ * (kvz_fp8_pack_pages).  tail: device [B][2][Hkv][16][128] FP8 or NULL.  Other fields and the
+ * output contract as for kvz_decode_attention. */
+typedef struct {
+  const uint16_t* q;            /* device [B][Hq][128] BF16                                      */
+  float* out;                   /* device [B][Hq][128] fp32                                      */
+  const uint8_t* arena;         /* fused: FP8 pool arena                                         */
+  uint64_t arena_bytes;
+  const kvz_group_meta* meta;   /* fused: [n_phys_pages][Hkv][2]                                 */
+  const uint8_t* bases;         /* fused: [Hkv][2][2][128]                                       */
+  const uint8_t* pages;         /* uncompressed: [n_phys_pages][2][Hkv][2048]                    */
+  int32_t n_phys_pages;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* n_comp_pages;
+  const uint8_t* tail;
+  int32_t batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages, splits;
+  uint32_t format;              /* KVZ_FP8_E4M3 or KVZ_FP8_E5M2                                  */
+  float sm_scale, k_scale, v_scale;
+  void* workspace;              /* >= kvz_attn_workspace_bytes(...), 256-B aligned               */
+  uint64_t workspace_bytes;
+} kvz_fp8_attn_args;
+
+/* Bytes of device state, and pool creation, for a pool of FP8 tiles: kvz_pool_state_bytes /
+ * kvz_pool_init with 128-byte granules (capacity arena_bytes/128 - 1 granules, one guard
+ * granule).  kvz_slot_alloc/free, kvz_pool_stats and kvz_pool_capacity work on it unchanged
+ * (in its granules); only kvz_fp8_encode_pages writes tiles into it. */
+int kvz_fp8_pool_state_bytes(uint64_t arena_bytes, uint64_t* state_bytes);
+int kvz_fp8_pool_init(kvz_pool** out, void* d_arena, uint64_t arena_bytes, void* d_state,
+                      uint64_t state_bytes, hipStream_t s);
+
+/* Calibrate one base set of FP8 pages ([GAAC] "Lossless KV Compression": per dim, the windows
+ * of 8 and 16 exponents holding the most values, inside [0, 15] (E4M3) or [0, 31] (E5M2); ties
+ * to the smallest base).  Only src and src_stride of the n items are read.  d_hist: device
+ * [128][32] uint32 scratch (overwritten).  d_bases: device [2][128] uint8 out (b3 then b4). */
+int kvz_fp8_calibrate(const kvz_fp8_item* d_items, int32_t n, uint32_t format, uint32_t* d_hist,
+                      uint8_t* d_bases, hipStream_t s);
+
+/* Encode completed FP8 pages: classify the groups of each tile, keep it uncompressed when its
+ * escapes exceed 64 bytes (or with KVZ_ENC_FORCE_RAW), allocate its run from an FP8 pool (same
+ * rule and order as kvz_slot_alloc), write the record and the metadata.  KVZ_EINVAL if the pool
+ * was not made by kvz_fp8_pool_init.  Each item's dst must be distinct. */
+int kvz_fp8_encode_pages(kvz_pool* p, const kvz_fp8_item* d_items, int32_t n, uint32_t format,
+                         uint32_t flags, hipStream_t s);
+
+/* Decompress-first for FP8 tiles: rebuild every tile of n_pages physical pages (d_meta device
+ * [n_pages][Hkv][2]) into the uncompressed FP8 pages d_dst [n_pages][2][Hkv][2048] (the FP8
+ * chunk layout; byte-identical to kvz_fp8_pack_pages of the natural pages).  A tile that is not
+ * stored, carries other tags or does not lie inside arena_bytes becomes zeros. */
+int kvz_fp8_decompress_pages(const void* d_arena, uint64_t arena_bytes,
+                             const kvz_group_meta* d_meta, const uint8_t* d_bases,
+                             int64_t n_pages, int32_t num_kv_heads, uint32_t format,
+                             uint8_t* d_dst, hipStream_t s);
+
+/* Lay out natural FP8 pages (device [n_pages][2][Hkv][16][128]) in the FP8 chunk layout
+ * (device [n_pages][2][Hkv][2048]): the uncompressed FP8 cache of kvz_fp8_raw_decode_attention. */
+int kvz_fp8_pack_pages(const uint8_t* d_src, uint8_t* d_dst, int64_t n_pages,
+                       int32_t num_kv_heads, hipStream_t s);
+
+/* Fused decode attention over FP8 tiles: records are rebuilt bit-exactly in registers and the
+ * FP8 values converted exactly to BF16 for the MFMA products ([GAAC] "Attention with On-the-Fly
+ * Decompression").  A page whose tiles carry other tags is skipped. */
+int kvz_fp8_decode_attention(const kvz_fp8_attn_args* a, hipStream_t s);
+
+/* The same attention over uncompressed FP8 pages (the FP8 baseline). */
+int kvz_fp8_raw_decode_attention(const kvz_fp8_attn_args* a, hipStream_t s);
+
 /* Workspace bytes the attention calls (kvz_decode_attention, kvz_gaac_decode_attention,
  * kvz_bf16_decode_attention) need for these sizes.  splits = 0: enough for the automatic
  * split count of every one of them (the group-adaptive format uses twice as many splits). */
