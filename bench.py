@@ -43,6 +43,7 @@ FORCED = 0.05
 SEED = 2
 VARIANT_LAYERS, VARIANT_U_MAX = 8, 3.0
 GAAC_LAYERS = 8
+FP8_LAYERS = 8
 N_PHYS = B * N_COMP
 SCALE = 1.0 / math.sqrt(128.0)
 
@@ -126,6 +127,7 @@ def main():
     ap.add_argument("--no-baseline", action="store_true")
     ap.add_argument("--no-variant", action="store_true")
     ap.add_argument("--no-gaac", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="for hardware-counter runs: one layer of fused and baseline attention "
                          "(3 launches each) and a 1 GiB device copy as a traffic reference")
@@ -257,6 +259,8 @@ def main():
     read_peak = stream_read_peak(timed)
     variant = None if args.no_variant else compressible_variant(args, dev, seq_lens, n_comp, ws)
     gaac_leg = None if args.no_gaac else gaac_format(args, dev, seq_lens, n_comp, ws)
+    fp8_leg = None if args.no_fp8 else {name: fp8_format(args, dev, seq_lens, n_comp, ws, fmt)
+                                        for name, fmt in (("e4m3", 0), ("e5m2", 1))}
     del g_attn, g_comp
     cpu = None if args.no_cpu_baseline else cpu_baseline(layers)
 
@@ -308,6 +312,7 @@ def main():
                                                (float(np.median(enc_layer_us)) * 1e-6) / 1e9, 1)},
         "compressible_variant": variant,
         "gaac_format": gaac_leg,
+        "fp8_formats": fp8_leg,
     }
     print(json.dumps(line), flush=True)
     arena.close()
@@ -426,6 +431,100 @@ def gaac_format(args, dev, seq_lens, n_comp, ws):
            "decompress_first_us_per_layer": round(dfirst_us, 2)}
     log(f"gaac format: fused {res['gaac']:.1f} us/layer vs bf16 {res['bf16']:.1f} "
         f"(storage ratio {out['storage_ratio_vs_bf16']}, raw tiles {raw_tiles:.4f})")
+    return out
+
+
+def fp8_format(args, dev, seq_lens, n_comp, ws, fmt):
+    """The third page format (the exponent code on FP8 KV) on the headline shape, 8 layers: KV
+    from the BF16 data model with u~U[-3,3] (so every value lies inside E4M3's range) and 5%
+    forced blocks, converted to FP8; bases per layer calibrated on another sample of the layer.
+    Fused attention over the coded tiles vs the uncompressed FP8 kernel (checked bit-identical at
+    equal split counts) vs decompress-first, and the storage ratios."""
+    import torch
+    from decode_attention_kvz_amd import kvz, paged, synth
+    name = ("e4m3", "e5m2")[fmt]
+    arena = paged.SlotArena(FP8_LAYERS * (N_PHYS + B) * HKV * 2 * 2048 + (16 << 20), device=dev,
+                            fp8=True)
+    rng = np.random.default_rng(SEED + 7)
+    layers = []
+    for layer in range(FP8_LAYERS):
+        cal = synth.fp8_kv_pages(4, 32, HKV, seed=SEED, fmt=fmt, layer=layer, u_max=3.0,
+                                 forced_frac=FORCED, sample=1, device=dev)
+        bases = paged.fp8_calibrate(cal, fmt)
+        del cal
+        pages = synth.fp8_kv_pages(B, N_COMP + 1, HKV, seed=SEED, fmt=fmt, layer=layer, u_max=3.0,
+                                   forced_frac=FORCED, device=dev)
+        block_table = rng.permutation(N_PHYS).reshape(B, N_COMP).astype(np.int32)
+        meta = paged.new_meta_table(N_PHYS, HKV, device=dev)
+        items = paged.fp8_page_items(pages, [(b, p) for b in range(B) for p in range(N_COMP)],
+                                     meta, block_table.reshape(-1), bases)
+        d_items = paged.fp8_encode(arena, items, fmt)
+        inv = torch.as_tensor(np.argsort(block_table.reshape(-1)), device=dev)
+        store = paged.pack_fp8_pages(pages[:, :N_COMP].reshape(N_PHYS, 2, HKV, 16, 128)[inv])
+        layers.append(dict(meta=meta, bases=bases, store=store,
+                           block_table=torch.from_numpy(block_table).to(dev),
+                           tail=pages[:, N_COMP].contiguous(),
+                           q=synth.queries(B, HQ, seed=SEED * 1000 + layer, device=dev),
+                           out=torch.empty((B, HQ, 128), dtype=torch.float32, device=dev)))
+        torch.cuda.synchronize()
+        del d_items, pages
+    st = arena.stats()
+    rec = st["live_granules"] * 128 / FP8_LAYERS
+    # a compressed tile takes 15 (E4M3) or 13 (E5M2) granules of 128 bytes, an uncompressed 16
+    comp_gran = 15 if fmt == 0 else 13
+    raw_tiles = (st["live_granules"] - comp_gran * st["live_runs"]) / (16 - comp_gran) / st["live_runs"]
+
+    def call(L, fused, out, splits):
+        if fused:
+            kvz.kvz_fp8_decode_attention(L["q"], out, fmt, arena.arena, L["meta"], L["bases"],
+                                         L["block_table"], seq_lens, n_comp, L["tail"], SCALE,
+                                         1.0, 1.0, ws, splits)
+        else:
+            kvz.kvz_fp8_raw_decode_attention(L["q"], out, fmt, L["store"], L["block_table"],
+                                             seq_lens, n_comp, L["tail"], SCALE, 1.0, 1.0, ws,
+                                             HKV, splits)
+    res = {}
+    for mode in ("fused", "fp8"):
+        res[mode] = graph_us_per_layer(
+            lambda: [call(L, mode == "fused", L["out"], args.splits) for L in layers],
+            FP8_LAYERS, args)
+    L = layers[-1]
+    same = [torch.empty_like(L["out"]) for _ in range(2)]
+    call(L, True, same[0], 16)
+    call(L, False, same[1], 16)
+    torch.cuda.synchronize()
+    assert torch.equal(same[0], same[1]), "FP8 fused attention differs from the FP8 kernel"
+    for L in layers:
+        del L["store"]
+    scratch = torch.empty((N_PHYS, 2, HKV, 2048), dtype=torch.uint8, device=dev)
+
+    def dfirst():
+        for L in layers:
+            paged.fp8_decompress_pages(arena, L["meta"], L["bases"], fmt, scratch)
+            kvz.kvz_fp8_raw_decode_attention(L["q"], L["out"], fmt, scratch, L["block_table"],
+                                             seq_lens, n_comp, L["tail"], SCALE, 1.0, 1.0, ws,
+                                             HKV, args.splits)
+    dfirst_us = graph_us_per_layer(dfirst, FP8_LAYERS, args)
+    arena.close()
+    small = N_PHYS * 4 + B * 2 * HKV * 16 * 128 + B * HQ * 128 * 2 + B * HQ * 128 * 4
+    alg = rec + N_PHYS * HKV * 16 + HKV * 512 + small
+    alg_fp8 = N_PHYS * HKV * 2 * 2048 + small
+    fp8_bytes = N_PHYS * HKV * 2 * 2048
+    out = {"label": f"exponent code on FP8 {name.upper()} KV (third format), headline shape, KV "
+                    "data model u~U[-3,3] with 5% forced blocks converted to FP8, 8 layers, "
+                    "per-layer bases calibrated on another sample of the layer",
+           "record_bytes_per_layer": int(rec),
+           "storage_ratio_vs_fp8": round(fp8_bytes / rec, 4),
+           "storage_ratio_vs_bf16": round(2 * fp8_bytes / rec, 4),
+           "raw_tile_fraction": round(raw_tiles, 4),
+           "fused_us_per_layer": round(res["fused"], 2),
+           "fused_achieved_GBps": round(alg / (res["fused"] * 1e-6) / 1e9, 1),
+           "fp8_kernel_us_per_layer": round(res["fp8"], 2),
+           "fp8_kernel_achieved_GBps": round(alg_fp8 / (res["fp8"] * 1e-6) / 1e9, 1),
+           "speedup_vs_fp8_kernel": round(res["fp8"] / res["fused"], 4),
+           "decompress_first_us_per_layer": round(dfirst_us, 2)}
+    log(f"fp8 {name}: fused {res['fused']:.1f} us/layer vs fp8 kernel {res['fp8']:.1f} "
+        f"(storage ratio vs FP8 {out['storage_ratio_vs_fp8']}, raw tiles {raw_tiles:.4f})")
     return out
 
 
