@@ -10,7 +10,7 @@
 //
 // Allocation and free follow item order exactly (the i-th item of class k pops bin k from the
 // top, or pushes onto it; frontier requests get prefix-summed offsets), computed in parallel as
-// a three-pass scan over tiles of 4096 items: count the classes per tile, scan the tiles in one
+// a three-pass scan over tiles of 1024 items: count the classes per tile, scan the tiles in one
 // workgroup, then assign (or push) per tile.  Calls of more than kMaxTiles tiles run as
 // consecutive chunks.  The per-tile counts and bases live in a fixed scratch area of the pool
 // state, so the pool needs no memory beyond the state the caller allocated.
@@ -25,7 +25,8 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 
-constexpr int kIpt = 8;   // items per thread: the loads of a tile's 4096 items are in flight together
+constexpr int kIpt = 2;   // items per thread (tiles of 1024 items: small calls still spread over several
+                          // workgroups; measured 89 -> 69 us for a 9,216-group completion + free)
 constexpr int kTile = kThreads * kIpt;
 constexpr int kMaxTiles = 2 * kThreads;   // tiles per chunk: the scan pass takes 2 per thread
 constexpr int kChunkItems = kTile * kMaxTiles;

@@ -355,7 +355,7 @@ def _random_tags(rng, n, p_raw):
 
 
 def test_slot_pool_calls_spanning_many_tiles_match_model():
-    """Calls of several 4096-item tiles: frontier offsets, bin pops that run out part-way,
+    """Calls of many 1024-item tiles: frontier offsets, bin pops that run out part-way,
     exhaustion in a later tile, and frees spanning tiles all equal the pool model."""
     announce("slot pool: multi-tile calls")
     rng = np.random.default_rng(61)
@@ -379,8 +379,8 @@ def test_slot_pool_calls_spanning_many_tiles_match_model():
 
 
 def test_slot_alloc_call_larger_than_one_chunk_matches_model():
-    """One call of 4 Mi + 5000 items (two chunks of the tiled allocator): bin state and the
-    frontier's request prefix carry from the first chunk into the second."""
+    """One call of 1 Mi + 5000 items (two chunks of the tiled allocator: 1024 tiles of 1024
+    items each): bin state and the frontier's request prefix carry into the second chunk."""
     announce("slot pool: call of more than one chunk")
     rng = np.random.default_rng(62)
     arena = paged.SlotArena(400_001 * 256)
@@ -389,10 +389,10 @@ def test_slot_alloc_call_larger_than_one_chunk_matches_model():
     seed_tags = np.concatenate([_random_tags(rng, 3000, 0.0), np.full((500, 4), 0xFF, np.uint8)])
     offs = _alloc_and_check(arena, model, seed_tags)
     _free(arena, model, [(int(o), t.tolist()) for o, t in zip(offs, seed_tags)])
-    n = 4 * 1024 * 1024 + 5000
+    n = 1024 * 1024 + 5000
     tags = np.full((n, 4), 60, dtype=np.uint8)
     tags[rng.random(n) < 0.3, 0] = 0xFF             # classes 0 and 1 only ...
-    late = 4 * 1024 * 1024 + rng.choice(5000, 300, replace=False)
+    late = 1024 * 1024 + rng.choice(5000, 300, replace=False)
     tags[late] = 0xFF                                # ... until the second chunk: class 4
     _alloc_and_check(arena, model, tags)
     _check_stats(arena, model)
