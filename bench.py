@@ -49,7 +49,7 @@ SCALE = 1.0 / math.sqrt(128.0)
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_qwen8k_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "decode_attention_kvz_amd", "csrc", f)
-                  for f in ("attention.hip", "kvz_internal.h", "gaac_internal.h")]
+                  for f in ("attention.hip", "kvz_internal.h", "gaac_internal.h", "fp8_internal.h")]
 
 
 def log(msg):
@@ -434,20 +434,15 @@ def gaac_format(args, dev, seq_lens, n_comp, ws):
     return out
 
 
-def fp8_format(args, dev, seq_lens, n_comp, ws, fmt):
-    """The third page format (the exponent code on FP8 KV) on the headline shape, 8 layers: KV
-    from the BF16 data model with u~U[-3,3] (so every value lies inside E4M3's range) and 5%
-    forced blocks, converted to FP8; bases per layer calibrated on another sample of the layer.
-    Fused attention over the coded tiles vs the uncompressed FP8 kernel (checked bit-identical at
-    equal split counts) vs decompress-first, and the storage ratios."""
+def build_fp8_layers(arena, n_layers, dev, fmt):
+    """Layers of the headline shape in FP8 (fmt 0 = E4M3, 1 = E5M2) for the FP8 tiles: KV from the
+    BF16 data model with u~U[-3,3] and 5% forced blocks converted to FP8, bases calibrated on
+    another sample of the layer; plus the uncompressed FP8 page store."""
     import torch
-    from decode_attention_kvz_amd import kvz, paged, synth
-    name = ("e4m3", "e5m2")[fmt]
-    arena = paged.SlotArena(FP8_LAYERS * (N_PHYS + B) * HKV * 2 * 2048 + (16 << 20), device=dev,
-                            fp8=True)
+    from decode_attention_kvz_amd import paged, synth
     rng = np.random.default_rng(SEED + 7)
     layers = []
-    for layer in range(FP8_LAYERS):
+    for layer in range(n_layers):
         cal = synth.fp8_kv_pages(4, 32, HKV, seed=SEED, fmt=fmt, layer=layer, u_max=3.0,
                                  forced_frac=FORCED, sample=1, device=dev)
         bases = paged.fp8_calibrate(cal, fmt)
@@ -468,6 +463,21 @@ def fp8_format(args, dev, seq_lens, n_comp, ws, fmt):
                            out=torch.empty((B, HQ, 128), dtype=torch.float32, device=dev)))
         torch.cuda.synchronize()
         del d_items, pages
+    return layers
+
+
+def fp8_format(args, dev, seq_lens, n_comp, ws, fmt):
+    """The third page format (the exponent code on FP8 KV) on the headline shape, 8 layers: KV
+    from the BF16 data model with u~U[-3,3] (so every value lies inside E4M3's range) and 5%
+    forced blocks, converted to FP8; bases per layer calibrated on another sample of the layer.
+    Fused attention over the coded tiles vs the uncompressed FP8 kernel (checked bit-identical at
+    equal split counts) vs decompress-first, and the storage ratios."""
+    import torch
+    from decode_attention_kvz_amd import kvz, paged
+    name = ("e4m3", "e5m2")[fmt]
+    arena = paged.SlotArena(FP8_LAYERS * (N_PHYS + B) * HKV * 2 * 2048 + (16 << 20), device=dev,
+                            fp8=True)
+    layers = build_fp8_layers(arena, FP8_LAYERS, dev, fmt)
     st = arena.stats()
     rec = st["live_granules"] * 128 / FP8_LAYERS
     # a compressed tile takes 15 (E4M3) or 13 (E5M2) granules of 128 bytes, an uncompressed 16
@@ -635,7 +645,7 @@ def pmc_probe(args, dev):
     """Launches for a counter run: a 1 GiB device-to-device copy (reads and writes exactly
     1 GiB; the reference that scales FETCH_SIZE / WRITE_SIZE), then 3 fused and 3 baseline
     attention calls on layer 0 of the workload, then 3 calls over the same layer in the
-    group-adaptive format."""
+    group-adaptive format, then 3 fused and 3 uncompressed calls over an FP8 E4M3 layer."""
     import torch
     from decode_attention_kvz_amd import kvz, paged
     src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
@@ -665,6 +675,19 @@ def pmc_probe(args, dev):
     torch.cuda.synchronize()
     log(f"pmc probe: GAAC layer {garena.stats()['live_granules'] * 256} record bytes")
     garena.close()
+    farena = paged.SlotArena((N_PHYS + B) * HKV * 2 * 2048 + (16 << 20), device=dev, fp8=True)
+    F8 = build_fp8_layers(farena, 1, dev, 0)[0]
+    for _ in range(3):
+        kvz.kvz_fp8_decode_attention(F8["q"], F8["out"], 0, farena.arena, F8["meta"], F8["bases"],
+                                     F8["block_table"], seq_lens, n_comp, F8["tail"], SCALE, 1.0,
+                                     1.0, ws, args.splits)
+    for _ in range(3):
+        kvz.kvz_fp8_raw_decode_attention(F8["q"], F8["out"], 0, F8["store"], F8["block_table"],
+                                         seq_lens, n_comp, F8["tail"], SCALE, 1.0, 1.0, ws, HKV,
+                                         args.splits)
+    torch.cuda.synchronize()
+    log(f"pmc probe: FP8 E4M3 layer {farena.stats()['live_granules'] * 128} record bytes")
+    farena.close()
     log(f"pmc probe done: {st['live_granules'] * 256} record bytes in the layer, algorithmic "
         f"{alg_bytes_per_layer(st['live_granules'] * 256):.0f} bytes per call; kernel source "
         f"sha256 {kernel_source_sha()}")
