@@ -7,6 +7,7 @@ import torch
 
 from decode_attention_kvz_amd import kvz, paged, synth
 from oracle import fp8
+from oracle.alloc import SlotPoolModel
 from oracle.cache import Fp8OracleCache
 
 from gpu_util import announce, check_rows, sm_scale
@@ -311,3 +312,103 @@ def test_full_size_qwen8k_layer_sampled(fmt):
     got = lay.fused(q, 0.5, 2.0).cpu().numpy()
     for b in (0, 13):
         check_rows(got[b], ref[b], what=f"b={b}")
+
+
+def test_churn_reuses_freed_runs_like_the_pool_model():
+    """Encode FP8 tiles of both formats into one FP8 pool, free a random subset, encode more:
+    the freed 13-, 15- and 16-granule runs are reused from their bins exactly as the oracle's
+    pool model says, the records are byte-identical to the oracle's, and every stored tile
+    decodes back to its input (decompress-first into the FP8 chunk layout)."""
+    announce("fp8 pool churn")
+    rng = np.random.default_rng(94)
+    arena = paged.SlotArena(600 * 128 * 16, fp8=True)
+    model = SlotPoolModel(arena.stats()["capacity_granules"])   # one pool for both formats
+    live = []                            # (fmt, meta row on device, page, kind, bases)
+    for rnd in range(3):
+        for fmt in FORMATS:
+            pages = synth.fp8_kv_pages(1, 6, 2, seed=95 + 10 * rnd + fmt, fmt=fmt,
+                                       forced_frac=0.6 if rnd == 1 else 0.05, device="cuda")
+            if rnd == 2:                 # a few tiles too wide for the escape slot
+                p = pages.cpu().numpy()
+                p[0, 0, :, :] = rng.integers(0, 0x70, p[0, 0].shape)
+                pages = torch.from_numpy(p).cuda()
+            bases = paged.fp8_calibrate(pages, fmt)
+            meta = paged.new_meta_table(6, 2)
+            items = paged.fp8_page_items(pages, [(0, p) for p in range(6)], meta, list(range(6)), bases)
+            d = paged.fp8_encode(arena, items, fmt)
+            torch.cuda.synchronize()
+            nat, bh = pages.cpu().numpy(), bases.cpu().numpy()
+            tiles = [(p, h, kind) for p in range(6) for h in range(2) for kind in range(2)]
+            enc = [fp8.encode_tile(nat[0, p, kind, h], kind, fmt, bh[h, kind, 0], bh[h, kind, 1])
+                   for p, h, kind in tiles]
+            offs = model.alloc([fp8.tags_of(raw, fmt) for raw, _ in enc])
+            m = meta.cpu().numpy()
+            arena_h = arena.arena.cpu().numpy()
+            for (p, h, kind), (raw, rec), off in zip(tiles, enc, offs):
+                got_off = int.from_bytes(m[p, h, kind, :4].tobytes(), "little")
+                assert got_off == off and list(m[p, h, kind, 4:]) == fp8.tags_of(raw, fmt)
+                np.testing.assert_array_equal(arena_h[off * 128: off * 128 + rec.size], rec)
+                live.append((fmt, meta, (p, h, kind), nat[0, p, kind, h], bases, off,
+                             fp8.tags_of(raw, fmt)))
+            del d
+            st = arena.stats()
+            assert st["frontier_granules"] == model.frontier
+            assert st["free_runs"] == [len(model.bins[k]) for k in range(5)]
+            assert st["live_runs"] == model.live_runs and st["live_granules"] == model.live_granules
+        # free a random half of what is live
+        order = rng.permutation(len(live))
+        victims = [live[i] for i in order[: len(live) // 2]]
+        live = [live[i] for i in order[len(live) // 2:]]
+        ptrs = torch.from_numpy(np.asarray(
+            [v[1].data_ptr() + ((v[2][0] * 2 + v[2][1]) * 2 + v[2][2]) * 8 for v in victims],
+            dtype=np.int64)).cuda()
+        kvz.kvz_slot_free(arena.pool, ptrs)
+        model.free([(v[5], v[6]) for v in victims])
+        torch.cuda.synchronize()
+    assert any(len(model.bins[k]) for k in (1, 3, 4))
+    # every live tile still decodes to its input
+    for fmt, meta, (p, h, kind), page, bases, off, tags in live:
+        out = paged.fp8_decompress_pages(arena, meta, bases, fmt).cpu().numpy()
+        np.testing.assert_array_equal(out[p, kind, h], fp8.raw_tile(page, kind))
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_graph_replays_match_eager(fmt):
+    """Fused and uncompressed FP8 attention captured in HIP graphs: every replay, with eager work
+    and synchronization in between, equals the eager call."""
+    announce(f"fp8 {NAME[fmt]} graph replay")
+    cal = synth.fp8_kv_pages(1, 8, 8, seed=96, fmt=fmt, sample=1, device="cuda")
+    bases = paged.fp8_calibrate(cal, fmt)
+    pages = synth.fp8_kv_pages(4, 33, 8, seed=96, fmt=fmt, device="cuda")
+    lay = Fp8Layer(pages, [16 * 32 + 9, 16 * 20, 16 * 32 + 16, 7], [32, 20, 32, 0], fmt, bases,
+                   seed=96)
+    q = synth.queries(4, 32, seed=97, device="cuda")
+    for fused in (True, False):
+        eager = (lay.fused if fused else lay.raw)(q, 0.5, 2.0).clone()
+        out = torch.zeros_like(eager)
+        ws = paged.workspace(4, 32, 8, lay.block_table.shape[1])
+        store = None
+        if not fused:
+            nat = torch.zeros((lay.n_phys, 2, 8, 16, 128), dtype=torch.uint8, device="cuda")
+            for b in range(4):
+                nc = int(lay.n_comp[b])
+                if nc:
+                    nat[torch.as_tensor(lay.phys_of[b, :nc], device="cuda", dtype=torch.long)] = pages[b, :nc]
+            store = paged.pack_fp8_pages(nat)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            if fused:
+                kvz.kvz_fp8_decode_attention(q, out, fmt, lay.arena.arena, lay.meta, bases,
+                                             lay.block_table, lay.seq_lens, lay.n_comp, lay.tail,
+                                             sm_scale(), 0.5, 2.0, ws)
+            else:
+                kvz.kvz_fp8_raw_decode_attention(q, out, fmt, store, lay.block_table, lay.seq_lens,
+                                                 lay.n_comp, lay.tail, sm_scale(), 0.5, 2.0, ws, 8)
+        for rep in range(4):
+            out.fill_(float("nan"))
+            _ = (q.float() * 2).sum()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, eager), f"fused={fused} replay {rep}"
