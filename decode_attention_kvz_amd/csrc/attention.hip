@@ -590,25 +590,48 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
       uint32_t len = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) len += gaac_escape_bytes((m8 >> (2 * j)) & 3u);
-      uint32_t pos = gaac_exclusive_scan(len, lane);
-      // no raw group in the wave: each lane has at most four escape bytes (one per 4-bit
-      // group), all inside the two dwords fetched here once for the tile
       const bool any_raw = __ballot((m8 & 0xAAu) != 0u) != 0ull;
-      uint32_t win = 0;
-      if (!any_raw && __ballot(len != 0u)) {
+      auto bases_of = [&](int j, uint32_t& b3lo, uint32_t& b3hi, uint32_t& b4lo, uint32_t& b4hi) {
+        if (is_k) {
+          b3lo = kb3[j][0];
+          b3hi = kb3[j][1];
+          b4lo = kb4[j][0];
+          b4hi = kb4[j][1];
+        } else {
+          b3lo = b3hi = ((vb3 >> (8 * j)) & 0xFFu) * 0x01010101u;
+          b4lo = b4hi = ((vb4 >> (8 * j)) & 0xFFu) * 0x01010101u;
+        }
+      };
+      if (!any_raw) {
+        // No raw group in the wave (the common case): a lane has at most four one-byte
+        // escapes, all in the two dwords at its first escape byte; the four groups are one
+        // straight-line block (no branch per group), so their dependent chains interleave.
+        const uint32_t pos = gaac_exclusive_scan_small(len);
         const int q = (int)(pos >> 2);
         const uint32_t d0 = (uint32_t)__shfl((int)t.esc, q, 64);
         const uint32_t d1 = (uint32_t)__shfl((int)t.esc, q + 1, 64);
-        win = __builtin_amdgcn_alignbit(d1, d0, 8u * (pos & 3u));
+        uint32_t win = __builtin_amdgcn_alignbit(d1, d0, 8u * (pos & 3u));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t mode = (m8 >> (2 * j)) & 3u;
+          const uint32_t esc = win & 0xFFu;        // this group's byte if it is a 4-bit group
+          win = mode == kGaacMode4 ? win >> 8 : win;
+          uint32_t b3lo, b3hi, b4lo, b4hi;
+          bases_of(j, b3lo, b3hi, b4lo, b4hi);
+          const uint32_t low24 = gaac_low24(t.code, j);
+          ops[j] = gaac_restore_group_spread(t.c[j].x, t.c[j].y, s_spread3[low24 & 0xFFFu],
+                                             s_spread3[low24 >> 12], mode, esc, 0u, b3lo, b3hi,
+                                             b4lo, b4hi, false);
+        }
+        return;
       }
+      // Some raw group in the wave: up to 20 escape bytes per lane, fetched group by group.
+      uint32_t pos = gaac_exclusive_scan(len, lane);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t mode = (m8 >> (2 * j)) & 3u;
         uint32_t esc = 0, esc_hi = 0;
-        if (!any_raw) {
-          esc = win & 0xFFu;                      // this group's byte if it is a 4-bit group
-          if (mode == kGaacMode4) win >>= 8;
-        } else if (__ballot(mode != kGaacMode3)) {
+        if (__ballot(mode != kGaacMode3)) {
           const int q = (int)(pos >> 2);
           const uint32_t d0 = (uint32_t)__shfl((int)t.esc, q, 64);
           const uint32_t d1 = (uint32_t)__shfl((int)t.esc, q + 1, 64);
@@ -619,19 +642,11 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
           pos += gaac_escape_bytes(mode);
         }
         uint32_t b3lo, b3hi, b4lo, b4hi;
-        if (is_k) {
-          b3lo = kb3[j][0];
-          b3hi = kb3[j][1];
-          b4lo = kb4[j][0];
-          b4hi = kb4[j][1];
-        } else {
-          b3lo = b3hi = ((vb3 >> (8 * j)) & 0xFFu) * 0x01010101u;
-          b4lo = b4hi = ((vb4 >> (8 * j)) & 0xFFu) * 0x01010101u;
-        }
+        bases_of(j, b3lo, b3hi, b4lo, b4hi);
         const uint32_t low24 = gaac_low24(t.code, j);
         ops[j] = gaac_restore_group_spread(t.c[j].x, t.c[j].y, s_spread3[low24 & 0xFFFu],
                                            s_spread3[low24 >> 12], mode, esc, esc_hi, b3lo, b3hi,
-                                           b4lo, b4hi, any_raw);
+                                           b4lo, b4hi, true);
       }
     };
     // FP8 tile -> the four operand chunks (BF16).  Uncompressed: each block's 8 bytes are
@@ -651,27 +666,11 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
       uint32_t len = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) len += fp8_escape_bytes<FK>((m8 >> (2 * j)) & 3u);
+      // E5M2 raw groups escape two bytes; E4M3 groups never more than one
       const bool any_raw = FK == KVZ_FP8_E5M2 && __ballot((m8 & 0xAAu) != 0u) != 0ull;
-      uint32_t lo = 0, hi = 0;
-      if (__ballot(len != 0u)) {
-        const uint32_t pos = gaac_exclusive_scan(len, lane);
-        const int q = (int)(pos >> 2);
-        const uint32_t d0 = (uint32_t)__shfl((int)t.esc, q, 64);
-        const uint32_t d1 = (uint32_t)__shfl((int)t.esc, q + 1, 64);
-        const uint32_t d2 = (uint32_t)__shfl((int)t.esc, q + 2, 64);
-        const uint32_t sh = 8u * (pos & 3u);
-        lo = __builtin_amdgcn_alignbit(d1, d0, sh);
-        hi = __builtin_amdgcn_alignbit(d2, d1, sh);
-      }
       const uint32_t w[4] = {t.a.x, t.a.y, t.a.z, t.a.w};
       const uint32_t cw[3] = {t.b.x, t.b.y, t.b.z};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t mode = (m8 >> (2 * j)) & 3u;
-        const uint32_t esc = lo;
-        const uint32_t nb8 = 8u * fp8_escape_bytes<FK>(mode);
-        lo = __builtin_amdgcn_alignbit(hi, lo, nb8);
-        hi = nb8 ? hi >> nb8 : hi;
+      auto group = [&](int j, uint32_t mode, uint32_t esc, bool wave_has_raw) {
         uint32_t b3lo, b3hi, b4lo, b4hi;
         if (is_k) {
           b3lo = kb3[j][0];
@@ -686,8 +685,43 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
         fp8_sm_xy<FK>(w, j, X, Y);
         const uint32_t low24 = gaac_low24(cw, j);
         const uint2 f = fp8_restore_group<FK>(X, Y, s_spread3[low24 & 0xFFFu], s_spread3[low24 >> 12],
-                                              mode, esc, b3lo, b3hi, b4lo, b4hi, any_raw);
+                                              mode, esc, b3lo, b3hi, b4lo, b4hi, wave_has_raw);
         ops[j] = fp8x8_to_bf16<FK>(f.x, f.y);
+      };
+      if (!any_raw) {
+        // at most four one-byte escapes per lane, in the two dwords at its first escape byte;
+        // the four groups are one straight-line block (no branch per group)
+        const uint32_t pos = gaac_exclusive_scan_small(len);
+        const int q = (int)(pos >> 2);
+        const uint32_t d0 = (uint32_t)__shfl((int)t.esc, q, 64);
+        const uint32_t d1 = (uint32_t)__shfl((int)t.esc, q + 1, 64);
+        uint32_t win = __builtin_amdgcn_alignbit(d1, d0, 8u * (pos & 3u));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t mode = (m8 >> (2 * j)) & 3u;
+          const uint32_t esc = win & 0xFFu;
+          win = fp8_escape_bytes<FK>(mode) ? win >> 8 : win;
+          group(j, mode, esc, false);
+        }
+        return;
+      }
+      // a raw E5M2 group in the wave: up to 8 escape bytes per lane, a 64-bit window
+      const uint32_t pos = gaac_exclusive_scan(len, lane);
+      const int q = (int)(pos >> 2);
+      const uint32_t d0 = (uint32_t)__shfl((int)t.esc, q, 64);
+      const uint32_t d1 = (uint32_t)__shfl((int)t.esc, q + 1, 64);
+      const uint32_t d2 = (uint32_t)__shfl((int)t.esc, q + 2, 64);
+      const uint32_t sh = 8u * (pos & 3u);
+      uint32_t lo = __builtin_amdgcn_alignbit(d1, d0, sh);
+      uint32_t hi = __builtin_amdgcn_alignbit(d2, d1, sh);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t mode = (m8 >> (2 * j)) & 3u;
+        const uint32_t esc = lo;
+        const uint32_t nb8 = 8u * fp8_escape_bytes<FK>(mode);
+        lo = __builtin_amdgcn_alignbit(hi, lo, nb8);
+        hi = nb8 ? hi >> nb8 : hi;
+        group(j, mode, esc, true);
       }
     };
     auto process = [&](const PageBuf& buf, int i) {

@@ -39,6 +39,19 @@ __device__ __forceinline__ uint32_t gaac_exclusive_scan(uint32_t v, int lane) {
   return sum;
 }
 
+// The same scan for v < 8 (at most four one-byte escapes per lane): three bits.
+__device__ __forceinline__ uint32_t gaac_exclusive_scan_small(uint32_t v) {
+  uint32_t sum = 0;
+#pragma unroll
+  for (int bit = 0; bit < 3; ++bit) {
+    const uint64_t m = __ballot((v >> bit) & 1u);
+    const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    sum += below << bit;
+  }
+  return sum;
+}
+
 // Block j's 24 low-code bits from a lane's 12 code bytes (3 dwords, little-endian).
 __device__ __forceinline__ uint32_t gaac_low24(const uint32_t (&cw)[3], int j) {
   switch (j) {
