@@ -1,6 +1,6 @@
-// Paged split-K GQA decode attention over losslessly compressed BF16 pages (two formats, each
-// restored bit-exactly in registers), and the same kernel over uncompressed BF16 pages (the
-// baseline).
+// Paged split-K GQA decode attention over losslessly compressed KV pages (three formats, each
+// restored bit-exactly in registers), and the same kernel over uncompressed BF16 and FP8 pages
+// (the baselines).
 //
 // Follows "GAAC: Lossless KV Compression for Bandwidth-Efficient LLM Inference on Personal
 // Devices", section "Attention with On-the-Fly Decompression": compressed tiles and their
@@ -9,9 +9,11 @@
 // The restore and the K/V operand layouts follow "ZipFusion: Fusing Lossless KV Decompression
 // with Attention for Efficient LLM Decoding", section "How it works".
 //
-// Three page formats share the kernel: BF16 (the baseline), the exponent-coded 12-bit pages,
-// and the group-adaptive additive code ("GAAC: ...", section "Lossless KV Compression"), whose
-// tiles are rebuilt with calibrated per-dim bases.
+// Five page formats share the kernel: BF16 (the baseline), the exponent-coded 12-bit pages, the
+// group-adaptive additive code ("GAAC: ...", section "Lossless KV Compression"), whose tiles are
+// rebuilt with calibrated per-dim bases, and FP8 pages (E4M3 / E5M2) uncompressed or in the same
+// group-adaptive code on the FP8 exponent field ("GAAC: ...", appendix "Relation to FP8 KV"),
+// converted exactly to BF16 in registers for the MFMA products.
 //
 // Work decomposition (one wave = one unit = (sequence b, KV head, split s)):
 //   * a unit walks a contiguous range of its sequence's pages (the tail page counts as the

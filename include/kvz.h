@@ -1,6 +1,6 @@
 /*
- * kvz.h - lossless 12-bit exponent-coded BF16 KV pages and fused paged decode attention
- *         for AMD Instinct MI355X (gfx950).
+ * kvz.h - lossless exponent-coded KV pages (12-bit BF16 pages; group-adaptive BF16 and FP8
+ *         tiles) and fused paged decode attention for AMD Instinct MI355X (gfx950).
  *
  * The operations follow two pages:
  *   [ZF]   "ZipFusion: Fusing Lossless KV Decompression with Attention for Efficient LLM
@@ -8,9 +8,11 @@
  *          register restore; 8-byte group metadata; the memory manager).
  *   [GAAC] "GAAC: Lossless KV Compression for Bandwidth-Efficient LLM Inference on Personal
  *          Devices" - sections "Attention with On-the-Fly Decompression" (compressed blocks and
- *          the BF16 tail share one softmax; no decompressed copy in device memory) and
+ *          the BF16 tail share one softmax; no decompressed copy in device memory),
  *          "Block-Wise Compression Scheduling" (fill-then-finalize; fixed-capacity slots in two
- *          storage classes; a block that does not fit keeps its BF16 form).
+ *          storage classes; a block that does not fit keeps its BF16 form), "Lossless KV
+ *          Compression" (the group-adaptive code of the second and third formats) and
+ *          appendix "Relation to FP8 KV" (the code on FP8 KV).
  *
  * Format (readings where the pages are silent are marked *):
  *   - A page holds 16 tokens.  Per (layer, KV head) its K and its V are each one GROUP of four
