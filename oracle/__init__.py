@@ -1,4 +1,5 @@
-"""CPU oracle for the exponent-coded BF16 KV format and decode attention over it.
+"""CPU oracle for the exponent-coded KV formats (12-bit BF16 pages, group-adaptive BF16 and FP8
+tiles), the slot-pool model, and decode attention over them.
 
 TEST INFRASTRUCTURE ONLY.  Imported by tests/, by the smoke check in __graft_entry__ and by
 the CPU-baseline leg of bench.py; never by the HIP library or its binding, and it imports
