@@ -111,3 +111,45 @@ def test_gaac_entry_points_reject_bad_arguments_on_the_host():
     assert lib.kvz_gaac_decode_attention(ctypes.byref(args), ctypes.c_void_p(260), None) == kvz.KVZ_EINVAL
     args.head_dim = 64
     assert lib.kvz_gaac_decode_attention(ctypes.byref(args), p, None) == kvz.KVZ_EUNSUPPORTED
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="libkvz.so not built")
+def test_fp8_entry_points_reject_bad_arguments_on_the_host():
+    """The FP8 format's calls validate their arguments before anything reaches a device; an FP8
+    pool has twice the granules (128 bytes) of a BF16 pool over the same arena."""
+    from decode_attention_kvz_amd import kvz
+    lib = kvz._lib
+    p = ctypes.c_void_p(256)
+    assert kvz.kvz_fp8_pool_state_bytes(1 << 20) >= kvz.kvz_pool_state_bytes(1 << 20)
+    with pytest.raises(kvz.KvzError):
+        kvz.kvz_fp8_pool_state_bytes(200)                                          # < 2 granules
+    assert lib.kvz_fp8_calibrate(p, 1, 7, p, p, None) == kvz.KVZ_EINVAL          # unknown format
+    assert lib.kvz_fp8_calibrate(None, 1, 0, p, p, None) == kvz.KVZ_EINVAL       # items null
+    assert lib.kvz_fp8_calibrate(p, 1, 1, ctypes.c_void_p(258), p, None) == kvz.KVZ_EINVAL
+    assert lib.kvz_fp8_encode_pages(None, p, 1, 0, 0, None) == kvz.KVZ_EINVAL    # no pool
+    assert lib.kvz_fp8_decompress_pages(p, 4096, p, p, 1, 8, 2, p, None) == kvz.KVZ_EINVAL
+    assert lib.kvz_fp8_decompress_pages(p, 4096, p, p, -1, 8, 0, p, None) == kvz.KVZ_EINVAL
+    assert lib.kvz_fp8_decompress_pages(p, 4096, ctypes.c_void_p(260), p, 1, 8, 0, p, None) == kvz.KVZ_EINVAL
+    assert lib.kvz_fp8_decompress_pages(p, 4096, p, p, 0, 8, 1, p, None) == kvz.KVZ_OK
+    assert lib.kvz_fp8_pack_pages(p, p, -1, 8, None) == kvz.KVZ_EINVAL
+    assert lib.kvz_fp8_pack_pages(ctypes.c_void_p(257), p, 1, 8, None) == kvz.KVZ_EINVAL
+    assert lib.kvz_fp8_pack_pages(p, p, 0, 8, None) == kvz.KVZ_OK
+    args = kvz.Fp8AttnArgs(q=256, out=256, arena=256, arena_bytes=1 << 20, meta=256, bases=None,
+                           pages=256, n_phys_pages=1, block_table=256, seq_lens=256,
+                           n_comp_pages=256, tail=None, batch=1, num_q_heads=8, num_kv_heads=2,
+                           head_dim=128, page_size=16, max_pages=1, splits=1, format=0,
+                           sm_scale=0.1, k_scale=1.0, v_scale=1.0, workspace=256,
+                           workspace_bytes=1 << 20)
+    assert lib.kvz_fp8_decode_attention(None, None) == kvz.KVZ_EINVAL
+    assert lib.kvz_fp8_decode_attention(ctypes.byref(args), None) == kvz.KVZ_EINVAL      # no bases
+    args.bases = 260
+    assert lib.kvz_fp8_decode_attention(ctypes.byref(args), None) == kvz.KVZ_EINVAL      # misaligned
+    args.bases, args.arena_bytes = 256, 1024
+    assert lib.kvz_fp8_decode_attention(ctypes.byref(args), None) == kvz.KVZ_EINVAL      # arena < 2048
+    args.pages = 264
+    assert lib.kvz_fp8_raw_decode_attention(ctypes.byref(args), None) == kvz.KVZ_EINVAL  # pages misaligned
+    args.format = 3
+    assert lib.kvz_fp8_decode_attention(ctypes.byref(args), None) == kvz.KVZ_EINVAL
+    assert lib.kvz_fp8_raw_decode_attention(ctypes.byref(args), None) == kvz.KVZ_EINVAL
+    args.format, args.head_dim = 1, 64
+    assert lib.kvz_fp8_decode_attention(ctypes.byref(args), None) == kvz.KVZ_EUNSUPPORTED
