@@ -908,20 +908,75 @@ __device__ __forceinline__ float block_reduce(float v, float* s_red, bool is_max
   return r;
 }
 
+// Splits merged from registers when the batch's split map is the uniform one (sequence b owns
+// splits b*S .. b*S+S-1): every partial of (b, head) is loaded in the same round trip as the
+// lengths that confirm the map.  Larger S, or a ragged map, takes the general path.
+constexpr int kSpecSplits = 16;
+
 __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(
     const float* ws_ml, const float* ws_o, float* out, const int32_t* seq_lens,
     const int32_t* n_comp_v, bool has_tail, int max_pages, int B, int Hq, int G, int S_avg) {
   __shared__ float s_w[kMaxSplits];
   __shared__ float s_red[kCombineThreads / 64];
   __shared__ float s_part[kCombineThreads];
+  __shared__ float s_ml[2][kSpecSplits];
   const int bh = blockIdx.x;
   const int b = bh / Hq, h = bh % Hq;
   const int kvh = h / G, g = h % G;
   const int t = threadIdx.x;
+  const int d = t & (KVZ_HEAD_DIM - 1);
+  const int half = t >> 7;                                 // 256 threads: two per dim
+  const int32_t slen = seq_lens[b];
+  // speculative loads of the uniform map's partials (issued before the map is known)
+  const bool spec = S_avg <= kSpecSplits;
+  const size_t ubase = (size_t)kvh * B * S_avg;
+  float m_sp = -INFINITY, l_sp = 0.f;
+  float o_sp[kSpecSplits / 2];
+  if (spec) {
+    const size_t u0 = ubase + (size_t)b * S_avg;
+    if (t < S_avg) {
+      m_sp = ws_ml[((u0 + t) * G + g) * 2];
+      l_sp = ws_ml[((u0 + t) * G + g) * 2 + 1];
+    }
+#pragma unroll
+    for (int i = 0; i < kSpecSplits / 2; ++i) {
+      const int sp = half + 2 * i;
+      o_sp[i] = sp < S_avg ? ws_o[((u0 + sp) * G + g) * KVZ_HEAD_DIM + d] : 0.f;
+    }
+  }
   const SplitOf so = split_of(n_comp_v, seq_lens, has_tail, max_pages, B, S_avg, 0, b);
   const int S = so.sb;
-  // the partials of split base+sp of this KV head
-  auto unit_of = [&](int sp) { return (size_t)kvh * B * S_avg + so.base + sp; };
+  if (spec && so.base == b * S_avg && S == S_avg) {
+    if (t < S) {
+      s_ml[0][t] = m_sp;
+      s_ml[1][t] = l_sp;
+    }
+    __syncthreads();
+    float M = -INFINITY;
+    for (int sp = 0; sp < S; ++sp) M = fmaxf(M, s_ml[0][sp]);
+    float L = 0.f, acc = 0.f;
+    for (int sp = 0; sp < S; ++sp) {
+      const float m = s_ml[0][sp];
+      L += ((m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - M)) * s_ml[1][sp];
+    }
+#pragma unroll
+    for (int i = 0; i < kSpecSplits / 2; ++i) {
+      const int sp = half + 2 * i;
+      if (sp < S) {
+        const float m = s_ml[0][sp];
+        acc += ((m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - M)) * o_sp[i];
+      }
+    }
+    s_part[t] = acc;
+    __syncthreads();
+    if (t < KVZ_HEAD_DIM) {
+      const float o = (s_part[t] + s_part[t + KVZ_HEAD_DIM]) / L;
+      out[(size_t)bh * KVZ_HEAD_DIM + d] = slen <= 0 ? 0.f : o;
+    }
+    return;
+  }
+  // general path: any split map, any S
+  auto unit_of = [&](int sp) { return ubase + so.base + sp; };
   float m_loc = -INFINITY;
   for (int sp = t; sp < S; sp += kCombineThreads) m_loc = fmaxf(m_loc, ws_ml[(unit_of(sp) * G + g) * 2]);
   const float M = block_reduce(m_loc, s_red, true);
@@ -934,16 +989,15 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(
     l_loc += w * ws_ml[ug * 2 + 1];
   }
   const float L = block_reduce(l_loc, s_red, false);   // its barrier also publishes s_w
-  const int d = t & (KVZ_HEAD_DIM - 1);
   float acc = 0.f;
 #pragma unroll 4
-  for (int sp = t >> 7; sp < S; sp += kCombineThreads / KVZ_HEAD_DIM)
+  for (int sp = half; sp < S; sp += kCombineThreads / KVZ_HEAD_DIM)
     acc += s_w[sp] * ws_o[(unit_of(sp) * G + g) * KVZ_HEAD_DIM + d];
   s_part[t] = acc;
   __syncthreads();
   if (t < KVZ_HEAD_DIM) {
     const float o = (s_part[t] + s_part[t + KVZ_HEAD_DIM]) / L;
-    out[(size_t)bh * KVZ_HEAD_DIM + d] = seq_lens[b] <= 0 ? 0.f : o;
+    out[(size_t)bh * KVZ_HEAD_DIM + d] = slen <= 0 ? 0.f : o;
   }
 }
 
