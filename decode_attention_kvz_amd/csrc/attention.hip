@@ -382,9 +382,11 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
   using PageBuf = typename PageBufOf<FMT>::type;
   // group-adaptive tiles: a 16 KiB table from four packed 3-bit codes to four bytes, filled by
   // the whole workgroup before any wave leaves (one LDS read replaces the bit-field spreading)
+  // (FP8 tiles: entries and bases are kept shifted into the FP8 exponent field)
+  constexpr uint32_t kFieldShift = FMT == kFmtFp8c ? Fp8Fmt<FK>::kFracBits : 0u;
   __shared__ uint32_t s_spread3[CODED ? 4096 : 1];
   if constexpr (CODED) {
-    for (int x = threadIdx.x; x < 4096; x += 256) s_spread3[x] = gaac_spread3((uint32_t)x);
+    for (int x = threadIdx.x; x < 4096; x += 256) s_spread3[x] = gaac_spread3((uint32_t)x) << kFieldShift;
     __syncthreads();
   }
   const int lane = threadIdx.x & 63;
@@ -435,12 +437,12 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
       const int dim = 32 * j + 8 * (lane >> 4);
       const uint2 b3 = *reinterpret_cast<const uint2*>(kbase + dim);
       const uint2 b4 = *reinterpret_cast<const uint2*>(kbase + 128 + dim);
-      kb3[j][0] = b3.x;
-      kb3[j][1] = b3.y;
-      kb4[j][0] = b4.x;
-      kb4[j][1] = b4.y;
-      vb3 |= (uint32_t)vbase[32 * j + (lane & 31)] << (8 * j);
-      vb4 |= (uint32_t)vbase[128 + 32 * j + (lane & 31)] << (8 * j);
+      kb3[j][0] = b3.x << kFieldShift;
+      kb3[j][1] = b3.y << kFieldShift;
+      kb4[j][0] = b4.x << kFieldShift;
+      kb4[j][1] = b4.y << kFieldShift;
+      vb3 |= ((uint32_t)vbase[32 * j + (lane & 31)] << kFieldShift) << (8 * j);
+      vb4 |= ((uint32_t)vbase[128 + 32 * j + (lane & 31)] << kFieldShift) << (8 * j);
     }
   }
   const int pc_end = p1 < n_comp ? p1 : n_comp;
@@ -589,9 +591,6 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
         return;
       }
       const uint32_t m8 = (t.mode >> (8 * (lane & 3))) & 0xFFu;
-      uint32_t len = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) len += gaac_escape_bytes((m8 >> (2 * j)) & 3u);
       const bool any_raw = __ballot((m8 & 0xAAu) != 0u) != 0ull;
       auto bases_of = [&](int j, uint32_t& b3lo, uint32_t& b3hi, uint32_t& b4lo, uint32_t& b4hi) {
         if (is_k) {
@@ -600,15 +599,16 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
           b4lo = kb4[j][0];
           b4hi = kb4[j][1];
         } else {
-          b3lo = b3hi = ((vb3 >> (8 * j)) & 0xFFu) * 0x01010101u;
-          b4lo = b4hi = ((vb4 >> (8 * j)) & 0xFFu) * 0x01010101u;
+          b3lo = b3hi = __builtin_amdgcn_perm(0u, vb3, 0x01010101u * j);   // byte j, four times
+          b4lo = b4hi = __builtin_amdgcn_perm(0u, vb4, 0x01010101u * j);
         }
       };
       if (!any_raw) {
         // No raw group in the wave (the common case): a lane has at most four one-byte
-        // escapes, all in the two dwords at its first escape byte; the four groups are one
-        // straight-line block (no branch per group), so their dependent chains interleave.
-        const uint32_t pos = gaac_exclusive_scan_small(len);
+        // escapes (one per 4-bit group, i.e. per mode with bit 0 set), all in the two dwords at
+        // its first escape byte; the four groups are one straight-line block (no branch per
+        // group), so their dependent chains interleave.
+        const uint32_t pos = gaac_exclusive_scan_small(__builtin_popcount(m8 & 0x55u));
         const int q = (int)(pos >> 2);
         const uint32_t d0 = (uint32_t)__shfl((int)t.esc, q, 64);
         const uint32_t d1 = (uint32_t)__shfl((int)t.esc, q + 1, 64);
@@ -628,6 +628,9 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
         return;
       }
       // Some raw group in the wave: up to 20 escape bytes per lane, fetched group by group.
+      uint32_t len = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) len += gaac_escape_bytes((m8 >> (2 * j)) & 3u);
       uint32_t pos = gaac_exclusive_scan(len, lane);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -665,9 +668,6 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
         return;
       }
       const uint32_t m8 = (t.mode >> (8 * (lane & 3))) & 0xFFu;
-      uint32_t len = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) len += fp8_escape_bytes<FK>((m8 >> (2 * j)) & 3u);
       // E5M2 raw groups escape two bytes; E4M3 groups never more than one
       const bool any_raw = FK == KVZ_FP8_E5M2 && __ballot((m8 & 0xAAu) != 0u) != 0ull;
       const uint32_t w[4] = {t.a.x, t.a.y, t.a.z, t.a.w};
@@ -680,8 +680,8 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
           b4lo = kb4[j][0];
           b4hi = kb4[j][1];
         } else {
-          b3lo = b3hi = ((vb3 >> (8 * j)) & 0xFFu) * 0x01010101u;
-          b4lo = b4hi = ((vb4 >> (8 * j)) & 0xFFu) * 0x01010101u;
+          b3lo = b3hi = __builtin_amdgcn_perm(0u, vb3, 0x01010101u * j);   // byte j, four times
+          b4lo = b4hi = __builtin_amdgcn_perm(0u, vb4, 0x01010101u * j);
         }
         uint32_t X, Y;
         fp8_sm_xy<FK>(w, j, X, Y);
@@ -691,9 +691,11 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
         ops[j] = fp8x8_to_bf16<FK>(f.x, f.y);
       };
       if (!any_raw) {
-        // at most four one-byte escapes per lane, in the two dwords at its first escape byte;
-        // the four groups are one straight-line block (no branch per group)
-        const uint32_t pos = gaac_exclusive_scan_small(len);
+        // at most four one-byte escapes per lane (E4M3: modes 1 and 2, the two bits of the mode
+        // differ; E5M2 here: mode 1), in the two dwords at its first escape byte; the four
+        // groups are one straight-line block (no branch per group)
+        const uint32_t ones = FK == KVZ_FP8_E4M3 ? (m8 ^ (m8 >> 1)) & 0x55u : m8 & 0x55u;
+        const uint32_t pos = gaac_exclusive_scan_small(__builtin_popcount(ones));
         const int q = (int)(pos >> 2);
         const uint32_t d0 = (uint32_t)__shfl((int)t.esc, q, 64);
         const uint32_t d1 = (uint32_t)__shfl((int)t.esc, q + 1, 64);
@@ -708,6 +710,9 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
         return;
       }
       // a raw E5M2 group in the wave: up to 8 escape bytes per lane, a 64-bit window
+      uint32_t len = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) len += fp8_escape_bytes<FK>((m8 >> (2 * j)) & 3u);
       const uint32_t pos = gaac_exclusive_scan(len, lane);
       const int q = (int)(pos >> 2);
       const uint32_t d0 = (uint32_t)__shfl((int)t.esc, q, 64);

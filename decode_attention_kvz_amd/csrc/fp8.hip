@@ -326,9 +326,10 @@ __global__ __launch_bounds__(256) void fp8_decompress_kernel(const uint8_t* aren
     uint32_t X, Y;
     fp8_sm_xy<FK>(w, j, X, Y);
     const uint32_t low24 = gaac_low24(cw, j);
-    *reinterpret_cast<uint2*>(out + fp8_chunk_offset(j, lane)) =
-        fp8_restore_group<FK>(X, Y, gaac_spread3(low24 & 0xFFFu), gaac_spread3(low24 >> 12), mode,
-                              esc, b3lo, b3hi, b4lo, b4hi, true);
+    constexpr uint32_t kMw = F::kFracBits;   // codes and bases in the exponent field
+    *reinterpret_cast<uint2*>(out + fp8_chunk_offset(j, lane)) = fp8_restore_group<FK>(
+        X, Y, gaac_spread3(low24 & 0xFFFu) << kMw, gaac_spread3(low24 >> 12) << kMw, mode, esc,
+        b3lo << kMw, b3hi << kMw, b4lo << kMw, b4hi << kMw, true);
   }
 }
 

@@ -92,10 +92,6 @@ __device__ __forceinline__ uint4 fp8x8_to_bf16(uint32_t f0, uint32_t f1) {
   return r;
 }
 
-// Four bits of x (bits 0..3) -> bit 0 of one byte each.
-__device__ __forceinline__ uint32_t fp8_spread1(uint32_t x) {
-  return ((x & 0xFu) * 0x00204081u) & 0x01010101u;
-}
 // Four 2-bit fields of x (bits 0..7) -> bits 0..1 of one byte each.
 __device__ __forceinline__ uint32_t fp8_spread2(uint32_t x) {
   return (x & 3u) | (((x >> 2) & 3u) << 8) | (((x >> 4) & 3u) << 16) | (((x >> 6) & 3u) << 24);
@@ -104,28 +100,30 @@ __device__ __forceinline__ uint32_t fp8_spread2(uint32_t x) {
 // The FP8 bytes of one group (values 0..3 -> .x, 4..7 -> .y) from its sign+fraction bytes X, Y,
 // its low 3 code bits spread to bytes (c0: values 0..3, c1: 4..7), its mode and escape bits
 // (4-bit: one byte, bit i = code bit 3 of value i; raw: EW-3 bits per value), and the bases
-// of its values as bytes.  Exponents are assembled per byte (e <= 31 never carries) and placed
-// above the fraction bits with one shift-or.  The raw path only when `wave_has_raw`.
+// of its values as bytes.  Codes and bases come already shifted left by the fraction width,
+// i.e. in the exponent field of each byte; e <= 2^EW - 1 never carries out of the field, so the
+// FP8 byte is one three-way add of code, base and sign+fraction.  E5M2 raw groups only when
+// `wave_has_raw` (an E4M3 raw group escapes one bit per value, like a 4-bit group, and is
+// always handled).
 template <int FK>
 __device__ __forceinline__ uint2 fp8_restore_group(uint32_t X, uint32_t Y, uint32_t c0, uint32_t c1,
                                                    uint32_t mode, uint32_t esc, uint32_t b3lo,
                                                    uint32_t b3hi, uint32_t b4lo, uint32_t b4hi,
                                                    bool wave_has_raw) {
-  constexpr uint32_t kMw = Fp8Fmt<FK>::kFracBits;
-  const bool one_bit = mode == kFp8Mode4 || (FK == KVZ_FP8_E4M3 && mode == kFp8ModeRaw);
-  const uint32_t h4 = one_bit ? esc : 0u;
-  c0 |= fp8_spread1(h4) << 3;
-  c1 |= fp8_spread1(h4 >> 4) << 3;
+  constexpr int kMw = (int)Fp8Fmt<FK>::kFracBits;
+  const bool m4 = mode == kFp8Mode4;
+  const bool raw = (FK == KVZ_FP8_E4M3 || wave_has_raw) && mode == kFp8ModeRaw;
+  const bool one_bit = m4 || (FK == KVZ_FP8_E4M3 && raw);
+  gaac_or_bits<3 + kMw>(one_bit ? (esc & 0xFFu) : 0u, c0, c1);
   if constexpr (FK == KVZ_FP8_E5M2) {
-    if (wave_has_raw && mode == kFp8ModeRaw) {
-      c0 |= fp8_spread2(esc & 0xFFu) << 3;
-      c1 |= fp8_spread2((esc >> 8) & 0xFFu) << 3;
+    if (raw) {
+      c0 |= fp8_spread2(esc & 0xFFu) << (3 + kMw);
+      c1 |= fp8_spread2((esc >> 8) & 0xFFu) << (3 + kMw);
     }
   }
-  const uint32_t base0 = mode == kFp8Mode3 ? b3lo : (mode == kFp8Mode4 ? b4lo : 0u);
-  const uint32_t base1 = mode == kFp8Mode3 ? b3hi : (mode == kFp8Mode4 ? b4hi : 0u);
-  const uint32_t e0 = c0 + base0, e1 = c1 + base1;
-  return make_uint2((e0 << kMw) | X, (e1 << kMw) | Y);
+  const uint32_t base0 = m4 ? b4lo : (raw ? 0u : b3lo);
+  const uint32_t base1 = m4 ? b4hi : (raw ? 0u : b3hi);
+  return make_uint2(c0 + base0 + X, c1 + base1 + Y);
 }
 
 }  // namespace kvz

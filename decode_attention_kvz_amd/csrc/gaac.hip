@@ -280,15 +280,12 @@ __global__ __launch_bounds__(256) void gaac_decompress_kernel(const uint8_t* are
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const uint32_t mode = (modes >> (2 * j)) & 3u;
-    uint32_t esc = 0, esc_hi = 0;
-    if (mode == kGaacMode4) {
-      esc = rec[at++];
-    } else if (mode == kGaacModeRaw) {
-      esc = (uint32_t)rec[at] | ((uint32_t)rec[at + 1] << 8) | ((uint32_t)rec[at + 2] << 16) |
-            ((uint32_t)rec[at + 3] << 24);
-      esc_hi = rec[at + 4];
-      at += 5;
-    }
+    const uint32_t nb = gaac_escape_bytes(mode);
+    uint64_t e = 0;
+    for (uint32_t k = 0; k < nb; ++k)      // never past the slot, whatever the mode plane says
+      if (at + k < kGaacSlotBytes) e |= (uint64_t)rec[at + k] << (8 * k);
+    at += nb;
+    const uint32_t esc = (uint32_t)e, esc_hi = (uint32_t)(e >> 32);
     uint32_t b3lo, b3hi, b4lo, b4hi;
     group_bases(tb, kind, j, lane, b3lo, b3hi, b4lo, b4hi);
     const uint2 sm = *reinterpret_cast<const uint2*>(rec + 512 * j + 8 * lane);

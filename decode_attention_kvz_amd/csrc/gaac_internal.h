@@ -70,9 +70,21 @@ __device__ __forceinline__ uint32_t gaac_spread3(uint32_t x) {
 __device__ __forceinline__ uint32_t gaac_spread5(uint32_t x) {
   return (x & 31u) | (((x >> 5) & 31u) << 8) | (((x >> 10) & 31u) << 16) | (((x >> 15) & 31u) << 24);
 }
-// Four bits of x (bits 0..3) -> bit 0 of one byte each (the shifted copies do not overlap).
-__device__ __forceinline__ uint32_t gaac_spread1(uint32_t x) {
-  return ((x & 0xFu) * 0x00204081u) & 0x01010101u;
+// Bit BIT of the four bytes of c0 / c1 <- bits 0..3 / 4..7 of h (h < 256).  t = h | h<<7 |
+// h<<14 | h<<21 holds bit i of h at bit 8i (i < 4) and at bit 8(i-4)+4 (i >= 4), and no other
+// bit of h reaches those positions; two shift-ors and two masked merges, no multiply.
+template <int BIT>
+__device__ __forceinline__ void gaac_or_bits(uint32_t h, uint32_t& c0, uint32_t& c1) {
+  static_assert(BIT >= 0 && BIT < 8, "a bit of a byte");
+  constexpr uint32_t m = 0x01010101u << BIT;
+  uint32_t t = h | (h << 7);
+  t |= t << 14;
+  c0 |= (t << BIT) & m;
+  if constexpr (BIT >= 4) c1 |= (t << (BIT - 4)) & m;
+  else c1 |= (t >> (4 - BIT)) & m;
+}
+__device__ __forceinline__ void gaac_or_bit3(uint32_t h, uint32_t& c0, uint32_t& c1) {
+  gaac_or_bits<3>(h, c0, c1);
 }
 
 // Rebuild the 8 BF16 values of one group (4 dwords, value 2m in the low half of dword m).
@@ -85,9 +97,7 @@ __device__ __forceinline__ uint4 gaac_restore_group(uint32_t sm0, uint32_t sm1, 
                                                     uint32_t b4hi) {
   uint32_t c0 = gaac_spread3(low24 & 0xFFFu);
   uint32_t c1 = gaac_spread3(low24 >> 12);
-  const uint32_t h4 = mode == kGaacMode4 ? esc : 0u;
-  c0 |= gaac_spread1(h4) << 3;
-  c1 |= gaac_spread1(h4 >> 4) << 3;
+  gaac_or_bit3(mode == kGaacMode4 ? (esc & 0xFFu) : 0u, c0, c1);
   if (mode == kGaacModeRaw) {
     c0 |= gaac_spread5(esc & 0xFFFFFu) << 3;
     c1 |= gaac_spread5((esc >> 20) | (esc_hi << 12)) << 3;
@@ -109,21 +119,22 @@ __device__ __forceinline__ uint4 gaac_restore_group(uint32_t sm0, uint32_t sm1, 
 }
 
 // The same rebuild from codes already spread to bytes (c0/c1: the low 3 code bits of values
-// 0..3 / 4..7, one per byte); the raw path only when `wave_has_raw` (wave-uniform).
+// 0..3 / 4..7, one per byte).  Raw groups only when `wave_has_raw` (wave-uniform); without it
+// every group is 3-bit or 4-bit and the base is a two-way choice.
 __device__ __forceinline__ uint4 gaac_restore_group_spread(uint32_t sm0, uint32_t sm1, uint32_t c0,
                                                            uint32_t c1, uint32_t mode, uint32_t esc,
                                                            uint32_t esc_hi, uint32_t b3lo,
                                                            uint32_t b3hi, uint32_t b4lo,
                                                            uint32_t b4hi, bool wave_has_raw) {
-  const uint32_t h4 = mode == kGaacMode4 ? esc : 0u;
-  c0 |= gaac_spread1(h4) << 3;
-  c1 |= gaac_spread1(h4 >> 4) << 3;
-  if (wave_has_raw && mode == kGaacModeRaw) {
+  const bool m4 = mode == kGaacMode4;
+  const bool raw = wave_has_raw && mode == kGaacModeRaw;
+  gaac_or_bit3(m4 ? (esc & 0xFFu) : 0u, c0, c1);
+  if (raw) {
     c0 |= gaac_spread5(esc & 0xFFFFFu) << 3;
     c1 |= gaac_spread5((esc >> 20) | (esc_hi << 12)) << 3;
   }
-  const uint32_t base0 = mode == kGaacMode3 ? b3lo : (mode == kGaacMode4 ? b4lo : 0u);
-  const uint32_t base1 = mode == kGaacMode3 ? b3hi : (mode == kGaacMode4 ? b4hi : 0u);
+  const uint32_t base0 = m4 ? b4lo : (raw ? 0u : b3lo);
+  const uint32_t base1 = m4 ? b4hi : (raw ? 0u : b3hi);
   const uint32_t e0 = c0 + base0, e1 = c1 + base1;
   const uint32_t h0 = (sm0 & 0x80808080u) | ((e0 >> 1) & 0x7F7F7F7Fu);
   const uint32_t l0 = (sm0 & 0x7F7F7F7Fu) | ((e0 << 7) & 0x80808080u);
