@@ -163,6 +163,14 @@ __device__ __forceinline__ uint4 restore_if_coded(uint4 c, uint32_t tag) {
   return restore_chunk(c.x, c.y, c.z, tag * 0x01010101u);
 }
 
+// A score in log2 units, rounded as a product of its own: with contraction the compiler may
+// fuse this multiply into the later subtraction of the running max, and the largest score of
+// a page would then give exp2 of the product's rounding error instead of exactly 1.
+__device__ __forceinline__ float scaled_score(float s, float scale) {
+#pragma clang fp contract(off)
+  return s * scale;
+}
+
 template <int GB>
 struct Softmax {
   float m_run = -INFINITY;
@@ -580,54 +588,60 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
       }
       }
     };
-    // GAAC tile -> the four operand chunks.  Each lane finds its escape bytes by an exclusive
-    // scan of the lanes' escape counts; lanes 0..31 hold the 128-byte escape area as dwords and
-    // a lane fetches the two dwords covering its group's bytes (a group's five bytes never
-    // reach past the area, so the second dword is always one of those 32).
+    // The bases of block j of this lane's values, as bytes (group-adaptive and FP8 tiles).
+    auto bases_of = [&](bool is_k, int j, uint32_t& b3lo, uint32_t& b3hi, uint32_t& b4lo,
+                        uint32_t& b4hi) {
+      if (is_k) {
+        b3lo = kb3[j][0];
+        b3hi = kb3[j][1];
+        b4lo = kb4[j][0];
+        b4hi = kb4[j][1];
+      } else {
+        b3lo = b3hi = __builtin_amdgcn_perm(0u, vb3, 0x01010101u * j);   // byte j, four times
+        b4lo = b4hi = __builtin_amdgcn_perm(0u, vb4, 0x01010101u * j);
+      }
+    };
+    // The lane's mode byte (four 2-bit group modes) of a coded tile.
+    auto mode_byte = [&](uint32_t mode_dword) { return (mode_dword >> (8 * (lane & 3))) & 0xFFu; };
+    // GAAC tile with no raw group in the wave (the common case) -> the four operand chunks.
+    // Each lane finds its escape bytes by an exclusive scan of the lanes' escape counts; lanes
+    // 0..31 hold the 128-byte escape area as dwords.  A lane has at most four one-byte escapes
+    // (one per 4-bit group, i.e. per mode with bit 0 set), all in the two dwords at its first
+    // escape byte; the four groups are one straight-line block (no branch), so their dependent
+    // chains interleave.
+    auto gaac_fast = [&](const GaacTileLoad& t, uint32_t m8, bool is_k, uint4 (&ops)[4]) {
+      const uint32_t pos = gaac_exclusive_scan_small(__builtin_popcount(m8 & 0x55u));
+      const int q = (int)(pos >> 2);
+      const uint32_t d0 = (uint32_t)__shfl((int)t.esc, q, 64);
+      const uint32_t d1 = (uint32_t)__shfl((int)t.esc, q + 1, 64);
+      uint32_t win = __builtin_amdgcn_alignbit(d1, d0, 8u * (pos & 3u));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t mode = (m8 >> (2 * j)) & 3u;
+        const uint32_t esc = win & 0xFFu;        // this group's byte if it is a 4-bit group
+        win = mode == kGaacMode4 ? win >> 8 : win;
+        uint32_t b3lo, b3hi, b4lo, b4hi;
+        bases_of(is_k, j, b3lo, b3hi, b4lo, b4hi);
+        const uint32_t low24 = gaac_low24(t.code, j);
+        ops[j] = gaac_restore_group_spread(t.c[j].x, t.c[j].y, s_spread3[low24 & 0xFFFu],
+                                           s_spread3[low24 >> 12], mode, esc, 0u, b3lo, b3hi,
+                                           b4lo, b4hi, false);
+      }
+    };
+    // Any GAAC tile -> the four operand chunks.  With a raw group in the wave a lane has up to
+    // 20 escape bytes, fetched group by group (a group's five bytes never reach past the area,
+    // so the second dword is always one of the 32).
     auto gaac_ops = [&](const GaacTileLoad& t, bool raw, bool is_k, uint4 (&ops)[4]) {
       if (raw) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) ops[j] = t.c[j];
         return;
       }
-      const uint32_t m8 = (t.mode >> (8 * (lane & 3))) & 0xFFu;
-      const bool any_raw = __ballot((m8 & 0xAAu) != 0u) != 0ull;
-      auto bases_of = [&](int j, uint32_t& b3lo, uint32_t& b3hi, uint32_t& b4lo, uint32_t& b4hi) {
-        if (is_k) {
-          b3lo = kb3[j][0];
-          b3hi = kb3[j][1];
-          b4lo = kb4[j][0];
-          b4hi = kb4[j][1];
-        } else {
-          b3lo = b3hi = __builtin_amdgcn_perm(0u, vb3, 0x01010101u * j);   // byte j, four times
-          b4lo = b4hi = __builtin_amdgcn_perm(0u, vb4, 0x01010101u * j);
-        }
-      };
-      if (!any_raw) {
-        // No raw group in the wave (the common case): a lane has at most four one-byte
-        // escapes (one per 4-bit group, i.e. per mode with bit 0 set), all in the two dwords at
-        // its first escape byte; the four groups are one straight-line block (no branch per
-        // group), so their dependent chains interleave.
-        const uint32_t pos = gaac_exclusive_scan_small(__builtin_popcount(m8 & 0x55u));
-        const int q = (int)(pos >> 2);
-        const uint32_t d0 = (uint32_t)__shfl((int)t.esc, q, 64);
-        const uint32_t d1 = (uint32_t)__shfl((int)t.esc, q + 1, 64);
-        uint32_t win = __builtin_amdgcn_alignbit(d1, d0, 8u * (pos & 3u));
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t mode = (m8 >> (2 * j)) & 3u;
-          const uint32_t esc = win & 0xFFu;        // this group's byte if it is a 4-bit group
-          win = mode == kGaacMode4 ? win >> 8 : win;
-          uint32_t b3lo, b3hi, b4lo, b4hi;
-          bases_of(j, b3lo, b3hi, b4lo, b4hi);
-          const uint32_t low24 = gaac_low24(t.code, j);
-          ops[j] = gaac_restore_group_spread(t.c[j].x, t.c[j].y, s_spread3[low24 & 0xFFFu],
-                                             s_spread3[low24 >> 12], mode, esc, 0u, b3lo, b3hi,
-                                             b4lo, b4hi, false);
-        }
+      const uint32_t m8 = mode_byte(t.mode);
+      if (!__ballot((m8 & 0xAAu) != 0u)) {
+        gaac_fast(t, m8, is_k, ops);
         return;
       }
-      // Some raw group in the wave: up to 20 escape bytes per lane, fetched group by group.
       uint32_t len = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) len += gaac_escape_bytes((m8 >> (2 * j)) & 3u);
@@ -647,18 +661,52 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
           pos += gaac_escape_bytes(mode);
         }
         uint32_t b3lo, b3hi, b4lo, b4hi;
-        bases_of(j, b3lo, b3hi, b4lo, b4hi);
+        bases_of(is_k, j, b3lo, b3hi, b4lo, b4hi);
         const uint32_t low24 = gaac_low24(t.code, j);
         ops[j] = gaac_restore_group_spread(t.c[j].x, t.c[j].y, s_spread3[low24 & 0xFFFu],
                                            s_spread3[low24 >> 12], mode, esc, esc_hi, b3lo, b3hi,
                                            b4lo, b4hi, true);
       }
     };
-    // FP8 tile -> the four operand chunks (BF16).  Uncompressed: each block's 8 bytes are
-    // converted.  Compressed: the lane's escape bytes (at most 8) start at an exclusive scan of
-    // the lanes' escape counts; lanes 0..15 hold the 64-byte escape area as dwords and three
-    // lane shuffles give every lane a 64-bit window from its first escape byte, consumed group
-    // by group.  Exponents are rebuilt per byte and placed above the fraction bits.
+    // One group of a compressed FP8 tile -> its operand chunk (BF16): sign+fraction bytes from
+    // the lane's words, codes from the spread table, exponents rebuilt per byte in the exponent
+    // field, then the exact conversion.
+    auto fp8_group = [&](const Fp8TileLoad& t, bool is_k, int j, uint32_t mode, uint32_t esc,
+                         bool wave_has_raw) {
+      uint32_t b3lo, b3hi, b4lo, b4hi;
+      bases_of(is_k, j, b3lo, b3hi, b4lo, b4hi);
+      const uint32_t w[4] = {t.a.x, t.a.y, t.a.z, t.a.w};
+      const uint32_t cw[3] = {t.b.x, t.b.y, t.b.z};
+      uint32_t X, Y;
+      fp8_sm_xy<FK>(w, j, X, Y);
+      const uint32_t low24 = gaac_low24(cw, j);
+      const uint2 f = fp8_restore_group<FK>(X, Y, s_spread3[low24 & 0xFFFu], s_spread3[low24 >> 12],
+                                            mode, esc, b3lo, b3hi, b4lo, b4hi, wave_has_raw);
+      return fp8x8_to_bf16<FK>(f.x, f.y);
+    };
+    // Compressed FP8 tile with at most one escape byte per group (every E4M3 tile; E5M2 without
+    // a raw group in the wave): at most four per lane (E4M3: modes 1 and 2, the two bits of the
+    // mode differ; E5M2: mode 1), in the two dwords at its first escape byte (lanes 0..15 hold
+    // the 64-byte escape area); the four groups are one straight-line block.
+    auto fp8_fast = [&](const Fp8TileLoad& t, uint32_t m8, bool is_k, uint4 (&ops)[4]) {
+      const uint32_t ones = FK == KVZ_FP8_E4M3 ? (m8 ^ (m8 >> 1)) & 0x55u : m8 & 0x55u;
+      const uint32_t pos = gaac_exclusive_scan_small(__builtin_popcount(ones));
+      const int q = (int)(pos >> 2);
+      const uint32_t d0 = (uint32_t)__shfl((int)t.esc, q, 64);
+      const uint32_t d1 = (uint32_t)__shfl((int)t.esc, q + 1, 64);
+      uint32_t win = __builtin_amdgcn_alignbit(d1, d0, 8u * (pos & 3u));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t mode = (m8 >> (2 * j)) & 3u;
+        const uint32_t esc = win & 0xFFu;
+        win = fp8_escape_bytes<FK>(mode) ? win >> 8 : win;
+        ops[j] = fp8_group(t, is_k, j, mode, esc, false);
+      }
+    };
+    // Any FP8 tile -> the four operand chunks.  Uncompressed: each block's 8 bytes are
+    // converted.  A raw E5M2 group in the wave: up to 8 escape bytes per lane; three lane
+    // shuffles give every lane a 64-bit window from its first escape byte, consumed group by
+    // group.
     auto fp8_ops = [&](const Fp8TileLoad& t, bool raw, bool is_k, uint4 (&ops)[4]) {
       if (raw) {
         ops[0] = fp8x8_to_bf16<FK>(t.a.x, t.a.y);
@@ -667,49 +715,12 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
         ops[3] = fp8x8_to_bf16<FK>(t.b.z, t.b.w);
         return;
       }
-      const uint32_t m8 = (t.mode >> (8 * (lane & 3))) & 0xFFu;
+      const uint32_t m8 = mode_byte(t.mode);
       // E5M2 raw groups escape two bytes; E4M3 groups never more than one
-      const bool any_raw = FK == KVZ_FP8_E5M2 && __ballot((m8 & 0xAAu) != 0u) != 0ull;
-      const uint32_t w[4] = {t.a.x, t.a.y, t.a.z, t.a.w};
-      const uint32_t cw[3] = {t.b.x, t.b.y, t.b.z};
-      auto group = [&](int j, uint32_t mode, uint32_t esc, bool wave_has_raw) {
-        uint32_t b3lo, b3hi, b4lo, b4hi;
-        if (is_k) {
-          b3lo = kb3[j][0];
-          b3hi = kb3[j][1];
-          b4lo = kb4[j][0];
-          b4hi = kb4[j][1];
-        } else {
-          b3lo = b3hi = __builtin_amdgcn_perm(0u, vb3, 0x01010101u * j);   // byte j, four times
-          b4lo = b4hi = __builtin_amdgcn_perm(0u, vb4, 0x01010101u * j);
-        }
-        uint32_t X, Y;
-        fp8_sm_xy<FK>(w, j, X, Y);
-        const uint32_t low24 = gaac_low24(cw, j);
-        const uint2 f = fp8_restore_group<FK>(X, Y, s_spread3[low24 & 0xFFFu], s_spread3[low24 >> 12],
-                                              mode, esc, b3lo, b3hi, b4lo, b4hi, wave_has_raw);
-        ops[j] = fp8x8_to_bf16<FK>(f.x, f.y);
-      };
-      if (!any_raw) {
-        // at most four one-byte escapes per lane (E4M3: modes 1 and 2, the two bits of the mode
-        // differ; E5M2 here: mode 1), in the two dwords at its first escape byte; the four
-        // groups are one straight-line block (no branch per group)
-        const uint32_t ones = FK == KVZ_FP8_E4M3 ? (m8 ^ (m8 >> 1)) & 0x55u : m8 & 0x55u;
-        const uint32_t pos = gaac_exclusive_scan_small(__builtin_popcount(ones));
-        const int q = (int)(pos >> 2);
-        const uint32_t d0 = (uint32_t)__shfl((int)t.esc, q, 64);
-        const uint32_t d1 = (uint32_t)__shfl((int)t.esc, q + 1, 64);
-        uint32_t win = __builtin_amdgcn_alignbit(d1, d0, 8u * (pos & 3u));
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t mode = (m8 >> (2 * j)) & 3u;
-          const uint32_t esc = win & 0xFFu;
-          win = fp8_escape_bytes<FK>(mode) ? win >> 8 : win;
-          group(j, mode, esc, false);
-        }
+      if (FK == KVZ_FP8_E4M3 || !__ballot((m8 & 0xAAu) != 0u)) {
+        fp8_fast(t, m8, is_k, ops);
         return;
       }
-      // a raw E5M2 group in the wave: up to 8 escape bytes per lane, a 64-bit window
       uint32_t len = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) len += fp8_escape_bytes<FK>((m8 >> (2 * j)) & 3u);
@@ -728,7 +739,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
         const uint32_t nb8 = 8u * fp8_escape_bytes<FK>(mode);
         lo = __builtin_amdgcn_alignbit(hi, lo, nb8);
         hi = nb8 ? hi >> nb8 : hi;
-        group(j, mode, esc, true);
+        ops[j] = fp8_group(t, is_k, j, mode, esc, true);
       }
     };
     auto process = [&](const PageBuf& buf, int i) {
@@ -758,7 +769,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kops[j]), as_bf16x8(qop[j]), sacc, 0, 0, 0);
       float sv[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sv[r] = sacc[r] * p.scale_log2;
+      for (int r = 0; r < 4; ++r) sv[r] = scaled_score(sacc[r], p.scale_log2);
       if constexpr (FMT == kFmtGaac) {
         gaac_ops(buf.v, vt != 0u, false, vop);
       } else if constexpr (FMT == kFmtFp8c) {
@@ -843,7 +854,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int tok = 4 * (lane >> 4) + r;
-      sv[r] = tok < n_tail ? sacc[r] * p.scale_log2 : -INFINITY;
+      sv[r] = tok < n_tail ? scaled_score(sacc[r], p.scale_log2) : -INFINITY;
     }
     sm.page(sv, vop, lane);
   }
