@@ -1,6 +1,7 @@
 // Library-wide entry points: version, error text, device check.
 #include "kvz_internal.h"
 
+#include <atomic>
 #include <cstring>
 #include <string>
 
@@ -20,17 +21,19 @@ int check_hip(hipError_t e, const char* what) {
   return set_error(KVZ_EHIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
+// Compute units of the current device, queried once per device (threads may race to fill an
+// entry; they store the same value).
 int device_cus() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 }  // namespace kvz

@@ -173,6 +173,36 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _dev(name, t, dtype=None, shape=None, min_bytes=None):
+    """A device-memory argument: a contiguous GPU tensor, of `dtype` and `shape` when given
+    (None entries match any size), holding at least `min_bytes`.  The library cannot tell a
+    host pointer or a short buffer from a good one, so these are checked before the call."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None:
+        if t.dim() != len(shape) or any(w is not None and int(g) != int(w)
+                                        for g, w in zip(t.shape, shape)):
+            raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if min_bytes is not None and _nbytes(t) < min_bytes:
+        raise ValueError(f"{name} holds {_nbytes(t)} bytes, needs at least {min_bytes}")
+    return t
+
+
+def _torch():
+    import torch
+    return torch
+
+
 def _stream(stream=None):
     import torch
     s = stream if stream is not None else torch.cuda.current_stream()
@@ -200,6 +230,8 @@ def kvz_pool_state_bytes(arena_bytes: int) -> int:
 
 def kvz_pool_init(arena, state, stream=None):
     """arena, state: uint8 device tensors.  Returns the opaque pool handle."""
+    _dev("arena", arena)
+    _dev("state", state)
     h = ctypes.c_void_p()
     _check(_lib.kvz_pool_init(ctypes.byref(h), _ptr(arena), arena.numel() * arena.element_size(),
                               _ptr(state), state.numel() * state.element_size(), _stream(stream)))
@@ -213,21 +245,28 @@ def kvz_pool_destroy(pool) -> None:
 def kvz_slot_alloc(pool, tags, off, stream=None) -> None:
     """tags: uint8 [n, 4] device; off: int32/uint32 [n] device (receives offsets)."""
     n = tags.shape[0]
+    _dev("tags", tags, min_bytes=4 * n)
+    _dev("off", off, min_bytes=4 * n)
     _check(_lib.kvz_slot_alloc(pool, _ptr(tags), _ptr(off), n, _stream(stream)))
 
 
 def kvz_slot_free(pool, meta_ptrs, stream=None) -> None:
     """meta_ptrs: int64 [n] device tensor of device pointers to kvz_group_meta."""
+    _dev("meta_ptrs", meta_ptrs, dtype=_torch().int64)
     _check(_lib.kvz_slot_free(pool, _ptr(meta_ptrs), meta_ptrs.shape[0], _stream(stream)))
 
 
 def kvz_encode_pages(pool, items, n: int, flags: int = 0, stream=None) -> None:
     """items: device tensor holding n kvz_encode_item records (ENCODE_ITEM_DTYPE)."""
+    _dev("items", items, min_bytes=n * ENCODE_ITEM_DTYPE.itemsize)
     _check(_lib.kvz_encode_pages(pool, _ptr(items), n, flags, _stream(stream)))
 
 
 def kvz_decode_block(arena, refs, n: int, out, stream=None) -> None:
     """refs: device tensor of n kvz_block_ref records; out: int16/uint16 [n, 16, 32] device."""
+    _dev("arena", arena)
+    _dev("refs", refs, min_bytes=n * BLOCK_REF_DTYPE.itemsize)
+    _dev("out", out, min_bytes=n * 16 * 32 * 2)
     _check(_lib.kvz_decode_block(_ptr(arena), arena.numel() * arena.element_size(), _ptr(refs),
                                  n, _ptr(out), _stream(stream)))
 
@@ -239,8 +278,37 @@ def kvz_attn_workspace_bytes(batch, num_q_heads, num_kv_heads, max_pages, splits
     return out.value
 
 
+def _check_attn_common(q, out, block_table, seq_lens, n_comp_pages, workspace, hkv,
+                       tail=None, tail_dtype=None, tail_bytes_per_value=2):
+    """The arguments every decode-attention call shares: q [B,Hq,128] bf16, out [B,Hq,128] fp32,
+    block_table [B,max_pages] int32, seq_lens / n_comp_pages [B] int32, the tail page
+    [B,2,Hkv,16,128] (or None) and the workspace."""
+    torch = _torch()
+    _dev("q", q, dtype=torch.bfloat16, shape=(None, None, 128))
+    bsz, hq = q.shape[0], q.shape[1]
+    _dev("out", out, dtype=torch.float32, shape=(bsz, hq, 128))
+    _dev("block_table", block_table, dtype=torch.int32, shape=(bsz, None))
+    _dev("seq_lens", seq_lens, dtype=torch.int32, shape=(bsz,))
+    _dev("n_comp_pages", n_comp_pages, dtype=torch.int32, shape=(bsz,))
+    _dev("workspace", workspace)
+    if tail is not None:
+        _dev("tail", tail, dtype=tail_dtype, min_bytes=bsz * 2 * hkv * 16 * 128 * tail_bytes_per_value)
+
+
+def _check_meta(meta):
+    """Per-layer metadata [n_phys_pages, Hkv, ...]: 16 bytes (the K and V group records) per
+    (physical page, KV head)."""
+    _dev("meta", meta)
+    if meta.dim() < 2 or _nbytes(meta) != meta.shape[0] * meta.shape[1] * 16:
+        raise ValueError("meta must be [n_phys_pages, Hkv, ...] with 16 bytes per (page, KV head)")
+
+
 def _attn_args(q, out, arena, meta, block_table, seq_lens, n_comp_pages, tail, sm_scale,
                workspace, splits):
+    _check_meta(meta)
+    _dev("arena", arena)
+    _check_attn_common(q, out, block_table, seq_lens, n_comp_pages, workspace, meta.shape[1],
+                       tail=tail, tail_dtype=_torch().bfloat16)
     bsz, hq, hd = q.shape
     return AttnArgs(q=q.data_ptr(), out=out.data_ptr(), arena=arena.data_ptr(),
                  arena_bytes=arena.numel() * arena.element_size(), meta=meta.data_ptr(),
@@ -267,8 +335,8 @@ def kvz_gaac_decode_attention(q, out, arena, meta, bases, block_table, seq_lens,
                               tail, sm_scale: float, workspace, splits: int = 0,
                               stream=None) -> None:
     """As kvz_decode_attention over group-adaptive tiles; bases [Hkv,2,2,128] uint8 device."""
-    if bases.numel() < meta.shape[1] * 512:
-        raise ValueError("bases too small")
+    _check_meta(meta)
+    _dev("bases", bases, min_bytes=meta.shape[1] * 512)
     a = _attn_args(q, out, arena, meta, block_table, seq_lens, n_comp_pages, tail, sm_scale,
                    workspace, splits)
     _check(_lib.kvz_gaac_decode_attention(ctypes.byref(a), _ptr(bases), _stream(stream)))
@@ -276,6 +344,8 @@ def kvz_gaac_decode_attention(q, out, arena, meta, bases, block_table, seq_lens,
 
 def kvz_bf16_pack_pages(src, dst, stream=None) -> None:
     """src [n_pages,2,Hkv,16,128] bf16 natural pages -> dst [n_pages,2,Hkv,4,1024] uint8."""
+    _dev("src", src, dtype=_torch().bfloat16, shape=(None, 2, None, 16, 128))
+    _dev("dst", dst, min_bytes=_nbytes(src))
     _check(_lib.kvz_bf16_pack_pages(_ptr(src), _ptr(dst), src.shape[0], src.shape[2],
                                     _stream(stream)))
 
@@ -283,6 +353,10 @@ def kvz_bf16_pack_pages(src, dst, stream=None) -> None:
 def kvz_bf16_decode_attention(q, out, pages, block_table, seq_lens, n_comp_pages, tail,
                               sm_scale: float, workspace, num_kv_heads: int, splits: int = 0,
                               stream=None) -> None:
+    """The BF16 baseline: pages [n_phys,2,Hkv,4,1024] uint8 (kvz_bf16_pack_pages)."""
+    _dev("pages", pages, min_bytes=pages.shape[0] * 2 * num_kv_heads * 4096)
+    _check_attn_common(q, out, block_table, seq_lens, n_comp_pages, workspace, num_kv_heads,
+                       tail=tail, tail_dtype=_torch().bfloat16)
     bsz, hq, hd = q.shape
     a = Bf16AttnArgs(q=q.data_ptr(), out=out.data_ptr(), pages=pages.data_ptr(),
                      n_phys_pages=pages.shape[0], block_table=block_table.data_ptr(), seq_lens=seq_lens.data_ptr(),
@@ -306,9 +380,10 @@ def kvz_pool_stats(pool, stream=None) -> dict:
 
 def kvz_decompress_pages(arena, meta, dst, stream=None) -> None:
     """meta: [n_pages, Hkv, 2, 8] uint8; dst: n_pages * 2 * Hkv * 4096 bytes."""
+    _check_meta(meta)
     n_pages, hkv = meta.shape[0], meta.shape[1]
-    if dst.numel() * dst.element_size() < n_pages * 2 * hkv * 4096:
-        raise ValueError("dst too small")
+    _dev("arena", arena)
+    _dev("dst", dst, min_bytes=n_pages * 2 * hkv * 4096)
     _check(_lib.kvz_decompress_pages(_ptr(arena), arena.numel() * arena.element_size(), _ptr(meta),
                                      n_pages, hkv, _ptr(dst), _stream(stream)))
 
@@ -329,21 +404,25 @@ def kvz_pool_capacity(stats: dict, num_layers: int, num_kv_heads: int) -> dict:
 def kvz_gaac_calibrate(items, n: int, hist, bases, stream=None) -> None:
     """items: device kvz_encode_item records (pages of one (layer, K|V, KV head)); hist: device
     >= 128*256 uint32 scratch; bases: device uint8 [2, 128] out (b3, b4)."""
-    if hist.numel() * hist.element_size() < 128 * 256 * 4 or bases.numel() < 256:
-        raise ValueError("hist or bases too small")
+    _dev("items", items, min_bytes=n * ENCODE_ITEM_DTYPE.itemsize)
+    _dev("hist", hist, min_bytes=128 * 256 * 4)
+    _dev("bases", bases, min_bytes=256)
     _check(_lib.kvz_gaac_calibrate(_ptr(items), n, _ptr(hist), _ptr(bases), _stream(stream)))
 
 
 def kvz_gaac_encode_pages(pool, items, n: int, flags: int = 0, stream=None) -> None:
     """items: device tensor holding n kvz_gaac_item records (GAAC_ITEM_DTYPE)."""
+    _dev("items", items, min_bytes=n * GAAC_ITEM_DTYPE.itemsize)
     _check(_lib.kvz_gaac_encode_pages(pool, _ptr(items), n, flags, _stream(stream)))
 
 
 def kvz_gaac_decompress_pages(arena, meta, bases, dst, stream=None) -> None:
     """meta: [n_pages, Hkv, 2, 8] uint8; bases: [Hkv, 2, 2, 128] uint8; dst: n_pages*2*Hkv*4096 B."""
+    _check_meta(meta)
     n_pages, hkv = meta.shape[0], meta.shape[1]
-    if dst.numel() * dst.element_size() < n_pages * 2 * hkv * 4096 or bases.numel() < hkv * 512:
-        raise ValueError("dst or bases too small")
+    _dev("arena", arena)
+    _dev("bases", bases, min_bytes=hkv * 512)
+    _dev("dst", dst, min_bytes=n_pages * 2 * hkv * 4096)
     _check(_lib.kvz_gaac_decompress_pages(_ptr(arena), arena.numel() * arena.element_size(),
                                           _ptr(meta), _ptr(bases), n_pages, hkv, _ptr(dst),
                                           _stream(stream)))
@@ -357,6 +436,8 @@ def kvz_fp8_pool_state_bytes(arena_bytes: int) -> int:
 
 def kvz_fp8_pool_init(arena, state, stream=None):
     """A pool of FP8 tiles (128-byte granules).  arena, state: uint8 device tensors."""
+    _dev("arena", arena)
+    _dev("state", state)
     h = ctypes.c_void_p()
     _check(_lib.kvz_fp8_pool_init(ctypes.byref(h), _ptr(arena),
                                   arena.numel() * arena.element_size(), _ptr(state),
@@ -367,21 +448,25 @@ def kvz_fp8_pool_init(arena, state, stream=None):
 def kvz_fp8_calibrate(items, n: int, fmt: int, hist, bases, stream=None) -> None:
     """items: device kvz_fp8_item records (pages of one (layer, K|V, KV head)); hist: device
     >= 128*32 uint32 scratch; bases: device uint8 [2, 128] out (b3, b4)."""
-    if hist.numel() * hist.element_size() < 128 * 32 * 4 or bases.numel() < 256:
-        raise ValueError("hist or bases too small")
+    _dev("items", items, min_bytes=n * FP8_ITEM_DTYPE.itemsize)
+    _dev("hist", hist, min_bytes=128 * 32 * 4)
+    _dev("bases", bases, min_bytes=256)
     _check(_lib.kvz_fp8_calibrate(_ptr(items), n, fmt, _ptr(hist), _ptr(bases), _stream(stream)))
 
 
 def kvz_fp8_encode_pages(pool, items, n: int, fmt: int, flags: int = 0, stream=None) -> None:
     """items: device tensor holding n kvz_fp8_item records (FP8_ITEM_DTYPE)."""
+    _dev("items", items, min_bytes=n * FP8_ITEM_DTYPE.itemsize)
     _check(_lib.kvz_fp8_encode_pages(pool, _ptr(items), n, fmt, flags, _stream(stream)))
 
 
 def kvz_fp8_decompress_pages(arena, meta, bases, fmt: int, dst, stream=None) -> None:
     """meta: [n_pages, Hkv, 2, 8] uint8; bases: [Hkv, 2, 2, 128] uint8; dst: n_pages*2*Hkv*2048 B."""
+    _check_meta(meta)
     n_pages, hkv = meta.shape[0], meta.shape[1]
-    if dst.numel() * dst.element_size() < n_pages * 2 * hkv * 2048 or bases.numel() < hkv * 512:
-        raise ValueError("dst or bases too small")
+    _dev("arena", arena)
+    _dev("bases", bases, min_bytes=hkv * 512)
+    _dev("dst", dst, min_bytes=n_pages * 2 * hkv * 2048)
     _check(_lib.kvz_fp8_decompress_pages(_ptr(arena), arena.numel() * arena.element_size(),
                                          _ptr(meta), _ptr(bases), n_pages, hkv, fmt, _ptr(dst),
                                          _stream(stream)))
@@ -389,8 +474,8 @@ def kvz_fp8_decompress_pages(arena, meta, bases, fmt: int, dst, stream=None) -> 
 
 def kvz_fp8_pack_pages(src, dst, stream=None) -> None:
     """src [n_pages,2,Hkv,16,128] uint8 natural FP8 pages -> dst [n_pages,2,Hkv,2048] uint8."""
-    if dst.numel() * dst.element_size() < src.numel() * src.element_size():
-        raise ValueError("dst too small")
+    _dev("src", src, dtype=_torch().uint8, shape=(None, 2, None, 16, 128))
+    _dev("dst", dst, min_bytes=_nbytes(src))
     _check(_lib.kvz_fp8_pack_pages(_ptr(src), _ptr(dst), src.shape[0], src.shape[2],
                                    _stream(stream)))
 
@@ -398,6 +483,8 @@ def kvz_fp8_pack_pages(src, dst, stream=None) -> None:
 def _fp8_args(q, out, fmt, block_table, seq_lens, n_comp_pages, tail, sm_scale, k_scale, v_scale,
               workspace, splits, num_kv_heads, n_phys, arena=None, meta=None, bases=None,
               pages=None):
+    _check_attn_common(q, out, block_table, seq_lens, n_comp_pages, workspace, num_kv_heads,
+                       tail=tail, tail_dtype=_torch().uint8, tail_bytes_per_value=1)
     bsz, hq, hd = q.shape
     return Fp8AttnArgs(
         q=q.data_ptr(), out=out.data_ptr(), arena=None if arena is None else arena.data_ptr(),
@@ -418,8 +505,9 @@ def kvz_fp8_decode_attention(q, out, fmt: int, arena, meta, bases, block_table, 
                              workspace, splits: int = 0, stream=None) -> None:
     """Fused attention over FP8 tiles.  meta [n_phys,Hkv,2,8] uint8; bases [Hkv,2,2,128] uint8;
     tail [B,2,Hkv,16,128] uint8 (FP8) or None."""
-    if bases.numel() < meta.shape[1] * 512:
-        raise ValueError("bases too small")
+    _check_meta(meta)
+    _dev("arena", arena)
+    _dev("bases", bases, min_bytes=meta.shape[1] * 512)
     a = _fp8_args(q, out, fmt, block_table, seq_lens, n_comp_pages, tail, sm_scale, k_scale,
                   v_scale, workspace, splits, meta.shape[1], meta.shape[0], arena=arena,
                   meta=meta, bases=bases)
@@ -431,12 +519,15 @@ def kvz_fp8_raw_decode_attention(q, out, fmt: int, pages, block_table, seq_lens,
                                  workspace, num_kv_heads: int, splits: int = 0,
                                  stream=None) -> None:
     """The FP8 baseline: pages [n_phys,2,Hkv,2048] uint8 (kvz_fp8_pack_pages)."""
+    _dev("pages", pages, min_bytes=pages.shape[0] * 2 * num_kv_heads * 2048)
     a = _fp8_args(q, out, fmt, block_table, seq_lens, n_comp_pages, tail, sm_scale, k_scale,
                   v_scale, workspace, splits, num_kv_heads, pages.shape[0], pages=pages)
     _check(_lib.kvz_fp8_raw_decode_attention(ctypes.byref(a), _stream(stream)))
 
 
 def kvz_stream_read(buf, sink, workgroups: int = 0, stream=None) -> None:
+    _dev("buf", buf)
+    _dev("sink", sink)
     _check(_lib.kvz_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
                                 workgroups, _stream(stream)))
 

@@ -153,3 +153,45 @@ def test_fp8_entry_points_reject_bad_arguments_on_the_host():
     assert lib.kvz_fp8_raw_decode_attention(ctypes.byref(args), None) == kvz.KVZ_EINVAL
     args.format, args.head_dim = 1, 64
     assert lib.kvz_fp8_decode_attention(ctypes.byref(args), None) == kvz.KVZ_EUNSUPPORTED
+
+
+def test_binding_rejects_host_and_misshapen_tensors_before_the_call():
+    """The binding checks device-memory arguments (GPU tensor, contiguous, dtype, shape, size)
+    before any library call: a host pointer or a short buffer would reach a kernel otherwise."""
+    torch = pytest.importorskip("torch")
+    from decode_attention_kvz_amd import kvz
+    b, hq, hkv = 2, 8, 2
+    q = torch.zeros((b, hq, 128), dtype=torch.bfloat16)
+    out = torch.zeros((b, hq, 128), dtype=torch.float32)
+    meta = torch.zeros((4, hkv, 2, 8), dtype=torch.uint8)
+    bt = torch.zeros((b, 4), dtype=torch.int32)
+    lens = torch.zeros((b,), dtype=torch.int32)
+    ws = torch.zeros((1 << 16,), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kvz.kvz_decode_attention(q, out, ws, meta, bt, lens, lens, None, 0.1, ws)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kvz.kvz_fp8_pack_pages(torch.zeros((1, 2, hkv, 16, 128), dtype=torch.uint8),
+                               torch.zeros((1,), dtype=torch.uint8))
+    with pytest.raises(ValueError, match="required"):
+        kvz.kvz_stream_read(None, None)
+    # the checker itself, on tensors that claim to live on the GPU (no memory is touched)
+
+    class FakeDev:
+        def __init__(self, t):
+            self.t, self.is_cuda = t, True
+
+        def __getattr__(self, k):
+            return getattr(self.t, k)
+
+    dq = FakeDev(q)
+    assert kvz._dev("q", dq, dtype=torch.bfloat16, shape=(None, None, 128)) is dq
+    with pytest.raises(ValueError, match="must be torch.float32"):
+        kvz._dev("out", dq, dtype=torch.float32)
+    with pytest.raises(ValueError, match="shape"):
+        kvz._dev("out", FakeDev(out[:, :4].contiguous()), shape=(b, hq, 128))
+    with pytest.raises(ValueError, match="contiguous"):
+        kvz._dev("q", FakeDev(q.transpose(0, 1)))
+    with pytest.raises(ValueError, match="at least"):
+        kvz._dev("ws", FakeDev(ws), min_bytes=(1 << 16) + 1)
+    with pytest.raises(ValueError, match="16 bytes"):
+        kvz._check_meta(FakeDev(torch.zeros((4, hkv, 8), dtype=torch.uint8)))
