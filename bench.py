@@ -42,6 +42,13 @@ U_MAX = 5.0
 FORCED = 0.05
 SEED = 2
 VARIANT_LAYERS, VARIANT_U_MAX = 8, 3.0
+# The other workload shapes, timed as labelled extras (not the headline): name, batch, query
+# heads, KV heads, compressed pages per sequence (no tail page), distinct layers, u_max, forced
+# fraction, seed, stress values.
+OTHER_CONFIGS = [
+    ("llama2k", 32, 32, 8, 128, 32, 3.0, 0.05, 1, False),
+    ("single131k", 1, 32, 8, 8192, 4, 3.0, 0.10, 4, True),
+]
 GAAC_LAYERS = 8
 FP8_LAYERS = 8
 N_PHYS = B * N_COMP
@@ -128,6 +135,8 @@ def main():
     ap.add_argument("--no-variant", action="store_true")
     ap.add_argument("--no-gaac", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-other", action="store_true",
+                    help="skip the other workload shapes (2K batch of 32, one 131K sequence)")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="for hardware-counter runs: one layer of fused and baseline attention "
                          "(3 launches each) and a 1 GiB device copy as a traffic reference")
@@ -265,6 +274,7 @@ def main():
     traffic = committed_traffic()
     read_peak = stream_read_peak(timed)
     variant = None if args.no_variant else compressible_variant(args, dev, seq_lens, n_comp, ws)
+    others = None if args.no_other else {c[0]: other_config(args, dev, *c) for c in OTHER_CONFIGS}
     gaac_leg = None if args.no_gaac else gaac_format(args, dev, seq_lens, n_comp, ws)
     fp8_leg = None if args.no_fp8 else {name: fp8_format(args, dev, seq_lens, n_comp, ws, fmt)
                                         for name, fmt in (("e4m3", 0), ("e5m2", 1))}
@@ -318,6 +328,7 @@ def main():
                            "input_GBps": round(N_PHYS * HKV * 2 * 4096 /
                                                (float(np.median(enc_layer_us)) * 1e-6) / 1e9, 1)},
         "compressible_variant": variant,
+        "other_configs": others,
         "gaac_format": gaac_leg,
         "fp8_formats": fp8_leg,
     }
@@ -408,10 +419,11 @@ def gaac_format(args, dev, seq_lens, n_comp, ws):
     # same split count -> the same arithmetic on the same values: bit-identical outputs
     L = layers[-1]
     same = [torch.empty_like(L["out"]) for _ in range(2)]
+    ws16 = paged.workspace(B, HQ, HKV, N_COMP, 16, device=dev)
     kvz.kvz_gaac_decode_attention(L["q"], same[0], arena.arena, L["meta"], L["bases"],
-                                  L["block_table"], seq_lens, n_comp, L["tail"], SCALE, ws, 16)
+                                  L["block_table"], seq_lens, n_comp, L["tail"], SCALE, ws16, 16)
     kvz.kvz_bf16_decode_attention(L["q"], same[1], L["store"], L["block_table"], seq_lens, n_comp,
-                                  L["tail"], SCALE, ws, HKV, 16)
+                                  L["tail"], SCALE, ws16, HKV, 16)
     torch.cuda.synchronize()
     assert torch.equal(same[0], same[1]), "GAAC attention differs from the BF16 kernel"
     for L in layers:
@@ -491,14 +503,17 @@ def fp8_format(args, dev, seq_lens, n_comp, ws, fmt):
     comp_gran = 15 if fmt == 0 else 13
     raw_tiles = (st["live_granules"] - comp_gran * st["live_runs"]) / (16 - comp_gran) / st["live_runs"]
 
+    ws16 = paged.workspace(B, HQ, HKV, N_COMP, 16, device=dev)
+
     def call(L, fused, out, splits):
+        w = ws16 if splits == 16 else ws
         if fused:
             kvz.kvz_fp8_decode_attention(L["q"], out, fmt, arena.arena, L["meta"], L["bases"],
                                          L["block_table"], seq_lens, n_comp, L["tail"], SCALE,
-                                         1.0, 1.0, ws, splits)
+                                         1.0, 1.0, w, splits)
         else:
             kvz.kvz_fp8_raw_decode_attention(L["q"], out, fmt, L["store"], L["block_table"],
-                                             seq_lens, n_comp, L["tail"], SCALE, 1.0, 1.0, ws,
+                                             seq_lens, n_comp, L["tail"], SCALE, 1.0, 1.0, w,
                                              HKV, splits)
     res = {}
     for mode in ("fused", "fp8"):
@@ -645,6 +660,71 @@ def compressible_variant(args, dev, seq_lens, n_comp, ws):
            "speedup_vs_bf16_kernel": round(res[False] / res[True], 4)}
     log(f"compressible variant: fused {res[True]:.1f} us/layer vs bf16 {res[False]:.1f} "
         f"(raw fraction {out['raw_block_fraction']})")
+    return out
+
+
+def other_config(args, dev, name, bsz, hq, hkv, n_comp, n_layers, u_max, forced, seed, stress):
+    """Another workload shape: n_layers distinct layers of bsz sequences of n_comp compressed
+    pages each (no tail page), fused attention vs the BF16 kernel, per layer (graph replays over
+    the layers, so no layer is served from cache)."""
+    import torch
+    from decode_attention_kvz_amd import kvz, paged, synth
+    n_phys = bsz * n_comp
+    arena = paged.SlotArena(n_layers * n_phys * hkv * 2 * 4096 + (16 << 20), device=dev)
+    rng = np.random.default_rng(seed)
+    layers = []
+    for layer in range(n_layers):
+        pages = synth.kv_pages(bsz, n_comp, hkv, seed=seed, layer=layer, u_max=u_max,
+                               forced_frac=forced, stress=stress, device=dev)
+        bt = rng.permutation(n_phys).reshape(bsz, n_comp).astype(np.int32)
+        meta = paged.new_meta_table(n_phys, hkv, device=dev)
+        items = paged.page_items(pages, [(b, p) for b in range(bsz) for p in range(n_comp)], meta,
+                                 bt.reshape(-1))
+        kvz.kvz_encode_pages(arena.pool, torch.from_numpy(np.ascontiguousarray(items)).to(dev),
+                             n_phys * hkv * 2, 0)
+        inv = torch.as_tensor(np.argsort(bt.reshape(-1)), device=dev)
+        store = paged.pack_bf16_pages(pages.reshape(n_phys, 2, hkv, 16, 128)[inv])
+        layers.append(dict(meta=meta, block_table=torch.from_numpy(bt).to(dev), store=store,
+                           q=synth.queries(bsz, hq, seed=seed * 1000 + layer, device=dev),
+                           out=torch.empty((bsz, hq, 128), dtype=torch.float32, device=dev)))
+        torch.cuda.synchronize()
+        del pages, items
+    st = arena.stats()
+    rec = st["live_granules"] * 256 / n_layers
+    seq_lens = torch.full((bsz,), 16 * n_comp, dtype=torch.int32, device=dev)
+    ncomp = torch.full((bsz,), n_comp, dtype=torch.int32, device=dev)
+    ws = paged.workspace(bsz, hq, hkv, n_comp, args.splits, device=dev)
+    res = {}
+    for fused in (True, False):
+        def run():
+            for L in layers:
+                if fused:
+                    kvz.kvz_decode_attention(L["q"], L["out"], arena.arena, L["meta"],
+                                             L["block_table"], seq_lens, ncomp, None, SCALE, ws,
+                                             args.splits)
+                else:
+                    kvz.kvz_bf16_decode_attention(L["q"], L["out"], L["store"], L["block_table"],
+                                                  seq_lens, ncomp, None, SCALE, ws, hkv, args.splits)
+        res[fused] = graph_us_per_layer(run, n_layers, args)
+    io = n_phys * (hkv * 16 + 4) + bsz * hq * 128 * (2 + 4)   # metadata, block table, q, out
+    alg = rec + io
+    alg_bf16 = n_phys * hkv * 2 * 4096 + io
+    out = {"label": f"{bsz} sequence(s) x {16 * n_comp} tokens, {hq}/{hkv} heads, {n_layers} "
+                    f"distinct layers, u~U[-{u_max:g},{u_max:g}], {forced:.0%} forced-raw blocks"
+                    + (", stress values" if stress else ""),
+           "record_bytes_per_layer": int(rec),
+           "raw_block_fraction": round(st["live_raw_blocks"] / (st["live_runs"] * 4), 4),
+           "fused_us_per_layer": round(res[True], 2),
+           "fused_achieved_GBps": round(alg / (res[True] * 1e-6) / 1e9, 1),
+           "fused_hbm_frac": round(alg / (res[True] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+           "bf16_us_per_layer": round(res[False], 2),
+           "bf16_hbm_frac": round(alg_bf16 / (res[False] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+           "speedup_vs_bf16_kernel": round(res[False] / res[True], 4)}
+    for L in layers:
+        del L["store"]
+    arena.close()
+    log(f"{name}: fused {res[True]:.1f} us/layer ({out['fused_hbm_frac']:.1%} of HBM peak) vs "
+        f"bf16 {res[False]:.1f} ({out['bf16_hbm_frac']:.1%})")
     return out
 
 

@@ -15,17 +15,18 @@
 // group-adaptive code on the FP8 exponent field ("GAAC: ...", appendix "Relation to FP8 KV"),
 // converted exactly to BF16 in registers for the MFMA products.
 //
-// Work decomposition (one wave = one unit = (sequence b, KV head, split s)):
-//   * a unit walks a contiguous range of its sequence's pages (the tail page counts as the
-//     last page); per page it loads the four K and four V blocks of its KV head (16 bytes per
-//     lane per block: a compressed chunk is 12 bytes and the next 4 are ignored), restores them
-//     in registers, and runs
+// Work decomposition (one workgroup = one unit = (sequence b, KV head, split s)):
+//   * a unit covers a contiguous range of its sequence's pages (the tail page counts as the
+//     last page); each of its four waves walks one consecutive quarter; per page a wave loads
+//     the four K and four V blocks of its KV head (16 bytes per lane per block: a compressed
+//     chunk is 12 bytes and the next 4 are ignored), restores them in registers, and runs
 //       S[16 tokens x 16 heads] = K_page(16x128) . Q^T   as 4 x v_mfma_f32_16x16x32_bf16,
 //       O[32 heads x 128]      += P(32x16) . V_page    as 4 x 2 x v_mfma_f32_32x32x16_bf16,
 //     with P split into bf16 hi + lo parts so that P is carried to ~2^-17 relative;
 //   * the query group (G <= 16 heads sharing the KV head) is the MFMA's head dimension;
 //   * online softmax in base 2 per head; rows of O are rescaled only when a head's max rises;
-//   * every unit writes (m, l, O) for its heads; attn_combine merges the splits.
+//   * the four waves' (m, l, O) are merged in LDS; a unit then writes the normalized output
+//     (one split per sequence: no further launch) or its partial, which attn_combine merges.
 #include "fp8_internal.h"
 
 #include <math.h>
@@ -398,8 +399,10 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
     __syncthreads();
   }
   const int lane = threadIdx.x & 63;
-  const int unit = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // unit = kvh * U + k: a workgroup's four waves take four consecutive splits of one KV head
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // unit = kvh * U + k = the workgroup: split k of KV head kvh, whose page range its four waves
+  // divide into four consecutive quarters (merged in LDS at the end)
+  const int unit = blockIdx.x;
   const int U = p.B * p.S;                 // splits per KV head
   if (unit >= U * p.Hkv) return;
   const int kvh = unit / U;
@@ -412,8 +415,10 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
   const int n_comp = so.n_comp;
   const int n_tail = so.n_tail;
   const int total = so.total;
-  const int p0 = (int)(((int64_t)s * total) / so.sb);
-  const int p1 = (int)(((int64_t)(s + 1) * total) / so.sb);
+  const int P0 = (int)(((int64_t)s * total) / so.sb);       // the workgroup's pages
+  const int P1 = (int)(((int64_t)(s + 1) * total) / so.sb);
+  const int p0 = P0 + (int)(((int64_t)wave * (P1 - P0)) / 4);   // this wave's quarter
+  const int p1 = P0 + (int)(((int64_t)(wave + 1) * (P1 - P0)) / 4);
 
   // Q as the column operand of the 16x16x32 product: head lane%16, dims 32j + 8*(lane/16) + i.
   const int head = lane & 15;
@@ -867,38 +872,50 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
   float l_tot = sm.l_run + lane_xor(sm.l_run, 16);
   l_tot += lane_xor(l_tot, 32);          // lane h (h < 16) now holds l of head h
   constexpr int NR = GB <= 8 ? 4 : 8;
-  const bool empty_seq = p.seq_lens[b] <= 0;
-  float* out_bh = p.out + ((size_t)b * p.Hq + (size_t)kvh * p.G) * KVZ_HEAD_DIM;
 
-  if (p.S == 1) {
-    // the only split: normalize in place
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const int row = 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-      const float l_row = __shfl(l_tot, row & 15, 64);
-      if (row < p.G) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          out_bh[(size_t)row * KVZ_HEAD_DIM + 32 * j + (lane & 31)] = empty_seq ? 0.f : sm.o[j][r] / l_row;
-      }
-    }
-    return;
-  }
-
-  // partial results of this unit: (m, l) per head and the unnormalized O rows
-  if (lane < p.G) {
-    p.ws_ml[((size_t)unit * p.G + lane) * 2 + 0] = sm.m_run;
-    p.ws_ml[((size_t)unit * p.G + lane) * 2 + 1] = l_tot;
+  // The four waves' (m, l) per head and unnormalized O rows meet in LDS; one merge per
+  // (head, dim): M = max m_w, L = sum l_w 2^(m_w - M), O = sum O_w 2^(m_w - M), in wave order.
+  __shared__ float s_m[4][16], s_l[4][16];
+  __shared__ float s_o[4][GB * KVZ_HEAD_DIM];
+  if (lane < 16) {
+    s_m[wave][lane] = sm.m_run;
+    s_l[wave][lane] = l_tot;
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
       const int row = 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-      if (row < p.G) p.ws_o[((size_t)unit * p.G + row) * KVZ_HEAD_DIM + 32 * j + (lane & 31)] = sm.o[j][r];
+      if (row < p.G) s_o[wave][row * KVZ_HEAD_DIM + 32 * j + (lane & 31)] = sm.o[j][r];
     }
   }
-
+  __syncthreads();
+  const bool empty_seq = p.seq_lens[b] <= 0;
+  for (int idx = threadIdx.x; idx < p.G * KVZ_HEAD_DIM; idx += 256) {
+    const int h = idx / KVZ_HEAD_DIM, d = idx % KVZ_HEAD_DIM;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][h]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = s_m[w][h];
+      const float c = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      L += c * s_l[w][h];
+      O += c * s_o[w][idx];
+    }
+    if (p.S == 1) {
+      // the only split: normalize in place
+      p.out[((size_t)b * p.Hq + (size_t)kvh * p.G + h) * KVZ_HEAD_DIM + d] = empty_seq ? 0.f : O / L;
+    } else {
+      // the partial result of this unit
+      p.ws_o[((size_t)unit * p.G + h) * KVZ_HEAD_DIM + d] = O;
+      if (d == 0) {
+        p.ws_ml[((size_t)unit * p.G + h) * 2 + 0] = M;
+        p.ws_ml[((size_t)unit * p.G + h) * 2 + 1] = L;
+      }
+    }
+  }
 }
 
 // Merge the splits of every (sequence, query head): M = max m_s, L = sum l_s 2^(m_s - M),
@@ -1017,19 +1034,19 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(
   }
 }
 
-// Split count: one workgroup (4 splits) per CU - the 2-page prefetch ring keeps enough bytes in
-// flight with 4 waves per CU, and measured as fast or faster than 2 workgroups per CU on every
-// workload shape - with at least 4 pages per split.  Workgroup counts that are not a multiple of
-// the CU count leave some CUs one workgroup more than others (measured 10-20% slower).
-// The group-adaptive tiles' restore has long dependent latencies (ballots, lane shuffles), so
-// that format runs two workgroups per CU (two waves per SIMD) to overlap them.
-constexpr int kGaacWavesPerCu = 8;
+// Split count: one workgroup (one split, its four waves) per CU - the 2-page prefetch ring keeps
+// enough bytes in flight with 4 waves per CU, and measured as fast or faster than 2 workgroups
+// per CU on every workload shape - with at least 4 pages per wave.  Workgroup counts that are
+// not a multiple of the CU count leave some CUs one workgroup more than others (measured 10-20%
+// slower).  The coded tiles' restore has long dependent latencies (ballots, lane shuffles), so
+// those formats run two workgroups per CU (two waves per SIMD) to overlap them.
+constexpr int kCodedWgsPerCu = 2;
 
-int choose_splits(int B, int Hkv, int max_pages, int n_cu, int waves_per_cu = 4) {
+int choose_splits(int B, int Hkv, int max_pages, int n_cu, int wgs_per_cu = 1) {
   const int64_t units = (int64_t)(B * Hkv > 0 ? B * Hkv : 1);
   const int64_t pages = (int64_t)max_pages + 1;
-  int64_t S = ((int64_t)waves_per_cu * n_cu + units - 1) / units;
-  const int64_t by_pages = (pages + 3) / 4;
+  int64_t S = ((int64_t)wgs_per_cu * n_cu + units - 1) / units;
+  const int64_t by_pages = (pages + 15) / 16;
   if (S > by_pages) S = by_pages;
   if (S > kMaxSplits) S = kMaxSplits;
   return (int)(S < 1 ? 1 : S);
@@ -1093,7 +1110,7 @@ int launch_attention(const CommonArgs& a, const uint8_t* kv, const kvz_group_met
   if (a.splits < 0 || a.splits > kMaxSplits) return set_error(KVZ_EINVAL, "splits out of range");
   const int S = a.splits ? a.splits
                          : choose_splits(a.batch, a.num_kv_heads, a.max_pages, device_cus(),
-                                         CODED ? kGaacWavesPerCu : 4);
+                                         CODED ? kCodedWgsPerCu : 1);
   uint64_t ml_bytes, need;
   workspace_layout(a.batch, a.num_q_heads, a.num_kv_heads, S, &ml_bytes, &need);
   if (a.workspace_bytes < need) return set_error(KVZ_EINVAL, "workspace too small");
@@ -1123,7 +1140,7 @@ int launch_attention(const CommonArgs& a, const uint8_t* kv, const kvz_group_met
   p.scale_log2 = a.sm_scale * a.k_scale * 1.4426950408889634f;
   p.v_scale = a.v_scale;
 
-  const dim3 grid((unsigned)((units + 3) / 4));
+  const dim3 grid((unsigned)units);
   if (G <= 4)
     hipLaunchKernelGGL((attn_split_kernel<4, FMT, FK>), grid, dim3(256), 0, s, p);
   else if (G <= 8)
@@ -1152,7 +1169,7 @@ extern "C" int kvz_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int3
   if (splits > kMaxSplits) return set_error(KVZ_EINVAL, "splits out of range");
   // sized for the format with the most splits, so one workspace serves every format
   const int S = splits ? splits
-                       : choose_splits(batch, num_kv_heads, max_pages, device_cus(), kGaacWavesPerCu);
+                       : choose_splits(batch, num_kv_heads, max_pages, device_cus(), kCodedWgsPerCu);
   uint64_t ml, total;
   workspace_layout(batch, num_q_heads, num_kv_heads, S, &ml, &total);
   *bytes = total < 256 ? 256 : total;
