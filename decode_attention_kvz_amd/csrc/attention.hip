@@ -944,7 +944,7 @@ __device__ __forceinline__ float block_reduce(float v, float* s_red, bool is_max
 // Splits merged from registers when the batch's split map is the uniform one (sequence b owns
 // splits b*S .. b*S+S-1): every partial of (b, head) is loaded in the same round trip as the
 // lengths that confirm the map.  Larger S, or a ragged map, takes the general path.
-constexpr int kSpecSplits = 16;
+constexpr int kSpecSplits = 32;
 
 __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(
     const float* ws_ml, const float* ws_o, float* out, const int32_t* seq_lens,
