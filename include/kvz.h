@@ -145,10 +145,11 @@ typedef struct {
                                    tokens past its compressed pages                             */
   int32_t batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages;
   int32_t splits;               /* split-K: pieces per sequence on average, 0..4096; 0 =
-                                   automatic (even over the device's CUs).  With S > 1 a piece
-                                   holds at most ceil(W / (B*S)) pages (W = the batch's pages),
-                                   so longer sequences are cut into more pieces; equal lengths
-                                   give exactly S pieces each                                    */
+                                   automatic (one piece per CU).  A piece is one workgroup whose
+                                   four waves each take a quarter of its pages and merge in LDS.
+                                   With S > 1 a piece holds at most ceil(W / (B*S)) pages (W =
+                                   the batch's pages), so longer sequences are cut into more
+                                   pieces; equal lengths give exactly S pieces each              */
   float sm_scale;
   void* workspace;              /* device, >= kvz_attn_workspace_bytes(...), 256-B aligned; calls
                                    that share a workspace must be ordered on one stream         */
@@ -388,9 +389,10 @@ int kvz_fp8_decode_attention(const kvz_fp8_attn_args* a, hipStream_t s);
 /* The same attention over uncompressed FP8 pages (the FP8 baseline). */
 int kvz_fp8_raw_decode_attention(const kvz_fp8_attn_args* a, hipStream_t s);
 
-/* Workspace bytes the attention calls (kvz_decode_attention, kvz_gaac_decode_attention,
- * kvz_bf16_decode_attention) need for these sizes.  splits = 0: enough for the automatic
- * split count of every one of them (the group-adaptive format uses twice as many splits). */
+/* Workspace bytes the attention calls (kvz_decode_attention, kvz_bf16_decode_attention,
+ * kvz_gaac_decode_attention, kvz_fp8_decode_attention, kvz_fp8_raw_decode_attention) need for
+ * these sizes.  splits = 0: enough for the automatic split count of every one of them (the
+ * coded tiles - group-adaptive and FP8 - use twice as many splits). */
 int kvz_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                              int32_t max_pages, int32_t splits, uint64_t* bytes);
 
