@@ -54,18 +54,39 @@ __global__ __launch_bounds__(256) void classify_kernel(const kvz_encode_item* it
   const kvz_encode_item it = items[item];
   const bool aligned = ((((uintptr_t)it.src) & 15u) == 0) && ((it.src_stride & 7u) == 0);
   uint32_t tags = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    // membership only matters here, so read the block in K chunk order for both kinds
-    const uint4 w = load_chunk(it.src, it.src_stride, KVZ_KIND_K, j, lane, aligned);
-    uint32_t lo = 255u, hi = 0u;
-    chunk_exp_range(w, lo, hi);
-    lo = wave_min(lo);
-    hi = wave_max(hi);
+  auto tag_of = [&](uint32_t lo, uint32_t hi) {
     const uint32_t b = lo & 0xFEu;
-    uint32_t tag = (hi <= b + 15u) ? (b >> 1) : KVZ_RAW_TAG;
-    if (flags & KVZ_ENC_FORCE_RAW) tag = KVZ_RAW_TAG;
-    tags |= tag << (8 * j);
+    return (hi <= b + 15u && !(flags & KVZ_ENC_FORCE_RAW)) ? (b >> 1) : KVZ_RAW_TAG;
+  };
+  if (aligned) {
+    // Only membership matters here, so read the page row by row: load k of lane l is the 16
+    // bytes of row l/16 + 4k at dims 8(l%16)..+7, always in block (l%16)/4; each load covers
+    // 1 KB of whole rows.  The 16 lanes of a block differ in lane bits 0, 1, 4 and 5.
+    uint32_t lo = 255u, hi = 0u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint4 w = *reinterpret_cast<const uint4*>(
+          it.src + (size_t)((lane >> 4) + 4 * k) * it.src_stride + 8 * (lane & 15));
+      chunk_exp_range(w, lo, hi);
+    }
+#pragma unroll
+    for (int d = 1; d <= 32; d <<= 1) {
+      if (d == 4 || d == 8) continue;
+      lo = min(lo, (uint32_t)__shfl_xor((int)lo, d, 64));
+      hi = max(hi, (uint32_t)__shfl_xor((int)hi, d, 64));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)   // block j's range sits in lane 4j (and its partners)
+      tags |= tag_of((uint32_t)__builtin_amdgcn_readlane((int)lo, 4 * j),
+                     (uint32_t)__builtin_amdgcn_readlane((int)hi, 4 * j)) << (8 * j);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 w = load_chunk(it.src, it.src_stride, KVZ_KIND_K, j, lane, false);
+      uint32_t lo = 255u, hi = 0u;
+      chunk_exp_range(w, lo, hi);
+      tags |= tag_of(wave_min(lo), wave_max(hi)) << (8 * j);
+    }
   }
   if (lane == 0) {
     *reinterpret_cast<uint32_t*>(it.dst->tag) = tags;

@@ -57,6 +57,34 @@ def test_encode_tiny_config_matches_oracle_bytes(force_raw):
         assert 0 < oc.pool.raw_blocks < 256
 
 
+@pytest.mark.parametrize("stride,shift", [(136, 0), (131, 1)])
+def test_encode_from_strided_sources_matches_oracle(stride, shift):
+    """Items whose token rows are `stride` elements apart, the first one `shift` elements past a
+    16-byte boundary: the 16-byte path with a row stride other than 128 (136) and the
+    element-wise path (odd stride, misaligned base) both give the oracle's records."""
+    announce(f"encode strided sources stride={stride} shift={shift}")
+    pages = synth.kv_pages(1, 8, 2, seed=21, forced_frac=0.10)
+    nat = synth.bits(pages)[0]                                # [8, 2, 2, 16, 128]
+    flat = nat.transpose(0, 2, 1, 3, 4).reshape(-1, 16, 128)  # item order (page, head, K/V)
+    n = flat.shape[0]
+    buf = np.zeros((n, 16, stride), dtype=np.uint16)
+    buf[:, :, :128] = flat
+    dev = torch.zeros(shift + buf.size + 8, dtype=torch.int16, device="cuda")
+    dev[shift:shift + buf.size] = torch.from_numpy(buf.reshape(-1).view(np.int16)).cuda()
+    base = dev.data_ptr() + 2 * shift
+    meta = paged.new_meta_table(8, 2)
+    kinds = [i % 2 for i in range(n)]
+    items = torch.from_numpy(kvz.encode_items([base + 2 * i * 16 * stride for i in range(n)],
+                                              [meta.data_ptr() + 8 * i for i in range(n)],
+                                              stride, kinds)).cuda()
+    arena = paged.SlotArena(256 * 1024)
+    kvz.kvz_encode_pages(arena.pool, items, n, 0)
+    torch.cuda.synchronize()
+    oc = OracleCache(256 * 1024)
+    assert _meta_items(meta.cpu().numpy(), range(8), 2) == oc.encode(flat, kinds)
+    np.testing.assert_array_equal(arena.arena.cpu().numpy(), oc.arena)
+
+
 def test_decode_block_bit_exact_and_matches_oracle():
     announce("decode_block tiny config")
     pages = synth.kv_pages(1, 16, 2, seed=0, forced_frac=0.10)
