@@ -422,6 +422,188 @@ __global__ __launch_bounds__(kThreads) void pool_clear_meta_kernel(kvz_group_met
   }
 }
 
+// Calls of up to 4,096 items run in one workgroup, in one launch instead of three (allocation)
+// or four (free): each thread takes a contiguous run of up to PER items and the ranks come from
+// two block scans (class counts, then frontier granules).  Both the allocation and the free rule
+// depend on item order only - an item's rank among the items of its class, and the granules all
+// earlier frontier requests asked for - so this gives the same offsets, bins and counters as
+// the tiled passes above.  Measured encode + free (graph replays): 576 items 41.6 -> 22.2 us
+// (PER 2), 1,152 items 43.4 -> 25.9 us, 4,032 items 48.9 -> 43.7 us (PER 8); larger calls stay
+// tiled (one workgroup took 37 us instead of 21 us for 9,216 items).
+constexpr int kSmallPerLo = 2;                          // up to 1,024 items
+constexpr int kSmallPerHi = 8;                          // up to 4,096 items
+constexpr int kSmallItems = kThreads * kSmallPerHi;
+
+template <int kSmallPer, class Access>
+__global__ __launch_bounds__(kThreads) void pool_alloc_small_kernel(PoolHdr* hdr,
+                                                                    const uint32_t* bins,
+                                                                    Access acc, int n) {
+  __shared__ ScanShared sh;
+  __shared__ uint64_t s_red[kWaves];
+  if (hdr->magic != kPoolMagic) return;
+  const int per = (n + kThreads - 1) / kThreads;
+  const int i0 = (int)threadIdx.x * per;
+  int key[kSmallPer];
+#pragma unroll
+  for (int u = 0; u < kSmallPer; ++u) key[u] = (u < per && i0 + u < n) ? alloc_cls(acc, i0 + u) : -1;
+  uint64_t cnt[kBins];
+#pragma unroll
+  for (int k = 0; k < kBins; ++k) cnt[k] = hdr->bin_cnt[k];
+  const uint64_t f0 = hdr->frontier;
+  const uint64_t cap = hdr->capacity;
+  uint32_t lcnt[kBins];
+#pragma unroll
+  for (int k = 0; k < kBins; ++k) lcnt[k] = 0;
+#pragma unroll
+  for (int u = 0; u < kSmallPer; ++u)
+#pragma unroll
+    for (int k = 0; k < kBins; ++k) lcnt[k] += key[u] == k ? 1u : 0u;
+  uint32_t kbase[kBins], ktot[kBins];
+  block_scan_cols<kBins>(lcnt, kbase, ktot, sh.wave, sh.pre, sh.tot);
+  // rank of each item among its class: below the bin's count it pops the bin from the top,
+  // otherwise it asks the frontier for its run (prefix of every earlier request of the call)
+  uint32_t pos[kSmallPer];     // bin slot, or granules requested before it by this thread
+  uint32_t z = 0;
+#pragma unroll
+  for (int u = 0; u < kSmallPer; ++u) {
+    const int k = key[u];
+    pos[u] = 0;
+    if (k < 0) continue;
+    const uint64_t rank = pick(kbase, k);
+#pragma unroll
+    for (int j = 0; j < kBins; ++j) kbase[j] += j == k ? 1u : 0u;
+    const uint64_t ck = cnt[k];
+    if (rank < ck) {
+      pos[u] = (uint32_t)(hdr->bin_base[k] + ck - 1 - rank);
+    } else {
+      pos[u] = z;
+      key[u] = k + kBins;      // marks a frontier request
+      z += run_granules((uint32_t)k);
+    }
+  }
+  uint32_t zv[1] = {z}, zex[1], ztot[1];
+  block_scan_cols<1>(zv, zex, ztot, sh.wave, sh.pre, sh.tot);
+  uint64_t my_granted = 0, my_runs = 0, my_gran = 0, my_raw = 0, my_fail = 0;
+  uint32_t off[kSmallPer];
+#pragma unroll
+  for (int u = 0; u < kSmallPer; ++u) {
+    off[u] = KVZ_OFF_NONE;
+    const int kk = key[u];
+    if (kk < 0) continue;
+    const bool frontier = kk >= kBins;
+    const int k = frontier ? kk - kBins : kk;
+    const uint32_t g = run_granules((uint32_t)k);
+    if (frontier) {
+      const uint64_t start = f0 + zex[0] + pos[u];
+      if (start + g <= cap) {
+        off[u] = (uint32_t)start;
+        my_granted += g;
+      }
+    } else {
+      off[u] = bins[pos[u]];
+    }
+    if (off[u] != KVZ_OFF_NONE || !frontier) {
+      my_runs += 1;
+      my_gran += g;
+      my_raw += (uint32_t)k;
+    } else {
+      my_fail += 1;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kSmallPer; ++u)
+    if (key[u] >= 0) acc.set_off(i0 + u, off[u]);
+  const uint64_t granted = block_sum(my_granted, s_red);
+  const uint64_t runs = block_sum(my_runs, s_red);
+  const uint64_t gran = block_sum(my_gran, s_red);
+  const uint64_t raw = block_sum(my_raw, s_red);
+  const uint64_t fail = block_sum(my_fail, s_red);
+  // every thread read the header before the scans' barriers; one workgroup writes it back
+  if (threadIdx.x < kBins) {
+    const int k = (int)threadIdx.x;
+    const uint64_t tk = pick(ktot, k);
+    hdr->bin_cnt[k] = cnt[k] - (tk < cnt[k] ? tk : cnt[k]);
+  }
+  if (threadIdx.x == 0) {
+    hdr->frontier = f0 + granted;
+    hdr->live_runs += runs;
+    hdr->live_granules += gran;
+    hdr->live_raw_blocks += raw;
+    hdr->enospc += fail;
+  }
+}
+
+// The free of up to kSmallItems records in one workgroup: the i-th freed run of class k in item
+// order goes to bin slot count + i (dropped and counted as a bad free if the bin is full); every
+// listed record is cleared after all of them have been read.
+template <int kSmallPer>
+__global__ __launch_bounds__(kThreads) void pool_free_small_kernel(PoolHdr* hdr, uint32_t* bins,
+                                                                   kvz_group_meta* const* metas,
+                                                                   int n) {
+  __shared__ ScanShared sh;
+  __shared__ uint64_t s_red[kWaves];
+  if (hdr->magic != kPoolMagic) return;
+  const int per = (n + kThreads - 1) / kThreads;
+  const int i0 = (int)threadIdx.x * per;
+  kvz_group_meta* m[kSmallPer];
+  uint2 rec[kSmallPer];
+#pragma unroll
+  for (int u = 0; u < kSmallPer; ++u) m[u] = (u < per && i0 + u < n) ? metas[i0 + u] : nullptr;
+#pragma unroll
+  for (int u = 0; u < kSmallPer; ++u)
+    rec[u] = m[u] ? *reinterpret_cast<const uint2*>(m[u]) : make_uint2(KVZ_OFF_NONE, 0u);
+  uint64_t cnt[kBins];
+#pragma unroll
+  for (int k = 0; k < kBins; ++k) cnt[k] = hdr->bin_cnt[k];
+  uint32_t lcnt[kBins];
+#pragma unroll
+  for (int k = 0; k < kBins; ++k) lcnt[k] = 0;
+  int key[kSmallPer];
+#pragma unroll
+  for (int u = 0; u < kSmallPer; ++u) {
+    key[u] = rec[u].x != KVZ_OFF_NONE ? (int)n_raw_of(rec[u].y) : -1;
+#pragma unroll
+    for (int k = 0; k < kBins; ++k) lcnt[k] += key[u] == k ? 1u : 0u;
+  }
+  uint32_t kbase[kBins], ktot[kBins];
+  block_scan_cols<kBins>(lcnt, kbase, ktot, sh.wave, sh.pre, sh.tot);   // orders all reads above
+  uint64_t my_runs = 0, my_gran = 0, my_raw = 0, my_bad = 0;
+#pragma unroll
+  for (int u = 0; u < kSmallPer; ++u) {
+    const int k = key[u];
+    if (k < 0) continue;
+    const uint64_t slot = cnt[k] + pick(kbase, k);
+#pragma unroll
+    for (int j = 0; j < kBins; ++j) kbase[j] += j == k ? 1u : 0u;
+    if (slot < hdr->bin_cap[k]) {
+      bins[hdr->bin_base[k] + slot] = rec[u].x;
+      my_runs += 1;
+      my_gran += run_granules((uint32_t)k);
+      my_raw += (uint32_t)k;
+    } else {
+      my_bad += 1;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kSmallPer; ++u)
+    if (m[u]) *reinterpret_cast<uint2*>(m[u]) = make_uint2(KVZ_OFF_NONE, 0u);
+  const uint64_t runs = block_sum(my_runs, s_red);
+  const uint64_t gran = block_sum(my_gran, s_red);
+  const uint64_t raw = block_sum(my_raw, s_red);
+  const uint64_t bad = block_sum(my_bad, s_red);
+  if (threadIdx.x < kBins) {
+    const int k = (int)threadIdx.x;
+    const uint64_t c = cnt[k] + pick(ktot, k);
+    hdr->bin_cnt[k] = c < hdr->bin_cap[k] ? c : hdr->bin_cap[k];
+  }
+  if (threadIdx.x == 0) {
+    hdr->live_runs -= runs;
+    hdr->live_granules -= gran;
+    hdr->live_raw_blocks -= raw;
+    hdr->bad_frees += bad;
+  }
+}
+
 __global__ void pool_init_kernel(PoolHdr* hdr, uint64_t capacity, PoolHdr tmpl) {
   if (threadIdx.x == 0 && blockIdx.x == 0) {
     *hdr = tmpl;
@@ -446,6 +628,15 @@ int run_alloc(kvz_pool* p, Access acc, int n, hipStream_t s) {
   PoolHdr* hdr = (PoolHdr*)p->state;
   const uint32_t* bins = (const uint32_t*)((uint8_t*)p->state + kPoolHdrBytes);
   PoolScratch* sc = (PoolScratch*)p->scratch;
+  if (n <= kSmallItems) {
+    if (n <= kThreads * kSmallPerLo)
+      hipLaunchKernelGGL((pool_alloc_small_kernel<kSmallPerLo, Access>), dim3(1), dim3(kThreads), 0,
+                         s, hdr, bins, acc, n);
+    else
+      hipLaunchKernelGGL((pool_alloc_small_kernel<kSmallPerHi, Access>), dim3(1), dim3(kThreads), 0,
+                         s, hdr, bins, acc, n);
+    return check_hip(hipGetLastError(), "slot alloc launch");
+  }
   for (int first = 0; first < n; first += kChunkItems) {
     const int n_end = n - first < kChunkItems ? n : first + kChunkItems;
     const int tiles = (n_end - first + kTile - 1) / kTile;
@@ -569,6 +760,15 @@ extern "C" int kvz_slot_free(kvz_pool* p, kvz_group_meta* const* d_metas, int32_
   uint32_t* bins = (uint32_t*)((uint8_t*)p->state + kPoolHdrBytes);
   PoolScratch* sc = (PoolScratch*)p->scratch;
   const FreeAccess acc{d_metas};
+  if (n <= kSmallItems) {
+    if (n <= kThreads * kSmallPerLo)
+      hipLaunchKernelGGL(pool_free_small_kernel<kSmallPerLo>, dim3(1), dim3(kThreads), 0, s, hdr,
+                         bins, d_metas, n);
+    else
+      hipLaunchKernelGGL(pool_free_small_kernel<kSmallPerHi>, dim3(1), dim3(kThreads), 0, s, hdr,
+                         bins, d_metas, n);
+    return check_hip(hipGetLastError(), "slot free launch");
+  }
   for (int first = 0; first < n; first += kChunkItems) {
     const int n_end = n - first < kChunkItems ? n : first + kChunkItems;
     const int tiles = (n_end - first + kTile - 1) / kTile;

@@ -406,6 +406,32 @@ def test_slot_pool_calls_spanning_many_tiles_match_model():
     assert model.enospc > 0 and (offs2 != OFF_NONE).sum() > 6000
 
 
+@pytest.mark.parametrize("small,big", [(1024, 1025), (4096, 4097)])
+def test_slot_pool_one_workgroup_and_tiled_calls_at_the_boundary(small, big):
+    """Calls of up to 1,024 items run in one workgroup with 2 items per thread, up to 4,096 with
+    8, larger ones in tiles: calls on both sides of each switch, alternating, for allocation
+    (bin pops that run out, frontier) and free, all equal the pool model."""
+    announce(f"slot pool: call sizes {small} / {big}")
+    rng = np.random.default_rng(63 + small)
+    arena = paged.SlotArena((35 * small + 1) * 256)
+    model = SlotPoolModel(arena.stats()["capacity_granules"])
+    ta, tb = _random_tags(rng, small, 0.15), _random_tags(rng, big, 0.3)
+    a = _alloc_and_check(arena, model, ta)
+    b = _alloc_and_check(arena, model, tb)
+    _check_stats(arena, model)
+    assert (a != OFF_NONE).all() and (b != OFF_NONE).all()
+    live_a = [(int(o), t.tolist()) for o, t in zip(a, ta)]
+    live_b = [(int(o), t.tolist()) for o, t in zip(b, tb)]
+    _free(arena, model, live_a + live_b[:1])           # `big` records
+    _check_stats(arena, model)
+    _free(arena, model, live_b[1:])                    # `small` records
+    _check_stats(arena, model)
+    _alloc_and_check(arena, model, _random_tags(rng, small, 0.5))   # pops, bins run dry
+    _check_stats(arena, model)
+    _alloc_and_check(arena, model, _random_tags(rng, big, 0.05))
+    _check_stats(arena, model)
+
+
 def test_slot_alloc_call_larger_than_one_chunk_matches_model():
     """One call of 1 Mi + 5000 items (two chunks of the tiled allocator: 1024 tiles of 1024
     items each): bin state and the frontier's request prefix carry into the second chunk."""
