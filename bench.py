@@ -142,8 +142,9 @@ def main():
                          "(3 launches each) and a 1 GiB device copy as a traffic reference")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs on exactly one GPU: the path has no multi-GPU form in this build "
-              "(see DESIGN.md for how it would shard).", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path (its (sequence, "
+              "KV head) units are independent, so a multi-GPU version would place KV heads, or "
+              "page ranges of long sequences, on different GPUs).", file=sys.stderr)
         sys.exit(2)
 
     import torch

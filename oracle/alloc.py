@@ -10,7 +10,7 @@ What it follows:
     reuse by another; a group's blocks are located from the first block's offset plus prefix-
     summed sizes, so the four blocks of a group are one contiguous run.
 
-Readings (listed in DESIGN.md): slots are 768 B (3 granules of 256 B) and 1024 B (4 granules);
+Readings: slots are 768 B (3 granules of 256 B) and 1024 B (4 granules);
 a group takes one contiguous run of 12 + n_raw granules.  Free runs are kept in five LIFO bins
 keyed by n_raw.  Allocation, in item order: pop the bin for that n_raw if it is not empty;
 otherwise take the run from the frontier.  Frontier requests of one call are served as a

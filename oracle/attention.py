@@ -13,7 +13,7 @@ The attention itself is the plain definition, computed in float64:
     s_t = sm_scale * sum_d q[h, d] * K[t, g, d],   g = h // (Hq / Hkv),
     o[h, :] = sum_t exp(s_t - max s) V[t, g, :] / sum_t exp(s_t - max s).
 
-Readings (listed in DESIGN.md): query head h uses KV head h // (Hq/Hkv); the scale is passed in;
+Readings: query head h uses KV head h // (Hq/Hkv); the scale is passed in;
 tokens 0 .. 16*n_comp-1 come from compressed pages via the block table, the remaining
 seq_len - 16*n_comp (0..16) from the tail; a sequence of length 0 gives an all-zero output row.
 NaN and Inf are carried by IEEE float64 arithmetic.

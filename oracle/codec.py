@@ -19,7 +19,7 @@ Decoding", section "How it works":
 BF16 fields follow the BF16 word description of the same page and the field split printed in
 "ExANS: Exponent Aligned Asymmetric Numeral Systems", section "Encoding Pipeline".
 
-Readings taken where the page leaves a step open (each is also listed in the design doc):
+Readings taken where the page leaves a step open (each is also stated in include/kvz.h):
   * block j of a group is tokens 0..15 x dims [32j, 32j+32);
   * element order inside a block (storage order) is the MFMA operand order, see storage_coords();
   * a block is 64 chunks of 8 values; a compressed chunk is 12 bytes (8 low bytes, then a

@@ -24,7 +24,7 @@ E4M3 ("e4m3fn": 1 sign, 4 exponent bits with bias 7, 3 fraction bits; exponent 1
 is NaN; no infinities) and E5M2 (1 sign, 5 exponent bits with bias 15, 2 fraction bits; exponent
 31 is infinity with fraction 0, NaN otherwise).  Exponent field 0 holds zeros and subnormals.
 
-Readings taken where the pages leave a step open (each is also listed in the design doc):
+Readings taken where the pages leave a step open (each is also stated in include/kvz.h):
   * the code is GAAC's, unchanged, applied to the FP8 exponent field (4 or 5 bits): the kept
     part is sign + fraction (4 bits in E4M3, 3 in E5M2); a raw group stores the 1 (E4M3) or 2
     (E5M2) exponent bits above the low three; so the all-3-bit case is 4 + 3 + 0.25 = 7.25 and

@@ -23,7 +23,7 @@ Devices":
     codes, 64 of mode tags, and an escape slot whose capacity is 128 bytes (32 used on average,
     96 unused).
 
-Readings taken where the pages leave a step open (each is also listed in the design doc):
+Readings taken where the pages leave a step open (each is also stated in include/kvz.h):
   * a tile is one page's K (or V) for one KV head: 16 tokens x 128 dims;
   * the groups of eight in attention-access order are the chunks of the other format
     (codec.storage_coords): group g = 64*j + c is chunk c of the 32-dim block j;

@@ -174,7 +174,7 @@ def test_binding_rejects_host_and_misshapen_tensors_before_the_call():
                                torch.zeros((1,), dtype=torch.uint8))
     with pytest.raises(ValueError, match="required"):
         kvz.kvz_stream_read(None, None)
-    # the checker itself, on tensors that claim to live on the GPU (no memory is touched)
+    # the argument check itself, on tensors that claim to live on the GPU (no memory is touched)
 
     class FakeDev:
         def __init__(self, t):
