@@ -135,6 +135,8 @@ def main():
     ap.add_argument("--no-variant", action="store_true")
     ap.add_argument("--no-gaac", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-online", action="store_true",
+                    help="skip the online page-completion leg (64 sequences, 32 layers)")
     ap.add_argument("--no-other", action="store_true",
                     help="skip the other workload shapes (2K batch of 32, one 131K sequence)")
     ap.add_argument("--pmc-probe", action="store_true",
@@ -276,6 +278,7 @@ def main():
     read_peak = stream_read_peak(timed)
     variant = None if args.no_variant else compressible_variant(args, dev, seq_lens, n_comp, ws)
     others = None if args.no_other else {c[0]: other_config(args, dev, *c) for c in OTHER_CONFIGS}
+    online = None if args.no_online else online_completion(args, dev)
     gaac_leg = None if args.no_gaac else gaac_format(args, dev, seq_lens, n_comp, ws)
     fp8_leg = None if args.no_fp8 else {name: fp8_format(args, dev, seq_lens, n_comp, ws, fmt)
                                         for name, fmt in (("e4m3", 0), ("e5m2", 1))}
@@ -330,6 +333,7 @@ def main():
                                                (float(np.median(enc_layer_us)) * 1e-6) / 1e9, 1)},
         "compressible_variant": variant,
         "other_configs": others,
+        "online_completion": online,
         "gaac_format": gaac_leg,
         "fp8_formats": fp8_leg,
     }
@@ -662,6 +666,47 @@ def compressible_variant(args, dev, seq_lens, n_comp, ws):
     log(f"compressible variant: fused {res[True]:.1f} us/layer vs bf16 {res[False]:.1f} "
         f"(raw fraction {out['raw_block_fraction']})")
     return out
+
+
+def online_completion(args, dev):
+    """Online page completion at the 64-sequence, 32-layer, 8-KV-head shape with staggered
+    phases: every step 4 sequences complete a page, so 4 x 32 layers x 8 heads x K|V = 2,048
+    groups are encoded and, in steady state, as many are freed.  One graph per step: free the
+    2,048 groups the previous step stored, then encode the new ones into the same metadata (the
+    freed runs are reused, deterministic in item order).  Forced-raw fraction 0 / 10 / 50 %."""
+    import torch
+    from decode_attention_kvz_amd import kvz, paged, synth
+    n_seq, n_layers, hkv = 4, 32, 8
+    res = {}
+    for forced in (0.0, 0.10, 0.50):
+        # the completing pages: sequence s, "page" = layer (one 16-token page per layer)
+        pages = synth.kv_pages(n_seq, n_layers, hkv, seed=31, u_max=3.0, forced_frac=forced,
+                               device=dev)
+        arena = paged.SlotArena(64 << 20, device=dev)
+        meta = paged.new_meta_table(n_seq * n_layers, hkv, device=dev)
+        ids = [(s, l) for s in range(n_seq) for l in range(n_layers)]
+        items = paged.page_items(pages, ids, meta, list(range(len(ids))))
+        n = items.size // kvz.ENCODE_ITEM_DTYPE.itemsize
+        d_items = torch.from_numpy(np.ascontiguousarray(items)).to(dev)
+        ptrs = torch.from_numpy(meta.data_ptr() + np.arange(n, dtype=np.int64) * 8).to(dev)
+        kvz.kvz_encode_pages(arena.pool, d_items, n)
+
+        def step():
+            kvz.kvz_slot_free(arena.pool, ptrs)
+            kvz.kvz_encode_pages(arena.pool, d_items, n)
+        us = graph_us_per_layer(step, 1, args)
+        st = arena.stats()
+        rec = st["live_granules"] * 256
+        raw = st["live_raw_blocks"] / max(st["live_runs"] * 4, 1)
+        res[f"forced_{int(forced * 100)}pct"] = {
+            "groups_per_step": n, "us_per_step": round(us, 1),
+            "raw_block_fraction": round(raw, 4),
+            "bytes_read": n * 4096, "bytes_written": int(rec + n * 8),
+            "GBps": round((n * 4096 + rec + n * 8) / (us * 1e-6) / 1e9, 1)}
+        log(f"online completion, {n} groups/step, forced {forced:.0%}: {us:.1f} us/step "
+            f"(raw fraction {raw:.3f})")
+        del arena
+    return res
 
 
 def other_config(args, dev, name, bsz, hq, hkv, n_comp, n_layers, u_max, forced, seed, stress):

@@ -238,18 +238,19 @@ def test_slot_alloc_free_churn_matches_model():
     assert model.enospc > 0, "the churn should have exhausted the pool at least once"
 
 
-@pytest.mark.parametrize("forced", [0.0, 0.10, 0.50])
-def test_online_page_completion_churn(forced):
+@pytest.mark.parametrize("forced,n_layers", [(0.0, 4), (0.10, 4), (0.50, 4), (0.10, 32)])
+def test_online_page_completion_churn(forced, n_layers):
     """Online encode at page completion with frees and reuse across layers (64 sequences,
-    8 KV heads, 4 layers, staggered phases): offsets and tags equal the oracle pool model and
-    classification after every step; live groups decode to their source pages."""
-    announce(f"online churn forced={forced}")
+    8 KV heads, 4 layers with a small arena that runs out, or all 32 layers of the online
+    workload with room for every page, staggered phases): offsets and tags equal the oracle
+    pool model and classification after every step; live groups decode to their source pages."""
+    announce(f"online churn forced={forced} layers={n_layers}")
     rng = np.random.default_rng(int(forced * 100) + 3)
-    n_seq, hkv, n_layers, page_bank = 64, 8, 4, 16
+    n_seq, hkv, page_bank = 64, 8, 16
     bank = synth.kv_pages(n_seq, page_bank, hkv, seed=3, forced_frac=forced, device="cuda")
     bank_h = synth.bits(bank)                                  # [S, 16, 2, Hkv, 16, 128]
     max_pages = 64
-    arena_bytes = 96 << 20
+    arena_bytes = (96 << 20) if n_layers == 4 else (1 << 30)
     arena = paged.SlotArena(arena_bytes)
     model = SlotPoolModel(pool_capacity_granules(arena.arena.numel()))
     metas = [paged.new_meta_table(n_seq * max_pages, hkv) for _ in range(n_layers)]
