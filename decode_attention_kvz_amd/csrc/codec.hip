@@ -14,7 +14,7 @@
 // kvz_encode_pages = classify (one wave per item) -> allocate (pool.hip, one workgroup, item
 // order) -> pack (one wave per item).  The item's metadata slot carries the tags from classify
 // to allocate and the offset from allocate to pack, so the encoder needs no scratch memory.
-#include "kvz_internal.h"
+#include "encode_internal.h"
 
 namespace kvz {
 
@@ -32,30 +32,6 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
   for (int d = 32; d >= 1; d >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, d, 64));
   return v;
 }
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// One item per wave: its source pointer and row stride are wave-uniform.  A buffer resource
-// over its 16 rows keeps them in SGPRs (the pointer read from the item is generic, and flat
-// loads of it were issued one round trip apart).
-__device__ __forceinline__ uint32_t uniform_row_bytes(uint32_t src_stride) {
-  return 2u * (uint32_t)__builtin_amdgcn_readfirstlane((int)src_stride);
-}
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint16_t* src, uint32_t row_bytes) {
-  const uint64_t u = (uint64_t)(uintptr_t)src;
-  const uint64_t su = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(u >> 32)) << 32) |
-                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
-  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((uintptr_t)su), 0,
-                                           (int)(15u * row_bytes + 2u * KVZ_HEAD_DIM), 0x00020000);
-}
-// Cache policy of the source loads.  A bulk call (prefill: every page of a layer, far more than
-// the caches hold) loads non-temporally (bit "nt"), each page is read once by classify and once
-// by pack: 130,816 groups in 283 us vs 333 us with cached loads.  A decode step's completion
-// (recently written tail pages, often still in the last-level cache) keeps cached loads: 9,216
-// groups in 65.3 us vs 69.2 us non-temporal.  Calls above this many items stream.
-constexpr int kStreamItems = 32768;   // 128 MiB of BF16 source
-constexpr int kCachedLoad = 0;
-constexpr int kStreamLoad = 2;
 
 __device__ __forceinline__ uint32_t exp_of(uint32_t w) { return (w >> 7) & 0xFFu; }
 
@@ -131,44 +107,14 @@ __global__ __launch_bounds__(256) void pack_kernel(const kvz_encode_item* items,
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= n) return;
   const kvz_encode_item it = items[item];
-  const bool aligned = ((((uintptr_t)it.src) & 15u) == 0) && ((it.src_stride & 7u) == 0);
   // Every load of the item (its metadata, then its source) is issued before the first store:
   // a store into the arena may alias the source as far as the compiler knows, so a load left
   // after one waits for it.
-  // (metadata tables are device memory: a global load, whose wait the compiler counts exactly)
-  typedef __attribute__((address_space(1))) const uint64_t global_u64;
-  const uint64_t mt = *(global_u64*)(it.dst);   // little-endian: off, then tag[0..3]
+  const uint64_t mt = load_meta_record(it.dst);
   const uint32_t off = (uint32_t)mt;
   const uint32_t tags = (uint32_t)(mt >> 32);
   uint4 w[4];
-  if (aligned) {
-    const uint32_t row_bytes = uniform_row_bytes(it.src_stride);
-    const __amdgpu_buffer_rsrc_t r = page_rsrc(it.src, row_bytes);
-    if (__builtin_amdgcn_readfirstlane((int)it.kind) == KVZ_KIND_K) {
-      // chunk j of lane c: token c%16, dims 32j + 8(c/16)..+7 (16 contiguous bytes)
-      const int voff = (int)((uint32_t)(lane & 15) * row_bytes + 16u * (uint32_t)(lane >> 4));
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        w[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 64 * j, kPolicy));
-    } else {
-      // chunk j of lane c: dim 32j + c%32 of tokens 8(c/32)..+7 (one BF16 per row)
-      const int voff = (int)(8u * (uint32_t)(lane >> 5) * row_bytes + 2u * (uint32_t)(lane & 31));
-      uint32_t v[4][8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          v[j][i] = __builtin_amdgcn_raw_buffer_load_b16(r, voff, (int)((uint32_t)i * row_bytes) + 64 * j,
-                                                         kPolicy);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        w[j] = make_uint4(v[j][0] | (v[j][1] << 16), v[j][2] | (v[j][3] << 16),
-                          v[j][4] | (v[j][5] << 16), v[j][6] | (v[j][7] << 16));
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = load_chunk(it.src, it.src_stride, it.kind, j, lane, false);
-  }
+  load_item_chunks<kPolicy>(it.src, it.src_stride, it.kind, lane, w);
   // an offset only comes from the allocator; the run must still lie inside the pool
   if (off == KVZ_OFF_NONE || (uint64_t)off + run_granules(n_raw_of(tags)) > capacity) return;
   uint8_t* blk = arena + (size_t)off * KVZ_GRANULE_BYTES;

@@ -1,0 +1,80 @@
+// Source loads of the page-completion encoders (codec.hip, gaac.hip): one item (one K or V
+// page of one KV head, 16 rows of 128 BF16 values) per wave.
+#pragma once
+
+#include "kvz_internal.h"
+
+namespace kvz {
+
+// Cache policy of the source loads.  A bulk call (prefill: every page of a layer, far more than
+// the caches hold) loads non-temporally (bit "nt"): each page is read once by the classify pass
+// and once by the pack pass (exponent-coded pages of an 8K layer, 130,816 groups: 286 us vs 333
+// us with cached loads).  A decode step's completion (recently written tail pages, often still
+// in the last-level cache) keeps cached loads (9,216 groups: 65.3 us vs 69.2 us non-temporal).
+// Calls above this many items stream.
+constexpr int kStreamItems = 32768;   // 128 MiB of BF16 source
+constexpr int kCachedLoad = 0;
+constexpr int kStreamLoad = 2;
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// The item's source pointer and row stride are wave-uniform.  A buffer resource over its 16
+// rows keeps them in SGPRs: the pointer read from the item is generic, and flat loads of it
+// were issued a round trip apart (a flat load may alias the arena stores and waits on both
+// counters).
+__device__ __forceinline__ uint32_t uniform_row_bytes(uint32_t src_stride) {
+  return 2u * (uint32_t)__builtin_amdgcn_readfirstlane((int)src_stride);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint16_t* src, uint32_t row_bytes) {
+  const uint64_t u = (uint64_t)(uintptr_t)src;
+  const uint64_t su = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(u >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((uintptr_t)su), 0,
+                                           (int)(15u * row_bytes + 2u * KVZ_HEAD_DIM), 0x00020000);
+}
+
+__device__ __forceinline__ bool item_aligned(const uint16_t* src, uint32_t stride) {
+  return ((((uintptr_t)src) & 15u) == 0) && ((stride & 7u) == 0);
+}
+
+// The four chunks (blocks 0..3) of the item in lane order, as load_chunk gives them, with every
+// load issued before any is used.  K chunk j of lane c: token c%16, dims 32j + 8(c/16)..+7 (16
+// contiguous bytes); V: dim 32j + c%32 of tokens 8(c/32)..+7 (one value per row).
+template <int kPolicy>
+__device__ __forceinline__ void load_item_chunks(const uint16_t* src, uint32_t stride, uint32_t kind,
+                                                 int lane, uint4 (&w)[4]) {
+  if (item_aligned(src, stride)) {
+    const uint32_t row_bytes = uniform_row_bytes(stride);
+    const __amdgpu_buffer_rsrc_t r = page_rsrc(src, row_bytes);
+    if (__builtin_amdgcn_readfirstlane((int)kind) == KVZ_KIND_K) {
+      const int voff = (int)((uint32_t)(lane & 15) * row_bytes + 16u * (uint32_t)(lane >> 4));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 64 * j, kPolicy));
+    } else {
+      const int voff = (int)(8u * (uint32_t)(lane >> 5) * row_bytes + 2u * (uint32_t)(lane & 31));
+      uint32_t v[4][8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          v[j][i] = __builtin_amdgcn_raw_buffer_load_b16(r, voff, (int)((uint32_t)i * row_bytes) + 64 * j,
+                                                         kPolicy);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = make_uint4(v[j][0] | (v[j][1] << 16), v[j][2] | (v[j][3] << 16),
+                          v[j][4] | (v[j][5] << 16), v[j][6] | (v[j][7] << 16));
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = load_chunk(src, stride, kind, j, lane, false);
+  }
+}
+
+// An item's metadata record (device memory) as one global load: off, then tag[0..3].
+__device__ __forceinline__ uint64_t load_meta_record(const kvz_group_meta* m) {
+  typedef __attribute__((address_space(1))) const uint64_t global_u64;
+  return *(global_u64*)(m);
+}
+
+}  // namespace kvz

@@ -15,6 +15,7 @@
 // allocate (pool.hip, same rule as the first format, runs of 12 or 16 granules) -> pack.
 // kvz_gaac_decompress_pages rebuilds whole pages into the raw chunk layout.
 #include "gaac_internal.h"
+#include "encode_internal.h"
 
 namespace kvz {
 
@@ -148,20 +149,21 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
 }
 
 // Modes of every group, escape total, raw fallback; tags and "not stored" go to the metadata.
+template <int kPolicy>
 __global__ __launch_bounds__(256) void gaac_classify_kernel(const kvz_gaac_item* items, int n,
                                                             uint32_t flags) {
   const int lane = threadIdx.x & 63;
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= n) return;
   const kvz_gaac_item it = items[item];
-  const bool aligned = ((((uintptr_t)it.src) & 15u) == 0) && ((it.src_stride & 7u) == 0);
+  uint4 w[4];
+  load_item_chunks<kPolicy>(it.src, it.src_stride, it.kind, lane, w);
   uint32_t esc = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     uint32_t b3lo, b3hi, b4lo, b4hi;
     group_bases(it.bases, it.kind, j, lane, b3lo, b3hi, b4lo, b4hi);
-    const uint4 w = load_chunk(it.src, it.src_stride, it.kind, j, lane, aligned);
-    esc += gaac_escape_bytes(gaac_code_group(w, b3lo, b3hi, b4lo, b4hi).mode);
+    esc += gaac_escape_bytes(gaac_code_group(w[j], b3lo, b3hi, b4lo, b4hi).mode);
   }
   const uint32_t total = wave_sum(esc);
   const bool raw = (flags & KVZ_ENC_FORCE_RAW) || total > kGaacEscapeSlot;
@@ -172,23 +174,26 @@ __global__ __launch_bounds__(256) void gaac_classify_kernel(const kvz_gaac_item*
 }
 
 // Write each placed tile: raw chunk layout, or the planes and the escape bytes.
+template <int kPolicy>
 __global__ __launch_bounds__(256) void gaac_pack_kernel(const kvz_gaac_item* items, int n,
                                                         uint8_t* arena, uint64_t capacity) {
   const int lane = threadIdx.x & 63;
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= n) return;
   const kvz_gaac_item it = items[item];
-  const uint32_t off = it.dst->off;
-  const uint32_t tags = *reinterpret_cast<const uint32_t*>(it.dst->tag);
+  // every load of the item (metadata, then source) before the first store into the arena
+  const uint64_t mt = load_meta_record(it.dst);
+  uint4 w[4];
+  load_item_chunks<kPolicy>(it.src, it.src_stride, it.kind, lane, w);
+  const uint32_t off = (uint32_t)mt;
+  const uint32_t tags = (uint32_t)(mt >> 32);
   const bool raw = tags == kGaacTagsRaw;
   if (off == KVZ_OFF_NONE || (uint64_t)off + (raw ? 16u : 12u) > capacity) return;
-  const bool aligned = ((((uintptr_t)it.src) & 15u) == 0) && ((it.src_stride & 7u) == 0);
   uint8_t* rec = arena + (size_t)off * KVZ_GRANULE_BYTES;
   if (raw) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<uint4*>(rec + j * kRawBlockBytes + kRawChunkBytes * lane) =
-          load_chunk(it.src, it.src_stride, it.kind, j, lane, aligned);
+      *reinterpret_cast<uint4*>(rec + j * kRawBlockBytes + kRawChunkBytes * lane) = w[j];
     return;
   }
   GroupCode g[4];
@@ -197,8 +202,7 @@ __global__ __launch_bounds__(256) void gaac_pack_kernel(const kvz_gaac_item* ite
   for (int j = 0; j < 4; ++j) {
     uint32_t b3lo, b3hi, b4lo, b4hi;
     group_bases(it.bases, it.kind, j, lane, b3lo, b3hi, b4lo, b4hi);
-    g[j] = gaac_code_group(load_chunk(it.src, it.src_stride, it.kind, j, lane, aligned), b3lo,
-                           b3hi, b4lo, b4hi);
+    g[j] = gaac_code_group(w[j], b3lo, b3hi, b4lo, b4hi);
     esc_len += gaac_escape_bytes(g[j].mode);
     modes |= g[j].mode << (2 * j);
   }
@@ -321,13 +325,21 @@ extern "C" int kvz_gaac_encode_pages(kvz_pool* p, const kvz_gaac_item* d_items, 
   if (!d_items) return set_error(KVZ_EINVAL, "items pointer is null");
   if (flags & ~KVZ_ENC_FORCE_RAW) return set_error(KVZ_EINVAL, "unknown encode flag");
   const int grid = (n + 3) / 4;
-  hipLaunchKernelGGL(gaac_classify_kernel, dim3(grid), dim3(256), 0, s, d_items, (int)n, flags);
+  const bool stream = n > kStreamItems;
+  if (stream)
+    hipLaunchKernelGGL(gaac_classify_kernel<kStreamLoad>, dim3(grid), dim3(256), 0, s, d_items, (int)n, flags);
+  else
+    hipLaunchKernelGGL(gaac_classify_kernel<kCachedLoad>, dim3(grid), dim3(256), 0, s, d_items, (int)n, flags);
   int rc = check_hip(hipGetLastError(), "gaac classify launch");
   if (rc != KVZ_OK) return rc;
   rc = launch_alloc_for_gaac_items(p, d_items, n, s);
   if (rc != KVZ_OK) return rc;
-  hipLaunchKernelGGL(gaac_pack_kernel, dim3(grid), dim3(256), 0, s, d_items, (int)n,
-                     (uint8_t*)p->arena, p->capacity);
+  if (stream)
+    hipLaunchKernelGGL(gaac_pack_kernel<kStreamLoad>, dim3(grid), dim3(256), 0, s, d_items, (int)n,
+                       (uint8_t*)p->arena, p->capacity);
+  else
+    hipLaunchKernelGGL(gaac_pack_kernel<kCachedLoad>, dim3(grid), dim3(256), 0, s, d_items, (int)n,
+                       (uint8_t*)p->arena, p->capacity);
   return check_hip(hipGetLastError(), "gaac pack launch");
 }
 
