@@ -1,5 +1,5 @@
-// Source loads of the page-completion encoders (codec.hip, gaac.hip): one item (one K or V
-// page of one KV head, 16 rows of 128 BF16 values) per wave.
+// Source loads of the page-completion encoders (codec.hip, gaac.hip, fp8.hip): one item (one K
+// or V page of one KV head, 16 rows of 128 values) per wave.
 #pragma once
 
 #include "kvz_internal.h"
@@ -25,12 +25,15 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint32_t uniform_row_bytes(uint32_t src_stride) {
   return 2u * (uint32_t)__builtin_amdgcn_readfirstlane((int)src_stride);
 }
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint16_t* src, uint32_t row_bytes) {
+// (value_bytes: 2 for BF16 pages, 1 for FP8 pages; a row holds 128 values)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const void* src, uint32_t row_bytes,
+                                                            uint32_t value_bytes = 2) {
   const uint64_t u = (uint64_t)(uintptr_t)src;
   const uint64_t su = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(u >> 32)) << 32) |
                       (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
   return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((uintptr_t)su), 0,
-                                           (int)(15u * row_bytes + 2u * KVZ_HEAD_DIM), 0x00020000);
+                                           (int)(15u * row_bytes + value_bytes * KVZ_HEAD_DIM),
+                                           0x00020000);
 }
 
 __device__ __forceinline__ bool item_aligned(const uint16_t* src, uint32_t stride) {

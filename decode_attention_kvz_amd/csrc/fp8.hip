@@ -14,6 +14,7 @@
 // kvz_fp8_decompress_pages rebuilds tiles into the FP8 chunk layout; kvz_fp8_pack_pages lays
 // natural pages out in it.
 #include "fp8_internal.h"
+#include "encode_internal.h"
 
 namespace kvz {
 
@@ -91,6 +92,40 @@ __device__ __forceinline__ uint2 fp8_load_chunk(const uint8_t* src, uint32_t str
                     v[4] | (v[5] << 8) | (v[6] << 16) | (v[7] << 24));
 }
 
+// The four chunks of an FP8 item as fp8_load_chunk gives them, every load issued before any is
+// used, through a buffer resource over the page's rows (source pointer and stride are
+// wave-uniform; see encode_internal.h).
+template <int kPolicy>
+__device__ __forceinline__ void fp8_load_item_chunks(const uint8_t* src, uint32_t stride,
+                                                     uint32_t kind, int lane, bool aligned,
+                                                     uint2 (&w)[4]) {
+  if (aligned) {
+    const uint32_t row = (uint32_t)__builtin_amdgcn_readfirstlane((int)stride);
+    const __amdgpu_buffer_rsrc_t r = page_rsrc(src, row, 1);
+    if (__builtin_amdgcn_readfirstlane((int)kind) == KVZ_KIND_K) {
+      const int voff = (int)((uint32_t)(lane & 15) * row + 8u * (uint32_t)(lane >> 4));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, 32 * j, kPolicy));
+    } else {
+      const int voff = (int)(8u * (uint32_t)(lane >> 5) * row + (uint32_t)(lane & 31));
+      uint32_t v[4][8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          v[j][i] = __builtin_amdgcn_raw_buffer_load_b8(r, voff, (int)((uint32_t)i * row) + 32 * j, kPolicy);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = make_uint2(v[j][0] | (v[j][1] << 8) | (v[j][2] << 16) | (v[j][3] << 24),
+                          v[j][4] | (v[j][5] << 8) | (v[j][6] << 16) | (v[j][7] << 24));
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = fp8_load_chunk(src, stride, kind, j, lane, false);
+  }
+}
+
 struct Fp8GroupCode {
   uint32_t mode;     // 0 = 3-bit, 1 = 4-bit, 2 = raw
   uint32_t low24;    // low 3 code bits of values 0..7
@@ -165,21 +200,21 @@ __device__ __forceinline__ bool fp8_src_aligned(const kvz_fp8_item& it) {
 }
 
 // Modes of every group, escape total, fallback; tags and "not stored" go to the metadata.
-template <int FK>
+template <int FK, int kPolicy>
 __global__ __launch_bounds__(256) void fp8_classify_kernel(const kvz_fp8_item* items, int n,
                                                            uint32_t flags) {
   const int lane = threadIdx.x & 63;
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= n) return;
   const kvz_fp8_item it = items[item];
-  const bool aligned = fp8_src_aligned(it);
+  uint2 w[4];
+  fp8_load_item_chunks<kPolicy>(it.src, it.src_stride, it.kind, lane, fp8_src_aligned(it), w);
   uint32_t esc = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     uint32_t b3lo, b3hi, b4lo, b4hi;
     fp8_group_bases(it.bases, it.kind, j, lane, b3lo, b3hi, b4lo, b4hi);
-    const uint2 w = fp8_load_chunk(it.src, it.src_stride, it.kind, j, lane, aligned);
-    esc += fp8_escape_bytes<FK>(fp8_code_group<FK>(w, b3lo, b3hi, b4lo, b4hi).mode);
+    esc += fp8_escape_bytes<FK>(fp8_code_group<FK>(w[j], b3lo, b3hi, b4lo, b4hi).mode);
   }
   const uint32_t total = fp8_wave_sum(esc);
   const bool raw = (flags & KVZ_ENC_FORCE_RAW) || total > kFp8EscSlot;
@@ -206,7 +241,7 @@ __device__ __forceinline__ void fp8_sm_pack(const Fp8GroupCode (&g)[4], uint32_t
 }
 
 // Write each placed tile: the FP8 chunk layout, or the planes and the escape bytes.
-template <int FK>
+template <int FK, int kPolicy>
 __global__ __launch_bounds__(256) void fp8_pack_kernel(const kvz_fp8_item* items, int n,
                                                        uint8_t* arena, uint64_t capacity) {
   using F = Fp8Fmt<FK>;
@@ -214,17 +249,18 @@ __global__ __launch_bounds__(256) void fp8_pack_kernel(const kvz_fp8_item* items
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= n) return;
   const kvz_fp8_item it = items[item];
-  const uint32_t off = it.dst->off;
-  const uint32_t tags = *reinterpret_cast<const uint32_t*>(it.dst->tag);
+  // every load of the item (metadata, then source) before the first store into the arena
+  const uint64_t mt = load_meta_record(it.dst);
+  uint2 cw8[4];
+  fp8_load_item_chunks<kPolicy>(it.src, it.src_stride, it.kind, lane, fp8_src_aligned(it), cw8);
+  const uint32_t off = (uint32_t)mt;
+  const uint32_t tags = (uint32_t)(mt >> 32);
   const bool raw = tags == kFp8TagsRaw;
   if (off == KVZ_OFF_NONE || (uint64_t)off + run_granules(n_raw_of(tags)) > capacity) return;
-  const bool aligned = fp8_src_aligned(it);
   uint8_t* rec = arena + (size_t)off * kFp8Granule;
   if (raw) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<uint2*>(rec + fp8_chunk_offset(j, lane)) =
-          fp8_load_chunk(it.src, it.src_stride, it.kind, j, lane, aligned);
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<uint2*>(rec + fp8_chunk_offset(j, lane)) = cw8[j];
     return;
   }
   Fp8GroupCode g[4];
@@ -233,8 +269,7 @@ __global__ __launch_bounds__(256) void fp8_pack_kernel(const kvz_fp8_item* items
   for (int j = 0; j < 4; ++j) {
     uint32_t b3lo, b3hi, b4lo, b4hi;
     fp8_group_bases(it.bases, it.kind, j, lane, b3lo, b3hi, b4lo, b4hi);
-    g[j] = fp8_code_group<FK>(fp8_load_chunk(it.src, it.src_stride, it.kind, j, lane, aligned),
-                              b3lo, b3hi, b4lo, b4hi);
+    g[j] = fp8_code_group<FK>(cw8[j], b3lo, b3hi, b4lo, b4hi);
     esc_len += fp8_escape_bytes<FK>(g[j].mode);
     modes |= g[j].mode << (2 * j);
   }
@@ -383,20 +418,28 @@ extern "C" int kvz_fp8_encode_pages(kvz_pool* p, const kvz_fp8_item* d_items, in
   if (!d_items) return set_error(KVZ_EINVAL, "items pointer is null");
   if (flags & ~KVZ_ENC_FORCE_RAW) return set_error(KVZ_EINVAL, "unknown encode flag");
   const int grid = (n + 3) / 4;
-  if (format == KVZ_FP8_E4M3)
-    hipLaunchKernelGGL(fp8_classify_kernel<KVZ_FP8_E4M3>, dim3(grid), dim3(256), 0, s, d_items, (int)n, flags);
-  else
-    hipLaunchKernelGGL(fp8_classify_kernel<KVZ_FP8_E5M2>, dim3(grid), dim3(256), 0, s, d_items, (int)n, flags);
+  const bool stream = n > kStreamItems;
+#define KVZ_FP8_LAUNCH(kernel, ...)                                                             \
+  do {                                                                                          \
+    if (format == KVZ_FP8_E4M3) {                                                               \
+      if (stream)                                                                               \
+        hipLaunchKernelGGL((kernel<KVZ_FP8_E4M3, kStreamLoad>), dim3(grid), dim3(256), 0, s, __VA_ARGS__); \
+      else                                                                                      \
+        hipLaunchKernelGGL((kernel<KVZ_FP8_E4M3, kCachedLoad>), dim3(grid), dim3(256), 0, s, __VA_ARGS__); \
+    } else {                                                                                    \
+      if (stream)                                                                               \
+        hipLaunchKernelGGL((kernel<KVZ_FP8_E5M2, kStreamLoad>), dim3(grid), dim3(256), 0, s, __VA_ARGS__); \
+      else                                                                                      \
+        hipLaunchKernelGGL((kernel<KVZ_FP8_E5M2, kCachedLoad>), dim3(grid), dim3(256), 0, s, __VA_ARGS__); \
+    }                                                                                           \
+  } while (0)
+  KVZ_FP8_LAUNCH(fp8_classify_kernel, d_items, (int)n, flags);
   int rc = check_hip(hipGetLastError(), "fp8 classify launch");
   if (rc != KVZ_OK) return rc;
   rc = launch_alloc_for_fp8_items(p, d_items, n, s);
   if (rc != KVZ_OK) return rc;
-  if (format == KVZ_FP8_E4M3)
-    hipLaunchKernelGGL(fp8_pack_kernel<KVZ_FP8_E4M3>, dim3(grid), dim3(256), 0, s, d_items, (int)n,
-                       (uint8_t*)p->arena, p->capacity);
-  else
-    hipLaunchKernelGGL(fp8_pack_kernel<KVZ_FP8_E5M2>, dim3(grid), dim3(256), 0, s, d_items, (int)n,
-                       (uint8_t*)p->arena, p->capacity);
+  KVZ_FP8_LAUNCH(fp8_pack_kernel, d_items, (int)n, (uint8_t*)p->arena, p->capacity);
+#undef KVZ_FP8_LAUNCH
   return check_hip(hipGetLastError(), "fp8 pack launch");
 }
 
