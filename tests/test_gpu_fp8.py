@@ -153,6 +153,44 @@ def test_calibration_matches_oracle(fmt):
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("stride,shift", [(136, 0), (131, 1)])
+def test_encode_from_strided_sources_matches_oracle(fmt, stride, shift):
+    """Items whose token rows are `stride` bytes apart, the first one `shift` bytes past an
+    8-byte boundary: the buffer-load path with a row stride other than 128 (136) and the
+    byte-wise path (odd stride, misaligned base) both give the oracle's tiles and metadata."""
+    announce(f"fp8 {NAME[fmt]} encode strided sources stride={stride} shift={shift}")
+    cal = synth.fp8_kv_pages(1, 6, 2, seed=84, fmt=fmt, forced_frac=0.0, sample=1, device="cuda")
+    bases = paged.fp8_calibrate(cal, fmt)
+    pages = synth.fp8_kv_pages(1, 8, 2, seed=84, fmt=fmt, forced_frac=0.2)
+    nat = pages.cpu().numpy()[0]                              # [8, 2, 2, 16, 128] uint8
+    flat = nat.transpose(0, 2, 1, 3, 4).reshape(-1, 16, 128)  # item order (page, head, K/V)
+    n = flat.shape[0]
+    kinds = [i % 2 for i in range(n)]
+    heads = [(i // 2) % 2 for i in range(n)]
+    buf = np.zeros((n, 16, stride), dtype=np.uint8)
+    buf[:, :, :128] = flat
+    dev = torch.zeros(shift + buf.size + 8, dtype=torch.uint8, device="cuda")
+    dev[shift:shift + buf.size] = torch.from_numpy(buf.reshape(-1)).cuda()
+    base = dev.data_ptr() + shift
+    meta = paged.new_meta_table(8, 2)
+    items = torch.from_numpy(kvz.gaac_items(
+        [base + i * 16 * stride for i in range(n)], [meta.data_ptr() + 8 * i for i in range(n)],
+        stride, kinds, [bases.data_ptr() + (heads[i] * 2 + kinds[i]) * 256 for i in range(n)])).cuda()
+    arena = paged.SlotArena(256 * 1024, fp8=True)
+    kvz.kvz_fp8_encode_pages(arena.pool, items, n, fmt)
+    torch.cuda.synchronize()
+    bh = bases.cpu().numpy()
+    oc = Fp8OracleCache(arena.arena.numel(), fmt)
+    metas = oc.encode(flat, kinds, [(bh[heads[i], kinds[i], 0], bh[heads[i], kinds[i], 1])
+                                    for i in range(n)])
+    m = meta.cpu().numpy().reshape(-1, 8)
+    for i in range(n):
+        off = int.from_bytes(m[i, :4].tobytes(), "little")
+        assert (off, [int(x) for x in m[i, 4:]]) == (metas[i][0], list(metas[i][1])), i
+    np.testing.assert_array_equal(arena.arena.cpu().numpy(), oc.arena)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("force_raw,stress", [(False, False), (True, False), (False, True)])
 def test_encode_matches_oracle_arena_and_meta(fmt, force_raw, stress):
     """2 sequences x 9 pages x 4 KV heads, bases from another sample of the layer: the whole

@@ -106,6 +106,44 @@ def test_encode_matches_oracle_arena_and_meta(force_raw, stress):
         assert n_raw_tiles < len(metas)
 
 
+@pytest.mark.parametrize("stride,shift", [(136, 0), (131, 1)])
+def test_encode_from_strided_sources_matches_oracle(stride, shift):
+    """Items whose token rows are `stride` elements apart, the first one `shift` elements past a
+    16-byte boundary: the buffer-load path with a row stride other than 128 (136) and the
+    element-wise path (odd stride, misaligned base) both give the oracle's tiles and metadata."""
+    announce(f"gaac encode strided sources stride={stride} shift={shift}")
+    cal = synth.kv_pages(1, 6, 2, seed=74, u_max=3.0, forced_frac=0.0, sample=1, device="cuda")
+    bases = paged.gaac_calibrate(cal)
+    pages = synth.kv_pages(1, 8, 2, seed=74, u_max=3.0, forced_frac=0.2)
+    nat = synth.bits(pages)[0]                                # [8, 2, 2, 16, 128]
+    flat = nat.transpose(0, 2, 1, 3, 4).reshape(-1, 16, 128)  # item order (page, head, K/V)
+    n = flat.shape[0]
+    kinds = [i % 2 for i in range(n)]
+    heads = [(i // 2) % 2 for i in range(n)]
+    buf = np.zeros((n, 16, stride), dtype=np.uint16)
+    buf[:, :, :128] = flat
+    dev = torch.zeros(shift + buf.size + 8, dtype=torch.int16, device="cuda")
+    dev[shift:shift + buf.size] = torch.from_numpy(buf.reshape(-1).view(np.int16)).cuda()
+    base = dev.data_ptr() + 2 * shift
+    meta = paged.new_meta_table(8, 2)
+    items = torch.from_numpy(kvz.gaac_items(
+        [base + 2 * i * 16 * stride for i in range(n)], [meta.data_ptr() + 8 * i for i in range(n)],
+        stride, kinds, [bases.data_ptr() + (heads[i] * 2 + kinds[i]) * 256 for i in range(n)])).cuda()
+    arena_bytes = 256 * 1024
+    arena = paged.SlotArena(arena_bytes)
+    kvz.kvz_gaac_encode_pages(arena.pool, items, n)
+    torch.cuda.synchronize()
+    bh = bases.cpu().numpy()
+    oc = GaacOracleCache(arena_bytes)
+    metas = oc.encode_gaac(flat, kinds, [(bh[heads[i], kinds[i], 0], bh[heads[i], kinds[i], 1])
+                                         for i in range(n)])
+    m = meta.cpu().numpy().reshape(-1, 8)
+    for i in range(n):
+        off = int.from_bytes(m[i, :4].tobytes(), "little")
+        assert (off, [int(x) for x in m[i, 4:]]) == (metas[i][0], list(metas[i][1])), i
+    np.testing.assert_array_equal(arena.arena.cpu().numpy(), oc.arena)
+
+
 def test_decompress_matches_oracle_decode():
     """Decompress every tile of a layer (compressed and raw tiles, an unstored one) into the raw
     chunk layout: equal to the oracle's all-raw record of the input page."""
