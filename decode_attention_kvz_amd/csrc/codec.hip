@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256) void classify_kernel(const kvz_encode_item* it
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= n) return;
   const kvz_encode_item it = items[item];
-  const bool aligned = ((((uintptr_t)it.src) & 15u) == 0) && ((it.src_stride & 7u) == 0);
+  const bool aligned = item_aligned(it.src, it.src_stride);
   uint32_t tags = 0;
   auto tag_of = [&](uint32_t lo, uint32_t hi) {
     const uint32_t b = lo & 0xFEu;
