@@ -36,8 +36,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const void* src, uin
                                            0x00020000);
 }
 
+// The buffer path addresses the 16 rows with 32-bit offsets (the resource size is a signed 32-bit
+// count): rows farther apart than this take the element-wise path.
+constexpr uint32_t kMaxBufferRowBytes = (0x7FFFFFFFu - 256u) / 15u;
+
 __device__ __forceinline__ bool item_aligned(const uint16_t* src, uint32_t stride) {
-  return ((((uintptr_t)src) & 15u) == 0) && ((stride & 7u) == 0);
+  return ((((uintptr_t)src) & 15u) == 0) && ((stride & 7u) == 0) &&
+         2ull * stride <= kMaxBufferRowBytes;
 }
 
 // The four chunks (blocks 0..3) of the item in lane order, as load_chunk gives them, with every

@@ -196,7 +196,8 @@ __device__ __forceinline__ uint32_t fp8_wave_sum(uint32_t v) {
 }
 
 __device__ __forceinline__ bool fp8_src_aligned(const kvz_fp8_item& it) {
-  return ((((uintptr_t)it.src) & 7u) == 0) && ((it.src_stride & 7u) == 0);
+  return ((((uintptr_t)it.src) & 7u) == 0) && ((it.src_stride & 7u) == 0) &&
+         it.src_stride <= kMaxBufferRowBytes;
 }
 
 // Modes of every group, escape total, fallback; tags and "not stored" go to the metadata.

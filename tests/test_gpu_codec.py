@@ -85,6 +85,33 @@ def test_encode_from_strided_sources_matches_oracle(stride, shift):
     np.testing.assert_array_equal(arena.arena.cpu().numpy(), oc.arena)
 
 
+def test_encode_rows_farther_apart_than_32bit_offsets():
+    """A row stride whose 16 rows span more than 2 GiB (beyond the 32-bit offsets of the
+    buffer-load path) takes the element-wise path and still gives the oracle's records."""
+    announce("encode with a 2.2 GB row span")
+    stride = 72 * 1024 * 1024                                 # elements, a multiple of 8
+    pages = synth.kv_pages(1, 1, 1, seed=23, forced_frac=0.0)
+    nat = synth.bits(pages)[0, 0]                             # [2 (K,V), 1, 16, 128]
+    flat = nat[:, 0]                                          # items K, V
+    span = 15 * stride + 128
+    dev = torch.zeros(2 * span, dtype=torch.int16, device="cuda")
+    for i in range(2):
+        for t in range(16):
+            at = i * span + t * stride
+            dev[at:at + 128] = torch.from_numpy(flat[i, t].view(np.int16)).cuda()
+    meta = paged.new_meta_table(1, 1)
+    items = torch.from_numpy(kvz.encode_items([dev.data_ptr() + 2 * i * span for i in range(2)],
+                                              [meta.data_ptr() + 8 * i for i in range(2)],
+                                              stride, [0, 1])).cuda()
+    arena = paged.SlotArena(64 * 1024)
+    kvz.kvz_encode_pages(arena.pool, items, 2, 0)
+    torch.cuda.synchronize()
+    del dev
+    oc = OracleCache(64 * 1024)
+    assert _meta_items(meta.cpu().numpy(), range(1), 1) == oc.encode(flat, [0, 1])
+    np.testing.assert_array_equal(arena.arena.cpu().numpy(), oc.arena)
+
+
 def test_decode_block_bit_exact_and_matches_oracle():
     announce("decode_block tiny config")
     pages = synth.kv_pages(1, 16, 2, seed=0, forced_frac=0.10)
