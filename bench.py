@@ -131,6 +131,8 @@ def main():
     ap.add_argument("--layers", type=int, default=LAYERS,
                     help="layers per step (the workload has 36; fewer is for quick checks only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-all-cores", action="store_true",
+                    help=argparse.SUPPRESS)   # the child process of the all-cores oracle timing
     ap.add_argument("--no-baseline", action="store_true")
     ap.add_argument("--no-variant", action="store_true")
     ap.add_argument("--no-gaac", action="store_true")
@@ -143,11 +145,23 @@ def main():
                     help="for hardware-counter runs: one layer of fused and baseline attention "
                          "(3 launches each) and a 1 GiB device copy as a traffic reference")
     args = ap.parse_args()
+    if args.cpu_all_cores:        # child process: host only, never touches the GPU
+        print(json.dumps(cpu_all_cores()), flush=True)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path (its (sequence, "
               "KV head) units are independent, so a multi-GPU version would place KV heads, or "
               "page ranges of long sequences, on different GPUs).", file=sys.stderr)
         sys.exit(2)
+
+    # the all-cores oracle timing runs in a child process started now, before this process
+    # touches the GPU; it waits for a line on its stdin before working
+    all_cores_child = None
+    if not args.no_cpu_baseline and not args.pmc_probe:
+        import subprocess
+        all_cores_child = subprocess.Popen(
+            [sys.executable, "-u", os.path.abspath(__file__), "--cpu-all-cores"],
+            stdin=subprocess.PIPE, stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
 
     import torch
     from decode_attention_kvz_amd import kvz, paged
@@ -283,7 +297,7 @@ def main():
     fp8_leg = None if args.no_fp8 else {name: fp8_format(args, dev, seq_lens, n_comp, ws, fmt)
                                         for name, fmt in (("e4m3", 0), ("e5m2", 1))}
     del g_attn, g_comp, g_step
-    cpu = None if args.no_cpu_baseline else cpu_baseline(layers)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(layers, all_cores_child)
 
     value = bf16_kv_layer * n_layers / (ms_step * 1e-3) / 1e9
     line = {
@@ -848,7 +862,7 @@ def pmc_probe(args, dev):
     arena.close()
 
 
-def cpu_baseline(layers):
+def cpu_baseline(layers, all_cores_child=None):
     """The oracle on a bounded sample: decode + fp64 attention of layer 0 (all 16 sequences, all
     KV heads, 8192 tokens each), inputs encoded by the oracle itself outside the timed region."""
     import contextlib
@@ -889,13 +903,110 @@ def cpu_baseline(layers):
         dt = time.perf_counter() - t0
     bytes_eff = B * CTX * HKV * 128 * 2 * 2
     log(f"cpu baseline: {dt:.1f}s for one layer ({bytes_eff / dt / 1e9:.4f} GB/s)")
+    all_cores = cpu_all_cores_result(all_cores_child)
     return {"value": round(bytes_eff / dt / 1e9, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "all_cores": all_cores,
             "sample": "layer 0 of the workload (16 sequences x 8192 tokens, 8 KV / 32 query heads; "
                       "1/36 of a step's attention): oracle block decode + fp64 attention, "
                       "1 thread, inputs encoded by the oracle beforehand",
             "encode_GBps": round(enc_bytes / dt_enc / 1e9, 5),
             "encode_sample": "the oracle encode of the same layer's 130,816 groups, 1 thread "
                              "(GB/s of BF16 input)"}
+
+
+def cpu_all_cores_result(child):
+    """Release the all-cores child (started before the GPU was touched) and read its JSON line;
+    None if there is none or it failed."""
+    if child is None:
+        return None
+    try:
+        out, _ = child.communicate("go\n", timeout=300)
+        res = json.loads(out.strip().splitlines()[-1])
+    except Exception as e:   # pragma: no cover - reported, not fatal
+        child.kill()
+        log(f"cpu baseline, all cores: failed ({e})")
+        return None
+    log(f"cpu baseline, all cores: {res['seconds']:.1f}s for one layer ({res['value']:.4f} GB/s, "
+        f"{res['cores']} worker processes)")
+    return res
+
+
+_PAR = {}
+
+
+def _par_encode(b):
+    from oracle.cache import OracleCache
+    flat = _PAR["nat"][b, :N_COMP].transpose(0, 2, 1, 3, 4).reshape(-1, 16, 128)   # (p, h, K/V)
+    oc = OracleCache(_PAR["seq_arena"])
+    metas = oc.encode(flat, [i % 2 for i in range(flat.shape[0])])
+    return oc.arena, metas
+
+
+def _par_attention(b):
+    from oracle import attention
+    with _one_thread():
+        out = attention.decode_attention(_PAR["q"], _PAR["arena"], _PAR["meta_table"],
+                                         _PAR["block_table"], [CTX] * B, [N_COMP] * B,
+                                         _PAR["nat"][:, N_COMP], SCALE, batch_indices=[b])
+    return out[b]
+
+
+def _one_thread():
+    import contextlib
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(limits=1)
+    except ImportError:   # pragma: no cover
+        return contextlib.nullcontext()
+
+
+def cpu_all_cores():
+    """The oracle's decode + fp64 attention of one layer of the workload on the host's cores:
+    forked worker processes, one sequence each at a time (up to 16, the host share of one GPU),
+    one BLAS thread each.  The layer is regenerated here on the host with the same seeds (the
+    host generator draws other values than the device one: the same shapes and distribution,
+    not the same numbers); each sequence is encoded by the oracle into its own arena, in the
+    workers, outside the timed region."""
+    import multiprocessing as mp
+    if sys.stdin.readline().strip() != "go":   # the parent ended or did not ask
+        return None
+    from decode_attention_kvz_amd import synth
+    pages = synth.kv_pages(B, N_COMP + 1, HKV, seed=SEED, layer=0, u_max=U_MAX, forced_frac=FORCED)
+    _PAR["nat"] = synth.bits(pages)                # [B, 512, 2, Hkv, 16, 128]
+    del pages
+    _PAR["q"] = synth.bits(synth.queries(B, HQ, seed=SEED * 1000))
+    _PAR["seq_arena"] = (N_COMP * HKV * 2 + 16) * 4096
+    workers = max(1, min(os.cpu_count() or 1, 16, B))
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers) as pool:
+        enc = pool.map(_par_encode, range(B))
+    # one arena: sequence b's records at b * seq_arena bytes; page (b, p) is physical page b*512+p
+    _PAR["arena"] = np.concatenate([a for a, _ in enc])
+    gran = _PAR["seq_arena"] // 256
+    meta_table = []
+    for b, (_, metas) in enumerate(enc):
+        for pp in range(N_COMP):
+            row = []
+            for h in range(HKV):
+                pair = []
+                for k in range(2):
+                    off, tags = metas[(pp * HKV + h) * 2 + k]
+                    pair.append((off if off == 0xFFFFFFFF else off + b * gran, tags))
+                row.append(pair)
+            meta_table.append(row)
+    _PAR["meta_table"] = meta_table
+    _PAR["block_table"] = np.arange(B * N_COMP, dtype=np.int64).reshape(B, N_COMP)
+    del enc
+    with ctx.Pool(workers) as pool:
+        t0 = time.perf_counter()
+        pool.map(_par_attention, range(B))
+        dt = time.perf_counter() - t0
+    bytes_eff = B * CTX * HKV * 128 * 2 * 2
+    return {"value": round(bytes_eff / dt / 1e9, 5), "unit": "GB/s", "cores": workers,
+            "seconds": round(dt, 2),
+            "sample": "layer 0 of the workload regenerated on the host (same seeds and shapes), "
+                      "oracle block decode + fp64 attention, one sequence per worker process, "
+                      "one BLAS thread each; oracle encode beforehand in the workers"}
 
 
 if __name__ == "__main__":
