@@ -53,6 +53,8 @@ struct AttnParams {
   float* out;                   // [B][Hq][128]
   float* ws_ml;                 // [units][G][2]
   float* ws_o;                  // [units][G][128]
+  uint32_t* ws_cnt;             // [Hkv][B] pieces of (sequence, KV head) done; zero between calls
+  int merge_in_kernel;          // the last piece of a (sequence, KV head) merges (no second launch)
   uint64_t arena_bytes;         // compressed only: groups must end 16 bytes before this
   int B, Hq, Hkv, G, max_pages, S, n_phys;
   float scale_log2;             // sm_scale (* k_scale for FP8) * log2(e)
@@ -246,6 +248,8 @@ struct Softmax {
 };
 
 constexpr int kMaxSplits = 4096;
+// Merging in the attention kernel: for automatic or given split counts up to this.
+constexpr int kInKernelMergeMax = 4;
 
 __device__ __forceinline__ int wave_incl_scan(int v) {
   const int lane = threadIdx.x & 63;
@@ -891,6 +895,9 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
   }
   __syncthreads();
   const bool empty_seq = p.seq_lens[b] <= 0;
+  // the only piece of its sequence normalizes in place
+  const bool direct = p.merge_in_kernel ? so.sb == 1 : p.S == 1;
+  const bool fused_merge = p.merge_in_kernel && !direct;
   for (int idx = threadIdx.x; idx < p.G * KVZ_HEAD_DIM; idx += 256) {
     const int h = idx / KVZ_HEAD_DIM, d = idx % KVZ_HEAD_DIM;
     float M = -INFINITY;
@@ -904,26 +911,95 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
       L += c * s_l[w][h];
       O += c * s_o[w][idx];
     }
-    if (p.S == 1) {
-      // the only split: normalize in place
+    float* po = p.ws_o + ((size_t)unit * p.G + h) * KVZ_HEAD_DIM + d;
+    float* pml = p.ws_ml + ((size_t)unit * p.G + h) * 2;
+    if (direct) {
       p.out[((size_t)b * p.Hq + (size_t)kvh * p.G + h) * KVZ_HEAD_DIM + d] = empty_seq ? 0.f : O / L;
-    } else {
-      // the partial result of this unit
-      p.ws_o[((size_t)unit * p.G + h) * KVZ_HEAD_DIM + d] = O;
+    } else if (fused_merge) {
+      // written through to memory (device-scope stores), read back by the merging piece
+      __hip_atomic_store(po, O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (d == 0) {
-        p.ws_ml[((size_t)unit * p.G + h) * 2 + 0] = M;
-        p.ws_ml[((size_t)unit * p.G + h) * 2 + 1] = L;
+        __hip_atomic_store(pml, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(pml + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    } else {
+      *po = O;
+      if (d == 0) {
+        pml[0] = M;
+        pml[1] = L;
       }
     }
+  }
+  if (!fused_merge) return;
+  // Merge in the kernel (split counts up to kInKernelMergeMax): each piece counts itself in at
+  // its (sequence, KV head) with one atomic add; the piece that arrives last merges every piece
+  // in piece order (the same sums whichever piece is last) and returns the counter to zero for
+  // the next call.  Only the partials and the counter pass between workgroups, and all of them
+  // with device-scope accesses: the partial stores above are written through past this
+  // chiplet's L2 (scope bit sc1), each wave waits for them to complete before the barrier that
+  // precedes the atomic, the atomic is device-coherent, and the merging piece reads the
+  // partials with device-scope loads issued after the atomic's result.  A release/acquire pair
+  // would instead write back and invalidate the whole L2 of the chiplet, once per workgroup:
+  // that measured slower than the separate merge launch, this is faster than it.
+  __shared__ uint32_t s_last;
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's partial stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t* cnt = p.ws_cnt + (size_t)kvh * p.B + b;
+    const uint32_t before = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t last = before + 1u == (uint32_t)so.sb ? 1u : 0u;
+    if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = last;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  const size_t u0 = (size_t)kvh * U + so.base;
+  for (int idx = threadIdx.x; idx < p.G * KVZ_HEAD_DIM; idx += 256) {
+    const int h = idx / KVZ_HEAD_DIM, d = idx % KVZ_HEAD_DIM;
+    const float* ml = p.ws_ml + (u0 * p.G + h) * 2;
+    const float* o = p.ws_o + u0 * p.G * KVZ_HEAD_DIM + (size_t)h * KVZ_HEAD_DIM + d;
+    auto ld = [](const float* q) { return __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+    const size_t mls = (size_t)p.G * 2, os = (size_t)p.G * KVZ_HEAD_DIM;
+    // pieces 0..3 in one round trip; a ragged batch's longer sequences loop over the rest
+    float mv[kInKernelMergeMax], lv[kInKernelMergeMax], ov[kInKernelMergeMax];
+#pragma unroll
+    for (int i = 0; i < kInKernelMergeMax; ++i) {
+      if (i < so.sb) {
+        mv[i] = ld(ml + i * mls);
+        lv[i] = ld(ml + i * mls + 1);
+        ov[i] = ld(o + i * os);
+      }
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kInKernelMergeMax; ++i)
+      if (i < so.sb) M = fmaxf(M, mv[i]);
+    for (int i = kInKernelMergeMax; i < so.sb; ++i) M = fmaxf(M, ld(ml + i * mls));
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int i = 0; i < kInKernelMergeMax; ++i) {
+      if (i < so.sb) {
+        const float c = mv[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv[i] - M);
+        L += c * lv[i];
+        O += c * ov[i];
+      }
+    }
+    for (int i = kInKernelMergeMax; i < so.sb; ++i) {
+      const float m = ld(ml + i * mls);
+      const float c = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
+      L += c * ld(ml + i * mls + 1);
+      O += c * ld(o + i * os);
+    }
+    p.out[((size_t)b * p.Hq + (size_t)kvh * p.G + h) * KVZ_HEAD_DIM + d] = empty_seq ? 0.f : O / L;
   }
 }
 
 // Merge the splits of every (sequence, query head): M = max m_s, L = sum l_s 2^(m_s - M),
 // out = sum O_s 2^(m_s - M) / L, over the sequence's S_b splits (split_of).  A sequence of
-// length 0 gives zeros.  A separate launch:
-// ordering the splits' partial writes before these reads needs no per-wave fence (a fence at
-// device scope writes back and invalidates the whole L2 of the issuing chiplet).
-// One workgroup of 256 threads per (sequence, query head), parallel over the splits.
+// length 0 gives zeros.  A separate launch, for split counts above kInKernelMergeMax (one long
+// sequence over many CUs: its pieces are merged in parallel here rather than serially by the
+// last piece).  One workgroup of 256 threads per (sequence, query head), parallel over the
+// splits.
 constexpr int kCombineThreads = 256;
 
 __device__ __forceinline__ float block_reduce(float v, float* s_red, bool is_max) {
@@ -1054,12 +1130,15 @@ int choose_splits(int B, int Hkv, int max_pages, int n_cu, int wgs_per_cu = 1) {
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
-// workspace = [m, l: units*G*2 f32][O: units*G*128 f32], 256-B aligned parts
-void workspace_layout(int B, int Hq, int Hkv, int S, uint64_t* ml_bytes, uint64_t* total) {
+// workspace = [counters: B*Hkv u32][m, l: units*G*2 f32][O: units*G*128 f32], 256-B aligned
+// parts; the counters are zero between calls (zero-filled once by the caller)
+void workspace_layout(int B, int Hq, int Hkv, int S, uint64_t* cnt_bytes, uint64_t* ml_bytes,
+                      uint64_t* total) {
   const uint64_t units = (uint64_t)B * Hkv * S;
   const uint64_t G = Hkv > 0 ? (uint64_t)(Hq / Hkv) : 0;
+  *cnt_bytes = align256((uint64_t)B * Hkv * sizeof(uint32_t));
   *ml_bytes = align256(units * G * 2 * sizeof(float));
-  *total = *ml_bytes + align256(units * G * KVZ_HEAD_DIM * sizeof(float));
+  *total = *cnt_bytes + *ml_bytes + align256(units * G * KVZ_HEAD_DIM * sizeof(float));
 }
 
 struct CommonArgs {
@@ -1111,8 +1190,8 @@ int launch_attention(const CommonArgs& a, const uint8_t* kv, const kvz_group_met
   const int S = a.splits ? a.splits
                          : choose_splits(a.batch, a.num_kv_heads, a.max_pages, device_cus(),
                                          CODED ? kCodedWgsPerCu : 1);
-  uint64_t ml_bytes, need;
-  workspace_layout(a.batch, a.num_q_heads, a.num_kv_heads, S, &ml_bytes, &need);
+  uint64_t cnt_bytes, ml_bytes, need;
+  workspace_layout(a.batch, a.num_q_heads, a.num_kv_heads, S, &cnt_bytes, &ml_bytes, &need);
   if (a.workspace_bytes < need) return set_error(KVZ_EINVAL, "workspace too small");
   const uint64_t units = (uint64_t)a.batch * a.num_kv_heads * S;
   if (units > 0x7FFFFFFFull) return set_error(KVZ_EINVAL, "too many units");
@@ -1127,8 +1206,11 @@ int launch_attention(const CommonArgs& a, const uint8_t* kv, const kvz_group_met
   p.tail = a.tail;
   p.bases = bases;
   p.out = a.out;
-  p.ws_ml = reinterpret_cast<float*>(a.workspace);
-  p.ws_o = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(a.workspace) + ml_bytes);
+  p.ws_cnt = reinterpret_cast<uint32_t*>(a.workspace);
+  p.ws_ml = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(a.workspace) + cnt_bytes);
+  p.ws_o = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(a.workspace) + cnt_bytes + ml_bytes);
+  // (a ragged batch can still give one sequence more pieces: the merge loops over them)
+  p.merge_in_kernel = S <= kInKernelMergeMax;
   p.arena_bytes = a.arena_bytes;
   p.n_phys = a.n_phys_pages;
   p.B = a.batch;
@@ -1148,7 +1230,7 @@ int launch_attention(const CommonArgs& a, const uint8_t* kv, const kvz_group_met
   else
     hipLaunchKernelGGL((attn_split_kernel<16, FMT, FK>), grid, dim3(256), 0, s, p);
   int rc = check_hip(hipGetLastError(), "attention launch");
-  if (rc != KVZ_OK || S == 1) return rc;
+  if (rc != KVZ_OK || S == 1 || p.merge_in_kernel) return rc;
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.batch * a.num_q_heads)),
                      dim3(kCombineThreads), 0, s,
                      p.ws_ml, p.ws_o, a.out, a.seq_lens, a.n_comp_pages, a.tail != nullptr,
@@ -1170,8 +1252,8 @@ extern "C" int kvz_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int3
   // sized for the format with the most splits, so one workspace serves every format
   const int S = splits ? splits
                        : choose_splits(batch, num_kv_heads, max_pages, device_cus(), kCodedWgsPerCu);
-  uint64_t ml, total;
-  workspace_layout(batch, num_q_heads, num_kv_heads, S, &ml, &total);
+  uint64_t cnt, ml, total;
+  workspace_layout(batch, num_q_heads, num_kv_heads, S, &cnt, &ml, &total);
   *bytes = total < 256 ? 256 : total;
   return KVZ_OK;
 }

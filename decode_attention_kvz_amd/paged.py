@@ -168,7 +168,7 @@ def decompress_pages(arena: "SlotArena", meta: torch.Tensor, out: torch.Tensor |
 def workspace(batch: int, num_q_heads: int, num_kv_heads: int, max_pages: int, splits: int = 0,
               device="cuda") -> torch.Tensor:
     nbytes = kvz.kvz_attn_workspace_bytes(batch, num_q_heads, num_kv_heads, max_pages, splits)
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)   # the merge counters start at 0
 
 
 # ---------------------------------------------------------------------------------------------

@@ -392,14 +392,20 @@ int kvz_fp8_raw_decode_attention(const kvz_fp8_attn_args* a, hipStream_t s);
 /* Workspace bytes the attention calls (kvz_decode_attention, kvz_bf16_decode_attention,
  * kvz_gaac_decode_attention, kvz_fp8_decode_attention, kvz_fp8_raw_decode_attention) need for
  * these sizes.  splits = 0: enough for the automatic split count of every one of them (the
- * coded tiles - group-adaptive and FP8 - use twice as many splits). */
+ * coded tiles - group-adaptive and FP8 - use twice as many splits).
+ * The workspace must be zero-filled once, before its first call: its first
+ * align256(4 * batch * num_kv_heads) bytes are per-(sequence, KV head) counters of the merge
+ * inside the attention kernel, which every completed call leaves at zero.  Zero-fill it again
+ * before reusing it for a larger batch * num_kv_heads (the counters then reach into bytes that
+ * held partial results). */
 int kvz_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                              int32_t max_pages, int32_t splits, uint64_t* bytes);
 
 /* Fused paged split-K GQA decode attention over compressed pages plus the BF16 tail: blocks
- * are restored bit-exactly in registers, never written back.  With one split per sequence the
- * attention kernel writes out directly; otherwise a second small kernel merges the splits'
- * partial softmax states from the workspace. */
+ * are restored bit-exactly in registers, never written back.  A sequence's only piece writes
+ * out directly; with up to 4 splits the last piece of each (sequence, KV head) to finish merges
+ * the pieces' partial softmax states inside the attention kernel; with more, a second small
+ * kernel merges them. */
 int kvz_decode_attention(const kvz_attn_args* a, hipStream_t s);
 
 /* Lay out n_pages natural BF16 pages (device [n_pages][2][Hkv][16][128]) as the baseline's

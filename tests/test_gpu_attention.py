@@ -101,6 +101,36 @@ def test_split_count_changes_output_only_by_rounding():
         check_rows(outs[-1][b], ref[b], what=f"seq {b}")
 
 
+@pytest.mark.parametrize("splits", [2, 3, 4])
+def test_in_kernel_split_merge_reads_this_calls_partials(splits):
+    """Split counts that merge inside the attention kernel: calls alternate between two query
+    sets on one workspace, 40 times; every output equals the first one for its queries bit for
+    bit (a merge that read a previous call's partials, or missed this call's, would differ),
+    and a ragged batch (one sequence cut into more pieces) matches the oracle."""
+    announce(f"in-kernel merge, splits={splits}")
+    pages = synth.kv_pages(6, 41, 8, seed=15, forced_frac=0.05, device="cuda")
+    seq_lens, n_comp = [16 * 40 + 7, 16 * 3, 16 * 40, 16 * 22 + 1, 5, 16 * 37 + 16], [40, 3, 40, 22, 0, 37]
+    arena, layer = _layer(pages, seq_lens, n_comp, seed=15)
+    qs = [synth.queries(6, 32, seed=150 + k, device="cuda") for k in range(2)]
+    ws = paged.workspace(6, 32, 8, layer.block_table.shape[1], splits, device="cuda")
+
+    def call(q):
+        out = torch.empty((6, 32, 128), dtype=torch.float32, device="cuda")
+        kvz.kvz_decode_attention(q, out, arena.arena, layer.meta, layer.block_table,
+                                 layer.seq_lens, layer.n_comp, layer.tail, sm_scale(), ws, splits)
+        return out
+    first = [call(q).clone() for q in qs]
+    outs = [call(qs[i % 2]) for i in range(40)]
+    torch.cuda.synchronize()
+    for i, o in enumerate(outs):
+        assert torch.equal(o, first[i % 2]), i
+    for k in range(2):
+        ref = oracle_attention_rows(layer, qs[k], sm_scale(), range(6))
+        got = first[k].cpu().numpy()
+        for b in range(6):
+            check_rows(got[b], ref[b], what=f"q{k} seq {b}")
+
+
 def test_non_finite_values_propagate_like_the_oracle():
     """NaN and Inf in K and V (stress values): the positions of non-finite outputs equal the
     oracle's."""
