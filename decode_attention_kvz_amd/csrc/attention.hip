@@ -138,6 +138,27 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
+// Two wait states, issued as an instruction of their own, between restored operands and the
+// matrix instructions that read them.  A VALU write of a VGPR must be at least two wait states
+// ahead of an MFMA that reads it.  Where the restored operands reach the products through a
+// join of the restore's branches (register copies at the end of each branch), the compiler was
+// seen to meet that distance with a copy, an s_waitcnt for the loads of the uncompressed branch
+// and one s_nop: counting the s_waitcnt as a wait state.  On the GPU that left the product
+// reading a stale operand register for some pages (compressed and uncompressed tiles of equal
+// values gave different scores).  With this nop ahead of the waitcnt the distance holds without
+// it; a build check keeps such padding out of every kernel.  The operands pass through the asm
+// statement, so the products cannot be scheduled above it.
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void operands_settled(uint4 (&ops)[4]) {
+  u32x4v a = __builtin_bit_cast(u32x4v, ops[0]), b = __builtin_bit_cast(u32x4v, ops[1]);
+  u32x4v c = __builtin_bit_cast(u32x4v, ops[2]), d = __builtin_bit_cast(u32x4v, ops[3]);
+  asm volatile("s_nop 1" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+  ops[0] = __builtin_bit_cast(uint4, a);
+  ops[1] = __builtin_bit_cast(uint4, b);
+  ops[2] = __builtin_bit_cast(uint4, c);
+  ops[3] = __builtin_bit_cast(uint4, d);
+}
+
 // Raw buffer resource over [base, base + bytes); loads beyond `bytes` return zeros.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t group_rsrc(const uint8_t* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, (int)bytes, 0x00020000);
@@ -166,12 +187,99 @@ __device__ __forceinline__ uint4 restore_if_coded(uint4 c, uint32_t tag) {
   return restore_chunk(c.x, c.y, c.z, tag * 0x01010101u);
 }
 
-// A score in log2 units, rounded as a product of its own: with contraction the compiler may
-// fuse this multiply into the later subtraction of the running max, and the largest score of
-// a page would then give exp2 of the product's rounding error instead of exactly 1.
-__device__ __forceinline__ float scaled_score(float s, float scale) {
+// A difference of raw scores in log2 units (a product of its own, never fused with the
+// subtraction before it: the largest score of a page then gives exactly exp2(0) = 1).
+__device__ __forceinline__ float to_log2(float d, float c) {
 #pragma clang fp contract(off)
-  return s * scale;
+  return d * c;
+}
+
+// Scores are kept in raw units (q.k, before the softmax scale) until the running max is
+// subtracted; the scale to log2 units is applied to the difference, so the rounding of a
+// large score times the scale never enters the weights.
+//
+// Pages with very large scores.  The bf16 matrix instruction sums its 32 products with an error
+// of a few units in the last place of the largest product (measured up to ~6 ulp on gfx950), so
+// a score of magnitude M carries an absolute error of ~6 M 2^-24.  Near 1e4 in log2 units (keys
+// holding sigma * 2^12 outliers against unit queries) two nearly tied top scores then get softmax
+// weights ~0.5% off.  On such pages (rare: none on data without outliers) the scores are
+// recomputed as an exact pair: the K values are split by magnitude into "big" elements (those
+// whose product with the largest query value can reach 2^9) and the rest, each half goes
+// through the same four products, and the score is carried as big + small.  The big half of a
+// row normally holds one product, which the instruction returns exactly; the small half's error
+// is a few ulp of 2^9.
+constexpr float kPreciseScoreMin = 256.f;   // in log2 units: scores this large take the pair path
+
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+
+// The exponent-field threshold (in bits 7..14 of each bf16 half, replicated to both halves)
+// from which a K value counts as big: with q_e the largest biased exponent of the wave's query
+// values, |q| < 2^(q_e - 126); a K value of biased exponent e has |k| < 2^(e - 126), so below the
+// threshold T = 262 - q_e every product is smaller than 2^(261 - q_e + q_e - 252) = 2^9.
+__device__ __forceinline__ uint32_t big_threshold(const uint4 (&qop)[4]) {
+  uint32_t e = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t w[4] = {qop[j].x, qop[j].y, qop[j].z, qop[j].w};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) e = max(e, max((w[m] >> 7) & 0xFFu, (w[m] >> 23) & 0xFFu));
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) e = max(e, (uint32_t)__shfl_xor((int)e, d, 64));
+  int t = 262 - (int)e;
+  t = t < 0 ? 0 : (t > 255 ? 255 : t);
+  return ((uint32_t)t << 7) * 0x00010001u;
+}
+
+// Split one dword of two bf16 values: small keeps the values whose exponent field is below the
+// threshold, big the others (small + big = w, one of each pair zero).
+__device__ __forceinline__ void split_big(uint32_t w, uint32_t thr2, uint32_t& small, uint32_t& big) {
+  const i16x2 e = __builtin_bit_cast(i16x2, w & 0x7F807F80u);
+  const i16x2 below = (e - __builtin_bit_cast(i16x2, thr2)) >> (i16x2){15, 15};   // 0xFFFF where e < thr
+  small = w & __builtin_bit_cast(uint32_t, below);
+  big = w ^ small;
+}
+
+// A page's raw scores as the exact pair big + small (see above).
+__device__ __forceinline__ void split_scores(const uint4 (&kops)[4], const uint4 (&qop)[4], uint32_t thr2,
+                                             float (&hi)[4], float (&lo)[4]) {
+  f32x4 sb = {0.f, 0.f, 0.f, 0.f}, ss = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint4 ks, kb;
+    split_big(kops[j].x, thr2, ks.x, kb.x);
+    split_big(kops[j].y, thr2, ks.y, kb.y);
+    split_big(kops[j].z, thr2, ks.z, kb.z);
+    split_big(kops[j].w, thr2, ks.w, kb.w);
+    sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb), as_bf16x8(qop[j]), sb, 0, 0, 0);
+    ss = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ks), as_bf16x8(qop[j]), ss, 0, 0, 0);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    hi[r] = sb[r];
+    lo[r] = __builtin_isfinite(sb[r]) ? ss[r] : 0.f;   // non-finite scores as on the plain path
+  }
+}
+
+// The largest of a page's scores per head (every lane of head lane%16 gets it).
+__device__ __forceinline__ float page_max(const float (&sv)[4]) {
+  float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+  mx = max_xor16(mx);
+  return max_xor32(mx);
+}
+
+// Whether a page's raw scores need the pair: some valid score is at least big_min (=
+// kPreciseScoreMin in log2 units) in magnitude and no more than near (= 40 in log2 units, 2^-40
+// in weight) below its head's running max before this page (a score further below carries no
+// weight in fp32; one above it is a new max).  Non-finite scores may take the pair too (their
+// low half is zero).  Written without short-circuit operators, so that it compiles to compares
+// and one scalar branch.  Wave-uniform.
+__device__ __forceinline__ bool needs_precise(const float (&sv)[4], float m_run, float big_min, float near) {
+  const float floor = m_run - near;
+  uint32_t big = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) big |= (uint32_t)(fabsf(sv[r]) >= big_min) & (uint32_t)(sv[r] >= floor);
+  return __ballot(big != 0u) != 0ull;
 }
 
 template <int GB>
@@ -185,18 +293,19 @@ struct Softmax {
     for (int j = 0; j < 4; ++j) o[j] = f32x16{};
   }
 
-  // sacc: scores of this lane (tokens 4*(lane/16)+r, head lane%16), already valid-masked and
-  // scaled by sm_scale*log2(e).  vop: the four V chunks of the page in operand order.
-  __device__ __forceinline__ void page(const float (&sv)[4], const uint4 (&vop)[4], int lane) {
-    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    mx = max_xor16(mx);
-    mx = max_xor32(mx);
+  // sv: raw scores q.k of this lane (tokens 4*(lane/16)+r, head lane%16), already
+  // valid-masked (-inf); sl: what the score is beyond sv (zero, or the small half of a split
+  // score: score = sv + sl); mx: page_max of the scores; c: the scale to log2 units
+  // (sm_scale * log2(e)).  The running max m_run is in raw units.  vop: the four V chunks of
+  // the page in operand order.
+  __device__ __forceinline__ void page(const float (&sv)[4], const float (&sl)[4], float mx,
+                                       const uint4 (&vop)[4], int lane, float c) {
     const float m_new = fmaxf(m_run, mx);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    const float alpha = __builtin_amdgcn_exp2f(to_log2(m_run - m_use, c));
     float pr[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) pr[r] = __builtin_amdgcn_exp2f(sv[r] - m_use);
+    for (int r = 0; r < 4; ++r) pr[r] = __builtin_amdgcn_exp2f(to_log2((sv[r] - m_use) + sl[r], c));
     l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
     m_run = m_new;
     if (__ballot(alpha != 1.0f)) rescale(alpha, lane);
@@ -437,6 +546,12 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
   }
 
   Softmax<GB> sm;
+  // pages with very large scores (see split_scores): the K split threshold, and the magnitude
+  // and the distance below the max that make a score count, in raw units
+  const uint32_t big_thr = big_threshold(qop);
+  const float c_log2 = p.scale_log2;
+  const float big_min = c_log2 > 0.f ? kPreciseScoreMin / c_log2 : INFINITY;
+  const float near = c_log2 > 0.f ? 40.f / c_log2 : INFINITY;
   // per-lane byte offsets of a chunk inside a compressed / raw block (loop invariant), so that
   // every page load is "uniform block base (SGPRs) + this offset"
   const uint32_t lane12 = kCompChunkBytes * lane;
@@ -773,12 +888,10 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
         for (int j = 0; j < 4; ++j) kops[j] = restore_if_coded(buf.k[j], (kt >> (8 * j)) & 0xFFu);
       }
       f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+      operands_settled(kops);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kops[j]), as_bf16x8(qop[j]), sacc, 0, 0, 0);
-      float sv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sv[r] = scaled_score(sacc[r], p.scale_log2);
       if constexpr (FMT == kFmtGaac) {
         gaac_ops(buf.v, vt != 0u, false, vop);
       } else if constexpr (FMT == kFmtFp8c) {
@@ -792,7 +905,17 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) vop[j] = restore_if_coded(buf.v[j], (vt >> (8 * j)) & 0xFFu);
       }
-      sm.page(sv, vop, lane);
+      // the V restore above overlaps the score products; the rare split (a separate block) and
+      // the softmax follow
+      float sv[4], sl[4] = {0.f, 0.f, 0.f, 0.f}, t[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sv[r] = t[r] = sacc[r];
+      if (needs_precise(sv, sm.m_run, big_min, near)) {
+        split_scores(kops, qop, big_thr, sv, sl);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) t[r] = sv[r] + sl[r];
+      }
+      sm.page(sv, sl, page_max(t), vop, lane, c_log2);
     };
 
     // Two one-page buffers in a ring: the loads of page i+1 are in flight while page i is
@@ -817,15 +940,15 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
   // n_tail tokens; masked V values are zeros, so they add nothing even where p is 0.
   if (n_tail > 0 && p0 <= n_comp && n_comp < p1) {
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-    uint4 vop[4];
+    uint4 kops[4], vop[4];
     if constexpr (IS_FP8) {
       const uint8_t* kt = static_cast<const uint8_t*>(p.tail) + (((size_t)b * 2 + 0) * p.Hkv + kvh) * 2048;
       const uint8_t* vt = static_cast<const uint8_t*>(p.tail) + (((size_t)b * 2 + 1) * p.Hkv + kvh) * 2048;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint2 k8 = *reinterpret_cast<const uint2*>(kt + (lane & 15) * 128 + 32 * j + 8 * (lane >> 4));
-        const uint4 kop = fp8x8_to_bf16<FK>(k8.x, k8.y);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kop), as_bf16x8(qop[j]), sacc, 0, 0, 0);
+        kops[j] = fp8x8_to_bf16<FK>(k8.x, k8.y);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kops[j]), as_bf16x8(qop[j]), sacc, 0, 0, 0);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -843,8 +966,8 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
       const uint16_t* vt = static_cast<const uint16_t*>(p.tail) + (((size_t)b * 2 + 1) * p.Hkv + kvh) * 2048;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint4 kop = *reinterpret_cast<const uint4*>(kt + (lane & 15) * 128 + 32 * j + 8 * (lane >> 4));
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kop), as_bf16x8(qop[j]), sacc, 0, 0, 0);
+        kops[j] = *reinterpret_cast<const uint4*>(kt + (lane & 15) * 128 + 32 * j + 8 * (lane >> 4));
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kops[j]), as_bf16x8(qop[j]), sacc, 0, 0, 0);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -859,13 +982,25 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
         vop[j] = make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
-    float sv[4];
+    float sv[4], sl[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int tok = 4 * (lane >> 4) + r;
-      sv[r] = tok < n_tail ? scaled_score(sacc[r], p.scale_log2) : -INFINITY;
+      sv[r] = tok < n_tail ? sacc[r] : -INFINITY;
     }
-    sm.page(sv, vop, lane);
+    float t[4] = {sv[0], sv[1], sv[2], sv[3]};
+    if (needs_precise(sv, sm.m_run, big_min, near)) {
+      split_scores(kops, qop, big_thr, sv, sl);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (4 * (lane >> 4) + r >= n_tail) {
+          sv[r] = -INFINITY;
+          sl[r] = 0.f;
+        }
+        t[r] = sv[r] + sl[r];
+      }
+    }
+    sm.page(sv, sl, page_max(t), vop, lane, c_log2);
   }
 
   if constexpr (IS_FP8) {   // the V dequantization scale, applied once to O
@@ -878,7 +1013,8 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
   constexpr int NR = GB <= 8 ? 4 : 8;
 
   // The four waves' (m, l) per head and unnormalized O rows meet in LDS; one merge per
-  // (head, dim): M = max m_w, L = sum l_w 2^(m_w - M), O = sum O_w 2^(m_w - M), in wave order.
+  // (head, dim): M = max m_w, L = sum l_w 2^((m_w - M) c), O = sum O_w 2^((m_w - M) c), in wave
+  // order (m: raw scores; c: the scale to log2 units).
   __shared__ float s_m[4][16], s_l[4][16];
   __shared__ float s_o[4][GB * KVZ_HEAD_DIM];
   if (lane < 16) {
@@ -907,7 +1043,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const float mw = s_m[w][h];
-      const float c = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      const float c = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(to_log2(mw - M, c_log2));
       L += c * s_l[w][h];
       O += c * s_o[w][idx];
     }
@@ -979,14 +1115,14 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
 #pragma unroll
     for (int i = 0; i < kInKernelMergeMax; ++i) {
       if (i < so.sb) {
-        const float c = mv[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv[i] - M);
+        const float c = mv[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(to_log2(mv[i] - M, c_log2));
         L += c * lv[i];
         O += c * ov[i];
       }
     }
     for (int i = kInKernelMergeMax; i < so.sb; ++i) {
       const float m = ld(ml + i * mls);
-      const float c = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
+      const float c = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(to_log2(m - M, c_log2));
       L += c * ld(ml + i * mls + 1);
       O += c * ld(o + i * os);
     }
@@ -994,8 +1130,9 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
   }
 }
 
-// Merge the splits of every (sequence, query head): M = max m_s, L = sum l_s 2^(m_s - M),
-// out = sum O_s 2^(m_s - M) / L, over the sequence's S_b splits (split_of).  A sequence of
+// Merge the splits of every (sequence, query head): M = max m_s, L = sum l_s 2^((m_s - M) c),
+// out = sum O_s 2^((m_s - M) c) / L, over the sequence's S_b splits (split_of); the maxima are
+// raw scores and c the scale to log2 units.  A sequence of
 // length 0 gives zeros.  A separate launch, for split counts above kInKernelMergeMax (one long
 // sequence over many CUs: its pieces are merged in parallel here rather than serially by the
 // last piece).  One workgroup of 256 threads per (sequence, query head), parallel over the
@@ -1024,7 +1161,8 @@ constexpr int kSpecSplits = 32;
 
 __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(
     const float* ws_ml, const float* ws_o, float* out, const int32_t* seq_lens,
-    const int32_t* n_comp_v, bool has_tail, int max_pages, int B, int Hq, int G, int S_avg) {
+    const int32_t* n_comp_v, bool has_tail, int max_pages, int B, int Hq, int G, int S_avg,
+    float c_log2) {
   __shared__ float s_w[kMaxSplits];
   __shared__ float s_red[kCombineThreads / 64];
   __shared__ float s_part[kCombineThreads];
@@ -1066,14 +1204,14 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(
     float L = 0.f, acc = 0.f;
     for (int sp = 0; sp < S; ++sp) {
       const float m = s_ml[0][sp];
-      L += ((m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - M)) * s_ml[1][sp];
+      L += ((m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(to_log2(m - M, c_log2))) * s_ml[1][sp];
     }
 #pragma unroll
     for (int i = 0; i < kSpecSplits / 2; ++i) {
       const int sp = half + 2 * i;
       if (sp < S) {
         const float m = s_ml[0][sp];
-        acc += ((m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - M)) * o_sp[i];
+        acc += ((m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(to_log2(m - M, c_log2))) * o_sp[i];
       }
     }
     s_part[t] = acc;
@@ -1093,7 +1231,7 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(
   for (int sp = t; sp < S; sp += kCombineThreads) {
     const size_t ug = unit_of(sp) * G + g;
     const float m = ws_ml[ug * 2];
-    const float w = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - M);
+    const float w = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(to_log2(m - M, c_log2));
     s_w[sp] = w;
     l_loc += w * ws_ml[ug * 2 + 1];
   }
@@ -1234,7 +1372,7 @@ int launch_attention(const CommonArgs& a, const uint8_t* kv, const kvz_group_met
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.batch * a.num_q_heads)),
                      dim3(kCombineThreads), 0, s,
                      p.ws_ml, p.ws_o, a.out, a.seq_lens, a.n_comp_pages, a.tail != nullptr,
-                     p.max_pages, p.B, p.Hq, G, S);
+                     p.max_pages, p.B, p.Hq, G, S, p.scale_log2);
   return check_hip(hipGetLastError(), "combine launch");
 }
 

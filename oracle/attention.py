@@ -21,6 +21,9 @@ NaN and Inf are carried by IEEE float64 arithmetic.
 Pins (tests/test_oracle_attention.py): pure-Python brute force on tiny inputs, torch's
 scaled_dot_product_attention in float64 on CPU, and closed forms (q = 0 gives the mean of V,
 constant V gives that V, one dominant logit gives that token's V, one token gives its V).
+softmax_weights_fp64 (the weights alone, used to report how many keys a test's softmax really
+spreads over) is pinned by closed forms (q = 0 gives 1/T each, a dominant logit gives one-hot)
+and by the brute-force weights.
 """
 from __future__ import annotations
 
@@ -55,6 +58,26 @@ def attention_values_fp64(q, k, v, sm_scale: float) -> np.ndarray:
             p = np.exp(s - m)
             out[h] = (p @ v[:, g, :]) / np.sum(p)
     return out
+
+
+def softmax_weights_fp64(q_bits, k_bits, sm_scale: float) -> np.ndarray:
+    """The softmax weights of one sequence: q_bits [Hq, D], k_bits [T, Hkv, D] (BF16 bit
+    patterns) -> float64 [Hq, T], w[h, t] = exp(s_t - max s) / sum_t exp(s_t - max s) with the
+    scores s_t of the definition above."""
+    q = codec.bf16_bits_to_f64(q_bits)
+    k = codec.bf16_bits_to_f64(k_bits)
+    hq = q.shape[0]
+    t, hkv, _ = k.shape
+    w = np.zeros((hq, t), dtype=np.float64)
+    if t == 0:
+        return w
+    group = hq // hkv
+    with np.errstate(invalid="ignore", over="ignore", divide="ignore"):
+        for h in range(hq):
+            s = sm_scale * (k[:, h // group, :] @ q[h])
+            p = np.exp(s - np.max(s))
+            w[h] = p / np.sum(p)
+    return w
 
 
 def gather_sequence(arena, meta_table, block_table_row, n_comp: int, tail_b, n_tail: int):

@@ -113,9 +113,26 @@ def run_bf16(layer: Layer, q: torch.Tensor, sm_scale: float, splits: int = 0) ->
     return out
 
 
-def oracle_attention_rows(layer: Layer, q: torch.Tensor, sm_scale: float, batch_indices):
+def _sequence_kv(pages, seq_lens, n_comp, b):
+    """K and V of sequence b in token order [T, Hkv, 128] (bit patterns) from the natural pages:
+    its compressed pages, then its tail tokens."""
+    nc = int(n_comp[b])
+    nt = int(seq_lens[b]) - 16 * nc
+    hkv = pages.shape[3]
+    k = pages[b, :nc, 0].transpose(0, 2, 1, 3).reshape(16 * nc, hkv, 128)
+    v = pages[b, :nc, 1].transpose(0, 2, 1, 3).reshape(16 * nc, hkv, 128)
+    if nt > 0:
+        k = np.concatenate([k, pages[b, nc, 0, :, :nt].transpose(1, 0, 2)])
+        v = np.concatenate([v, pages[b, nc, 1, :, :nt].transpose(1, 0, 2)])
+    return k, v
+
+
+def oracle_attention_rows(layer: Layer, q: torch.Tensor, sm_scale: float, batch_indices,
+                          effective: dict | None = None):
     """Oracle output for the listed sequences, computed from the natural pages (the values the
-    encoder received), not from anything the GPU wrote."""
+    encoder received), not from anything the GPU wrote.  With `effective` (a dict), also the
+    number of keys each query head's softmax spreads over, 1 / sum_t w_t^2 (1 for a one-hot
+    softmax, T for a uniform one), per sequence: effective[b] = [Hq] array."""
     from oracle import attention
     pages = synth.bits(layer.pages)                         # [B, P, 2, Hkv, 16, 128]
     qb = synth.bits(q)
@@ -123,16 +140,26 @@ def oracle_attention_rows(layer: Layer, q: torch.Tensor, sm_scale: float, batch_
     n_comp = layer.n_comp.cpu().numpy()
     out = {}
     for b in batch_indices:
-        nc = int(n_comp[b])
-        nt = int(seq_lens[b]) - 16 * nc
-        hkv = pages.shape[3]
-        k = pages[b, :nc, 0].transpose(0, 2, 1, 3).reshape(16 * nc, hkv, 128)
-        v = pages[b, :nc, 1].transpose(0, 2, 1, 3).reshape(16 * nc, hkv, 128)
-        if nt > 0:
-            k = np.concatenate([k, pages[b, nc, 0, :, :nt].transpose(1, 0, 2)])
-            v = np.concatenate([v, pages[b, nc, 1, :, :nt].transpose(1, 0, 2)])
+        k, v = _sequence_kv(pages, seq_lens, n_comp, b)
         out[b] = attention.attention_fp64(qb[b], k, v, sm_scale)
+        if effective is not None:
+            w = attention.softmax_weights_fp64(qb[b], k, sm_scale)
+            effective[b] = 1.0 / np.sum(w * w, axis=1) if w.shape[1] else np.zeros(w.shape[0])
     return out
+
+
+def report_effective(effective: dict, what: str) -> float:
+    """Print the smallest and median effective key count over the checked rows; return the
+    smallest."""
+    allv = np.concatenate([np.asarray(v) for v in effective.values()]) if effective else np.zeros(1)
+    announce(f"  {what}: effective keys per head min {allv.min():.1f} median "
+             f"{np.median(allv):.1f} over {len(effective)} sequences")
+    return float(allv.min())
+
+
+def scaled_queries(q: torch.Tensor, log2_scale: int) -> torch.Tensor:
+    """q times 2**log2_scale (exact in BF16 for these magnitudes): a broader softmax."""
+    return (q.float() * (2.0 ** log2_scale)).to(torch.bfloat16) if log2_scale else q
 
 
 def check_rows(got: np.ndarray, ref: np.ndarray, tol: float = MAX_REL, what: str = ""):

@@ -9,8 +9,8 @@ import torch
 
 from decode_attention_kvz_amd import kvz, paged, synth
 
-from gpu_util import (announce, build_layer, check_rows, oracle_attention_rows, run_bf16,
-                      run_fused, sm_scale)
+from gpu_util import (announce, build_layer, check_rows, oracle_attention_rows, report_effective,
+                      run_bf16, run_fused, scaled_queries, sm_scale)
 
 pytestmark = pytest.mark.gpu
 
@@ -108,7 +108,9 @@ def test_in_kernel_split_merge_reads_this_calls_partials(splits):
     bit (a merge that read a previous call's partials, or missed this call's, would differ),
     and a ragged batch (one sequence cut into more pieces) matches the oracle."""
     announce(f"in-kernel merge, splits={splits}")
-    pages = synth.kv_pages(6, 41, 8, seed=15, forced_frac=0.05, device="cuda")
+    # forced elements tiny (2^-16 sigma): every piece carries real softmax weight, so a stale or
+    # missing partial changes the output
+    pages = synth.kv_pages(6, 41, 8, seed=15, forced_frac=0.05, forced_exp=-16.0, device="cuda")
     seq_lens, n_comp = [16 * 40 + 7, 16 * 3, 16 * 40, 16 * 22 + 1, 5, 16 * 37 + 16], [40, 3, 40, 22, 0, 37]
     arena, layer = _layer(pages, seq_lens, n_comp, seed=15)
     qs = [synth.queries(6, 32, seed=150 + k, device="cuda") for k in range(2)]
@@ -125,10 +127,12 @@ def test_in_kernel_split_merge_reads_this_calls_partials(splits):
     for i, o in enumerate(outs):
         assert torch.equal(o, first[i % 2]), i
     for k in range(2):
-        ref = oracle_attention_rows(layer, qs[k], sm_scale(), range(6))
+        eff = {}
+        ref = oracle_attention_rows(layer, qs[k], sm_scale(), range(6), eff)
         got = first[k].cpu().numpy()
         for b in range(6):
             check_rows(got[b], ref[b], what=f"q{k} seq {b}")
+        report_effective({b: e for b, e in eff.items() if b != 4}, f"q{k}")
 
 
 def test_non_finite_values_propagate_like_the_oracle():
@@ -151,39 +155,102 @@ def test_non_finite_values_propagate_like_the_oracle():
 
 
 def _full_size_sampled(bsz, n_pages_total, n_comp_pages, tail_tokens, hq, hkv, u_max, forced,
-                       seed, samples):
+                       seed, samples, forced_exp=12.0, q_log2_scale=0, min_effective=None):
+    """One layer at full shape with the automatic split count: sampled rows against the oracle,
+    and every row of the fused kernel bit for bit against the uncompressed kernel (the same
+    split count; the restore is exact).  Reports how many keys the checked softmaxes spread
+    over and, with min_effective, requires more than that many for every checked head."""
     pages = synth.kv_pages(bsz, n_pages_total, hkv, seed=seed, u_max=u_max, forced_frac=forced,
-                           device="cuda")
-    q = synth.queries(bsz, hq, seed=seed, device="cuda")
+                           forced_exp=forced_exp, device="cuda")
+    q = scaled_queries(synth.queries(bsz, hq, seed=seed, device="cuda"), q_log2_scale)
     seq_lens = [16 * n_comp_pages + tail_tokens] * bsz
     arena, layer = _layer(pages, seq_lens, [n_comp_pages] * bsz, seed=seed)
-    got = run_fused(layer, arena, q, sm_scale()).cpu().numpy()
-    base = run_bf16(layer, q, sm_scale()).cpu().numpy()
-    ref = oracle_attention_rows(layer, q, sm_scale(), samples)
+    got_t = run_fused(layer, arena, q, sm_scale())
+    base_t = run_bf16(layer, q, sm_scale())
+    torch.cuda.synchronize()
+    assert torch.equal(got_t, base_t)
+    got, base = got_t.cpu().numpy(), base_t.cpu().numpy()
+    eff = {}
+    ref = oracle_attention_rows(layer, q, sm_scale(), samples, eff)
+    worst = 0.0
     for b in samples:
-        check_rows(got[b], ref[b], what=f"fused seq {b}")
+        worst = max(worst, check_rows(got[b], ref[b], what=f"fused seq {b}"))
         check_rows(base[b], ref[b], what=f"baseline seq {b}")
+    announce(f"  max row rel err {worst:.2e}")
+    lo = report_effective(eff, f"forced 2^{forced_exp:g} x{forced}, q x2^{q_log2_scale}")
+    if min_effective is not None:
+        assert lo > min_effective, f"softmax too concentrated for this check: {lo:.1f} keys"
     return arena
 
 
-def test_llama_shape_layer_sampled():
-    """Batch 32, 32 query / 8 KV heads, 2048 tokens, all pages compressed, 5% forced: one
-    layer at full shape with the automatic split count, checked on sampled sequences."""
-    announce("llama-shaped layer")
-    _full_size_sampled(32, 128, 128, 0, 32, 8, 3.0, 0.05, 1, [0, 17, 31])
+# Forced elements: as the workloads specify (+-sigma 2^12, which makes the softmax one-hot and
+# checks that the dominant key is found and its V restored), tiny (2^-16 sigma: the blocks still
+# go raw but no key dominates) and none.  The broad variants also scale q down by a power of two
+# so that every checked head spreads its softmax over more than 10 keys: accumulation over the
+# whole context and the split merge weights are then what the check measures.
+LLAMA_SAMPLES = [0, 4, 9, 13, 17, 22, 26, 31]
+QWEN_SAMPLES = [0, 2, 5, 7, 9, 11, 13, 15]
+DATA_VARIANTS = [
+    pytest.param(12.0, 1.0, 0, None, id="forced2^12"),
+    pytest.param(-16.0, 1.0, 0, None, id="forced2^-16"),
+    pytest.param(0.0, 0.0, 0, None, id="unforced"),
+    pytest.param(-16.0, 1.0, -3, 10.0, id="forced2^-16-broad"),
+    pytest.param(0.0, 0.0, -3, 10.0, id="unforced-broad"),
+]
 
 
-def test_qwen_shape_8k_layer_sampled():
+@pytest.mark.parametrize("forced_exp,forced_scale,q_log2,min_eff", DATA_VARIANTS)
+def test_llama_shape_layer_sampled(forced_exp, forced_scale, q_log2, min_eff):
+    """Batch 32, 32 query / 8 KV heads, 2048 tokens, all pages compressed, 5% of blocks with a
+    forced element: one layer at full shape with the automatic split count, 8 sequences."""
+    announce(f"llama-shaped layer forced=2^{forced_exp:g} q x2^{q_log2}")
+    _full_size_sampled(32, 128, 128, 0, 32, 8, 3.0, 0.05 * forced_scale, 1, LLAMA_SAMPLES,
+                       forced_exp, q_log2, min_eff)
+
+
+@pytest.mark.parametrize("forced_exp,forced_scale,q_log2,min_eff", DATA_VARIANTS)
+def test_qwen_shape_8k_layer_sampled(forced_exp, forced_scale, q_log2, min_eff):
     """Batch 16, 32 query / 8 KV heads, 8192 tokens: 511 compressed pages plus a 16-token
-    BF16 tail, u~U[-5,5], 5% forced: one layer at full shape, sampled sequences."""
-    announce("qwen-shaped 8k layer")
-    _full_size_sampled(16, 512, 511, 16, 32, 8, 5.0, 0.05, 2, [0, 15])
+    BF16 tail, u~U[-5,5], 5% forced: one layer at full shape (two pieces per sequence, merged
+    inside the attention kernel), 8 sequences."""
+    announce(f"qwen-shaped 8k layer forced=2^{forced_exp:g} q x2^{q_log2}")
+    _full_size_sampled(16, 512, 511, 16, 32, 8, 5.0, 0.05 * forced_scale, 2, QWEN_SAMPLES,
+                       forced_exp, q_log2, min_eff)
 
 
-def test_long_context_layer_sampled():
-    """Batch 1, 32 query / 8 KV heads, 131072 tokens, split-K across the chip."""
-    announce("131k-token layer")
-    _full_size_sampled(1, 8192, 8192, 0, 32, 8, 3.0, 0.10, 4, [0])
+@pytest.mark.parametrize("forced_exp,forced_scale,q_log2,min_eff", DATA_VARIANTS)
+def test_long_context_layer_sampled(forced_exp, forced_scale, q_log2, min_eff):
+    """Batch 1, 32 query / 8 KV heads, 131072 tokens: 32 pieces per KV head across the chip,
+    merged by the combine kernel's uniform-map path."""
+    announce(f"131k-token layer forced=2^{forced_exp:g} q x2^{q_log2}")
+    _full_size_sampled(1, 8192, 8192, 0, 32, 8, 3.0, 0.10 * forced_scale, 4, [0],
+                       forced_exp, q_log2, min_eff)
+
+
+@pytest.mark.parametrize("splits", [5, 8, 32, 33])
+def test_equal_length_batch_split_merge_matches_oracle(splits):
+    """Equal lengths give the uniform split map: up to 32 pieces per sequence the combine
+    kernel merges from its speculative loads, above that by its general path.  Non-degenerate
+    data (tiny forced elements, q scaled down), every row against the oracle."""
+    announce(f"equal-length batch, splits={splits}")
+    bsz, n_comp = 4, 96
+    pages = synth.kv_pages(bsz, n_comp + 1, 8, seed=18, forced_frac=0.05, forced_exp=-16.0,
+                           device="cuda")
+    q = scaled_queries(synth.queries(bsz, 32, seed=18, device="cuda"), -2)
+    seq_lens = [16 * n_comp + 11] * bsz
+    arena, layer = _layer(pages, seq_lens, [n_comp] * bsz, seed=18)
+    got_t = run_fused(layer, arena, q, sm_scale(), splits)
+    base_t = run_bf16(layer, q, sm_scale(), splits)
+    one_t = run_fused(layer, arena, q, sm_scale(), 1)
+    torch.cuda.synchronize()
+    assert torch.equal(got_t, base_t)
+    got, one = got_t.cpu().numpy(), one_t.cpu().numpy()
+    eff = {}
+    ref = oracle_attention_rows(layer, q, sm_scale(), range(bsz), eff)
+    for b in range(bsz):
+        check_rows(got[b], ref[b], what=f"seq {b}")
+        check_rows(got[b], one[b], tol=1e-5, what=f"seq {b} vs one piece")
+    assert report_effective(eff, f"splits {splits}") > 10.0
 
 
 @pytest.mark.parametrize("splits", [0, 3, 8])

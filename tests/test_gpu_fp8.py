@@ -125,7 +125,9 @@ def test_hardware_conversion_is_exact_for_every_byte(fmt):
                 assert np.array_equal(np.isfinite(g[h, r]), fin), name
                 assert np.array_equal(g[h, r][fin], want[h][fin].astype(np.float32)), name
     # the same values inside a compressed page: K zero everywhere except token 3, dim 0, where
-    # q's one-hot query picks it with an overwhelming score, so the output is V of token 3
+    # q's one-hot query picks it with an overwhelming score (k_scale 4 for E4M3, 1/32 for E5M2:
+    # ~229 in log2 units, so every other weight underflows to 0 and the scores stay on the
+    # plain fp32 path), so the output is V of token 3
     pages2 = torch.zeros((1, 2, 2, hkv, 16, 128), dtype=torch.uint8)
     one = 0x38 if fmt == kvz.KVZ_FP8_E4M3 else 0x3C
     big = 0x7E if fmt == kvz.KVZ_FP8_E4M3 else 0x7B      # the largest finite value
@@ -137,12 +139,21 @@ def test_hardware_conversion_is_exact_for_every_byte(fmt):
         lay2 = Fp8Layer(pages2, [16], [1], fmt, paged.fp8_calibrate(pages2, fmt), seed=2, flags=force)
         qh = torch.zeros((1, 8, 128), dtype=torch.bfloat16, device="cuda")
         qh[:, :, 0] = 1.0
-        got = lay2.fused(qh, 1000.0, 1.0).cpu().numpy().reshape(hkv, 4, 128)
+        k_scale = 4.0 if fmt == kvz.KVZ_FP8_E4M3 else 1.0 / 32.0
+        got = lay2.fused(qh, k_scale, 1.0).cpu().numpy().reshape(hkv, 4, 128)
         for h in range(hkv):
             fin = np.isfinite(want[h])
             for r in range(4):
                 assert np.array_equal(np.isfinite(got[h, r]), fin)
                 assert np.array_equal(got[h, r][fin], want[h][fin].astype(np.float32))
+        # a score 250 times larger takes the float64 score path: the chosen token's weight is
+        # then carried as bf16 hi + lo parts like any other (2^-17 relative)
+        got = lay2.fused(qh, 250.0 * k_scale, 1.0).cpu().numpy().reshape(hkv, 4, 128)
+        for h in range(hkv):
+            fin = np.isfinite(want[h])
+            for r in range(4):
+                assert np.array_equal(np.isfinite(got[h, r]), fin)
+                np.testing.assert_allclose(got[h, r][fin], want[h][fin], rtol=2.0 ** -16, atol=0)
 
 
 @pytest.mark.parametrize("fmt", FORMATS)

@@ -223,7 +223,8 @@ def test_full_size_qwen8k_layer_round_trip_and_ratio():
 # ---------------------------------------------------------------------------------------------
 # fused attention over group-adaptive tiles
 # ---------------------------------------------------------------------------------------------
-from gpu_util import check_rows, oracle_attention_rows, run_bf16, run_gaac, sm_scale  # noqa: E402
+from gpu_util import (check_rows, oracle_attention_rows, report_effective, run_bf16, run_gaac,  # noqa: E402
+                      scaled_queries, sm_scale)
 
 
 @pytest.mark.parametrize("hq,hkv", [(32, 8), (16, 2), (12, 4)])
@@ -275,16 +276,24 @@ def test_gaac_attention_raw_and_compressed_tiles_agree_bitwise():
     assert torch.equal(outs[0], outs[1])
 
 
-def test_gaac_attention_full_size_qwen8k_sampled():
+@pytest.mark.parametrize("forced_exp,q_log2,min_eff", [
+    pytest.param(12.0, 0, None, id="forced2^12"),
+    pytest.param(-16.0, 0, None, id="forced2^-16"),
+    pytest.param(-16.0, -3, 10.0, id="forced2^-16-broad"),
+])
+def test_gaac_attention_full_size_qwen8k_sampled(forced_exp, q_log2, min_eff):
     """The 8K workload's shape (16 x 511 compressed pages + the 16-token tail, u~U[-5,5]): rows
-    of 3 sequences against the oracle, all rows bit for bit against the uncompressed kernel
-    run with the same split count."""
-    announce("gaac attention full 8K")
+    of 8 sequences against the oracle, all rows bit for bit against the uncompressed kernel
+    run with the same split count.  Forced elements as specified (one-hot softmax), tiny, and
+    tiny with q scaled down (every checked head spreads over more than 10 keys)."""
+    announce(f"gaac attention full 8K forced=2^{forced_exp:g} q x2^{q_log2}")
     bsz, n_comp, hkv, hq = 16, 511, 8, 32
-    cal = synth.kv_pages(4, 32, hkv, seed=2, u_max=5.0, forced_frac=0.05, sample=1, device="cuda")
+    cal = synth.kv_pages(4, 32, hkv, seed=2, u_max=5.0, forced_frac=0.05, forced_exp=forced_exp,
+                         sample=1, device="cuda")
     bases = paged.gaac_calibrate(cal)
-    pages = synth.kv_pages(bsz, n_comp + 1, hkv, seed=2, u_max=5.0, forced_frac=0.05, device="cuda")
-    q = synth.queries(bsz, hq, seed=2, device="cuda")
+    pages = synth.kv_pages(bsz, n_comp + 1, hkv, seed=2, u_max=5.0, forced_frac=0.05,
+                           forced_exp=forced_exp, device="cuda")
+    q = scaled_queries(synth.queries(bsz, hq, seed=2, device="cuda"), q_log2)
     arena = paged.SlotArena(bsz * n_comp * hkv * 2 * 4096 + (16 << 20))
     layer = build_layer(arena, pages, [16 * n_comp + 16] * bsz, [n_comp] * bsz, seed=2,
                         gaac_bases=bases)
@@ -293,10 +302,15 @@ def test_gaac_attention_full_size_qwen8k_sampled():
     base = run_bf16(layer, q, sm_scale(), splits=16)
     torch.cuda.synchronize()
     assert torch.equal(same, base)
-    ref = oracle_attention_rows(layer, q, sm_scale(), [0, 7, 15])
+    samples = [0, 2, 5, 7, 9, 11, 13, 15]
+    eff = {}
+    ref = oracle_attention_rows(layer, q, sm_scale(), samples, eff)
     g = got.cpu().numpy()
-    for b in (0, 7, 15):
+    for b in samples:
         check_rows(g[b], ref[b], what=f"gaac 8K seq {b}")
+    lo = report_effective(eff, "gaac 8K")
+    if min_eff is not None:
+        assert lo > min_eff
 
 
 def test_gaac_attention_non_finite_values_propagate_like_the_oracle():

@@ -88,6 +88,32 @@ def test_closed_forms():
     assert not attention.attention_fp64(q, k[:0], v[:0], 0.1).any()
 
 
+def test_softmax_weights_closed_forms_and_brute_force():
+    rng = np.random.default_rng(15)
+    t = 40
+    k = _rand_bf16(rng, (t, 2, 128))
+    # q = 0: every key weighs 1/T
+    w0 = attention.softmax_weights_fp64(np.zeros((4, 128), dtype=np.uint16), k, 0.1)
+    np.testing.assert_allclose(w0, np.full((4, t), 1.0 / t), rtol=1e-14)
+    # one dominant logit: one-hot on that key, for the heads of its KV group only
+    q = _rand_bf16(rng, (4, 128))
+    kd = k.copy()
+    kd[9, 0, :] = _bf16(np.full(128, 64.0) * np.sign(codec.bf16_bits_to_f64(q[0])))
+    w = attention.softmax_weights_fp64(q, kd, 1.0)
+    assert w[0, 9] == 1.0 and w[0].sum() == 1.0
+    assert w[2].max() < 1.0
+    # brute force (pure Python exp over the scores)
+    qf, kf = codec.bf16_bits_to_f64(q), codec.bf16_bits_to_f64(k)
+    w = attention.softmax_weights_fp64(q, k, 0.2)
+    for h in range(4):
+        g = h // 2
+        s = [0.2 * sum(float(qf[h, d]) * float(kf[tt, g, d]) for d in range(128)) for tt in range(t)]
+        mx = max(s)
+        e = [math.exp(x - mx) for x in s]
+        for tt in range(t):
+            assert abs(w[h, tt] - e[tt] / sum(e)) <= 1e-13
+
+
 def test_paged_compressed_cache_equals_dense_attention():
     """Compressed pages read through the block table plus a ragged tail give exactly the
     attention of the plain dense K/V (one softmax over both, GAAC 'Attention with
