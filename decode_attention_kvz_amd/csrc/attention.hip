@@ -159,6 +159,19 @@ __device__ __forceinline__ void operands_settled(uint4 (&ops)[4]) {
   ops[3] = __builtin_bit_cast(uint4, d);
 }
 
+// Ten wait states ahead of the first read of a page's scores, after the V restore.  A VALU read
+// of a 16x16x32 product's result must be at least eight wait states after it.  Where an
+// uncompressed V block skips the V restore, the products were followed by a branch to the
+// block that reads the scores, and the compiler put nothing in between: the first compare then
+// read a score register before the last product had written it (the partial sum of the first
+// three products), so the choice of the exact score path for a page changed from run to run on
+// uncompressed tiles.  The scores pass through the asm statement, so every later read is of its
+// output, and the nops lie on every path from the products to those reads.  (Right after the
+// products, the statement would also keep the V restore from overlapping their latency.)
+__device__ __forceinline__ void scores_settled(f32x4& sacc) {
+  asm volatile("s_nop 7\n\ts_nop 1" : "+v"(sacc));
+}
+
 // Raw buffer resource over [base, base + bytes); loads beyond `bytes` return zeros.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t group_rsrc(const uint8_t* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, (int)bytes, 0x00020000);
@@ -907,6 +920,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
       }
       // the V restore above overlaps the score products; the rare split (a separate block) and
       // the softmax follow
+      scores_settled(sacc);
       float sv[4], sl[4] = {0.f, 0.f, 0.f, 0.f}, t[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) sv[r] = t[r] = sacc[r];
