@@ -31,6 +31,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 namespace kvz {
 
 namespace {
@@ -1390,10 +1392,53 @@ int launch_attention(const CommonArgs& a, const uint8_t* kv, const kvz_group_met
   return check_hip(hipGetLastError(), "combine launch");
 }
 
+// Device-resident scratch of the allocation-free attention call (kvz_decode_attention_noalloc):
+// the merge counters in a fixed area at the front (every call leaves them zero), then the
+// partial softmax states.  One copy per GPU, held while the library is loaded.
+constexpr uint64_t kScratchBytes = 16ull << 20;
+constexpr uint64_t kScratchCounterBytes = 64ull << 10;   // up to 16384 (sequence, KV head) pairs
+constexpr int kMaxDevices = 64;
+
+__global__ void zero_words_kernel(uint32_t* p, uint32_t n) {
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
 }  // namespace
 }  // namespace kvz
 
 using namespace kvz;
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxDevices];   // the device address of `scratch`, per device
+
+// The current device's scratch address, looked up (and its counter area zero-filled on stream
+// s) at the first call on that device.  The array's host-side name is not a device address:
+// every kernel argument and fill below uses the looked-up pointer.
+int scratch_of_current_device(hipStream_t s, uint8_t** out) {
+  int dev = 0;
+  int rc = check_hip(hipGetDevice(&dev), "hipGetDevice");
+  if (rc != KVZ_OK) return rc;
+  if (dev < 0 || dev >= kMaxDevices) return set_error(KVZ_EUNSUPPORTED, "device index out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    rc = check_hip(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (rc != KVZ_OK) return rc;
+    if (!ptr || (reinterpret_cast<uintptr_t>(ptr) & 255u))
+      return set_error(KVZ_EHIP, "scratch symbol has no 256-byte aligned device address");
+    hipLaunchKernelGGL(zero_words_kernel, dim3(64), dim3(256), 0, s, static_cast<uint32_t*>(ptr),
+                       (uint32_t)(kScratchCounterBytes / 4));
+    rc = check_hip(hipGetLastError(), "scratch counter fill");
+    if (rc != KVZ_OK) return rc;
+    g_scratch_ptr[dev] = static_cast<uint8_t*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return KVZ_OK;
+}
+}  // namespace
 
 extern "C" int kvz_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                         int32_t max_pages, int32_t splits, uint64_t* bytes) {
@@ -1417,6 +1462,37 @@ extern "C" int kvz_decode_attention(const kvz_attn_args* a, hipStream_t s) {
                a->page_size, a->max_pages, a->splits, a->sm_scale, a->workspace,
                a->workspace_bytes};
   return launch_attention<kFmtZf>(c, a->arena, a->meta, nullptr, s);
+}
+
+extern "C" int kvz_decode_attention_noalloc(const kvz_attn_args* a, hipStream_t s) {
+  if (!a) return set_error(KVZ_EINVAL, "args is null");
+  if (a->batch < 0 || a->num_q_heads <= 0 || a->num_kv_heads <= 0 || a->max_pages < 0 ||
+      a->splits < 0 || a->splits > kMaxSplits)
+    return set_error(KVZ_EINVAL, "bad sizes");
+  if (a->batch == 0) return KVZ_OK;
+  if (a->num_q_heads % a->num_kv_heads != 0)
+    return set_error(KVZ_EINVAL, "num_q_heads must be a multiple of num_kv_heads");
+  // the same split count and workspace layout as kvz_decode_attention
+  const int S = a->splits ? a->splits : choose_splits(a->batch, a->num_kv_heads, a->max_pages, device_cus());
+  uint64_t cnt_bytes, ml_bytes, need;
+  workspace_layout(a->batch, a->num_q_heads, a->num_kv_heads, S, &cnt_bytes, &ml_bytes, &need);
+  if (cnt_bytes > kScratchCounterBytes)
+    return set_error(KVZ_EINVAL, "batch * num_kv_heads above 16384: too large for the allocation-free call");
+  if (need - cnt_bytes > kScratchBytes - kScratchCounterBytes)
+    return set_error(KVZ_EINVAL, "the partial results of these sizes need " + std::to_string(need - cnt_bytes) +
+                                     " bytes, above the allocation-free call's " +
+                                     std::to_string(kScratchBytes - kScratchCounterBytes));
+  uint8_t* base = nullptr;
+  const int rc = scratch_of_current_device(s, &base);
+  if (rc != KVZ_OK) return rc;
+  // The counters of this call end where the fixed counter area ends, so its partial results
+  // start right after that area whatever the batch: counters of calls with other sizes (all
+  // zero between calls) never overlap partial results.
+  kvz_attn_args b = *a;
+  b.workspace = base + (kScratchCounterBytes - cnt_bytes);
+  b.workspace_bytes = kScratchBytes - (kScratchCounterBytes - cnt_bytes);
+  b.splits = S;
+  return kvz_decode_attention(&b, s);
 }
 
 extern "C" int kvz_gaac_decode_attention(const kvz_attn_args* a, const uint8_t* d_bases,

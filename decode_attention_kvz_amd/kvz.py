@@ -44,7 +44,7 @@ EXPORTED = [
     "kvz_pool_capacity", "kvz_gaac_calibrate", "kvz_gaac_encode_pages", "kvz_gaac_decompress_pages",
     "kvz_gaac_decode_attention", "kvz_fp8_pool_state_bytes", "kvz_fp8_pool_init",
     "kvz_fp8_calibrate", "kvz_fp8_encode_pages", "kvz_fp8_decompress_pages", "kvz_fp8_pack_pages",
-    "kvz_fp8_decode_attention", "kvz_fp8_raw_decode_attention",
+    "kvz_fp8_decode_attention", "kvz_fp8_raw_decode_attention", "kvz_decode_attention_noalloc",
 ]
 
 
@@ -156,6 +156,7 @@ _sig = {
     "kvz_fp8_pack_pages": ([_vp, _vp, ctypes.c_int64, ctypes.c_int32, _vp], ctypes.c_int),
     "kvz_fp8_decode_attention": ([ctypes.POINTER(Fp8AttnArgs), _vp], ctypes.c_int),
     "kvz_fp8_raw_decode_attention": ([ctypes.POINTER(Fp8AttnArgs), _vp], ctypes.c_int),
+    "kvz_decode_attention_noalloc": ([ctypes.POINTER(AttnArgs), _vp], ctypes.c_int),
 }
 for _name, (_args, _ret) in _sig.items():
     _f = getattr(_lib, _name)
@@ -279,7 +280,7 @@ def kvz_attn_workspace_bytes(batch, num_q_heads, num_kv_heads, max_pages, splits
 
 
 def _check_attn_common(q, out, block_table, seq_lens, n_comp_pages, workspace, hkv,
-                       tail=None, tail_dtype=None, tail_bytes_per_value=2):
+                       tail=None, tail_dtype=None, tail_bytes_per_value=2, allow_no_workspace=False):
     """The arguments every decode-attention call shares: q [B,Hq,128] bf16, out [B,Hq,128] fp32,
     block_table [B,max_pages] int32, seq_lens / n_comp_pages [B] int32, the tail page
     [B,2,Hkv,16,128] (or None) and the workspace."""
@@ -290,7 +291,8 @@ def _check_attn_common(q, out, block_table, seq_lens, n_comp_pages, workspace, h
     _dev("block_table", block_table, dtype=torch.int32, shape=(bsz, None))
     _dev("seq_lens", seq_lens, dtype=torch.int32, shape=(bsz,))
     _dev("n_comp_pages", n_comp_pages, dtype=torch.int32, shape=(bsz,))
-    _dev("workspace", workspace)
+    if workspace is not None or not allow_no_workspace:
+        _dev("workspace", workspace)
     if tail is not None:
         _dev("tail", tail, dtype=tail_dtype, min_bytes=bsz * 2 * hkv * 16 * 128 * tail_bytes_per_value)
 
@@ -329,6 +331,26 @@ def kvz_decode_attention(q, out, arena, meta, block_table, seq_lens, n_comp_page
     a = _attn_args(q, out, arena, meta, block_table, seq_lens, n_comp_pages, tail, sm_scale,
                    workspace, splits)
     _check(_lib.kvz_decode_attention(ctypes.byref(a), _stream(stream)))
+
+
+def kvz_decode_attention_noalloc(q, out, arena, meta, block_table, seq_lens, n_comp_pages, tail,
+                                 sm_scale: float, splits: int = 0, stream=None) -> None:
+    """kvz_decode_attention without a workspace: the library's device-resident scratch holds the
+    partial results (no device memory is allocated).  Same arguments otherwise."""
+    _check_meta(meta)
+    _dev("arena", arena)
+    _check_attn_common(q, out, block_table, seq_lens, n_comp_pages, None, meta.shape[1],
+                       tail=tail, tail_dtype=_torch().bfloat16, allow_no_workspace=True)
+    bsz, hq, hd = q.shape
+    a = AttnArgs(q=q.data_ptr(), out=out.data_ptr(), arena=arena.data_ptr(),
+                 arena_bytes=arena.numel() * arena.element_size(), meta=meta.data_ptr(),
+                 n_phys_pages=meta.shape[0], block_table=block_table.data_ptr(),
+                 seq_lens=seq_lens.data_ptr(), n_comp_pages=n_comp_pages.data_ptr(),
+                 tail=None if tail is None else tail.data_ptr(), batch=bsz, num_q_heads=hq,
+                 num_kv_heads=meta.shape[1], head_dim=hd, page_size=16,
+                 max_pages=block_table.shape[1], splits=splits, sm_scale=sm_scale,
+                 workspace=None, workspace_bytes=0)
+    _check(_lib.kvz_decode_attention_noalloc(ctypes.byref(a), _stream(stream)))
 
 
 def kvz_gaac_decode_attention(q, out, arena, meta, bases, block_table, seq_lens, n_comp_pages,

@@ -39,7 +39,8 @@
  * Conventions for every call:
  *   - Pointers named d_* or documented as "device" point to device memory owned by the caller
  *     (e.g. torch tensors).  The library never allocates or frees device memory; it owns only
- *     the small host-side pool handle.
+ *     the small host-side pool handle and, for kvz_decode_attention_noalloc, a static
+ *     device-resident scratch array (part of the loaded library, not a run-time allocation).
  *   - Calls that take a hipStream_t enqueue work on that stream and return without waiting,
  *     except kvz_pool_stats, which synchronizes the stream.
  *   - Return value: KVZ_OK or a negative KVZ_E* code; kvz_last_error() gives text (per thread).
@@ -407,6 +408,21 @@ int kvz_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_
  * the pieces' partial softmax states inside the attention kernel; with more, a second small
  * kernel merges them. */
 int kvz_decode_attention(const kvz_attn_args* a, hipStream_t s);
+
+/* Allocation-free variant of kvz_decode_attention, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and result, with the split-K partial results and merge counters in a
+ * device-resident scratch array of the library (16 MiB per GPU, held while the library is
+ * loaded) instead of a workspace.  a->workspace and a->workspace_bytes are ignored; every other
+ * argument is as for kvz_decode_attention.  The first call on a device looks up the array's
+ * device address (hipGetSymbolAddress) and zero-fills its counter area on stream s; nothing is
+ * allocated, by this or any later call.  Limits (KVZ_EINVAL beyond them, nothing launched):
+ * batch * num_kv_heads <= 16384, and batch * num_kv_heads * splits * (num_q_heads /
+ * num_kv_heads) * 520 bytes of partial results (rounded up to 256-byte parts) <= 16 MiB - 64 KiB,
+ * with splits the automatic count when 0.  All calls on one GPU share its array: calls that
+ * overlap in time on one GPU (other streams, other threads) race and give undefined results;
+ * order them on one stream.  Each completed call leaves the counters at zero. */
+int kvz_decode_attention_noalloc(const kvz_attn_args* a, hipStream_t s);
 
 /* Lay out n_pages natural BF16 pages (device [n_pages][2][Hkv][16][128]) as the baseline's
  * pages (device [n_pages][2][Hkv][4][64][16 B], the raw chunk layout). */
