@@ -31,6 +31,7 @@
 
 #include <math.h>
 
+#include <algorithm>
 #include <mutex>
 
 namespace kvz {
@@ -56,6 +57,7 @@ struct AttnParams {
   float* ws_ml;                 // [units][G][2]
   float* ws_o;                  // [units][G][128]
   uint32_t* ws_cnt;             // [Hkv][B] pieces of (sequence, KV head) done; zero between calls
+  uint32_t* ws_status;          // sticky flags (KVZ_WS_*): a counter found outside [0, pieces)
   int merge_in_kernel;          // the last piece of a (sequence, KV head) merges (no second launch)
   uint64_t arena_bytes;         // compressed only: groups must end 16 bytes before this
   int B, Hq, Hkv, G, max_pages, S, n_phys;
@@ -1101,6 +1103,11 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
     const uint32_t before = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint32_t last = before + 1u == (uint32_t)so.sb ? 1u : 0u;
     if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // a count at or above the number of pieces cannot come from a zeroed workspace (one that
+    // was not zero-filled, or reused for a larger batch * KV heads beyond the fixed counter
+    // area): this call's merge of the pair is then unreliable; the flag stays for the host
+    if (before >= (uint32_t)so.sb)
+      __hip_atomic_fetch_or(p.ws_status, KVZ_WS_BAD_COUNTER, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = last;
   }
   __syncthreads();
@@ -1112,35 +1119,59 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
     const float* o = p.ws_o + u0 * p.G * KVZ_HEAD_DIM + (size_t)h * KVZ_HEAD_DIM + d;
     auto ld = [](const float* q) { return __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
     const size_t mls = (size_t)p.G * 2, os = (size_t)p.G * KVZ_HEAD_DIM;
-    // pieces 0..3 in one round trip; a ragged batch's longer sequences loop over the rest
-    float mv[kInKernelMergeMax], lv[kInKernelMergeMax], ov[kInKernelMergeMax];
+    // Up to four pieces (the split counts that merge here): every load in one round trip.  A
+    // ragged batch can give a longer sequence more pieces: they are taken four at a time, each
+    // group's loads issued together, the maximum first, then the sums - in piece order either
+    // way, so the result does not depend on which piece merges.
+    float M = -INFINITY, L = 0.f, O = 0.f;
+    if (so.sb <= kInKernelMergeMax) {
+      float mv[kInKernelMergeMax], lv[kInKernelMergeMax], ov[kInKernelMergeMax];
 #pragma unroll
-    for (int i = 0; i < kInKernelMergeMax; ++i) {
-      if (i < so.sb) {
-        mv[i] = ld(ml + i * mls);
-        lv[i] = ld(ml + i * mls + 1);
-        ov[i] = ld(o + i * os);
+      for (int i = 0; i < kInKernelMergeMax; ++i) {
+        if (i < so.sb) {
+          mv[i] = ld(ml + i * mls);
+          lv[i] = ld(ml + i * mls + 1);
+          ov[i] = ld(o + i * os);
+        }
       }
-    }
-    float M = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < kInKernelMergeMax; ++i)
-      if (i < so.sb) M = fmaxf(M, mv[i]);
-    for (int i = kInKernelMergeMax; i < so.sb; ++i) M = fmaxf(M, ld(ml + i * mls));
-    float L = 0.f, O = 0.f;
+      for (int i = 0; i < kInKernelMergeMax; ++i)
+        if (i < so.sb) M = fmaxf(M, mv[i]);
 #pragma unroll
-    for (int i = 0; i < kInKernelMergeMax; ++i) {
-      if (i < so.sb) {
-        const float c = mv[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(to_log2(mv[i] - M, c_log2));
-        L += c * lv[i];
-        O += c * ov[i];
+      for (int i = 0; i < kInKernelMergeMax; ++i) {
+        if (i < so.sb) {
+          const float c = mv[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(to_log2(mv[i] - M, c_log2));
+          L += c * lv[i];
+          O += c * ov[i];
+        }
       }
-    }
-    for (int i = kInKernelMergeMax; i < so.sb; ++i) {
-      const float m = ld(ml + i * mls);
-      const float c = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(to_log2(m - M, c_log2));
-      L += c * ld(ml + i * mls + 1);
-      O += c * ld(o + i * os);
+    } else {
+      for (int i0 = 0; i0 < so.sb; i0 += kInKernelMergeMax) {
+        float mv[kInKernelMergeMax];
+#pragma unroll
+        for (int i = 0; i < kInKernelMergeMax; ++i) mv[i] = i0 + i < so.sb ? ld(ml + (i0 + i) * mls) : -INFINITY;
+#pragma unroll
+        for (int i = 0; i < kInKernelMergeMax; ++i) M = fmaxf(M, mv[i]);
+      }
+      for (int i0 = 0; i0 < so.sb; i0 += kInKernelMergeMax) {
+        float mv[kInKernelMergeMax], lv[kInKernelMergeMax], ov[kInKernelMergeMax];
+#pragma unroll
+        for (int i = 0; i < kInKernelMergeMax; ++i) {
+          if (i0 + i < so.sb) {
+            mv[i] = ld(ml + (i0 + i) * mls);
+            lv[i] = ld(ml + (i0 + i) * mls + 1);
+            ov[i] = ld(o + (i0 + i) * os);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < kInKernelMergeMax; ++i) {
+          if (i0 + i < so.sb) {
+            const float c = mv[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(to_log2(mv[i] - M, c_log2));
+            L += c * lv[i];
+            O += c * ov[i];
+          }
+        }
+      }
     }
     p.out[((size_t)b * p.Hq + (size_t)kvh * p.G + h) * KVZ_HEAD_DIM + d] = empty_seq ? 0.f : O / L;
   }
@@ -1284,15 +1315,26 @@ int choose_splits(int B, int Hkv, int max_pages, int n_cu, int wgs_per_cu = 1) {
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
-// workspace = [counters: B*Hkv u32][m, l: units*G*2 f32][O: units*G*128 f32], 256-B aligned
-// parts; the counters are zero between calls (zero-filled once by the caller)
-void workspace_layout(int B, int Hq, int Hkv, int S, uint64_t* cnt_bytes, uint64_t* ml_bytes,
-                      uint64_t* total) {
+// workspace = [status: 256 B, word 0 = sticky flags][counters: B*Hkv u32, in an area of at least
+// 64 KiB][m, l: units*G*2 f32][O: units*G*128 f32], 256-B aligned parts.  The status word and the
+// counters are zero between calls (zero-filled once by the caller).  Up to 16384 (sequence, KV
+// head) pairs the counter area has the same place and size for every call, so reusing one
+// workspace across sizes never puts counters over bytes that held partial results.
+constexpr uint64_t kWsStatusBytes = 256;
+constexpr uint64_t kWsMinCounterBytes = 64ull << 10;
+struct WsLayout {
+  uint64_t cnt_off, ml_off, o_off, total;
+};
+WsLayout workspace_layout(int B, int Hq, int Hkv, int S) {
   const uint64_t units = (uint64_t)B * Hkv * S;
   const uint64_t G = Hkv > 0 ? (uint64_t)(Hq / Hkv) : 0;
-  *cnt_bytes = align256((uint64_t)B * Hkv * sizeof(uint32_t));
-  *ml_bytes = align256(units * G * 2 * sizeof(float));
-  *total = *cnt_bytes + *ml_bytes + align256(units * G * KVZ_HEAD_DIM * sizeof(float));
+  const uint64_t cnt = std::max(kWsMinCounterBytes, align256((uint64_t)B * Hkv * sizeof(uint32_t)));
+  WsLayout w;
+  w.cnt_off = kWsStatusBytes;
+  w.ml_off = w.cnt_off + cnt;
+  w.o_off = w.ml_off + align256(units * G * 2 * sizeof(float));
+  w.total = w.o_off + align256(units * G * KVZ_HEAD_DIM * sizeof(float));
+  return w;
 }
 
 struct CommonArgs {
@@ -1344,9 +1386,8 @@ int launch_attention(const CommonArgs& a, const uint8_t* kv, const kvz_group_met
   const int S = a.splits ? a.splits
                          : choose_splits(a.batch, a.num_kv_heads, a.max_pages, device_cus(),
                                          CODED ? kCodedWgsPerCu : 1);
-  uint64_t cnt_bytes, ml_bytes, need;
-  workspace_layout(a.batch, a.num_q_heads, a.num_kv_heads, S, &cnt_bytes, &ml_bytes, &need);
-  if (a.workspace_bytes < need) return set_error(KVZ_EINVAL, "workspace too small");
+  const WsLayout wl = workspace_layout(a.batch, a.num_q_heads, a.num_kv_heads, S);
+  if (a.workspace_bytes < wl.total) return set_error(KVZ_EINVAL, "workspace too small");
   const uint64_t units = (uint64_t)a.batch * a.num_kv_heads * S;
   if (units > 0x7FFFFFFFull) return set_error(KVZ_EINVAL, "too many units");
 
@@ -1360,9 +1401,11 @@ int launch_attention(const CommonArgs& a, const uint8_t* kv, const kvz_group_met
   p.tail = a.tail;
   p.bases = bases;
   p.out = a.out;
-  p.ws_cnt = reinterpret_cast<uint32_t*>(a.workspace);
-  p.ws_ml = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(a.workspace) + cnt_bytes);
-  p.ws_o = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(a.workspace) + cnt_bytes + ml_bytes);
+  uint8_t* ws = static_cast<uint8_t*>(a.workspace);
+  p.ws_status = reinterpret_cast<uint32_t*>(ws);
+  p.ws_cnt = reinterpret_cast<uint32_t*>(ws + wl.cnt_off);
+  p.ws_ml = reinterpret_cast<float*>(ws + wl.ml_off);
+  p.ws_o = reinterpret_cast<float*>(ws + wl.o_off);
   // (a ragged batch can still give one sequence more pieces: the merge loops over them)
   p.merge_in_kernel = S <= kInKernelMergeMax;
   p.arena_bytes = a.arena_bytes;
@@ -1393,10 +1436,11 @@ int launch_attention(const CommonArgs& a, const uint8_t* kv, const kvz_group_met
 }
 
 // Device-resident scratch of the allocation-free attention call (kvz_decode_attention_noalloc):
-// the merge counters in a fixed area at the front (every call leaves them zero), then the
-// partial softmax states.  One copy per GPU, held while the library is loaded.
+// a workspace of 16 MiB in the layout above (status word and the fixed 64 KiB counter area,
+// which every call leaves zero, then the partial softmax states).  One copy per GPU, held while
+// the library is loaded.
 constexpr uint64_t kScratchBytes = 16ull << 20;
-constexpr uint64_t kScratchCounterBytes = 64ull << 10;   // up to 16384 (sequence, KV head) pairs
+constexpr uint64_t kScratchZeroBytes = kWsStatusBytes + kWsMinCounterBytes;
 constexpr int kMaxDevices = 64;
 
 __global__ void zero_words_kernel(uint32_t* p, uint32_t n) {
@@ -1430,7 +1474,7 @@ int scratch_of_current_device(hipStream_t s, uint8_t** out) {
     if (!ptr || (reinterpret_cast<uintptr_t>(ptr) & 255u))
       return set_error(KVZ_EHIP, "scratch symbol has no 256-byte aligned device address");
     hipLaunchKernelGGL(zero_words_kernel, dim3(64), dim3(256), 0, s, static_cast<uint32_t*>(ptr),
-                       (uint32_t)(kScratchCounterBytes / 4));
+                       (uint32_t)(kScratchZeroBytes / 4));
     rc = check_hip(hipGetLastError(), "scratch counter fill");
     if (rc != KVZ_OK) return rc;
     g_scratch_ptr[dev] = static_cast<uint8_t*>(ptr);
@@ -1449,9 +1493,7 @@ extern "C" int kvz_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int3
   // sized for the format with the most splits, so one workspace serves every format
   const int S = splits ? splits
                        : choose_splits(batch, num_kv_heads, max_pages, device_cus(), kCodedWgsPerCu);
-  uint64_t cnt, ml, total;
-  workspace_layout(batch, num_q_heads, num_kv_heads, S, &cnt, &ml, &total);
-  *bytes = total < 256 ? 256 : total;
+  *bytes = workspace_layout(batch, num_q_heads, num_kv_heads, S).total;
   return KVZ_OK;
 }
 
@@ -1474,25 +1516,43 @@ extern "C" int kvz_decode_attention_noalloc(const kvz_attn_args* a, hipStream_t 
     return set_error(KVZ_EINVAL, "num_q_heads must be a multiple of num_kv_heads");
   // the same split count and workspace layout as kvz_decode_attention
   const int S = a->splits ? a->splits : choose_splits(a->batch, a->num_kv_heads, a->max_pages, device_cus());
-  uint64_t cnt_bytes, ml_bytes, need;
-  workspace_layout(a->batch, a->num_q_heads, a->num_kv_heads, S, &cnt_bytes, &ml_bytes, &need);
-  if (cnt_bytes > kScratchCounterBytes)
+  if ((int64_t)a->batch * a->num_kv_heads > (int64_t)(kWsMinCounterBytes / 4))
     return set_error(KVZ_EINVAL, "batch * num_kv_heads above 16384: too large for the allocation-free call");
-  if (need - cnt_bytes > kScratchBytes - kScratchCounterBytes)
-    return set_error(KVZ_EINVAL, "the partial results of these sizes need " + std::to_string(need - cnt_bytes) +
+  const WsLayout wl = workspace_layout(a->batch, a->num_q_heads, a->num_kv_heads, S);
+  if (wl.total > kScratchBytes)
+    return set_error(KVZ_EINVAL, "the partial results of these sizes need " + std::to_string(wl.total - wl.ml_off) +
                                      " bytes, above the allocation-free call's " +
-                                     std::to_string(kScratchBytes - kScratchCounterBytes));
+                                     std::to_string(kScratchBytes - wl.ml_off));
   uint8_t* base = nullptr;
   const int rc = scratch_of_current_device(s, &base);
   if (rc != KVZ_OK) return rc;
-  // The counters of this call end where the fixed counter area ends, so its partial results
-  // start right after that area whatever the batch: counters of calls with other sizes (all
-  // zero between calls) never overlap partial results.
+  // the counter area is the fixed 64 KiB one for every size accepted here, so counters of calls
+  // with other sizes (all zero between calls) never overlap partial results
   kvz_attn_args b = *a;
-  b.workspace = base + (kScratchCounterBytes - cnt_bytes);
-  b.workspace_bytes = kScratchBytes - (kScratchCounterBytes - cnt_bytes);
+  b.workspace = base;
+  b.workspace_bytes = kScratchBytes;
   b.splits = S;
   return kvz_decode_attention(&b, s);
+}
+
+extern "C" int kvz_attn_workspace_status(const void* d_workspace, uint32_t* flags, hipStream_t s) {
+  if (!flags) return set_error(KVZ_EINVAL, "flags is null");
+  const uint8_t* ws = static_cast<const uint8_t*>(d_workspace);
+  if (!ws) {
+    uint8_t* base = nullptr;
+    const int rc = scratch_of_current_device(s, &base);
+    if (rc != KVZ_OK) return rc;
+    ws = base;
+  } else if (((uintptr_t)ws) & 255u) {
+    return set_error(KVZ_EINVAL, "workspace must be 256-byte aligned");
+  }
+  uint32_t v = 0;
+  int rc = check_hip(hipMemcpyAsync(&v, ws, sizeof(v), hipMemcpyDeviceToHost, s), "status copy");
+  if (rc != KVZ_OK) return rc;
+  rc = check_hip(hipStreamSynchronize(s), "hipStreamSynchronize");
+  if (rc != KVZ_OK) return rc;
+  *flags = v;
+  return KVZ_OK;
 }
 
 extern "C" int kvz_gaac_decode_attention(const kvz_attn_args* a, const uint8_t* d_bases,

@@ -31,6 +31,7 @@ KVZ_OFF_NONE = 0xFFFFFFFF
 KVZ_KIND_K = 0
 KVZ_KIND_V = 1
 KVZ_ENC_FORCE_RAW = 1
+KVZ_WS_BAD_COUNTER = 1
 GRANULE = 256
 KVZ_FP8_E4M3 = 0
 KVZ_FP8_E5M2 = 1
@@ -45,6 +46,7 @@ EXPORTED = [
     "kvz_gaac_decode_attention", "kvz_fp8_pool_state_bytes", "kvz_fp8_pool_init",
     "kvz_fp8_calibrate", "kvz_fp8_encode_pages", "kvz_fp8_decompress_pages", "kvz_fp8_pack_pages",
     "kvz_fp8_decode_attention", "kvz_fp8_raw_decode_attention", "kvz_decode_attention_noalloc",
+    "kvz_attn_workspace_status",
 ]
 
 
@@ -157,6 +159,7 @@ _sig = {
     "kvz_fp8_decode_attention": ([ctypes.POINTER(Fp8AttnArgs), _vp], ctypes.c_int),
     "kvz_fp8_raw_decode_attention": ([ctypes.POINTER(Fp8AttnArgs), _vp], ctypes.c_int),
     "kvz_decode_attention_noalloc": ([ctypes.POINTER(AttnArgs), _vp], ctypes.c_int),
+    "kvz_attn_workspace_status": ([_vp, ctypes.POINTER(ctypes.c_uint32), _vp], ctypes.c_int),
 }
 for _name, (_args, _ret) in _sig.items():
     _f = getattr(_lib, _name)
@@ -277,6 +280,17 @@ def kvz_attn_workspace_bytes(batch, num_q_heads, num_kv_heads, max_pages, splits
     _check(_lib.kvz_attn_workspace_bytes(batch, num_q_heads, num_kv_heads, max_pages, splits,
                                          ctypes.byref(out)))
     return out.value
+
+
+def kvz_attn_workspace_status(workspace=None, stream=None) -> int:
+    """The sticky KVZ_WS_* flags of an attention workspace (None: the allocation-free call's
+    scratch on the current device); synchronizes the stream."""
+    if workspace is not None:
+        _dev("workspace", workspace)
+    flags = ctypes.c_uint32()
+    _check(_lib.kvz_attn_workspace_status(None if workspace is None else workspace.data_ptr(),
+                                          ctypes.byref(flags), _stream(stream)))
+    return flags.value
 
 
 def _check_attn_common(q, out, block_table, seq_lens, n_comp_pages, workspace, hkv,

@@ -76,6 +76,10 @@ enum {
 #define KVZ_KIND_K 0u
 #define KVZ_KIND_V 1u
 #define KVZ_ENC_FORCE_RAW 1u    /* kvz_encode_pages flag: store every block raw */
+#define KVZ_WS_BAD_COUNTER 1u   /* kvz_attn_workspace_status flag: a merge counter was found at or
+                                   above its pair's number of pieces (workspace not zero-filled,
+                                   or reused beyond the fixed counter area); the merge of that
+                                   (sequence, KV head) in that call is unreliable */
 
 /* 8-byte metadata of one 4-block K or V group ([ZF] metadata paragraph). */
 typedef struct {
@@ -394,11 +398,15 @@ int kvz_fp8_raw_decode_attention(const kvz_fp8_attn_args* a, hipStream_t s);
  * kvz_gaac_decode_attention, kvz_fp8_decode_attention, kvz_fp8_raw_decode_attention) need for
  * these sizes.  splits = 0: enough for the automatic split count of every one of them (the
  * coded tiles - group-adaptive and FP8 - use twice as many splits).
- * The workspace must be zero-filled once, before its first call: its first
- * align256(4 * batch * num_kv_heads) bytes are per-(sequence, KV head) counters of the merge
- * inside the attention kernel, which every completed call leaves at zero.  Zero-fill it again
- * before reusing it for a larger batch * num_kv_heads (the counters then reach into bytes that
- * held partial results). */
+ * The workspace must be zero-filled once, before its first call.  Layout: a 256-byte status
+ * area (word 0: sticky KVZ_WS_* flags, see kvz_attn_workspace_status), then the per-(sequence,
+ * KV head) counters of the merge inside the attention kernel in an area of
+ * max(64 KiB, align256(4 * batch * num_kv_heads)) bytes, then the partial results.  Every
+ * completed call leaves the counters at zero.  Up to batch * num_kv_heads = 16384 the counter
+ * area is the same for every size, so one workspace can be reused across sizes without a new
+ * fill; beyond that, zero-fill it again before reusing it for a larger batch * num_kv_heads (its
+ * counters would reach into bytes that held partial results - a call that finds such a count
+ * sets KVZ_WS_BAD_COUNTER). */
 int kvz_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                              int32_t max_pages, int32_t splits, uint64_t* bytes);
 
@@ -415,14 +423,22 @@ int kvz_decode_attention(const kvz_attn_args* a, hipStream_t s);
  * device-resident scratch array of the library (16 MiB per GPU, held while the library is
  * loaded) instead of a workspace.  a->workspace and a->workspace_bytes are ignored; every other
  * argument is as for kvz_decode_attention.  The first call on a device looks up the array's
- * device address (hipGetSymbolAddress) and zero-fills its counter area on stream s; nothing is
- * allocated, by this or any later call.  Limits (KVZ_EINVAL beyond them, nothing launched):
- * batch * num_kv_heads <= 16384, and batch * num_kv_heads * splits * (num_q_heads /
- * num_kv_heads) * 520 bytes of partial results (rounded up to 256-byte parts) <= 16 MiB - 64 KiB,
- * with splits the automatic count when 0.  All calls on one GPU share its array: calls that
+ * device address (hipGetSymbolAddress) and zero-fills its status and counter areas on stream
+ * s; nothing is allocated, by this or any later call.  Limits (KVZ_EINVAL beyond them, nothing
+ * launched): batch * num_kv_heads <= 16384, and batch * num_kv_heads * splits * (num_q_heads /
+ * num_kv_heads) * 520 bytes of partial results (rounded up to 256-byte parts) <= 16 MiB - 64 KiB
+ * - 256 B, with splits the automatic count when 0.  All calls on one GPU share its array: calls that
  * overlap in time on one GPU (other streams, other threads) race and give undefined results;
  * order them on one stream.  Each completed call leaves the counters at zero. */
 int kvz_decode_attention_noalloc(const kvz_attn_args* a, hipStream_t s);
+
+/* The sticky status flags (KVZ_WS_*) of an attention workspace (device, 256-B aligned), or with
+ * d_workspace NULL of kvz_decode_attention_noalloc's scratch on the current device: synchronizes
+ * stream s, then copies the status word into *flags (0 when every call so far found its merge
+ * counters consistent).  The flags stay set until the caller zero-fills the workspace again
+ * (the scratch of the allocation-free call is never refilled: a set flag there means a call
+ * was abandoned or overlapped another).  KVZ_EINVAL for a null flags pointer. */
+int kvz_attn_workspace_status(const void* d_workspace, uint32_t* flags, hipStream_t s);
 
 /* Lay out n_pages natural BF16 pages (device [n_pages][2][Hkv][16][128]) as the baseline's
  * pages (device [n_pages][2][Hkv][4][64][16 B], the raw chunk layout). */

@@ -58,6 +58,8 @@ def test_noalloc_equals_workspace_call_twice_with_smaller_second(splits):
     # the first shape again after the smaller one: nothing left over changes it
     _, again = _both(arena1, layer1, q1, splits)
     assert torch.equal(again, ref1)
+    # every merge counter of the scratch was consistent
+    assert kvz.kvz_attn_workspace_status(None) == 0
 
 
 def test_noalloc_rejects_sizes_beyond_its_scratch():
