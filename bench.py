@@ -48,7 +48,11 @@ VARIANT_LAYERS, VARIANT_U_MAX = 8, 3.0
 OTHER_CONFIGS = [
     ("llama2k", 32, 32, 8, 128, 32, 3.0, 0.05, 1, False),
     ("single131k", 1, 32, 8, 8192, 4, 3.0, 0.10, 4, True),
+    # a ragged batch: one 32K-token sequence among 15 of 2K tokens (automatic split count 2, so
+    # the long sequence's many pieces are merged inside the attention kernel)
+    ("ragged32k", 16, 32, 8, [2048] + [128] * 15, 8, 3.0, 0.05, 5, False),
 ]
+BREAKDOWN_LAYERS = 8
 GAAC_LAYERS = 8
 FP8_LAYERS = 8
 N_PHYS = B * N_COMP
@@ -61,6 +65,20 @@ KERNEL_SOURCES = [os.path.join(ROOT, "decode_attention_kvz_amd", "csrc", f)
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def exponent_entropy(pages) -> dict:
+    """Shannon entropy in bits of the BF16 exponent field (bits 14..7) over the K values, the V
+    values and both, of pages [..., 2, Hkv, 16, 128] (the measure of the GAAC page, "Compression
+    Effectiveness and Generality", and the ExANS page, "Entropy and effective alphabet size")."""
+    import torch
+    e = (pages.contiguous().view(torch.int16).to(torch.int32) >> 7) & 0xFF
+    res = {}
+    for name, sel in (("k", e.select(-4, 0)), ("v", e.select(-4, 1)), ("kv", e)):
+        c = torch.bincount(sel.reshape(-1), minlength=256).double()
+        pr = c[c > 0] / c.sum()
+        res[name] = round(float(-(pr * torch.log2(pr)).sum()), 3)
+    return res
 
 
 def kernel_source_sha() -> str:
@@ -83,10 +101,11 @@ def baseline_bytes_per_layer() -> float:
             + B * HQ * 128 * 2 + B * HQ * 128 * 4)
 
 
-def build_layers(arena, n_layers, u_max, seed, with_baseline, dev, encode_us=None):
+def build_layers(arena, n_layers, u_max, seed, with_baseline, dev, encode_us=None, entropy=None):
     """Encode n_layers layers of the workload into `arena` (the prompt's pages, in bulk); return
     per-layer device buffers.  encode_us, if a list, receives each layer's kvz_encode_pages time
-    (HIP events around the call; item records already on the device)."""
+    (HIP events around the call; item records already on the device); entropy, if a dict,
+    receives the exponent entropy of layer 0's pages."""
     import torch
     from decode_attention_kvz_amd import kvz, paged, synth
     rng = np.random.default_rng(seed)
@@ -95,6 +114,8 @@ def build_layers(arena, n_layers, u_max, seed, with_baseline, dev, encode_us=Non
     for layer in range(n_layers):
         pages = synth.kv_pages(B, N_COMP + 1, HKV, seed=seed, layer=layer, u_max=u_max,
                                forced_frac=FORCED, device=dev)
+        if entropy is not None and layer == 0:
+            entropy.update(exponent_entropy(pages))
         block_table = rng.permutation(N_PHYS).reshape(B, N_COMP).astype(np.int32)
         meta = paged.new_meta_table(N_PHYS, HKV, device=dev)
         items = paged.page_items(pages, [(b, p) for b in range(B) for p in range(N_COMP)], meta,
@@ -141,6 +162,10 @@ def main():
                     help="skip the online page-completion leg (64 sequences, 32 layers)")
     ap.add_argument("--no-other", action="store_true",
                     help="skip the other workload shapes (2K batch of 32, one 131K sequence)")
+    ap.add_argument("--breakdown", action="store_true",
+                    help="only the attention time breakdown (loads / restore / computation, and "
+                         "the BF16 and decompress-first pipelines) at the 8K and 2K shapes")
+    ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="for hardware-counter runs: one layer of fused and baseline attention "
                          "(3 launches each) and a 1 GiB device copy as a traffic reference")
@@ -172,12 +197,17 @@ def main():
     if args.pmc_probe:
         pmc_probe(args, dev)
         return
+    if args.breakdown:
+        print(json.dumps({"breakdown": breakdown(args, dev)}), flush=True)
+        return
     n_layers = args.layers
 
     # ---------------- setup --------------------------------------------------------------
     arena = paged.SlotArena(n_layers * (N_PHYS + B) * HKV * 2 * 4096 + (16 << 20), device=dev)
     enc_layer_us = []
-    layers = build_layers(arena, n_layers, U_MAX, SEED, not args.no_baseline, dev, enc_layer_us)
+    entropy = {}
+    layers = build_layers(arena, n_layers, U_MAX, SEED, not args.no_baseline, dev, enc_layer_us,
+                          entropy)
     seq_lens = torch.full((B,), CTX, dtype=torch.int32, device=dev)
     n_comp = torch.full((B,), N_COMP, dtype=torch.int32, device=dev)
     ws = paged.workspace(B, HQ, HKV, N_COMP, args.splits, device=dev)
@@ -287,7 +317,7 @@ def main():
 
     for L in layers:
         L.pop("store", None)          # the baseline's stores are no longer needed
-    dfirst = decompress_first(args, arena, layers, seq_lens, n_comp, ws)
+    dfirst = decompress_first(args, arena, layers, seq_lens, n_comp, ws, N_PHYS, HKV)
     traffic = committed_traffic()
     read_peak = stream_read_peak(timed)
     variant = None if args.no_variant else compressible_variant(args, dev, seq_lens, n_comp, ws)
@@ -297,6 +327,7 @@ def main():
     fp8_leg = None if args.no_fp8 else {name: fp8_format(args, dev, seq_lens, n_comp, ws, fmt)
                                         for name, fmt in (("e4m3", 0), ("e5m2", 1))}
     del g_attn, g_comp, g_step
+    bdown = None if args.no_breakdown else breakdown(args, dev)
     cpu = None if args.no_cpu_baseline else cpu_baseline(layers, all_cores_child)
 
     value = bf16_kv_layer * n_layers / (ms_step * 1e-3) / 1e9
@@ -335,6 +366,7 @@ def main():
         "encode_free_us_per_step": round(enc_us, 1),
         "effective_attention_GBps": round(bf16_kv_layer / (us_layer_mean * 1e-6) / 1e9, 1),
         "raw_block_fraction": round(raw_frac, 4),
+        "exponent_entropy_bits": entropy,
         "record_bytes_per_layer": int(rec_bytes),
         "bf16_kv_bytes_per_layer": int(bf16_kv_layer),
         "baseline_bf16": baseline,
@@ -350,6 +382,7 @@ def main():
         "online_completion": online,
         "gaac_format": gaac_leg,
         "fp8_formats": fp8_leg,
+        "breakdown": bdown,
     }
     print(json.dumps(line), flush=True)
     arena.close()
@@ -624,19 +657,19 @@ def graph_us_per_layer(run, n_layers, args):
     return float(np.median(ts))
 
 
-def decompress_first(args, arena, layers, seq_lens, n_comp, ws):
+def decompress_first(args, arena, layers, seq_lens, n_comp, ws, n_phys, hkv):
     """The pipeline fused attention replaces: per layer, decompress every page of the layer into
     one reused uncompressed store (kvz_decompress_pages), then the uncompressed attention over
     it.  Also times the decompression alone."""
     import torch
     from decode_attention_kvz_amd import kvz, paged
-    scratch = torch.empty((N_PHYS, 2, HKV, 4, 1024), dtype=torch.uint8, device="cuda")
+    scratch = torch.empty((n_phys, 2, hkv, 4, 1024), dtype=torch.uint8, device="cuda")
 
     def both():
         for L in layers:
             paged.decompress_pages(arena, L["meta"], scratch)
             kvz.kvz_bf16_decode_attention(L["q"], L["out"], scratch, L["block_table"], seq_lens,
-                                          n_comp, L["tail"], SCALE, ws, HKV, args.splits)
+                                          n_comp, L.get("tail"), SCALE, ws, hkv, args.splits)
 
     def decomp_only():
         for L in layers:
@@ -687,7 +720,7 @@ def compressible_variant(args, dev, seq_lens, n_comp, ws):
         res[fused] = graph_us_per_layer(run, VARIANT_LAYERS, args)
     for L in layers:
         del L["store"]
-    dfirst = decompress_first(args, arena, layers, seq_lens, n_comp, ws)
+    dfirst = decompress_first(args, arena, layers, seq_lens, n_comp, ws, N_PHYS, HKV)
     arena.close()
     out = {"label": "same shape, u~U[-3,3] per-channel scale (compressible), 8 layers",
            "raw_block_fraction": round(st["live_raw_blocks"] / (st["live_runs"] * 4), 4),
@@ -744,37 +777,60 @@ def online_completion(args, dev):
     return res
 
 
-def other_config(args, dev, name, bsz, hq, hkv, n_comp, n_layers, u_max, forced, seed, stress):
-    """Another workload shape: n_layers distinct layers of bsz sequences of n_comp compressed
-    pages each (no tail page), fused attention vs the BF16 kernel, per layer (graph replays over
-    the layers, so no layer is served from cache)."""
+def other_layers(dev, bsz, hq, hkv, n_comp, n_layers, u_max, forced, seed, stress, entropy=None):
+    """n_layers distinct layers of bsz sequences with n_comp compressed pages each (an int, or a
+    list per sequence; no tail page), encoded into one arena in random physical order, with the
+    BF16 baseline's pages.  Returns the arena, the layers and the per-sequence page counts."""
     import torch
     from decode_attention_kvz_amd import kvz, paged, synth
-    n_phys = bsz * n_comp
+    counts = list(n_comp) if isinstance(n_comp, (list, tuple)) else [n_comp] * bsz
+    n_phys, max_pages = sum(counts), max(counts)
     arena = paged.SlotArena(n_layers * n_phys * hkv * 2 * 4096 + (16 << 20), device=dev)
     rng = np.random.default_rng(seed)
+    ids = [(b, p) for b in range(bsz) for p in range(counts[b])]
     layers = []
     for layer in range(n_layers):
-        pages = synth.kv_pages(bsz, n_comp, hkv, seed=seed, layer=layer, u_max=u_max,
+        pages = synth.kv_pages(bsz, max_pages, hkv, seed=seed, layer=layer, u_max=u_max,
                                forced_frac=forced, stress=stress, device=dev)
-        bt = rng.permutation(n_phys).reshape(bsz, n_comp).astype(np.int32)
+        if entropy is not None and layer == 0:
+            sel = torch.cat([pages[b, :counts[b]] for b in range(bsz)])
+            entropy.update(exponent_entropy(sel))
+            del sel
+        perm = rng.permutation(n_phys).astype(np.int32)
+        bt = np.zeros((bsz, max_pages), dtype=np.int32)
+        k = 0
+        for b in range(bsz):
+            bt[b, :counts[b]] = perm[k:k + counts[b]]
+            k += counts[b]
         meta = paged.new_meta_table(n_phys, hkv, device=dev)
-        items = paged.page_items(pages, [(b, p) for b in range(bsz) for p in range(n_comp)], meta,
-                                 bt.reshape(-1))
+        items = paged.page_items(pages, ids, meta, perm)
         kvz.kvz_encode_pages(arena.pool, torch.from_numpy(np.ascontiguousarray(items)).to(dev),
                              n_phys * hkv * 2, 0)
-        inv = torch.as_tensor(np.argsort(bt.reshape(-1)), device=dev)
-        store = paged.pack_bf16_pages(pages.reshape(n_phys, 2, hkv, 16, 128)[inv])
+        nat = torch.stack([pages[b, p] for b, p in ids])          # [n_phys, 2, Hkv, 16, 128]
+        store = paged.pack_bf16_pages(nat[torch.as_tensor(np.argsort(perm), device=dev)])
         layers.append(dict(meta=meta, block_table=torch.from_numpy(bt).to(dev), store=store,
                            q=synth.queries(bsz, hq, seed=seed * 1000 + layer, device=dev),
                            out=torch.empty((bsz, hq, 128), dtype=torch.float32, device=dev)))
         torch.cuda.synchronize()
-        del pages, items
+        del pages, items, nat
+    return arena, layers, counts
+
+
+def other_config(args, dev, name, bsz, hq, hkv, n_comp, n_layers, u_max, forced, seed, stress):
+    """Another workload shape: n_layers distinct layers of bsz sequences of n_comp compressed
+    pages each (no tail page), fused attention vs the BF16 kernel and vs decompress-first, per
+    layer (graph replays over the layers, so no layer is served from cache)."""
+    import torch
+    from decode_attention_kvz_amd import kvz, paged
+    entropy = {}
+    arena, layers, counts = other_layers(dev, bsz, hq, hkv, n_comp, n_layers, u_max, forced, seed,
+                                         stress, entropy)
+    n_phys, max_pages = sum(counts), max(counts)
     st = arena.stats()
     rec = st["live_granules"] * 256 / n_layers
-    seq_lens = torch.full((bsz,), 16 * n_comp, dtype=torch.int32, device=dev)
-    ncomp = torch.full((bsz,), n_comp, dtype=torch.int32, device=dev)
-    ws = paged.workspace(bsz, hq, hkv, n_comp, args.splits, device=dev)
+    seq_lens = torch.as_tensor([16 * c for c in counts], dtype=torch.int32, device=dev)
+    ncomp = torch.as_tensor(counts, dtype=torch.int32, device=dev)
+    ws = paged.workspace(bsz, hq, hkv, max_pages, args.splits, device=dev)
     res = {}
     for fused in (True, False):
         def run():
@@ -787,25 +843,111 @@ def other_config(args, dev, name, bsz, hq, hkv, n_comp, n_layers, u_max, forced,
                     kvz.kvz_bf16_decode_attention(L["q"], L["out"], L["store"], L["block_table"],
                                                   seq_lens, ncomp, None, SCALE, ws, hkv, args.splits)
         res[fused] = graph_us_per_layer(run, n_layers, args)
+    for L in layers:
+        del L["store"]
+    dfirst = decompress_first(args, arena, layers, seq_lens, ncomp, ws, n_phys, hkv)
     io = n_phys * (hkv * 16 + 4) + bsz * hq * 128 * (2 + 4)   # metadata, block table, q, out
     alg = rec + io
     alg_bf16 = n_phys * hkv * 2 * 4096 + io
-    out = {"label": f"{bsz} sequence(s) x {16 * n_comp} tokens, {hq}/{hkv} heads, {n_layers} "
-                    f"distinct layers, u~U[-{u_max:g},{u_max:g}], {forced:.0%} forced-raw blocks"
+    shape = (f"{bsz} sequence(s) x {16 * counts[0]} tokens" if len(set(counts)) == 1 else
+             f"{bsz} sequences: " + ", ".join(f"{counts.count(c)} x {16 * c}" for c in sorted(set(counts), reverse=True))
+             + " tokens")
+    out = {"label": f"{shape}, {hq}/{hkv} heads, {n_layers} distinct layers, "
+                    f"u~U[-{u_max:g},{u_max:g}], {forced:.0%} forced-raw blocks"
                     + (", stress values" if stress else ""),
            "record_bytes_per_layer": int(rec),
            "raw_block_fraction": round(st["live_raw_blocks"] / (st["live_runs"] * 4), 4),
+           "exponent_entropy_bits": entropy,
            "fused_us_per_layer": round(res[True], 2),
            "fused_achieved_GBps": round(alg / (res[True] * 1e-6) / 1e9, 1),
            "fused_hbm_frac": round(alg / (res[True] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
            "bf16_us_per_layer": round(res[False], 2),
            "bf16_hbm_frac": round(alg_bf16 / (res[False] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-           "speedup_vs_bf16_kernel": round(res[False] / res[True], 4)}
-    for L in layers:
-        del L["store"]
+           "speedup_vs_bf16_kernel": round(res[False] / res[True], 4),
+           "decompress_first": dfirst,
+           "fused_speedup_vs_decompress_first": round(dfirst["us_per_layer"] / res[True], 3)}
     arena.close()
     log(f"{name}: fused {res[True]:.1f} us/layer ({out['fused_hbm_frac']:.1%} of HBM peak) vs "
-        f"bf16 {res[False]:.1f} ({out['bf16_hbm_frac']:.1%})")
+        f"bf16 {res[False]:.1f} ({out['bf16_hbm_frac']:.1%}), decompress-first "
+        f"{dfirst['us_per_layer']:.1f}")
+    return out
+
+
+def breakdown(args, dev):
+    """The attention time split into KV loading, exponent decoding and computation (GAAC page,
+    "Attention Time Breakdown", Table 5), at the 8K workload and the 2K batch shape, 8 distinct
+    layers each.  The library's compile-time variants of the attention kernel time the page loads
+    alone (KVZ_PART_LOAD) and the loads with the in-register restore (KVZ_PART_LOAD_RESTORE);
+    decoding = (loads + restore) - loads, computation = full call - (loads + restore) (scores,
+    softmax, products, tail page, merge).  The uncompressed kernel gives its own loading and
+    computation, and decompress-first adds the standalone decompression of every page."""
+    import torch
+    from decode_attention_kvz_amd import kvz, paged
+    res = {}
+    # the 8K workload: the first BREAKDOWN_LAYERS layers, with its tail pages
+    arena = paged.SlotArena(BREAKDOWN_LAYERS * (N_PHYS + B) * HKV * 2 * 4096 + (16 << 20), device=dev)
+    layers = build_layers(arena, BREAKDOWN_LAYERS, U_MAX, SEED, True, dev)
+    lens = torch.full((B,), CTX, dtype=torch.int32, device=dev)
+    ncomp = torch.full((B,), N_COMP, dtype=torch.int32, device=dev)
+    ws = paged.workspace(B, HQ, HKV, N_COMP, args.splits, device=dev)
+    res["qwen8k"] = _breakdown_shape(args, arena, layers, lens, ncomp, ws, N_PHYS, HKV,
+                                     "16 sequences x 8192 tokens (511 pages + 16-token tail), "
+                                     "32/8 heads, u~U[-5,5], 5% forced-raw blocks")
+    arena.close()
+    del layers
+    torch.cuda.empty_cache()
+    name, bsz, hq, hkv, n_comp, _, u_max, forced, seed, stress = OTHER_CONFIGS[0]
+    arena, layers, counts = other_layers(dev, bsz, hq, hkv, n_comp, BREAKDOWN_LAYERS, u_max,
+                                         forced, seed, stress)
+    lens = torch.as_tensor([16 * c for c in counts], dtype=torch.int32, device=dev)
+    ncomp = torch.as_tensor(counts, dtype=torch.int32, device=dev)
+    ws = paged.workspace(bsz, hq, hkv, max(counts), args.splits, device=dev)
+    res[name] = _breakdown_shape(args, arena, layers, lens, ncomp, ws, sum(counts), hkv,
+                                 f"{bsz} sequences x {16 * n_comp} tokens, {hq}/{hkv} heads, "
+                                 f"u~U[-{u_max:g},{u_max:g}], {forced:.0%} forced-raw blocks")
+    arena.close()
+    return res
+
+
+def _breakdown_shape(args, arena, layers, lens, ncomp, ws, n_phys, hkv, label):
+    import torch
+    from decode_attention_kvz_amd import kvz, paged
+    n = len(layers)
+
+    def fused(part):
+        def run():
+            for L in layers:
+                kvz.kvz_decode_attention_part(L["q"], L["out"], arena.arena, L["meta"],
+                                              L["block_table"], lens, ncomp, L.get("tail"), SCALE,
+                                              ws, part, args.splits)
+        return graph_us_per_layer(run, n, args)
+
+    def bf16(part):
+        def run():
+            for L in layers:
+                kvz.kvz_bf16_decode_attention_part(L["q"], L["out"], L["store"], L["block_table"],
+                                                   lens, ncomp, L.get("tail"), SCALE, ws, hkv,
+                                                   part, args.splits)
+        return graph_us_per_layer(run, n, args)
+
+    t_full, t_load, t_rest = fused(kvz.KVZ_PART_ALL), fused(kvz.KVZ_PART_LOAD), fused(kvz.KVZ_PART_LOAD_RESTORE)
+    b_full, b_load = bf16(kvz.KVZ_PART_ALL), bf16(kvz.KVZ_PART_LOAD)
+    for L in layers:
+        del L["store"]
+    df = decompress_first(args, arena, layers, lens, ncomp, ws, n_phys, hkv)
+    r2 = lambda x: round(x, 2)
+    out = {"label": label + f", {n} distinct layers; us per layer",
+           "bf16_kernel": {"kv_loading": r2(b_load), "computation": r2(b_full - b_load),
+                           "measured_total": r2(b_full)},
+           "decompress_first": {"kv_loading": r2(b_load),
+                                "exponent_decoding": r2(df["decompress_us_per_layer"]),
+                                "computation": r2(b_full - b_load),
+                                "measured_total": r2(df["us_per_layer"])},
+           "fused": {"kv_loading": r2(t_load), "exponent_decoding": r2(t_rest - t_load),
+                     "computation": r2(t_full - t_rest), "measured_total": r2(t_full)}}
+    log(f"breakdown {label[:40]}...: fused load {t_load:.1f} + decode {t_rest - t_load:.1f} + "
+        f"compute {t_full - t_rest:.1f} = {t_full:.1f}; bf16 load {b_load:.1f} + compute "
+        f"{b_full - b_load:.1f} = {b_full:.1f}; decompress-first {df['us_per_layer']:.1f}")
     return out
 
 
@@ -905,6 +1047,7 @@ def cpu_baseline(layers, all_cores_child=None):
     log(f"cpu baseline: {dt:.1f}s for one layer ({bytes_eff / dt / 1e9:.4f} GB/s)")
     all_cores = cpu_all_cores_result(all_cores_child)
     return {"value": round(bytes_eff / dt / 1e9, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "all_cores": all_cores,
             "sample": "layer 0 of the workload (16 sequences x 8192 tokens, 8 KV / 32 query heads; "
                       "1/36 of a step's attention): oracle block decode + fp64 attention, "
@@ -912,6 +1055,18 @@ def cpu_baseline(layers, all_cores_child=None):
             "encode_GBps": round(enc_bytes / dt_enc / 1e9, 5),
             "encode_sample": "the oracle encode of the same layer's 130,816 groups, 1 thread "
                              "(GB/s of BF16 input)"}
+
+
+def cpu_model() -> str | None:
+    """The host CPU's model name (/proc/cpuinfo, as lscpu reports it)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_all_cores_result(child):

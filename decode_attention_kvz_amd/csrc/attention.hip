@@ -44,6 +44,12 @@ constexpr int kFmtGaac = 2;   // group-adaptive additive code
 constexpr int kFmtFp8 = 3;    // uncompressed FP8 pages (the FP8 baseline)
 constexpr int kFmtFp8c = 4;   // exponent-coded FP8 tiles
 
+// What an attention kernel instance computes: everything, or for the time breakdown only the
+// page loads, or the loads and the restore (values of KVZ_PART_* in the public header).
+constexpr int kModeFull = 0;
+constexpr int kModeLoad = 1;
+constexpr int kModeRestore = 2;
+
 struct AttnParams {
   const uint16_t* q;
   const uint8_t* kv;            // pool arena (compressed) or BF16 pages (baseline)
@@ -116,6 +122,18 @@ struct PageBufOf<kFmtFp8c> {
 };
 
 __device__ __forceinline__ float lane_xor(float x, int m) { return __shfl_xor(x, m, 64); }
+
+// XOR of the 32-bit words of a register value (keeps the breakdown variants' loads and restores
+// from being removed as unused).
+template <typename T>
+__device__ __forceinline__ uint32_t fold_words(const T& x) {
+  static_assert(sizeof(T) % 4 == 0, "whole words");
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(&x);
+  uint32_t a = 0;
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 4); ++i) a ^= w[i];
+  return a;
+}
 
 // max over this lane and lane^16 (v_permlane16_swap: rows 0<->1 and 2<->3 exchange)
 __device__ __forceinline__ float max_xor16(float x) {
@@ -512,7 +530,7 @@ __device__ __forceinline__ SplitOf split_of(const int32_t* n_comp_v, const int32
   return r;
 }
 
-template <int GB, int FMT, int FK = 0>
+template <int GB, int FMT, int FK = 0, int MODE = kModeFull>
 __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
   // COMP: pages are found through the pool metadata (exponent-coded, GAAC or FP8 tiles)
   constexpr bool COMP = FMT == kFmtZf || FMT == kFmtGaac || FMT == kFmtFp8c;
@@ -563,6 +581,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
   }
 
   Softmax<GB> sm;
+  uint32_t probe = 0;   // breakdown variants: what their loads and restores produced
   // pages with very large scores (see split_scores): the K split threshold, and the magnitude
   // and the distance below the max that make a score count, in raw units
   const uint32_t big_thr = big_threshold(qop);
@@ -885,6 +904,10 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
     };
     auto process = [&](const PageBuf& buf, int i) {
       if (!((ok_mask >> i) & 1ull)) return;
+      if constexpr (MODE == kModeLoad) {
+        probe ^= fold_words(buf);
+        return;
+      }
       uint32_t kt = 0xFFFFFFFFu, vt = 0xFFFFFFFFu;
       if constexpr (COMP) {
         kt = (uint32_t)__builtin_amdgcn_readlane((int)meta_l.y, i);
@@ -905,10 +928,12 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
         for (int j = 0; j < 4; ++j) kops[j] = restore_if_coded(buf.k[j], (kt >> (8 * j)) & 0xFFu);
       }
       f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-      operands_settled(kops);
+      if constexpr (MODE == kModeFull) {
+        operands_settled(kops);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kops[j]), as_bf16x8(qop[j]), sacc, 0, 0, 0);
+        for (int j = 0; j < 4; ++j)
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kops[j]), as_bf16x8(qop[j]), sacc, 0, 0, 0);
+      }
       if constexpr (FMT == kFmtGaac) {
         gaac_ops(buf.v, vt != 0u, false, vop);
       } else if constexpr (FMT == kFmtFp8c) {
@@ -921,6 +946,10 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
       } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j) vop[j] = restore_if_coded(buf.v[j], (vt >> (8 * j)) & 0xFFu);
+      }
+      if constexpr (MODE == kModeRestore) {
+        probe ^= fold_words(kops) ^ fold_words(vop);
+        return;
       }
       // the V restore above overlaps the score products; the rare split (a separate block) and
       // the softmax follow
@@ -956,7 +985,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
 
   // The tail page (natural layout [16][128], BF16 - or FP8 for the FP8 formats), masked to its
   // n_tail tokens; masked V values are zeros, so they add nothing even where p is 0.
-  if (n_tail > 0 && p0 <= n_comp && n_comp < p1) {
+  if (MODE == kModeFull && n_tail > 0 && p0 <= n_comp && n_comp < p1) {
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
     uint4 kops[4], vop[4];
     if constexpr (IS_FP8) {
@@ -1021,6 +1050,12 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
     sm.page(sv, sl, page_max(t), vop, lane, c_log2);
   }
 
+  if constexpr (MODE != kModeFull) {
+    // breakdown variants: nothing is merged or written (a store that never happens keeps the
+    // loads and restores alive)
+    if (probe == 0x7FC00001u && lane == 0) p.out[(size_t)b * p.Hq * KVZ_HEAD_DIM] = 1.f;
+    return;
+  }
   if constexpr (IS_FP8) {   // the V dequantization scale, applied once to O
 #pragma unroll
     for (int j = 0; j < 4; ++j) sm.o[j] *= p.v_scale;
@@ -1353,7 +1388,7 @@ struct CommonArgs {
   float k_scale = 1.f, v_scale = 1.f;   // FP8 formats only
 };
 
-template <int FMT, int FK = 0>
+template <int FMT, int FK = 0, int MODE = kModeFull>
 int launch_attention(const CommonArgs& a, const uint8_t* kv, const kvz_group_meta* meta,
                      const uint8_t* bases, hipStream_t s) {
   constexpr bool COMP = FMT == kFmtZf || FMT == kFmtGaac || FMT == kFmtFp8c;
@@ -1420,6 +1455,11 @@ int launch_attention(const CommonArgs& a, const uint8_t* kv, const kvz_group_met
   p.v_scale = a.v_scale;
 
   const dim3 grid((unsigned)units);
+  if constexpr (MODE != kModeFull) {   // breakdown variants: groups of up to 4 query heads
+    if (G > 4) return set_error(KVZ_EUNSUPPORTED, "the breakdown variants take up to 4 query heads per KV head");
+    hipLaunchKernelGGL((attn_split_kernel<4, FMT, FK, MODE>), grid, dim3(256), 0, s, p);
+    return check_hip(hipGetLastError(), "attention launch");
+  }
   if (G <= 4)
     hipLaunchKernelGGL((attn_split_kernel<4, FMT, FK>), grid, dim3(256), 0, s, p);
   else if (G <= 8)
@@ -1572,6 +1612,34 @@ extern "C" int kvz_bf16_decode_attention(const kvz_bf16_attn_args* a, hipStream_
                a->page_size, a->max_pages, a->splits, a->sm_scale, a->workspace,
                a->workspace_bytes};
   return launch_attention<kFmtBf16>(c, a->pages, nullptr, nullptr, s);
+}
+
+extern "C" int kvz_decode_attention_part(const kvz_attn_args* a, int32_t part, hipStream_t s) {
+  if (!a) return set_error(KVZ_EINVAL, "args is null");
+  CommonArgs c{a->q, a->out, a->arena_bytes, a->n_phys_pages, a->block_table, a->seq_lens,
+               a->n_comp_pages, a->tail, a->batch, a->num_q_heads, a->num_kv_heads, a->head_dim,
+               a->page_size, a->max_pages, a->splits, a->sm_scale, a->workspace,
+               a->workspace_bytes};
+  switch (part) {
+    case KVZ_PART_ALL: return launch_attention<kFmtZf>(c, a->arena, a->meta, nullptr, s);
+    case KVZ_PART_LOAD: return launch_attention<kFmtZf, 0, kModeLoad>(c, a->arena, a->meta, nullptr, s);
+    case KVZ_PART_LOAD_RESTORE:
+      return launch_attention<kFmtZf, 0, kModeRestore>(c, a->arena, a->meta, nullptr, s);
+    default: return set_error(KVZ_EINVAL, "part must be KVZ_PART_ALL, KVZ_PART_LOAD or KVZ_PART_LOAD_RESTORE");
+  }
+}
+
+extern "C" int kvz_bf16_decode_attention_part(const kvz_bf16_attn_args* a, int32_t part, hipStream_t s) {
+  if (!a) return set_error(KVZ_EINVAL, "args is null");
+  CommonArgs c{a->q, a->out, 0, a->n_phys_pages, a->block_table, a->seq_lens,
+               a->n_comp_pages, a->tail, a->batch, a->num_q_heads, a->num_kv_heads, a->head_dim,
+               a->page_size, a->max_pages, a->splits, a->sm_scale, a->workspace,
+               a->workspace_bytes};
+  switch (part) {
+    case KVZ_PART_ALL: return launch_attention<kFmtBf16>(c, a->pages, nullptr, nullptr, s);
+    case KVZ_PART_LOAD: return launch_attention<kFmtBf16, 0, kModeLoad>(c, a->pages, nullptr, nullptr, s);
+    default: return set_error(KVZ_EINVAL, "part must be KVZ_PART_ALL or KVZ_PART_LOAD");
+  }
 }
 
 extern "C" int kvz_fp8_decode_attention(const kvz_fp8_attn_args* a, hipStream_t s) {

@@ -32,6 +32,7 @@ KVZ_KIND_K = 0
 KVZ_KIND_V = 1
 KVZ_ENC_FORCE_RAW = 1
 KVZ_WS_BAD_COUNTER = 1
+KVZ_PART_ALL, KVZ_PART_LOAD, KVZ_PART_LOAD_RESTORE = 0, 1, 2
 GRANULE = 256
 KVZ_FP8_E4M3 = 0
 KVZ_FP8_E5M2 = 1
@@ -46,7 +47,7 @@ EXPORTED = [
     "kvz_gaac_decode_attention", "kvz_fp8_pool_state_bytes", "kvz_fp8_pool_init",
     "kvz_fp8_calibrate", "kvz_fp8_encode_pages", "kvz_fp8_decompress_pages", "kvz_fp8_pack_pages",
     "kvz_fp8_decode_attention", "kvz_fp8_raw_decode_attention", "kvz_decode_attention_noalloc",
-    "kvz_attn_workspace_status",
+    "kvz_attn_workspace_status", "kvz_decode_attention_part", "kvz_bf16_decode_attention_part",
 ]
 
 
@@ -160,6 +161,8 @@ _sig = {
     "kvz_fp8_raw_decode_attention": ([ctypes.POINTER(Fp8AttnArgs), _vp], ctypes.c_int),
     "kvz_decode_attention_noalloc": ([ctypes.POINTER(AttnArgs), _vp], ctypes.c_int),
     "kvz_attn_workspace_status": ([_vp, ctypes.POINTER(ctypes.c_uint32), _vp], ctypes.c_int),
+    "kvz_decode_attention_part": ([ctypes.POINTER(AttnArgs), ctypes.c_int32, _vp], ctypes.c_int),
+    "kvz_bf16_decode_attention_part": ([ctypes.POINTER(Bf16AttnArgs), ctypes.c_int32, _vp], ctypes.c_int),
 }
 for _name, (_args, _ret) in _sig.items():
     _f = getattr(_lib, _name)
@@ -347,6 +350,16 @@ def kvz_decode_attention(q, out, arena, meta, block_table, seq_lens, n_comp_page
     _check(_lib.kvz_decode_attention(ctypes.byref(a), _stream(stream)))
 
 
+def kvz_decode_attention_part(q, out, arena, meta, block_table, seq_lens, n_comp_pages, tail,
+                              sm_scale: float, workspace, part: int, splits: int = 0,
+                              stream=None) -> None:
+    """kvz_decode_attention restricted to a part of the kernel (KVZ_PART_*), for the time
+    breakdown; the partial variants leave out and the workspace as they are."""
+    a = _attn_args(q, out, arena, meta, block_table, seq_lens, n_comp_pages, tail, sm_scale,
+                   workspace, splits)
+    _check(_lib.kvz_decode_attention_part(ctypes.byref(a), part, _stream(stream)))
+
+
 def kvz_decode_attention_noalloc(q, out, arena, meta, block_table, seq_lens, n_comp_pages, tail,
                                  sm_scale: float, splits: int = 0, stream=None) -> None:
     """kvz_decode_attention without a workspace: the library's device-resident scratch holds the
@@ -403,6 +416,26 @@ def kvz_bf16_decode_attention(q, out, pages, block_table, seq_lens, n_comp_pages
                      workspace=workspace.data_ptr(),
                      workspace_bytes=workspace.numel() * workspace.element_size())
     _check(_lib.kvz_bf16_decode_attention(ctypes.byref(a), _stream(stream)))
+
+
+def kvz_bf16_decode_attention_part(q, out, pages, block_table, seq_lens, n_comp_pages, tail,
+                                   sm_scale: float, workspace, num_kv_heads: int, part: int,
+                                   splits: int = 0, stream=None) -> None:
+    """kvz_bf16_decode_attention restricted to a part of the kernel (KVZ_PART_ALL or
+    KVZ_PART_LOAD), for the time breakdown."""
+    _dev("pages", pages, min_bytes=pages.shape[0] * 2 * num_kv_heads * 4096)
+    _check_attn_common(q, out, block_table, seq_lens, n_comp_pages, workspace, num_kv_heads,
+                       tail=tail, tail_dtype=_torch().bfloat16)
+    bsz, hq, hd = q.shape
+    a = Bf16AttnArgs(q=q.data_ptr(), out=out.data_ptr(), pages=pages.data_ptr(),
+                     n_phys_pages=pages.shape[0], block_table=block_table.data_ptr(), seq_lens=seq_lens.data_ptr(),
+                     n_comp_pages=n_comp_pages.data_ptr(),
+                     tail=None if tail is None else tail.data_ptr(), batch=bsz, num_q_heads=hq,
+                     num_kv_heads=num_kv_heads, head_dim=hd, page_size=16,
+                     max_pages=block_table.shape[1], splits=splits, sm_scale=sm_scale,
+                     workspace=workspace.data_ptr(),
+                     workspace_bytes=workspace.numel() * workspace.element_size())
+    _check(_lib.kvz_bf16_decode_attention_part(ctypes.byref(a), part, _stream(stream)))
 
 
 def kvz_pool_stats(pool, stream=None) -> dict:

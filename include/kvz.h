@@ -76,6 +76,9 @@ enum {
 #define KVZ_KIND_K 0u
 #define KVZ_KIND_V 1u
 #define KVZ_ENC_FORCE_RAW 1u    /* kvz_encode_pages flag: store every block raw */
+#define KVZ_PART_ALL 0           /* kvz_*_decode_attention_part: the whole call                */
+#define KVZ_PART_LOAD 1          /* only the page loads of the attention kernel                */
+#define KVZ_PART_LOAD_RESTORE 2  /* the page loads and the in-register restore                 */
 #define KVZ_WS_BAD_COUNTER 1u   /* kvz_attn_workspace_status flag: a merge counter was found at or
                                    above its pair's number of pieces (workspace not zero-filled,
                                    or reused beyond the fixed counter area); the merge of that
@@ -417,6 +420,19 @@ int kvz_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_
  * kernel merges them. */
 int kvz_decode_attention(const kvz_attn_args* a, hipStream_t s);
 
+/* Measurement entry points for the attention time breakdown ([GAAC] "Attention Time
+ * Breakdown", Table 5: KV loading, exponent decoding and computation timed apart): the same
+ * arguments and launch as kvz_decode_attention / kvz_bf16_decode_attention, but part selects a
+ * compile-time variant of the attention kernel.  KVZ_PART_ALL is the full call (identical to
+ * the plain entry point).  KVZ_PART_LOAD issues exactly the page loads and waits of the full
+ * kernel and nothing else (no restore, no products, no softmax, no tail page, no merge);
+ * KVZ_PART_LOAD_RESTORE adds the in-register restore of every K and V block (the BF16 kernel
+ * has no restore, so it takes KVZ_PART_ALL and KVZ_PART_LOAD only).  The variants compute
+ * nothing useful: out and the workspace are left as they are.  They exist for groups of up to 4
+ * query heads per KV head (KVZ_EUNSUPPORTED beyond); KVZ_EINVAL for another part. */
+int kvz_decode_attention_part(const kvz_attn_args* a, int32_t part, hipStream_t s);
+int kvz_bf16_decode_attention_part(const kvz_bf16_attn_args* a, int32_t part, hipStream_t s);
+
 /* Allocation-free variant of kvz_decode_attention, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * the same kernels and result, with the split-K partial results and merge counters in a
@@ -445,10 +461,17 @@ int kvz_attn_workspace_status(const void* d_workspace, uint32_t* flags, hipStrea
 int kvz_bf16_pack_pages(const uint16_t* d_src, uint8_t* d_dst, int64_t n_pages,
                         int32_t num_kv_heads, hipStream_t s);
 
-/* Uncompressed baseline: the same attention over BF16 pages laid out by kvz_bf16_pack_pages. */
+/* Uncompressed baseline: the same attention over BF16 pages laid out by kvz_bf16_pack_pages -
+ * the uncompressed paged decode attention that both pages measure the fused kernel against
+ * ([GAAC] "Long-Context Attention Acceleration" and appendix "Attention Baseline Selection":
+ * paged attention over uncompressed BF16 KV in the same process; [ZF] "Evidence"). */
 int kvz_bf16_decode_attention(const kvz_bf16_attn_args* a, hipStream_t s);
 
-/* Copy the pool counters to *host_out; synchronizes stream s. */
+/* Copy the pool counters (capacity, frontier, free runs per size bin, live groups, granules and
+ * raw blocks, failed allocations and dropped frees) to *host_out; synchronizes stream s.  The memory-usage report of the slot pool
+ * ([ZF] "How it works", memory-manager paragraph: compressed and raw pages in one managed
+ * pool; [GAAC] "Block-Wise Compression Scheduling": two storage classes whose occupancy the
+ * serving layer tracks). */
 int kvz_pool_stats(kvz_pool* p, kvz_pool_stats_t* host_out, hipStream_t s);
 
 /* Capacity left for KV writes, for a scheduler's admission decision ([ZF] "How it works": the

@@ -304,3 +304,55 @@ def test_large_batch_split_map(ragged):
             assert (got[b] == 0).all()
     for b in rows:
         check_rows(got[b], ref[b], what=f"seq {b}")
+
+
+def test_breakdown_variants_run_and_full_part_equals_the_call():
+    """The measurement entry points: KVZ_PART_ALL is the attention call itself (bit for bit, fused
+    and BF16), the load-only and load+restore variants run on the same arguments, write
+    nothing to out and leave the merge counters at zero."""
+    announce("breakdown variants")
+    bsz, n_comp = 6, 40
+    pages = synth.kv_pages(bsz, n_comp + 1, 8, seed=19, forced_frac=0.05, forced_exp=-16.0,
+                           device="cuda")
+    q = synth.queries(bsz, 32, seed=19, device="cuda")
+    seq_lens = [16 * n_comp + 7] * bsz
+    arena, layer = _layer(pages, seq_lens, [n_comp] * bsz, seed=19)
+    want = run_fused(layer, arena, q, sm_scale(), 2)
+    want_bf16 = run_bf16(layer, q, sm_scale(), 2)
+    ws = paged.workspace(bsz, 32, 8, n_comp, 2)
+    got = torch.full_like(want, float("nan"))
+    kvz.kvz_decode_attention_part(q, got, arena.arena, layer.meta, layer.block_table,
+                                  layer.seq_lens, layer.n_comp, layer.tail, sm_scale(), ws,
+                                  kvz.KVZ_PART_ALL, 2)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
+    for part in (kvz.KVZ_PART_LOAD, kvz.KVZ_PART_LOAD_RESTORE):
+        untouched = torch.full_like(want, -7.0)
+        kvz.kvz_decode_attention_part(q, untouched, arena.arena, layer.meta, layer.block_table,
+                                      layer.seq_lens, layer.n_comp, layer.tail, sm_scale(), ws,
+                                      part, 2)
+        torch.cuda.synchronize()
+        assert (untouched == -7.0).all()
+    assert kvz.kvz_attn_workspace_status(ws) == 0
+    assert int(ws[:256 + 4 * bsz * 8].count_nonzero()) == 0
+    # the BF16 kernel's variants over the same pages
+    nat = torch.zeros((layer.meta.shape[0], 2, 8, 16, 128), dtype=torch.bfloat16, device="cuda")
+    for b in range(bsz):
+        phys = torch.as_tensor(layer.phys_of[b, :n_comp], device="cuda", dtype=torch.long)
+        nat[phys] = layer.pages[b, :n_comp]
+    store = paged.pack_bf16_pages(nat)
+    got_b = torch.full_like(want, float("nan"))
+    kvz.kvz_bf16_decode_attention_part(q, got_b, store, layer.block_table, layer.seq_lens,
+                                       layer.n_comp, layer.tail, sm_scale(), ws, 8,
+                                       kvz.KVZ_PART_ALL, 2)
+    untouched = torch.full_like(want, -7.0)
+    kvz.kvz_bf16_decode_attention_part(q, untouched, store, layer.block_table, layer.seq_lens,
+                                       layer.n_comp, layer.tail, sm_scale(), ws, 8,
+                                       kvz.KVZ_PART_LOAD, 2)
+    torch.cuda.synchronize()
+    assert torch.equal(got_b, want_bf16)
+    assert (untouched == -7.0).all()
+    with pytest.raises(kvz.KvzError):
+        kvz.kvz_bf16_decode_attention_part(q, untouched, store, layer.block_table, layer.seq_lens,
+                                           layer.n_comp, layer.tail, sm_scale(), ws, 8,
+                                           kvz.KVZ_PART_LOAD_RESTORE, 2)
