@@ -11,9 +11,11 @@
 // pipeline that the fused attention is compared against ("GAAC: ...", section "Attention Time
 // Breakdown", Table 5, the decompress-first column).
 //
-// kvz_encode_pages = classify (one wave per item) -> allocate (pool.hip, one workgroup, item
-// order) -> pack (one wave per item).  The item's metadata slot carries the tags from classify
-// to allocate and the offset from allocate to pack, so the encoder needs no scratch memory.
+// kvz_encode_pages: a decode step's completion (up to kOnePassMaxItems items) is one launch of
+// the one-pass encoder below (classify, allocate by decoupled look-back, pack from registers);
+// a bulk call is classify (one wave per item) -> allocate (pool.hip, multi-pass scan, item
+// order) -> pack (one wave per item), the item's metadata slot carrying the tags from classify
+// to allocate and the offset from allocate to pack.  Both give the same offsets.
 #include "encode_internal.h"
 
 namespace kvz {
@@ -134,6 +136,286 @@ __global__ __launch_bounds__(256) void pack_kernel(const kvz_encode_item* items,
   }
 }
 
+// One-pass encode: classify, allocate and pack in one launch, each item's source read once.
+// The launch is persistent: no more workgroups than fit on the device at once, workgroup b
+// taking tiles b, b + grid, b + 2 grid, ... (a tile: kEncWaves waves, IPW items per wave, in
+// item order), so every tile only waits for lower tiles, which are resident or done.  A tile
+// loads its items into registers, classifies them and publishes its count of items per size
+// class; then its 256 threads add up the published counts of every earlier tile (each thread
+// every 256th tile).  Summing every earlier record directly, rather than chaining through
+// inclusive prefixes (decoupled look-back), costs no extra round trip per 64 tiles when all
+// tiles start at once, as they do in a decode step's completion.  With those counts every item
+// gets exactly the offset of the item-order rule (a class's i-th item pops its bin from the top
+// while the bin lasts, later ones take prefix-summed frontier runs), then the tile packs from
+// registers.  Tile 0 also publishes the pool counters the launch starts from; the last tile
+// writes the bins' new counts and adds the launch's totals as if every request were granted; a
+// tile whose frontier requests do not fit subtracts them again and counts them as failed.
+//
+// Records pass between workgroups with agent-scope (sc1) stores and loads: a record's fields
+// are stored, the thread waits for those stores to complete (s_waitcnt vmcnt(0)), then the
+// status word is stored; a reader loads the status and only then the fields.
+constexpr int kEncWaves = 4;
+// calls up to this many items take the one-pass kernel (tiles <= kMaxEncodeTiles at two items per wave)
+constexpr int kOnePassMaxItems = 16384;
+static_assert(kOnePassMaxItems <= kMaxEncodeTiles * kEncWaves * 2, "look-back records");
+constexpr uint32_t kMaxSpins = 1u << 20;   // a wait that never ends marks its tile's items unstored
+
+__device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void add_agent(uint64_t* p, uint64_t v) {
+  if (v) atomicAdd(reinterpret_cast<unsigned long long*>(p), (unsigned long long)v);
+}
+
+template <int kPolicy, int IPW>
+__global__ __launch_bounds__(kEncWaves * 64) void encode_onepass_kernel(
+    const kvz_encode_item* items, int n, uint32_t flags, PoolHdr* hdr, const uint32_t* bins,
+    uint8_t* arena, EncodeSlot* slots, uint32_t epoch, int n_tiles) {
+  constexpr int kTileItems = kEncWaves * IPW;
+  __shared__ uint32_t s_cls[kTileItems];      // size class (raw blocks) of each item; 0xFF: none
+  __shared__ uint32_t s_rank[kTileItems];     // rank of each item among the launch's items of its class
+  __shared__ uint64_t s_start[kTileItems];    // frontier start of each item if it asks the frontier
+  __shared__ uint32_t s_snap[kBins];
+  __shared__ uint32_t s_ok;
+  __shared__ uint32_t s_part[kEncWaves][kBins + 1];
+  __shared__ uint64_t s_fail[kEncWaves][4];   // failed requests: count, granules, raw blocks
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  if (hdr->magic != kPoolMagic) return;   // host checked; never write through a bad state
+  const uint64_t cap = hdr->capacity;
+
+  for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+    // load and classify this wave's items
+    uint4 w[IPW][4];
+    uint32_t tags[IPW];
+    kvz_encode_item it[IPW];
+#pragma unroll
+    for (int u = 0; u < IPW; ++u) {
+      const int item = (tile * kEncWaves + wave) * IPW + u;
+      tags[u] = 0;
+      if (item < n) {
+        it[u] = items[item];
+        load_item_chunks<kPolicy>(it[u].src, it[u].src_stride, it[u].kind, lane, w[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < IPW; ++u) {
+      const int item = (tile * kEncWaves + wave) * IPW + u;
+      if (item >= n) {
+        if (lane == 0) s_cls[wave * IPW + u] = 0xFFu;
+        continue;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t lo = 255u, hi = 0u;
+        chunk_exp_range(w[u][j], lo, hi);
+        lo = wave_min(lo);
+        hi = wave_max(hi);
+        const uint32_t b = lo & 0xFEu;
+        const uint32_t tag = (hi <= b + 15u && !(flags & KVZ_ENC_FORCE_RAW)) ? (b >> 1) : KVZ_RAW_TAG;
+        tags[u] |= tag << (8 * j);
+      }
+      if (lane == 0) s_cls[wave * IPW + u] = n_raw_of(tags[u]);
+    }
+    __syncthreads();
+
+    // publish this tile's counts (tile 0 also the pool counters the launch starts from), then
+    // add up the counts of every earlier tile: each thread takes every 256th earlier tile and
+    // waits for its record of this launch
+    uint32_t agg[kBins];
+#pragma unroll
+    for (int k = 0; k < kBins; ++k) agg[k] = 0;
+    for (int i = 0; i < kTileItems; ++i) {
+      const uint32_t c = s_cls[i];
+#pragma unroll
+      for (int k = 0; k < kBins; ++k) agg[k] += c == (uint32_t)k ? 1u : 0u;
+    }
+    if (threadIdx.x == 0) {
+      EncodeSlot* me = slots + tile;
+#pragma unroll
+      for (int k = 0; k < kBins; ++k) st_agent(&me->agg[k], agg[k]);
+      if (tile == 0) {
+#pragma unroll
+        for (int k = 0; k < kBins; ++k) st_agent(&me->snap[k], (uint32_t)hdr->bin_cnt[k]);
+        const uint64_t f = hdr->frontier;
+        st_agent(&me->f0_lo, (uint32_t)f);
+        st_agent(&me->f0_hi, (uint32_t)(f >> 32));
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      st_agent(&me->status, (epoch << 2) | 1u);
+    }
+    uint32_t pre[kBins];
+#pragma unroll
+    for (int k = 0; k < kBins; ++k) pre[k] = 0;
+    bool ok = true;
+    for (int i = (int)threadIdx.x; i < tile; i += kEncWaves * 64) {
+      uint32_t spins = 0;
+      while ((ld_agent(&slots[i].status) >> 2) != epoch) {
+        if (++spins > kMaxSpins) {
+          ok = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+#pragma unroll
+      for (int k = 0; k < kBins; ++k) pre[k] += ld_agent(&slots[i].agg[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < kBins; ++k) {
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) pre[k] += (uint32_t)__shfl_xor((int)pre[k], d, 64);
+    }
+    const uint64_t okw = __ballot(!ok);
+    if (lane == 0) {
+#pragma unroll
+      for (int k = 0; k < kBins; ++k) s_part[wave][k] = pre[k];
+      s_part[wave][kBins] = okw ? 1u : 0u;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t snap[kBins];
+      uint64_t f0;
+      bool all_ok = true;
+#pragma unroll
+      for (int k = 0; k < kBins; ++k) pre[k] = 0;
+      for (int q = 0; q < kEncWaves; ++q) {
+#pragma unroll
+        for (int k = 0; k < kBins; ++k) pre[k] += s_part[q][k];
+        all_ok = all_ok && s_part[q][kBins] == 0u;
+      }
+      if (tile == 0) {
+#pragma unroll
+        for (int k = 0; k < kBins; ++k) snap[k] = (uint32_t)hdr->bin_cnt[k];
+        f0 = hdr->frontier;
+      } else {   // tile 0's record, seen complete by the wait above (thread 0 waited for it)
+#pragma unroll
+        for (int k = 0; k < kBins; ++k) snap[k] = ld_agent(&slots[0].snap[k]);
+        f0 = ((uint64_t)ld_agent(&slots[0].f0_hi) << 32) | ld_agent(&slots[0].f0_lo);
+      }
+      if (!all_ok) {   // never happens while every lower tile is resident or done
+#pragma unroll
+        for (int k = 0; k < kBins; ++k) snap[k] = 0;
+        f0 = cap;
+      }
+      // each item's rank in its class and, for a frontier request, where its run starts: the
+      // frontier requests of earlier tiles are the items of class k beyond the bin's count
+      uint64_t fnext = f0;
+#pragma unroll
+      for (int k = 0; k < kBins; ++k) {
+        s_snap[k] = snap[k];
+        if (pre[k] > snap[k]) fnext += (uint64_t)(pre[k] - snap[k]) * run_granules((uint32_t)k);
+      }
+      uint32_t run_k[kBins];
+#pragma unroll
+      for (int k = 0; k < kBins; ++k) run_k[k] = pre[k];
+      for (int i = 0; i < kTileItems; ++i) {
+        const uint32_t c = s_cls[i];
+        if (c == 0xFFu) continue;
+        uint32_t r = 0;
+#pragma unroll
+        for (int k = 0; k < kBins; ++k) {
+          if (c == (uint32_t)k) {
+            r = run_k[k];
+            run_k[k] += 1;
+          }
+        }
+        s_rank[i] = r;
+        s_start[i] = fnext;
+        if (r >= snap[c]) fnext += run_granules(c);
+      }
+      s_ok = all_ok ? 1u : 0u;
+      // the last tile knows every item of the launch: the bins' new counts, and the launch's
+      // totals as if every request were granted (tiles with failed requests correct them)
+      if (tile == n_tiles - 1) {
+        uint64_t runs = 0, gran = 0, raw = 0;
+#pragma unroll
+        for (int k = 0; k < kBins; ++k) {
+          const uint32_t tot = pre[k] + agg[k];
+          hdr->bin_cnt[k] = snap[k] - (tot < snap[k] ? tot : snap[k]);
+          runs += tot;
+          gran += (uint64_t)tot * run_granules((uint32_t)k);
+          raw += (uint64_t)tot * (uint32_t)k;
+        }
+        add_agent(&hdr->frontier, fnext - f0);
+        add_agent(&hdr->live_runs, runs);
+        add_agent(&hdr->live_granules, gran);
+        add_agent(&hdr->live_raw_blocks, raw);
+      }
+    }
+    __syncthreads();
+
+    // allocate this wave's items in item order, then pack them from registers
+    uint64_t fail = 0, fail_gran = 0, fail_raw = 0, fail_front = 0;
+#pragma unroll
+    for (int u = 0; u < IPW; ++u) {
+      const int idx = wave * IPW + u;
+      const int item = tile * kTileItems + idx;
+      if (item >= n) continue;
+      const uint32_t k = s_cls[idx];
+      const uint32_t rank = s_rank[idx];
+      const uint32_t z = run_granules(k);
+      uint32_t off = KVZ_OFF_NONE;
+      const bool from_bin = rank < s_snap[k];
+      if (from_bin) {
+        off = bins[hdr->bin_base[k] + s_snap[k] - 1u - rank];
+      } else if (s_start[idx] + z <= cap) {
+        off = (uint32_t)s_start[idx];
+      }
+      if (!s_ok) off = KVZ_OFF_NONE;
+      if (off == KVZ_OFF_NONE) {
+        fail += 1;
+        fail_gran += z;
+        fail_raw += k;
+        if (!from_bin) fail_front += z;
+      }
+      if (lane == 0) {
+        typedef __attribute__((address_space(1))) uint64_t global_u64;
+        *(global_u64*)(it[u].dst) = (uint64_t)off | ((uint64_t)tags[u] << 32);
+      }
+      if (off == KVZ_OFF_NONE) continue;
+      uint8_t* blk = arena + (size_t)off * KVZ_GRANULE_BYTES;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t tag = (tags[u] >> (8 * j)) & 0xFFu;
+        if (tag == KVZ_RAW_TAG) {
+          *reinterpret_cast<uint4*>(blk + kRawChunkBytes * lane) = w[u][j];
+        } else {
+          const uint3 c = compress_chunk(w[u][j], tag * 0x01010101u);
+          uint32_t* d = reinterpret_cast<uint32_t*>(blk + kCompChunkBytes * lane);
+          d[0] = c.x;
+          d[1] = c.y;
+          d[2] = c.z;
+        }
+        blk += block_bytes(tag);
+      }
+    }
+    // failed requests (a full pool): taken back out of the totals, counted as failed
+    if (lane == 0) {
+      s_fail[wave][0] = fail;
+      s_fail[wave][1] = fail_gran;
+      s_fail[wave][2] = fail_raw;
+      s_fail[wave][3] = fail_front;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint64_t f[4] = {0, 0, 0, 0};
+      for (int q = 0; q < kEncWaves; ++q)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) f[c] += s_fail[q][c];
+      if (f[0]) {
+        add_agent(&hdr->enospc, f[0]);
+        add_agent(&hdr->live_runs, (uint64_t)0 - f[0]);
+        add_agent(&hdr->live_granules, (uint64_t)0 - f[1]);
+        add_agent(&hdr->live_raw_blocks, (uint64_t)0 - f[2]);
+        add_agent(&hdr->frontier, (uint64_t)0 - f[3]);
+      }
+    }
+  }
+}
+
 // Step 4: natural-order BF16 [16 tokens][32 dims] of each referenced block.
 __global__ __launch_bounds__(256) void decode_block_kernel(const uint8_t* arena,
                                                            uint64_t arena_bytes,
@@ -249,23 +531,51 @@ extern "C" int kvz_encode_pages(kvz_pool* p, const kvz_encode_item* d_items, int
   if (n == 0) return KVZ_OK;
   if (!d_items) return set_error(KVZ_EINVAL, "items pointer is null");
   if (flags & ~KVZ_ENC_FORCE_RAW) return set_error(KVZ_EINVAL, "unknown encode flag");
-  const int grid = (n + 3) / 4;
-  const bool stream = n > kStreamItems;
-  if (stream)
-    hipLaunchKernelGGL(classify_kernel<kStreamLoad>, dim3(grid), dim3(256), 0, s, d_items, (int)n, flags);
-  else
-    hipLaunchKernelGGL(classify_kernel<kCachedLoad>, dim3(grid), dim3(256), 0, s, d_items, (int)n, flags);
-  int rc = check_hip(hipGetLastError(), "classify launch");
+  if (n > kOnePassMaxItems) {
+    // bulk (prefill) calls: classify, the multi-pass allocation, pack (each source read twice,
+    // every pass a fully parallel stream)
+    const int grid = (n + 3) / 4;
+    const bool stream = n > kStreamItems;
+    if (stream)
+      hipLaunchKernelGGL(classify_kernel<kStreamLoad>, dim3(grid), dim3(256), 0, s, d_items, (int)n, flags);
+    else
+      hipLaunchKernelGGL(classify_kernel<kCachedLoad>, dim3(grid), dim3(256), 0, s, d_items, (int)n, flags);
+    int rc = check_hip(hipGetLastError(), "classify launch");
+    if (rc != KVZ_OK) return rc;
+    rc = launch_alloc_for_items(p, d_items, n, s);
+    if (rc != KVZ_OK) return rc;
+    if (stream)
+      hipLaunchKernelGGL(pack_kernel<kStreamLoad>, dim3(grid), dim3(256), 0, s, d_items, (int)n,
+                         (uint8_t*)p->arena, p->capacity);
+    else
+      hipLaunchKernelGGL(pack_kernel<kCachedLoad>, dim3(grid), dim3(256), 0, s, d_items, (int)n,
+                         (uint8_t*)p->arena, p->capacity);
+    return check_hip(hipGetLastError(), "pack launch");
+  }
+  // a decode step's completion: one launch, each source read once
+  PoolHdr* hdr = (PoolHdr*)p->state;
+  const uint32_t* bins = (const uint32_t*)((uint8_t*)p->state + kPoolHdrBytes);
+  EncodeSlot* slots = (EncodeSlot*)p->enc_scratch;
+  const int ipw = n <= 4096 ? 1 : 2;
+  const void* fn = ipw == 1 ? (const void*)encode_onepass_kernel<kCachedLoad, 1>
+                            : (const void*)encode_onepass_kernel<kCachedLoad, 2>;
+  int per_cu = 0;
+  int rc = check_hip(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kEncWaves * 64, 0),
+                     "occupancy query");
   if (rc != KVZ_OK) return rc;
-  rc = launch_alloc_for_items(p, d_items, n, s);
-  if (rc != KVZ_OK) return rc;
-  if (stream)
-    hipLaunchKernelGGL(pack_kernel<kStreamLoad>, dim3(grid), dim3(256), 0, s, d_items, (int)n,
-                       (uint8_t*)p->arena, p->capacity);
+  const int resident = (per_cu > 0 ? per_cu : 1) * device_cus();
+  const int tiles = (n + kEncWaves * ipw - 1) / (kEncWaves * ipw);
+  const int grid = tiles < resident ? tiles : resident;
+  p->enc_epoch = p->enc_epoch % ((1u << 30) - 1u) + 1u;
+  if (ipw == 1)
+    hipLaunchKernelGGL((encode_onepass_kernel<kCachedLoad, 1>), dim3(grid), dim3(kEncWaves * 64), 0, s,
+                       d_items, n, flags, hdr, bins, (uint8_t*)p->arena, slots, p->enc_epoch, tiles);
   else
-    hipLaunchKernelGGL(pack_kernel<kCachedLoad>, dim3(grid), dim3(256), 0, s, d_items, (int)n,
-                       (uint8_t*)p->arena, p->capacity);
-  return check_hip(hipGetLastError(), "pack launch");
+    hipLaunchKernelGGL((encode_onepass_kernel<kCachedLoad, 2>), dim3(grid), dim3(kEncWaves * 64), 0, s,
+                       d_items, n, flags, hdr, bins, (uint8_t*)p->arena, slots, p->enc_epoch, tiles);
+  rc = check_hip(hipGetLastError(), "encode launch");
+  if (rc != KVZ_OK) return rc;
+  return KVZ_OK;
 }
 
 extern "C" int kvz_decode_block(const void* d_arena, uint64_t arena_bytes,

@@ -138,4 +138,23 @@ struct kvz_pool {
   int device;
   void* scratch;   // device: per-tile counts of the allocation / free passes (in the state buffer)
   uint32_t granule_bytes;   // 256 (BF16 formats) or 128 (FP8 tiles, kvz_fp8_pool_init)
+  void* enc_scratch;        // device: look-back records of the one-pass encoder (state buffer)
+  uint32_t enc_epoch;       // the last one-pass encode launch's number (1 .. 2^30 - 1, cycling)
 };
+
+namespace kvz {
+// Record of one tile of a one-pass encode launch: its items of each size class; tile 0's also
+// holds the bin counts and frontier that the launch started from.  status = epoch << 2 | 1 once
+// the record is complete; a record of another launch has another epoch.
+struct EncodeSlot {
+  uint32_t status;
+  uint32_t agg[kBins];
+  uint32_t snap[kBins];
+  uint32_t f0_lo, f0_hi;
+  uint32_t pad[19];
+};
+static_assert(sizeof(EncodeSlot) == 128, "one record per 128 bytes");
+constexpr int kMaxEncodeTiles = 16384;
+// records, then the ticket counter that orders the tiles of a launch
+constexpr uint64_t kEncodeScratchBytes = (uint64_t)kMaxEncodeTiles * sizeof(EncodeSlot) + 256;
+}  // namespace kvz

@@ -604,6 +604,10 @@ __global__ __launch_bounds__(kThreads) void pool_free_small_kernel(PoolHdr* hdr,
   }
 }
 
+__global__ void zero_words_kernel(uint32_t* p, uint32_t n) {
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
 __global__ void pool_init_kernel(PoolHdr* hdr, uint64_t capacity, PoolHdr tmpl) {
   if (threadIdx.x == 0 && blockIdx.x == 0) {
     *hdr = tmpl;
@@ -674,7 +678,8 @@ int pool_state_bytes_g(uint64_t arena_bytes, uint64_t granule, uint64_t* state_b
   if (capacity >= KVZ_OFF_NONE) return set_error(KVZ_EINVAL, "arena too large for 32-bit granule offsets");
   uint64_t cap[kBins], base[kBins], entries;
   bin_layout(capacity, cap, base, &entries);
-  *state_bytes = align256(kPoolHdrBytes + 4 * entries) + align256(sizeof(PoolScratch));
+  *state_bytes = align256(kPoolHdrBytes + 4 * entries) + align256(sizeof(PoolScratch)) +
+                 align256(kEncodeScratchBytes);
   return KVZ_OK;
 }
 
@@ -700,6 +705,12 @@ int pool_init_g(kvz_pool** out, void* d_arena, uint64_t arena_bytes, void* d_sta
   hipLaunchKernelGGL(pool_init_kernel, dim3(1), dim3(64), 0, s, (PoolHdr*)d_state, capacity, t);
   rc = check_hip(hipGetLastError(), "pool init launch");
   if (rc != KVZ_OK) return rc;
+  // the one-pass encoder's records and ticket start cleared (no record carries an epoch yet)
+  uint8_t* enc = (uint8_t*)d_state + align256(kPoolHdrBytes + 4 * entries) + align256(sizeof(PoolScratch));
+  hipLaunchKernelGGL(zero_words_kernel, dim3(256), dim3(256), 0, s, (uint32_t*)enc,
+                     (uint32_t)(kEncodeScratchBytes / 4));
+  rc = check_hip(hipGetLastError(), "pool init launch");
+  if (rc != KVZ_OK) return rc;
   kvz_pool* p = new (std::nothrow) kvz_pool;
   if (!p) return set_error(KVZ_EINVAL, "out of host memory");
   p->arena = d_arena;
@@ -710,6 +721,8 @@ int pool_init_g(kvz_pool** out, void* d_arena, uint64_t arena_bytes, void* d_sta
   p->device = dev;
   p->scratch = (uint8_t*)d_state + align256(kPoolHdrBytes + 4 * entries);
   p->granule_bytes = granule;
+  p->enc_scratch = enc;
+  p->enc_epoch = 0;
   *out = p;
   return KVZ_OK;
 }
