@@ -181,6 +181,13 @@ __device__ __forceinline__ void operands_settled(uint4 (&ops)[4]) {
   ops[3] = __builtin_bit_cast(uint4, d);
 }
 
+// The same two wait states for one operand (the P operand of the PV products).
+__device__ __forceinline__ void operand_settled(uint4& op) {
+  u32x4v a = __builtin_bit_cast(u32x4v, op);
+  asm volatile("s_nop 1" : "+v"(a));
+  op = __builtin_bit_cast(uint4, a);
+}
+
 // Ten wait states ahead of the first read of a page's scores, after the V restore.  A VALU read
 // of a 16x16x32 product's result must be at least eight wait states after it.  Where an
 // uncompressed V block skips the V restore, the products were followed by a branch to the
@@ -345,9 +352,12 @@ struct Softmax {
     m_run = m_new;
     if (__ballot(alpha != 1.0f)) rescale(alpha, lane);
 
-    // P as the row operand of the 32x32x16 product: lane holds head lane%32 and tokens
-    // 8*(lane/32)+0..7; this lane has tokens 4*(lane/16)+0..3 of head lane%16, lane+16 has
-    // the next four.  hi = bf16(p), lo = bf16(p - hi), both rounded to nearest even.
+    // P as the row operand of one 32x32x16 product per V chunk: hi = bf16(p) and lo =
+    // bf16(p - hi), both rounded to nearest even, in rows 0-15 (hi) and 16-31 (lo) for heads
+    // 0-15, so that O rows h and 16 + h accumulate the two halves (added up by fold()).  Lane l
+    // holds row l%32 and tokens 8*(l/32)+0..7; this lane has tokens 4*(l/16)+0..3 of head l%16
+    // and lane l^16 the other four of its eight: a lane of rows 0-15 takes that lane's hi, a lane
+    // of rows 16-31 its lo, in one exchange per pair of tokens.
     uint32_t hi[2], lo[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
@@ -357,20 +367,32 @@ struct Softmax {
       hi[m] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
       lo[m] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
     }
-    uint4 a_hi, a_lo;
-    a_hi.x = hi[0];
-    a_hi.y = hi[1];
-    a_hi.z = from_next_row(hi[0]);
-    a_hi.w = from_next_row(hi[1]);
-    a_lo.x = lo[0];
-    a_lo.y = lo[1];
-    a_lo.z = from_next_row(lo[0]);
-    a_lo.w = from_next_row(lo[1]);
+    const bool lo_rows = (lane & 16) != 0;
+    // v_permlane16_swap of a value with itself: result [1] gives rows 0 and 2 of lanes the values
+    // of rows 1 and 3, result [0] gives rows 1 and 3 the values of rows 0 and 2
+    const auto x0 = __builtin_amdgcn_permlane16_swap(lo_rows ? hi[0] : lo[0], lo_rows ? hi[0] : lo[0], false, false);
+    const auto x1 = __builtin_amdgcn_permlane16_swap(lo_rows ? hi[1] : lo[1], lo_rows ? hi[1] : lo[1], false, false);
+    const uint32_t got0 = lo_rows ? x0[0] : x0[1];
+    const uint32_t got1 = lo_rows ? x1[0] : x1[1];
+    uint4 a;
+    a.x = lo_rows ? got0 : hi[0];
+    a.y = lo_rows ? got1 : hi[1];
+    a.z = lo_rows ? lo[0] : got0;
+    a.w = lo_rows ? lo[1] : got1;
+    operand_settled(a);   // the same VALU -> MFMA distance as for the score operands
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a_hi), as_bf16x8(vop[j]), o[j], 0, 0, 0);
-      o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a_lo), as_bf16x8(vop[j]), o[j], 0, 0, 0);
-    }
+    for (int j = 0; j < 4; ++j)
+      o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(vop[j]), o[j], 0, 0, 0);
+  }
+
+  // O rows 16-31 (the lo halves) added into rows 0-15: register r + 8 holds row 16 + the row
+  // of register r.  Once, after the last page.
+  __device__ __forceinline__ void fold() {
+    constexpr int NR = GB <= 8 ? 4 : 8;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < NR; ++r) o[j][r] += o[j][r + 8];
   }
 
   // O tile register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4 (a query head of the group).
@@ -386,7 +408,10 @@ struct Softmax {
         a = lane < 32 ? a_lo : a_hi;
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) o[j][r] *= a;
+      for (int j = 0; j < 4; ++j) {
+        o[j][r] *= a;
+        o[j][r + 8] *= a;
+      }
     }
   }
 };
@@ -1056,6 +1081,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
     if (probe == 0x7FC00001u && lane == 0) p.out[(size_t)b * p.Hq * KVZ_HEAD_DIM] = 1.f;
     return;
   }
+  sm.fold();
   if constexpr (IS_FP8) {   // the V dequantization scale, applied once to O
 #pragma unroll
     for (int j = 0; j < 4; ++j) sm.o[j] *= p.v_scale;
