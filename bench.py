@@ -169,6 +169,9 @@ def main():
     ap.add_argument("--pmc-probe", action="store_true",
                     help="for hardware-counter runs: one layer of fused and baseline attention "
                          "(3 launches each) and a 1 GiB device copy as a traffic reference")
+    ap.add_argument("--pmc-shape", default="qwen8k", choices=["qwen8k", "llama2k", "single131k"],
+                    help="the layer shape of --pmc-probe (qwen8k: the workload, with the other "
+                         "formats; llama2k, single131k: the other shapes, fused and BF16 only)")
     args = ap.parse_args()
     if args.cpu_all_cores:        # child process: host only, never touches the GPU
         print(json.dumps(cpu_all_cores()), flush=True)
@@ -195,7 +198,10 @@ def main():
     torch.cuda.set_device(dev)
     kvz.kvz_device_check(0)
     if args.pmc_probe:
-        pmc_probe(args, dev)
+        if args.pmc_shape == "qwen8k":
+            pmc_probe(args, dev)
+        else:
+            pmc_probe_other(args, dev, next(c for c in OTHER_CONFIGS if c[0] == args.pmc_shape))
         return
     if args.breakdown:
         print(json.dumps({"breakdown": breakdown(args, dev)}), flush=True)
@@ -875,8 +881,8 @@ def other_config(args, dev, name, bsz, hq, hkv, n_comp, n_layers, u_max, forced,
 
 def breakdown(args, dev):
     """The attention time split into KV loading, exponent decoding and computation (GAAC page,
-    "Attention Time Breakdown", Table 5), at the 8K workload and the 2K batch shape, 8 distinct
-    layers each.  The library's compile-time variants of the attention kernel time the page loads
+    "Attention Time Breakdown", Table 5), at the 8K workload, the 2K batch shape (8 distinct
+    layers each) and the single 131K-token sequence (4 layers).  The library's compile-time variants of the attention kernel time the page loads
     alone (KVZ_PART_LOAD) and the loads with the in-register restore (KVZ_PART_LOAD_RESTORE);
     decoding = (loads + restore) - loads, computation = full call - (loads + restore) (scores,
     softmax, products, tail page, merge).  The uncompressed kernel gives its own loading and
@@ -896,16 +902,20 @@ def breakdown(args, dev):
     arena.close()
     del layers
     torch.cuda.empty_cache()
-    name, bsz, hq, hkv, n_comp, _, u_max, forced, seed, stress = OTHER_CONFIGS[0]
-    arena, layers, counts = other_layers(dev, bsz, hq, hkv, n_comp, BREAKDOWN_LAYERS, u_max,
-                                         forced, seed, stress)
-    lens = torch.as_tensor([16 * c for c in counts], dtype=torch.int32, device=dev)
-    ncomp = torch.as_tensor(counts, dtype=torch.int32, device=dev)
-    ws = paged.workspace(bsz, hq, hkv, max(counts), args.splits, device=dev)
-    res[name] = _breakdown_shape(args, arena, layers, lens, ncomp, ws, sum(counts), hkv,
-                                 f"{bsz} sequences x {16 * n_comp} tokens, {hq}/{hkv} heads, "
-                                 f"u~U[-{u_max:g},{u_max:g}], {forced:.0%} forced-raw blocks")
-    arena.close()
+    for name, bsz, hq, hkv, n_comp, n_layers, u_max, forced, seed, stress in OTHER_CONFIGS[:2]:
+        arena, layers, counts = other_layers(dev, bsz, hq, hkv, n_comp,
+                                             min(n_layers, BREAKDOWN_LAYERS), u_max, forced, seed,
+                                             stress)
+        lens = torch.as_tensor([16 * c for c in counts], dtype=torch.int32, device=dev)
+        ncomp = torch.as_tensor(counts, dtype=torch.int32, device=dev)
+        ws = paged.workspace(bsz, hq, hkv, max(counts), args.splits, device=dev)
+        res[name] = _breakdown_shape(args, arena, layers, lens, ncomp, ws, sum(counts), hkv,
+                                     f"{bsz} sequence(s) x {16 * n_comp} tokens, {hq}/{hkv} heads, "
+                                     f"u~U[-{u_max:g},{u_max:g}], {forced:.0%} forced-raw blocks"
+                                     + (", stress values" if stress else ""))
+        arena.close()
+        del layers
+        torch.cuda.empty_cache()
     return res
 
 
@@ -1001,6 +1011,38 @@ def pmc_probe(args, dev):
     log(f"pmc probe done: {st['live_granules'] * 256} record bytes in the layer, algorithmic "
         f"{alg_bytes_per_layer(st['live_granules'] * 256):.0f} bytes per call; kernel source "
         f"sha256 {kernel_source_sha()}")
+    arena.close()
+
+
+def pmc_probe_other(args, dev, cfg):
+    """Counter-run launches for another shape: the 1 GiB device copy (the byte counters' scale
+    reference), then 3 fused and 3 BF16 attention calls over one layer of the shape."""
+    import torch
+    from decode_attention_kvz_amd import kvz, paged
+    name, bsz, hq, hkv, n_comp, _, u_max, forced, seed, stress = cfg
+    src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    arena, layers, counts = other_layers(dev, bsz, hq, hkv, n_comp, 1, u_max, forced, seed, stress)
+    L = layers[0]
+    lens = torch.as_tensor([16 * c for c in counts], dtype=torch.int32, device=dev)
+    ncomp = torch.as_tensor(counts, dtype=torch.int32, device=dev)
+    ws = paged.workspace(bsz, hq, hkv, max(counts), args.splits, device=dev)
+    for _ in range(3):
+        kvz.kvz_decode_attention(L["q"], L["out"], arena.arena, L["meta"], L["block_table"], lens,
+                                 ncomp, None, SCALE, ws, args.splits)
+    for _ in range(3):
+        kvz.kvz_bf16_decode_attention(L["q"], L["out"], L["store"], L["block_table"], lens, ncomp,
+                                      None, SCALE, ws, hkv, args.splits)
+    torch.cuda.synchronize()
+    rec = arena.stats()["live_granules"] * 256
+    n_phys = sum(counts)
+    io = n_phys * (hkv * 16 + 4) + bsz * hq * 128 * (2 + 4)
+    log(f"pmc probe done: {rec} record bytes in the layer, algorithmic {rec + io} bytes per call "
+        f"(bf16 {n_phys * hkv * 2 * 4096 + io}); shape {name}; kernel source sha256 "
+        f"{kernel_source_sha()}")
     arena.close()
 
 
