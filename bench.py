@@ -250,8 +250,9 @@ def main():
                                           n_comp, L["tail"], SCALE, ws, HKV, args.splits)
 
     def complete_pages():
-        kvz.kvz_encode_pages(arena.pool, comp_items, n_comp_items)
-        kvz.kvz_slot_free(arena.pool, comp_ptrs)
+        # one launch: free the records the previous step stored (steady state), encode this
+        # step's completed pages into them
+        kvz.kvz_complete_pages(arena.pool, comp_ptrs, comp_items, n_comp_items)
 
     def capture(fn):
         """Eager warm-up calls, then a HIP graph of fn (host launch overhead cannot starve the
@@ -745,9 +746,10 @@ def compressible_variant(args, dev, seq_lens, n_comp, ws):
 def online_completion(args, dev):
     """Online page completion at the 64-sequence, 32-layer, 8-KV-head shape with staggered
     phases: every step 4 sequences complete a page, so 4 x 32 layers x 8 heads x K|V = 2,048
-    groups are encoded and, in steady state, as many are freed.  One graph per step: free the
-    2,048 groups the previous step stored, then encode the new ones into the same metadata (the
-    freed runs are reused, deterministic in item order).  Forced-raw fraction 0 / 10 / 50 %."""
+    groups are encoded and, in steady state, as many are freed.  One graph per step holding one
+    kvz_complete_pages launch: free the 2,048 groups the previous step stored, then encode the new
+    ones into the same metadata (the freed runs are reused, deterministic in item order).
+    Forced-raw fraction 0 / 10 / 50 %."""
     import torch
     from decode_attention_kvz_amd import kvz, paged, synth
     n_seq, n_layers, hkv = 4, 32, 8
@@ -766,9 +768,10 @@ def online_completion(args, dev):
         kvz.kvz_encode_pages(arena.pool, d_items, n)
 
         def step():
-            kvz.kvz_slot_free(arena.pool, ptrs)
-            kvz.kvz_encode_pages(arena.pool, d_items, n)
-        us = graph_us_per_layer(step, 1, args)
+            kvz.kvz_complete_pages(arena.pool, ptrs, d_items, n)
+        # eight steps per graph, as inside a captured decode step (not the launch of a
+        # one-node graph per step)
+        us = graph_us_per_layer(lambda: [step() for _ in range(8)], 8, args)
         st = arena.stats()
         rec = st["live_granules"] * 256
         raw = st["live_raw_blocks"] / max(st["live_runs"] * 4, 1)

@@ -138,23 +138,29 @@ struct kvz_pool {
   int device;
   void* scratch;   // device: per-tile counts of the allocation / free passes (in the state buffer)
   uint32_t granule_bytes;   // 256 (BF16 formats) or 128 (FP8 tiles, kvz_fp8_pool_init)
-  void* enc_scratch;        // device: look-back records of the one-pass encoder (state buffer)
+  void* enc_scratch;        // device: the one-pass encoder's records (state buffer)
   uint32_t enc_epoch;       // the last one-pass encode launch's number (1 .. 2^30 - 1, cycling)
 };
 
 namespace kvz {
-// Record of one tile of a one-pass encode launch: its items of each size class; tile 0's also
-// holds the bin counts and frontier that the launch started from.  status = epoch << 2 | 1 once
-// the record is complete; a record of another launch has another epoch.
+// Records of a one-pass page-completion launch (the encoder's scratch in the pool state):
+//  * one 128-byte slot per free tile: its counts of freed runs per size class, and status =
+//    epoch << 2 | state (1: counts complete, 3: its bin stores and clears complete); slot 0 also
+//    holds the bin counts and frontier the launch started from (state >= 1 once they are out),
+//    written by tile 0 whether it frees or encodes; bad: a free tile that could not free;
+//  * one 64-bit word per encode tile: epoch << 32 | its item counts per size class, 6 bits each.
+// A record of another launch has another epoch.
 struct EncodeSlot {
   uint32_t status;
   uint32_t agg[kBins];
   uint32_t snap[kBins];
   uint32_t f0_lo, f0_hi;
-  uint32_t pad[19];
+  uint32_t bad;
+  uint32_t pad[18];
 };
 static_assert(sizeof(EncodeSlot) == 128, "one record per 128 bytes");
-constexpr int kMaxEncodeTiles = 16384;
-// records, then the ticket counter that orders the tiles of a launch
-constexpr uint64_t kEncodeScratchBytes = (uint64_t)kMaxEncodeTiles * sizeof(EncodeSlot) + 256;
+constexpr int kMaxFreeSlots = 256;        // free tiles per launch (one waiting thread each)
+constexpr int kMaxEncodeTiles = 4096;     // encode tiles per launch
+constexpr uint64_t kEncodeScratchBytes =
+    (uint64_t)kMaxFreeSlots * sizeof(EncodeSlot) + (uint64_t)kMaxEncodeTiles * sizeof(uint64_t);
 }  // namespace kvz

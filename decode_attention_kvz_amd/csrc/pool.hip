@@ -549,12 +549,22 @@ __global__ __launch_bounds__(kThreads) void pool_free_small_kernel(PoolHdr* hdr,
   uint2 rec[kSmallPer];
 #pragma unroll
   for (int u = 0; u < kSmallPer; ++u) m[u] = (u < per && i0 + u < n) ? metas[i0 + u] : nullptr;
+  typedef __attribute__((address_space(1))) uint64_t global_u64;   // global, not flat, accesses
 #pragma unroll
-  for (int u = 0; u < kSmallPer; ++u)
-    rec[u] = m[u] ? *reinterpret_cast<const uint2*>(m[u]) : make_uint2(KVZ_OFF_NONE, 0u);
-  uint64_t cnt[kBins];
-#pragma unroll
-  for (int k = 0; k < kBins; ++k) cnt[k] = hdr->bin_cnt[k];
+  for (int u = 0; u < kSmallPer; ++u) {
+    const uint64_t v = m[u] ? *(const global_u64*)(m[u]) : (uint64_t)KVZ_OFF_NONE;
+    rec[u] = make_uint2((uint32_t)v, (uint32_t)(v >> 32));
+  }
+  // the header's per-class fields in LDS before any store (the bins share the state buffer with
+  // the header, so a field read after a bin store would be a new round trip per item; a
+  // register array indexed by class would live in scratch memory); the scan's barriers order
+  // these writes before every read
+  __shared__ uint64_t s_cnt[kBins], s_cap[kBins], s_base[kBins];
+  if (threadIdx.x < kBins) {
+    s_cnt[threadIdx.x] = hdr->bin_cnt[threadIdx.x];
+    s_cap[threadIdx.x] = hdr->bin_cap[threadIdx.x];
+    s_base[threadIdx.x] = hdr->bin_base[threadIdx.x];
+  }
   uint32_t lcnt[kBins];
 #pragma unroll
   for (int k = 0; k < kBins; ++k) lcnt[k] = 0;
@@ -572,11 +582,11 @@ __global__ __launch_bounds__(kThreads) void pool_free_small_kernel(PoolHdr* hdr,
   for (int u = 0; u < kSmallPer; ++u) {
     const int k = key[u];
     if (k < 0) continue;
-    const uint64_t slot = cnt[k] + pick(kbase, k);
+    const uint64_t slot = s_cnt[k] + pick(kbase, k);
 #pragma unroll
     for (int j = 0; j < kBins; ++j) kbase[j] += j == k ? 1u : 0u;
-    if (slot < hdr->bin_cap[k]) {
-      bins[hdr->bin_base[k] + slot] = rec[u].x;
+    if (slot < s_cap[k]) {
+      bins[s_base[k] + slot] = rec[u].x;
       my_runs += 1;
       my_gran += run_granules((uint32_t)k);
       my_raw += (uint32_t)k;
@@ -586,15 +596,15 @@ __global__ __launch_bounds__(kThreads) void pool_free_small_kernel(PoolHdr* hdr,
   }
 #pragma unroll
   for (int u = 0; u < kSmallPer; ++u)
-    if (m[u]) *reinterpret_cast<uint2*>(m[u]) = make_uint2(KVZ_OFF_NONE, 0u);
+    if (m[u]) *(global_u64*)(m[u]) = (uint64_t)KVZ_OFF_NONE;
   const uint64_t runs = block_sum(my_runs, s_red);
   const uint64_t gran = block_sum(my_gran, s_red);
   const uint64_t raw = block_sum(my_raw, s_red);
   const uint64_t bad = block_sum(my_bad, s_red);
   if (threadIdx.x < kBins) {
     const int k = (int)threadIdx.x;
-    const uint64_t c = cnt[k] + pick(ktot, k);
-    hdr->bin_cnt[k] = c < hdr->bin_cap[k] ? c : hdr->bin_cap[k];
+    const uint64_t c = s_cnt[k] + pick(ktot, k);
+    hdr->bin_cnt[k] = c < s_cap[k] ? c : s_cap[k];
   }
   if (threadIdx.x == 0) {
     hdr->live_runs -= runs;

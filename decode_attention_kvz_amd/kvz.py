@@ -40,7 +40,8 @@ FP8_GRANULE = 128
 
 EXPORTED = [
     "kvz_version", "kvz_last_error", "kvz_device_check", "kvz_pool_state_bytes", "kvz_pool_init",
-    "kvz_pool_destroy", "kvz_slot_alloc", "kvz_slot_free", "kvz_encode_pages", "kvz_decode_block",
+    "kvz_pool_destroy", "kvz_slot_alloc", "kvz_slot_free", "kvz_encode_pages", "kvz_complete_pages",
+    "kvz_decode_block",
     "kvz_attn_workspace_bytes", "kvz_decode_attention", "kvz_bf16_pack_pages",
     "kvz_bf16_decode_attention", "kvz_pool_stats", "kvz_stream_read", "kvz_decompress_pages",
     "kvz_pool_capacity", "kvz_gaac_calibrate", "kvz_gaac_encode_pages", "kvz_gaac_decompress_pages",
@@ -131,6 +132,8 @@ _sig = {
     "kvz_slot_alloc": ([_vp, _vp, _vp, ctypes.c_int32, _vp], ctypes.c_int),
     "kvz_slot_free": ([_vp, _vp, ctypes.c_int32, _vp], ctypes.c_int),
     "kvz_encode_pages": ([_vp, _vp, ctypes.c_int32, ctypes.c_uint32, _vp], ctypes.c_int),
+    "kvz_complete_pages": ([_vp, _vp, ctypes.c_int32, _vp, ctypes.c_int32, ctypes.c_uint32, _vp],
+                           ctypes.c_int),
     "kvz_decode_block": ([_vp, ctypes.c_uint64, _vp, ctypes.c_int32, _vp, _vp], ctypes.c_int),
     "kvz_attn_workspace_bytes": ([ctypes.c_int32] * 5 + [ctypes.POINTER(ctypes.c_uint64)],
                                  ctypes.c_int),
@@ -267,6 +270,19 @@ def kvz_encode_pages(pool, items, n: int, flags: int = 0, stream=None) -> None:
     """items: device tensor holding n kvz_encode_item records (ENCODE_ITEM_DTYPE)."""
     _dev("items", items, min_bytes=n * ENCODE_ITEM_DTYPE.itemsize)
     _check(_lib.kvz_encode_pages(pool, _ptr(items), n, flags, _stream(stream)))
+
+
+def kvz_complete_pages(pool, meta_ptrs, items, n: int, flags: int = 0, stream=None) -> None:
+    """kvz_slot_free(meta_ptrs) then kvz_encode_pages(items, n) in one call: meta_ptrs is an
+    int64 [n_free] device tensor of device pointers to kvz_group_meta (or None)."""
+    n_free = 0
+    if meta_ptrs is not None:
+        _dev("meta_ptrs", meta_ptrs, dtype=_torch().int64)
+        n_free = meta_ptrs.shape[0]
+    if n:
+        _dev("items", items, min_bytes=n * ENCODE_ITEM_DTYPE.itemsize)
+    _check(_lib.kvz_complete_pages(pool, _ptr(meta_ptrs) if n_free else None, n_free,
+                                   _ptr(items) if n else None, n, flags, _stream(stream)))
 
 
 def kvz_decode_block(arena, refs, n: int, out, stream=None) -> None:

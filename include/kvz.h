@@ -225,6 +225,17 @@ int kvz_slot_free(kvz_pool* p, kvz_group_meta* const* d_metas, int32_t n, hipStr
 int kvz_encode_pages(kvz_pool* p, const kvz_encode_item* d_items, int32_t n, uint32_t flags,
                      hipStream_t s);
 
+/* A decode step's page work in one launch: exactly kvz_slot_free(p, d_free, n_free) followed by
+ * kvz_encode_pages(p, d_items, n, flags) - the same offsets, records, bins and counters - for a
+ * step where finished sequences release their groups and completed pages are encoded ([ZF]
+ * "How it works", memory-manager paragraph: space freed by one sequence is reused by the next
+ * page; [GAAC] "Block-Wise Compression Scheduling": encode once, at completion).  A group may be
+ * both freed and re-encoded (its record is read by the free before the encode writes it).
+ * d_free: device array of n_free device pointers (may be null when n_free is 0); d_items:
+ * device [n].  Errors as for the two calls; nothing is launched on an argument error. */
+int kvz_complete_pages(kvz_pool* p, kvz_group_meta* const* d_free, int32_t n_free,
+                       const kvz_encode_item* d_items, int32_t n, uint32_t flags, hipStream_t s);
+
 /* Rebuild n blocks to natural order: d_out device [n][16 tokens][32 dims] BF16 ([ZF] step 4).
  * A block of a group that is not stored, or that does not lie inside the arena_bytes of
  * d_arena, decodes to zeros. */

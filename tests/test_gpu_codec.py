@@ -265,13 +265,15 @@ def test_slot_alloc_free_churn_matches_model():
     assert model.enospc > 0, "the churn should have exhausted the pool at least once"
 
 
-@pytest.mark.parametrize("forced,n_layers", [(0.0, 4), (0.10, 4), (0.50, 4), (0.10, 32)])
-def test_online_page_completion_churn(forced, n_layers):
+@pytest.mark.parametrize("forced,n_layers,fused", [(0.0, 4, False), (0.10, 4, False), (0.50, 4, False),
+                                                   (0.10, 32, False), (0.10, 4, True), (0.10, 32, True)])
+def test_online_page_completion_churn(forced, n_layers, fused):
     """Online encode at page completion with frees and reuse across layers (64 sequences,
     8 KV heads, 4 layers with a small arena that runs out, or all 32 layers of the online
     workload with room for every page, staggered phases): offsets and tags equal the oracle
-    pool model and classification after every step; live groups decode to their source pages."""
-    announce(f"online churn forced={forced} layers={n_layers}")
+    pool model and classification after every step; live groups decode to their source pages.
+    fused: each step's free and encode are one kvz_complete_pages call."""
+    announce(f"online churn forced={forced} layers={n_layers} fused={fused}")
     rng = np.random.default_rng(int(forced * 100) + 3)
     n_seq, hkv, page_bank = 64, 8, 16
     bank = synth.kv_pages(n_seq, page_bank, hkv, seed=3, forced_frac=forced, device="cuda")
@@ -287,6 +289,7 @@ def test_online_page_completion_churn(forced, n_layers):
     for step in range(160):
         # sequences that reached their target free every group and restart
         done = [s for s in range(n_seq) if length[s] >= target[s]]
+        d_free = None
         if done:
             ptrs, model_metas = [], []
             for s in done:
@@ -299,7 +302,9 @@ def test_online_page_completion_churn(forced, n_layers):
                         model_metas.extend(live.pop((layer, s, p)))
                 length[s] = 0
                 target[s] = rng.integers(32, 128)
-            kvz.kvz_slot_free(arena.pool, torch.from_numpy(np.asarray(ptrs, dtype=np.int64)).cuda())
+            d_free = torch.from_numpy(np.asarray(ptrs, dtype=np.int64)).cuda()
+            if not fused:
+                kvz.kvz_slot_free(arena.pool, d_free)
             model.free(model_metas)
         length += 1
         # pages that completed with this token: encode them in all layers
@@ -317,10 +322,15 @@ def test_online_page_completion_churn(forced, n_layers):
                         kinds.append(kind)
                         want_tags.append(bank_h[s, bp, kind, h])
                 keys.append((layer, s, p))
+        if fused and d_free is not None and not src:
+            kvz.kvz_complete_pages(arena.pool, d_free, None, 0)
         if src:
             items = kvz.encode_items(src, dst, 128, kinds)
             d_items = torch.from_numpy(items).cuda()
-            kvz.kvz_encode_pages(arena.pool, d_items, len(src))
+            if fused:
+                kvz.kvz_complete_pages(arena.pool, d_free, d_items, len(src))
+            else:
+                kvz.kvz_encode_pages(arena.pool, d_items, len(src))
             tags = _oracle_tags(np.stack(want_tags), kinds)
             offs = model.alloc([t.tolist() for t in tags])
             got = np.stack([m.cpu().numpy().reshape(-1, 8) for m in metas])   # [L, groups, 8]
