@@ -167,6 +167,9 @@ __global__ __launch_bounds__(256) void pack_kernel(const kvz_encode_item* items,
 // agent-scope (sc1) stores and loads: a record's fields are stored, the thread waits for those
 // stores to complete (s_waitcnt vmcnt(0)), then its status is stored; a reader loads the status
 // and only then the fields.  An encode tile's record is one 64-bit word (epoch and counts).
+// The epoch (the launch's number) is read from the pool state at the start of the launch and
+// advanced by its last workgroup, so every execution - a replay of a captured graph too - tags
+// its records anew.
 constexpr int kEncWaves = 4;
 constexpr int kEncThreads = kEncWaves * 64;
 constexpr int kFreePer = 4;                                  // listed groups per thread of a free tile
@@ -176,6 +179,8 @@ static_assert(kMaxFreeTiles <= kEncThreads, "one waiting thread per free tile");
 constexpr uint32_t kMaxSpins = 1u << 20;   // a wait that never ends marks its tile's items unstored
 constexpr uint32_t kStAgg = 1, kStDone = 3;                  // free-slot states (low two status bits)
 constexpr int kCountBits = 6;                                // per class in an encode record
+// the control area's words: launches completed, finished workgroups of the running launch
+constexpr int kCtlLaunches = 0, kCtlFinished = 1;
 
 __device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -255,8 +260,8 @@ __device__ __forceinline__ bool read_start(const EncodeSlot* slots, uint32_t epo
 template <int kPolicy, int IPW>
 __global__ __launch_bounds__(kEncThreads) void encode_onepass_kernel(
     const kvz_encode_item* items, int n, kvz_group_meta* const* frees, int n_free, uint32_t flags,
-    PoolHdr* hdr, uint32_t* bins, uint8_t* arena, EncodeSlot* slots, uint64_t* erec,
-    uint32_t epoch, int n_free_tiles, int n_tiles) {
+    PoolHdr* hdr, uint32_t* bins, uint8_t* arena, uint32_t* ctl, EncodeSlot* slots, uint64_t* erec,
+    int n_free_tiles, int n_tiles) {
   constexpr int kTileItems = kEncWaves * IPW;
   static_assert(kTileItems < (1 << kCountBits), "a tile's counts fit their record fields");
   typedef __attribute__((address_space(1))) uint64_t global_u64;
@@ -281,7 +286,15 @@ __global__ __launch_bounds__(kEncThreads) void encode_onepass_kernel(
   }
   const int Tf = n_free_tiles;
   const int G = gridDim.x;
-  if (threadIdx.x == 0) sh.bad = 0u;
+  // The launch's number tags its records: read from the device at the start (so a replayed
+  // graph gets a new one each time), advanced by the last workgroup to finish.
+  __shared__ uint32_t s_epoch;
+  if (threadIdx.x == 0) {
+    sh.bad = 0u;
+    s_epoch = ld_agent(ctl + kCtlLaunches) % ((1u << 30) - 1u) + 1u;
+  }
+  __syncthreads();
+  const uint32_t epoch = s_epoch;
   // tile 0 publishes the counters the launch starts from (read before its first store)
   if (blockIdx.x == 0 && threadIdx.x == 0) {
 #pragma unroll
@@ -587,18 +600,22 @@ __global__ __launch_bounds__(kEncThreads) void encode_onepass_kernel(
       }
       if (lane == 0) *(global_u64*)(it[u].dst) = (uint64_t)off | ((uint64_t)tags[u] << 32);
       if (off == KVZ_OFF_NONE) continue;
+      // non-temporal stores: the records stream to memory instead of staying dirty in the L2
+      // until the end of the launch
       uint8_t* blk = arena + (size_t)off * KVZ_GRANULE_BYTES;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t tag = (tags[u] >> (8 * j)) & 0xFFu;
         if (tag == KVZ_RAW_TAG) {
-          *reinterpret_cast<uint4*>(blk + kRawChunkBytes * lane) = w[u][j];
+          typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+          __builtin_nontemporal_store(__builtin_bit_cast(u32x4, w[u][j]),
+                                      reinterpret_cast<u32x4*>(blk + kRawChunkBytes * lane));
         } else {
           const uint3 c = compress_chunk(w[u][j], tag * 0x01010101u);
           uint32_t* d = reinterpret_cast<uint32_t*>(blk + kCompChunkBytes * lane);
-          d[0] = c.x;
-          d[1] = c.y;
-          d[2] = c.z;
+          __builtin_nontemporal_store(c.x, d);
+          __builtin_nontemporal_store(c.y, d + 1);
+          __builtin_nontemporal_store(c.z, d + 2);
         }
         blk += block_bytes(tag);
       }
@@ -623,6 +640,15 @@ __global__ __launch_bounds__(kEncThreads) void encode_onepass_kernel(
         add_agent(&hdr->live_raw_blocks, (uint64_t)0 - f[2]);
         add_agent(&hdr->frontier, (uint64_t)0 - f[3]);
       }
+    }
+  }
+  // every workgroup has read the launch's number: the last to finish advances it
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t before = __hip_atomic_fetch_add(ctl + kCtlFinished, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (before + 1u == gridDim.x) {
+      st_agent(ctl + kCtlFinished, 0u);
+      __hip_atomic_fetch_add(ctl + kCtlLaunches, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -751,7 +777,8 @@ int encode_onepass(kvz_pool* p, const kvz_encode_item* d_items, int n,
                    kvz_group_meta* const* d_free, int n_free, uint32_t flags, hipStream_t s) {
   PoolHdr* hdr = (PoolHdr*)p->state;
   uint32_t* bins = (uint32_t*)((uint8_t*)p->state + kPoolHdrBytes);
-  EncodeSlot* slots = (EncodeSlot*)p->enc_scratch;
+  uint32_t* ctl = (uint32_t*)p->enc_scratch;
+  EncodeSlot* slots = (EncodeSlot*)((uint8_t*)p->enc_scratch + kEncodeCtlBytes);
   uint64_t* erec = (uint64_t*)(slots + kMaxFreeSlots);
   const int ipw = n <= 4096 ? 1 : 2;
   const void* fn = ipw == 1 ? (const void*)encode_onepass_kernel<kCachedLoad, 1>
@@ -770,15 +797,14 @@ int encode_onepass(kvz_pool* p, const kvz_encode_item* d_items, int n,
   const int per_tile = kEncWaves * ipw;
   const int tiles = tf + (n + per_tile - 1) / per_tile;
   const int grid = tiles < resident ? tiles : resident;
-  p->enc_epoch = p->enc_epoch % ((1u << 30) - 1u) + 1u;
   if (ipw == 1)
     hipLaunchKernelGGL((encode_onepass_kernel<kCachedLoad, 1>), dim3(grid), dim3(kEncThreads), 0, s,
                        d_items, n, d_free, tf ? n_free : 0, flags, hdr, bins, (uint8_t*)p->arena,
-                       slots, erec, p->enc_epoch, tf, tiles);
+                       ctl, slots, erec, tf, tiles);
   else
     hipLaunchKernelGGL((encode_onepass_kernel<kCachedLoad, 2>), dim3(grid), dim3(kEncThreads), 0, s,
                        d_items, n, d_free, tf ? n_free : 0, flags, hdr, bins, (uint8_t*)p->arena,
-                       slots, erec, p->enc_epoch, tf, tiles);
+                       ctl, slots, erec, tf, tiles);
   return check_hip(hipGetLastError(), "encode launch");
 }
 

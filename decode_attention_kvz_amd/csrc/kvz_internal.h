@@ -139,11 +139,12 @@ struct kvz_pool {
   void* scratch;   // device: per-tile counts of the allocation / free passes (in the state buffer)
   uint32_t granule_bytes;   // 256 (BF16 formats) or 128 (FP8 tiles, kvz_fp8_pool_init)
   void* enc_scratch;        // device: the one-pass encoder's records (state buffer)
-  uint32_t enc_epoch;       // the last one-pass encode launch's number (1 .. 2^30 - 1, cycling)
 };
 
 namespace kvz {
-// Records of a one-pass page-completion launch (the encoder's scratch in the pool state):
+// The one-pass page-completion encoder's scratch in the pool state: a 256-byte control area
+// (word 0: launches completed, which numbers the next launch's records; word 1: workgroups of
+// the running launch that have finished, back to zero at its end), then the records of a launch:
 //  * one 128-byte slot per free tile: its counts of freed runs per size class, and status =
 //    epoch << 2 | state (1: counts complete, 3: its bin stores and clears complete); slot 0 also
 //    holds the bin counts and frontier the launch started from (state >= 1 once they are out),
@@ -161,6 +162,7 @@ struct EncodeSlot {
 static_assert(sizeof(EncodeSlot) == 128, "one record per 128 bytes");
 constexpr int kMaxFreeSlots = 256;        // free tiles per launch (one waiting thread each)
 constexpr int kMaxEncodeTiles = 4096;     // encode tiles per launch
-constexpr uint64_t kEncodeScratchBytes =
-    (uint64_t)kMaxFreeSlots * sizeof(EncodeSlot) + (uint64_t)kMaxEncodeTiles * sizeof(uint64_t);
+constexpr uint64_t kEncodeCtlBytes = 256;
+constexpr uint64_t kEncodeScratchBytes = kEncodeCtlBytes + (uint64_t)kMaxFreeSlots * sizeof(EncodeSlot) +
+                                         (uint64_t)kMaxEncodeTiles * sizeof(uint64_t);
 }  // namespace kvz

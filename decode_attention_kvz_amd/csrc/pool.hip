@@ -732,7 +732,6 @@ int pool_init_g(kvz_pool** out, void* d_arena, uint64_t arena_bytes, void* d_sta
   p->scratch = (uint8_t*)d_state + align256(kPoolHdrBytes + 4 * entries);
   p->granule_bytes = granule;
   p->enc_scratch = enc;
-  p->enc_epoch = 0;
   *out = p;
   return KVZ_OK;
 }

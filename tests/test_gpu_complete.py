@@ -8,6 +8,7 @@
   same records, arena bytes and counters after every step, for frees of one to six free tiles
   (up to 1,024 groups each), frees that include the records the encode then rewrites, and an
   arena that runs out.
+* A captured kvz_complete_pages replayed with new item records each time equals eager calls.
 """
 import numpy as np
 import pytest
@@ -175,3 +176,49 @@ def test_complete_pages_equals_free_then_encode(arena_mb):
             assert torch.equal(pools[0].arena[a0:a1], pools[1].arena[a0:a1]), (step, d)
     if arena_mb == 24:
         assert model.enospc > 0, "the small arena should run out"
+
+
+@pytest.mark.parametrize("n", [2048, 9216])
+def test_graph_replays_with_new_items_match_eager_calls(n):
+    """A captured kvz_complete_pages replayed with other item records each time (other source
+    pages, so other size classes per tile) gives what eager calls on a second pool give: each
+    launch numbers its records from the device, so a replay never takes the previous replay's
+    records for its own."""
+    announce(f"complete_pages graph replays with new items, {n} groups")
+    rng = np.random.default_rng(n)
+    bank, nat, tags = _bank(seed=9, forced=0.30)
+    pools = [paged.SlotArena(256 << 20) for _ in range(2)]
+    metas, ptrs, items = [], [], []
+    src0 = rng.integers(0, nat.shape[0], size=n)
+    for i in range(2):
+        m = torch.empty((n, 8), dtype=torch.uint8, device="cuda")
+        m[:, :4] = 0xFF
+        m[:, 4:] = 0
+        metas.append(m)
+        ptrs.append(torch.from_numpy(m.data_ptr() + np.arange(n, dtype=np.int64) * 8).cuda())
+        items.append(_items(bank, src0, m, np.arange(n)))
+    # warm-up, capture (the captured call runs once more on replay)
+    for _ in range(2):
+        kvz.kvz_complete_pages(pools[0].pool, ptrs[0], items[0], n)
+        kvz.kvz_complete_pages(pools[1].pool, ptrs[1], items[1], n)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        kvz.kvz_complete_pages(pools[0].pool, ptrs[0], items[0], n)
+    kvz.kvz_complete_pages(pools[1].pool, ptrs[1], items[1], n)   # the capture's turn, eagerly
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    for rep in range(6):
+        src = rng.integers(0, nat.shape[0], size=n)
+        items[0].copy_(_items(bank, src, metas[0], np.arange(n)))
+        items[1].copy_(_items(bank, src, metas[1], np.arange(n)))
+        torch.cuda.synchronize()
+        g.replay()
+        kvz.kvz_complete_pages(pools[1].pool, ptrs[1], items[1], n)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(metas[0].cpu().numpy(), metas[1].cpu().numpy(), err_msg=f"replay {rep}")
+        got, gtags = _records(metas[0], np.arange(n))
+        np.testing.assert_array_equal(gtags, tags[src])
+        assert pools[0].stats() == pools[1].stats(), rep
+        assert pools[0].stats()["enospc"] == 0
