@@ -17,16 +17,19 @@
 //
 // Work decomposition (one workgroup = one unit = (sequence b, KV head, split s)):
 //   * a unit covers a contiguous range of its sequence's pages (the tail page counts as the
-//     last page); each of its four waves walks one consecutive quarter; per page a wave loads
-//     the four K and four V blocks of its KV head (16 bytes per lane per block: a compressed
-//     chunk is 12 bytes and the next 4 are ignored), restores them in registers, and runs
+//     last page); each of its waves (8 for groups of up to 4 query heads, else 4) walks one
+//     consecutive part; per page a wave loads the four K and four V blocks of its KV head (16
+//     bytes per lane per block: a compressed chunk is 12 bytes and the next 4 are ignored),
+//     restores them in registers, and runs
 //       S[16 tokens x 16 heads] = K_page(16x128) . Q^T   as 4 x v_mfma_f32_16x16x32_bf16,
-//       O[32 heads x 128]      += P(32x16) . V_page    as 4 x 2 x v_mfma_f32_32x32x16_bf16,
-//     with P split into bf16 hi + lo parts so that P is carried to ~2^-17 relative;
+//       O[32 rows x 128]       += P(32x16) . V_page    as 4 x v_mfma_f32_32x32x16_bf16,
+//     with P split into bf16 hi + lo parts (rows h and 16 + h of P for head h) so that P is
+//     carried to ~2^-17 relative;
 //   * the query group (G <= 16 heads sharing the KV head) is the MFMA's head dimension;
 //   * online softmax in base 2 per head; rows of O are rescaled only when a head's max rises;
-//   * the four waves' (m, l, O) are merged in LDS; a unit then writes the normalized output
-//     (one split per sequence: no further launch) or its partial, which attn_combine merges.
+//   * the waves' (m, l, O) are merged in LDS; a unit then writes the normalized output (one
+//     split per sequence: no further launch) or its partial, merged in the kernel by the last
+//     piece to finish (up to 4 splits) or by attn_combine.
 #include "fp8_internal.h"
 
 #include <math.h>
@@ -555,8 +558,8 @@ __device__ __forceinline__ SplitOf split_of(const int32_t* n_comp_v, const int32
   return r;
 }
 
-template <int GB, int FMT, int FK = 0, int MODE = kModeFull>
-__global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
+template <int GB, int FMT, int FK = 0, int MODE = kModeFull, int NW = 4>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_split_kernel(AttnParams p) {
   // COMP: pages are found through the pool metadata (exponent-coded, GAAC or FP8 tiles)
   constexpr bool COMP = FMT == kFmtZf || FMT == kFmtGaac || FMT == kFmtFp8c;
   constexpr bool IS_FP8 = FMT == kFmtFp8 || FMT == kFmtFp8c;
@@ -568,7 +571,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
   constexpr uint32_t kFieldShift = FMT == kFmtFp8c ? Fp8Fmt<FK>::kFracBits : 0u;
   __shared__ uint32_t s_spread3[CODED ? 4096 : 1];
   if constexpr (CODED) {
-    for (int x = threadIdx.x; x < 4096; x += 256) s_spread3[x] = gaac_spread3((uint32_t)x) << kFieldShift;
+    for (int x = threadIdx.x; x < 4096; x += 64 * NW) s_spread3[x] = gaac_spread3((uint32_t)x) << kFieldShift;
     __syncthreads();
   }
   const int lane = threadIdx.x & 63;
@@ -590,8 +593,8 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
   const int total = so.total;
   const int P0 = (int)(((int64_t)s * total) / so.sb);       // the workgroup's pages
   const int P1 = (int)(((int64_t)(s + 1) * total) / so.sb);
-  const int p0 = P0 + (int)(((int64_t)wave * (P1 - P0)) / 4);   // this wave's quarter
-  const int p1 = P0 + (int)(((int64_t)(wave + 1) * (P1 - P0)) / 4);
+  const int p0 = P0 + (int)(((int64_t)wave * (P1 - P0)) / NW);   // this wave's part
+  const int p1 = P0 + (int)(((int64_t)(wave + 1) * (P1 - P0)) / NW);
 
   // Q as the column operand of the 16x16x32 product: head lane%16, dims 32j + 8*(lane/16) + i.
   const int head = lane & 15;
@@ -1094,8 +1097,8 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
   // The four waves' (m, l) per head and unnormalized O rows meet in LDS; one merge per
   // (head, dim): M = max m_w, L = sum l_w 2^((m_w - M) c), O = sum O_w 2^((m_w - M) c), in wave
   // order (m: raw scores; c: the scale to log2 units).
-  __shared__ float s_m[4][16], s_l[4][16];
-  __shared__ float s_o[4][GB * KVZ_HEAD_DIM];
+  __shared__ float s_m[NW][16], s_l[NW][16];
+  __shared__ float s_o[NW][GB * KVZ_HEAD_DIM];
   if (lane < 16) {
     s_m[wave][lane] = sm.m_run;
     s_l[wave][lane] = l_tot;
@@ -1113,14 +1116,14 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
   // the only piece of its sequence normalizes in place
   const bool direct = p.merge_in_kernel ? so.sb == 1 : p.S == 1;
   const bool fused_merge = p.merge_in_kernel && !direct;
-  for (int idx = threadIdx.x; idx < p.G * KVZ_HEAD_DIM; idx += 256) {
+  for (int idx = threadIdx.x; idx < p.G * KVZ_HEAD_DIM; idx += 64 * NW) {
     const int h = idx / KVZ_HEAD_DIM, d = idx % KVZ_HEAD_DIM;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][h]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][h]);
     float L = 0.f, O = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float mw = s_m[w][h];
       const float c = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(to_log2(mw - M, c_log2));
       L += c * s_l[w][h];
@@ -1174,7 +1177,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnParams p) {
   __syncthreads();
   if (!s_last) return;
   const size_t u0 = (size_t)kvh * U + so.base;
-  for (int idx = threadIdx.x; idx < p.G * KVZ_HEAD_DIM; idx += 256) {
+  for (int idx = threadIdx.x; idx < p.G * KVZ_HEAD_DIM; idx += 64 * NW) {
     const int h = idx / KVZ_HEAD_DIM, d = idx % KVZ_HEAD_DIM;
     const float* ml = p.ws_ml + (u0 * p.G + h) * 2;
     const float* o = p.ws_o + u0 * p.G * KVZ_HEAD_DIM + (size_t)h * KVZ_HEAD_DIM + d;
@@ -1356,13 +1359,18 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(
   }
 }
 
-// Split count: one workgroup (one split, its four waves) per CU - the 2-page prefetch ring keeps
-// enough bytes in flight with 4 waves per CU, and measured as fast or faster than 2 workgroups
-// per CU on every workload shape - with at least 4 pages per wave.  Workgroup counts that are
-// not a multiple of the CU count leave some CUs one workgroup more than others (measured 10-20%
-// slower).  The coded tiles' restore has long dependent latencies (ballots, lane shuffles), so
-// those formats run two workgroups per CU (two waves per SIMD) to overlap them.
+// Split count: one workgroup (one split) per CU, with at least 4 pages per wave.  A group of up
+// to 4 query heads per KV head (every workload shape here) runs 8 waves per workgroup, two per
+// SIMD: one wave's softmax and products overlap the other's loads, and the 8 partial results
+// meet in LDS rather than in more splits (measured against 4 waves per workgroup on one box:
+// the 2K batch 40.0 / 39.3 vs 41.5 / 40.0 us per layer, one 131K sequence 93.7 / 93.9 vs
+// 96.5 / 98.2, the ragged batch 46.6 vs 49.2, the 8K layer 86.4 vs 86.9).  Larger groups run 4
+// waves per workgroup; their coded tiles two workgroups per CU (two waves per SIMD).  Workgroup
+// counts that are not a multiple of the CU count leave some CUs one workgroup more than others
+// (measured 10-20% slower).
+constexpr int kSmallGroupWaves = 8;
 constexpr int kCodedWgsPerCu = 2;
+int wgs_per_cu(bool coded, int G) { return (coded && G > 4) ? kCodedWgsPerCu : 1; }
 
 int choose_splits(int B, int Hkv, int max_pages, int n_cu, int wgs_per_cu = 1) {
   const int64_t units = (int64_t)(B * Hkv > 0 ? B * Hkv : 1);
@@ -1446,7 +1454,7 @@ int launch_attention(const CommonArgs& a, const uint8_t* kv, const kvz_group_met
   if (a.splits < 0 || a.splits > kMaxSplits) return set_error(KVZ_EINVAL, "splits out of range");
   const int S = a.splits ? a.splits
                          : choose_splits(a.batch, a.num_kv_heads, a.max_pages, device_cus(),
-                                         CODED ? kCodedWgsPerCu : 1);
+                                         wgs_per_cu(CODED, G));
   const WsLayout wl = workspace_layout(a.batch, a.num_q_heads, a.num_kv_heads, S);
   if (a.workspace_bytes < wl.total) return set_error(KVZ_EINVAL, "workspace too small");
   const uint64_t units = (uint64_t)a.batch * a.num_kv_heads * S;
@@ -1483,11 +1491,13 @@ int launch_attention(const CommonArgs& a, const uint8_t* kv, const kvz_group_met
   const dim3 grid((unsigned)units);
   if constexpr (MODE != kModeFull) {   // breakdown variants: groups of up to 4 query heads
     if (G > 4) return set_error(KVZ_EUNSUPPORTED, "the breakdown variants take up to 4 query heads per KV head");
-    hipLaunchKernelGGL((attn_split_kernel<4, FMT, FK, MODE>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((attn_split_kernel<4, FMT, FK, MODE, kSmallGroupWaves>), grid,
+                       dim3(64 * kSmallGroupWaves), 0, s, p);
     return check_hip(hipGetLastError(), "attention launch");
   }
   if (G <= 4)
-    hipLaunchKernelGGL((attn_split_kernel<4, FMT, FK>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((attn_split_kernel<4, FMT, FK, kModeFull, kSmallGroupWaves>), grid,
+                       dim3(64 * kSmallGroupWaves), 0, s, p);
   else if (G <= 8)
     hipLaunchKernelGGL((attn_split_kernel<8, FMT, FK>), grid, dim3(256), 0, s, p);
   else
