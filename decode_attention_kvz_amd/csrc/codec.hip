@@ -168,8 +168,8 @@ __global__ __launch_bounds__(256) void pack_kernel(const kvz_encode_item* items,
 // stores to complete (s_waitcnt vmcnt(0)), then its status is stored; a reader loads the status
 // and only then the fields.  An encode tile's record is one 64-bit word (epoch and counts).
 // The epoch (the launch's number) is read from the pool state at the start of the launch and
-// advanced by its last workgroup, so every execution - a replay of a captured graph too - tags
-// its records anew.
+// advanced once every workgroup has read it, so every execution - a replay of a captured graph
+// too - tags its records anew.
 constexpr int kEncWaves = 4;
 constexpr int kEncThreads = kEncWaves * 64;
 constexpr int kFreePer = 4;                                  // listed groups per thread of a free tile
@@ -180,7 +180,7 @@ constexpr uint32_t kMaxSpins = 1u << 20;   // a wait that never ends marks its t
 constexpr uint32_t kStAgg = 1, kStDone = 3;                  // free-slot states (low two status bits)
 constexpr int kCountBits = 6;                                // per class in an encode record
 // the control area's words: launches completed, finished workgroups of the running launch
-constexpr int kCtlLaunches = 0, kCtlFinished = 1;
+constexpr int kCtlLaunches = 0, kCtlRead = 1;
 
 __device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -258,7 +258,7 @@ __device__ __forceinline__ bool read_start(const EncodeSlot* slots, uint32_t epo
 }
 
 template <int kPolicy, int IPW>
-__global__ __launch_bounds__(kEncThreads) void encode_onepass_kernel(
+__global__ __launch_bounds__(kEncThreads, 4) void encode_onepass_kernel(
     const kvz_encode_item* items, int n, kvz_group_meta* const* frees, int n_free, uint32_t flags,
     PoolHdr* hdr, uint32_t* bins, uint8_t* arena, uint32_t* ctl, EncodeSlot* slots, uint64_t* erec,
     int n_free_tiles, int n_tiles) {
@@ -287,11 +287,17 @@ __global__ __launch_bounds__(kEncThreads) void encode_onepass_kernel(
   const int Tf = n_free_tiles;
   const int G = gridDim.x;
   // The launch's number tags its records: read from the device at the start (so a replayed
-  // graph gets a new one each time), advanced by the last workgroup to finish.
+  // graph gets a new one each time).  Each workgroup then counts itself in (only once its read
+  // has returned); the one that completes the count has seen every workgroup's read, so it
+  // advances the number at its end (the count's result is only needed there).
   __shared__ uint32_t s_epoch;
+  uint32_t read_before = 0;
   if (threadIdx.x == 0) {
     sh.bad = 0u;
-    s_epoch = ld_agent(ctl + kCtlLaunches) % ((1u << 30) - 1u) + 1u;
+    const uint32_t launches = ld_agent(ctl + kCtlLaunches);
+    s_epoch = launches % ((1u << 30) - 1u) + 1u;
+    __builtin_amdgcn_s_waitcnt(0);
+    read_before = __hip_atomic_fetch_add(ctl + kCtlRead, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   const uint32_t epoch = s_epoch;
@@ -428,18 +434,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_onepass_kernel(
 
   // ---------------- encode tiles
   const int t_first = (int)blockIdx.x < Tf ? (int)blockIdx.x + G : (int)blockIdx.x;
-  // the launch's start counters, once per workgroup (tile 0 has them already)
-  if (threadIdx.x == kEncThreads - 1 && blockIdx.x != 0 && t_first < n_tiles && !read_start(slots, epoch, sh))
-    sh.bad = 1u;
-  // the bins after this launch's free: every free tile done (its stores and clears are out)
-  uint32_t freed[kBins] = {0u, 0u, 0u, 0u, 0u};
-  if ((int)threadIdx.x < Tf && t_first < n_tiles) {
-    if (wait_state(slots + threadIdx.x, epoch, kStDone) == 0u || ld_agent(&slots[threadIdx.x].bad))
-      sh.bad = 1u;
-#pragma unroll
-    for (int k = 0; k < kBins; ++k) freed[k] = ld_agent(&slots[threadIdx.x].agg[k]);
-  }
-  block_sum5(freed, sh);   // (its barriers also order the shared counters above)
+  uint32_t freed[kBins] = {0u, 0u, 0u, 0u, 0u};   // runs this launch's free put in each bin
   uint32_t carry[kBins] = {0u, 0u, 0u, 0u, 0u};   // inclusive prefix of this workgroup's last tile
 
   for (int tile = t_first; tile < n_tiles; tile += G) {
@@ -509,6 +504,20 @@ __global__ __launch_bounds__(kEncThreads) void encode_onepass_kernel(
     for (int k = 0; k < kBins; ++k) {
       pre[k] += carry[k];
       carry[k] = pre[k] + agg[k];
+    }
+    if (tile == t_first) {
+      // once per workgroup, after its first tile's loads and counts: the launch's start counters
+      // (tile 0 has them already) and the bins after this launch's free (every free tile done:
+      // its bin stores and clears are out)
+      if (threadIdx.x == kEncThreads - 1 && blockIdx.x != 0 && !read_start(slots, epoch, sh))
+        sh.bad = 1u;
+      if ((int)threadIdx.x < Tf) {
+        if (wait_state(slots + threadIdx.x, epoch, kStDone) == 0u || ld_agent(&slots[threadIdx.x].bad))
+          sh.bad = 1u;
+#pragma unroll
+        for (int k = 0; k < kBins; ++k) freed[k] = ld_agent(&slots[threadIdx.x].agg[k]);
+      }
+      block_sum5(freed, sh);   // (its barriers also order the shared counters above)
     }
     const bool ok = sh.bad == 0u;
 
@@ -642,14 +651,10 @@ __global__ __launch_bounds__(kEncThreads) void encode_onepass_kernel(
       }
     }
   }
-  // every workgroup has read the launch's number: the last to finish advances it
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t before = __hip_atomic_fetch_add(ctl + kCtlFinished, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (before + 1u == gridDim.x) {
-      st_agent(ctl + kCtlFinished, 0u);
-      __hip_atomic_fetch_add(ctl + kCtlLaunches, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+  // the workgroup that completed the count: every workgroup has read the launch's number
+  if (threadIdx.x == 0 && read_before + 1u == gridDim.x) {
+    st_agent(ctl + kCtlRead, 0u);
+    __hip_atomic_fetch_add(ctl + kCtlLaunches, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

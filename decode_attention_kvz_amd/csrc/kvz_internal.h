@@ -143,8 +143,9 @@ struct kvz_pool {
 
 namespace kvz {
 // The one-pass page-completion encoder's scratch in the pool state: a 256-byte control area
-// (word 0: launches completed, which numbers the next launch's records; word 1: workgroups of
-// the running launch that have finished, back to zero at its end), then the records of a launch:
+// (word 0: launches started and numbered, which numbers the next launch's records; word 1:
+// workgroups of the running launch that have read its number, back to zero once all have),
+// then the records of a launch:
 //  * one 128-byte slot per free tile: its counts of freed runs per size class, and status =
 //    epoch << 2 | state (1: counts complete, 3: its bin stores and clears complete); slot 0 also
 //    holds the bin counts and frontier the launch started from (state >= 1 once they are out),
