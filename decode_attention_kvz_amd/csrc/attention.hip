@@ -361,14 +361,16 @@ struct Softmax {
     // holds row l%32 and tokens 8*(l/32)+0..7; this lane has tokens 4*(l/16)+0..3 of head l%16
     // and lane l^16 the other four of its eight: a lane of rows 0-15 takes that lane's hi, a lane
     // of rows 16-31 its lo, in one exchange per pair of tokens.
+    // (each pair converted by one packed instruction, round to nearest even as for one value)
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
     uint32_t hi[2], lo[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      const __bf16 h0 = (__bf16)pr[2 * m], h1 = (__bf16)pr[2 * m + 1];
-      const float r0 = pr[2 * m] - (float)h0, r1 = pr[2 * m + 1] - (float)h1;
-      const __bf16 l0 = (__bf16)r0, l1 = (__bf16)r1;
-      hi[m] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-      lo[m] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+      const f32x2_t pp = {pr[2 * m], pr[2 * m + 1]};
+      hi[m] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pp, bf16x2_t));
+      const f32x2_t rr = {pp[0] - __uint_as_float(hi[m] << 16), pp[1] - __uint_as_float(hi[m] & 0xFFFF0000u)};
+      lo[m] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rr, bf16x2_t));
     }
     const bool lo_rows = (lane & 16) != 0;
     // v_permlane16_swap of a value with itself: result [1] gives rows 0 and 2 of lanes the values
