@@ -287,38 +287,40 @@ __global__ __launch_bounds__(kEncThreads, 4) void encode_onepass_kernel(
   const int Tf = n_free_tiles;
   const int G = gridDim.x;
   // The launch's number tags its records: read from the device at the start (so a replayed
-  // graph gets a new one each time).  Each workgroup then counts itself in (only once its read
-  // has returned); the one that completes the count has seen every workgroup's read, so it
-  // advances the number at its end (the count's result is only needed there).
+  // graph gets a new one each time), and taken - put in LDS for the tile's first barrier - once
+  // the workgroup's first loads are out, so that waiting for it costs nothing.  Then each
+  // workgroup counts itself in; the one that completes the count has seen every workgroup's
+  // read, so it advances the number at its end (the count's result is only needed there).
   __shared__ uint32_t s_epoch;
-  uint32_t read_before = 0;
+  uint32_t launches = 0, read_before = 0;
   if (threadIdx.x == 0) {
     sh.bad = 0u;
-    const uint32_t launches = ld_agent(ctl + kCtlLaunches);
-    s_epoch = launches % ((1u << 30) - 1u) + 1u;
-    __builtin_amdgcn_s_waitcnt(0);
-    read_before = __hip_atomic_fetch_add(ctl + kCtlRead, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  const uint32_t epoch = s_epoch;
-  // tile 0 publishes the counters the launch starts from (read before its first store)
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    launches = ld_agent(ctl + kCtlLaunches);
+    if (blockIdx.x == 0) {   // tile 0: the counters the launch starts from
 #pragma unroll
-    for (int k = 0; k < kBins; ++k) {
-      sh.snap[k] = (uint32_t)hdr->bin_cnt[k];
-      st_agent(&slots[0].snap[k], sh.snap[k]);
-    }
-    const uint64_t f0 = hdr->frontier;
-    sh.f0_lo = (uint32_t)f0;
-    sh.f0_hi = (uint32_t)(f0 >> 32);
-    st_agent(&slots[0].f0_lo, sh.f0_lo);
-    st_agent(&slots[0].f0_hi, sh.f0_hi);
-    if (Tf == 0) {   // tile 0 encodes: its slot only carries these counters
-      __builtin_amdgcn_s_waitcnt(0);
-      st_agent(&slots[0].status, (epoch << 2) | kStAgg);
+      for (int k = 0; k < kBins; ++k) sh.snap[k] = (uint32_t)hdr->bin_cnt[k];
+      const uint64_t f0 = hdr->frontier;
+      sh.f0_lo = (uint32_t)f0;
+      sh.f0_hi = (uint32_t)(f0 >> 32);
     }
   }
-  __syncthreads();
+  // (thread 0, before a barrier that the whole workgroup reaches; once per workgroup)
+  auto take_number = [&]() {
+    if (threadIdx.x != 0) return;
+    s_epoch = launches % ((1u << 30) - 1u) + 1u;
+    if (blockIdx.x == 0) {   // tile 0 publishes the start counters (its slot's status below)
+#pragma unroll
+      for (int k = 0; k < kBins; ++k) st_agent(&slots[0].snap[k], sh.snap[k]);
+      st_agent(&slots[0].f0_lo, sh.f0_lo);
+      st_agent(&slots[0].f0_hi, sh.f0_hi);
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // the read has returned (and the counters are out)
+    if (blockIdx.x == 0 && Tf == 0)  // tile 0 encodes: its slot only carries these counters
+      st_agent(&slots[0].status, ((launches % ((1u << 30) - 1u) + 1u) << 2) | kStAgg);
+    read_before = __hip_atomic_fetch_add(ctl + kCtlRead, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  uint32_t epoch = 0;   // from s_epoch after the first barrier past take_number
+  bool numbered = false;
 
   // ---------------- a free tile (at most one per workgroup: every free tile is in the first
   // round): kFreePer listed groups per thread, in item order
@@ -352,7 +354,10 @@ __global__ __launch_bounds__(kEncThreads, 4) void encode_onepass_kernel(
       }
       if (lane == 63) sh.part[wave][k] = incl_t[k];
     }
+    take_number();
+    numbered = true;
     __syncthreads();
+    epoch = s_epoch;
     uint32_t agg[kBins], rank0[kBins];
 #pragma unroll
     for (int k = 0; k < kBins; ++k) {
@@ -471,7 +476,12 @@ __global__ __launch_bounds__(kEncThreads, 4) void encode_onepass_kernel(
       }
       if (lane == 0) s_cls[wave * IPW + u] = n_raw_of(tags[u]);
     }
+    if (!numbered) take_number();
     __syncthreads();
+    if (!numbered) {
+      epoch = s_epoch;
+      numbered = true;
+    }
     uint32_t agg[kBins];
 #pragma unroll
     for (int k = 0; k < kBins; ++k) agg[k] = 0;
@@ -651,6 +661,7 @@ __global__ __launch_bounds__(kEncThreads, 4) void encode_onepass_kernel(
       }
     }
   }
+  if (!numbered) take_number();   // (the host gives every workgroup a tile; kept for safety)
   // the workgroup that completed the count: every workgroup has read the launch's number
   if (threadIdx.x == 0 && read_before + 1u == gridDim.x) {
     st_agent(ctl + kCtlRead, 0u);
