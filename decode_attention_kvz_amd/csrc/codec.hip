@@ -179,6 +179,7 @@ static_assert(kMaxFreeTiles <= kEncThreads, "one waiting thread per free tile");
 constexpr uint32_t kMaxSpins = 1u << 20;   // a wait that never ends marks its tile's items unstored
 constexpr uint32_t kStAgg = 1, kStDone = 3;                  // free-slot states (low two status bits)
 constexpr int kCountBits = 6;                                // per class in an encode record
+constexpr int kPollBatch = 4;                                // record loads in flight per thread
 // the control area's words: launches completed, finished workgroups of the running launch
 constexpr int kCtlLaunches = 0, kCtlRead = 1;
 
@@ -380,7 +381,7 @@ __global__ __launch_bounds__(kEncThreads, 4) void encode_onepass_kernel(
     // every free tile's counts (each published only after its records were read): the runs
     // freed by the tiles below this one, and leave to clear; then the launch's start counters
     uint32_t pre[kBins] = {0u, 0u, 0u, 0u, 0u};
-    if ((int)threadIdx.x < Tf) {
+    if ((int)threadIdx.x < Tf && (int)threadIdx.x != tile) {   // (its own records are read)
       if (wait_state(slots + threadIdx.x, epoch, kStAgg) == 0u) sh.bad = 1u;
       if ((int)threadIdx.x < tile) {
 #pragma unroll
@@ -499,16 +500,29 @@ __global__ __launch_bounds__(kEncThreads, 4) void encode_onepass_kernel(
 
     // the counts of the encode tiles between this workgroup's previous tile and this one
     uint32_t pre[kBins] = {0u, 0u, 0u, 0u, 0u};
+    // (every kEncThreads-th record below this tile per thread, kPollBatch loads in flight at
+    // once; only a record not yet published is polled again)
     const int lo = et - G + 1 > 0 ? et - G + 1 : 0;
-    for (int i = et - 1 - (int)threadIdx.x; i >= lo; i -= kEncThreads) {
-      const uint64_t r = wait_record(erec + i, epoch);
-      if (r == ~0ull) {
-        sh.bad = 1u;
-        break;
+    bool gave_up = false;
+    for (int i0 = et - 1 - (int)threadIdx.x; i0 >= lo && !gave_up; i0 -= kPollBatch * kEncThreads) {
+      uint64_t r[kPollBatch];
+#pragma unroll
+      for (int u = 0; u < kPollBatch; ++u) {
+        const int i = i0 - u * kEncThreads;
+        r[u] = i >= lo ? ld_agent64(erec + i) : (uint64_t)epoch << 32;
       }
 #pragma unroll
-      for (int k = 0; k < kBins; ++k) pre[k] += (uint32_t)(r >> (kCountBits * k)) & ((1u << kCountBits) - 1u);
+      for (int u = 0; u < kPollBatch; ++u) {
+        if ((uint32_t)(r[u] >> 32) != epoch && !gave_up) {
+          r[u] = wait_record(erec + (i0 - u * kEncThreads), epoch);
+          gave_up = r[u] == ~0ull;
+        }
+        if ((uint32_t)(r[u] >> 32) != epoch) continue;
+#pragma unroll
+        for (int k = 0; k < kBins; ++k) pre[k] += (uint32_t)(r[u] >> (kCountBits * k)) & ((1u << kCountBits) - 1u);
+      }
     }
+    if (gave_up) sh.bad = 1u;
     block_sum5(pre, sh);
 #pragma unroll
     for (int k = 0; k < kBins; ++k) {
