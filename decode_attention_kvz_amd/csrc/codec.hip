@@ -180,8 +180,9 @@ constexpr uint32_t kMaxSpins = 1u << 20;   // a wait that never ends marks its t
 constexpr uint32_t kStAgg = 1, kStDone = 3;                  // free-slot states (low two status bits)
 constexpr int kCountBits = 6;                                // per class in an encode record
 constexpr int kPollBatch = 4;                                // record loads in flight per thread
-// the control area's words: launches completed, finished workgroups of the running launch
-constexpr int kCtlLaunches = 0, kCtlRead = 1;
+// the control area's first two words, read and written as one 64-bit word: launches completed,
+// and the halt flag (set by a launch that gave up a wait; see the kernel)
+constexpr int kCtlLaunches = 0, kCtlHalted = 1;
 
 __device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -289,14 +290,21 @@ __global__ __launch_bounds__(kEncThreads, 4) void encode_onepass_kernel(
   const int G = gridDim.x;
   // The launch's number tags its records: read from the device at the start (so a replayed
   // graph gets a new one each time), and taken - put in LDS for the tile's first barrier - once
-  // the workgroup's first loads are out, so that waiting for it costs nothing.  Then each
-  // workgroup counts itself in; the one that completes the count has seen every workgroup's
-  // read, so it advances the number at its end (the count's result is only needed there).
-  __shared__ uint32_t s_epoch;
-  uint32_t launches = 0, read_before = 0;
+  // the workgroup's first loads are out, so that waiting for it costs nothing.  Every workgroup
+  // publishes a record or a slot status with it before the last tile's waits end; so the
+  // workgroup of the last tile, once those waits have all succeeded, has seen every read of the
+  // number, and it advances the number at its end.  If one of its waits gave up instead, a
+  // workgroup may not have started yet; started later, it would read the advanced number and
+  // could leave records that the next launch took for its own.  That launch therefore sets the
+  // halt flag with the number: a workgroup that reads the flag (a late one, or one of any later
+  // launch until the pool is initialised again) stores nothing and publishes nothing.
+  __shared__ uint32_t s_epoch;   // 0: halted
+  uint32_t launches = 0, halted = 0;
   if (threadIdx.x == 0) {
     sh.bad = 0u;
-    launches = ld_agent(ctl + kCtlLaunches);
+    const uint64_t c = ld_agent64(reinterpret_cast<const uint64_t*>(ctl));
+    launches = (uint32_t)c;
+    halted = (uint32_t)(c >> 32);
     if (blockIdx.x == 0) {   // tile 0: the counters the launch starts from
 #pragma unroll
       for (int k = 0; k < kBins; ++k) sh.snap[k] = (uint32_t)hdr->bin_cnt[k];
@@ -308,7 +316,9 @@ __global__ __launch_bounds__(kEncThreads, 4) void encode_onepass_kernel(
   // (thread 0, before a barrier that the whole workgroup reaches; once per workgroup)
   auto take_number = [&]() {
     if (threadIdx.x != 0) return;
-    s_epoch = launches % ((1u << 30) - 1u) + 1u;
+    s_epoch = halted ? 0u : launches % ((1u << 30) - 1u) + 1u;
+    if (halted) return;
+    if (flags & KVZ_ENC_SIMULATE_GIVE_UP) sh.bad = 1u;   // as if a wait of this workgroup gave up
     if (blockIdx.x == 0) {   // tile 0 publishes the start counters (its slot's status below)
 #pragma unroll
       for (int k = 0; k < kBins; ++k) st_agent(&slots[0].snap[k], sh.snap[k]);
@@ -318,10 +328,9 @@ __global__ __launch_bounds__(kEncThreads, 4) void encode_onepass_kernel(
     __builtin_amdgcn_s_waitcnt(0);   // the read has returned (and the counters are out)
     if (blockIdx.x == 0 && Tf == 0)  // tile 0 encodes: its slot only carries these counters
       st_agent(&slots[0].status, ((launches % ((1u << 30) - 1u) + 1u) << 2) | kStAgg);
-    read_before = __hip_atomic_fetch_add(ctl + kCtlRead, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
   uint32_t epoch = 0;   // from s_epoch after the first barrier past take_number
-  bool numbered = false;
+  bool numbered = false, last_tile = false;
 
   // ---------------- a free tile (at most one per workgroup: every free tile is in the first
   // round): kFreePer listed groups per thread, in item order
@@ -359,82 +368,84 @@ __global__ __launch_bounds__(kEncThreads, 4) void encode_onepass_kernel(
     numbered = true;
     __syncthreads();
     epoch = s_epoch;
-    uint32_t agg[kBins], rank0[kBins];
-#pragma unroll
-    for (int k = 0; k < kBins; ++k) {
-      uint32_t below = 0, tot = 0;
-#pragma unroll
-      for (int w = 0; w < kEncWaves; ++w) {
-        below += w < wave ? sh.part[w][k] : 0u;
-        tot += sh.part[w][k];
+    if (epoch != 0u) {   // (halted: this launch frees nothing)
+      uint32_t agg[kBins], rank0[kBins];
+  #pragma unroll
+      for (int k = 0; k < kBins; ++k) {
+        uint32_t below = 0, tot = 0;
+  #pragma unroll
+        for (int w = 0; w < kEncWaves; ++w) {
+          below += w < wave ? sh.part[w][k] : 0u;
+          tot += sh.part[w][k];
+        }
+        rank0[k] = below + incl_t[k] - mine[k];
+        agg[k] = tot;
       }
-      rank0[k] = below + incl_t[k] - mine[k];
-      agg[k] = tot;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-#pragma unroll
-      for (int k = 0; k < kBins; ++k) st_agent(&me->agg[k], agg[k]);
-      __builtin_amdgcn_s_waitcnt(0);
-      st_agent(&me->status, (epoch << 2) | kStAgg);
-    }
-    // every free tile's counts (each published only after its records were read): the runs
-    // freed by the tiles below this one, and leave to clear; then the launch's start counters
-    uint32_t pre[kBins] = {0u, 0u, 0u, 0u, 0u};
-    if ((int)threadIdx.x < Tf && (int)threadIdx.x != tile) {   // (its own records are read)
-      if (wait_state(slots + threadIdx.x, epoch, kStAgg) == 0u) sh.bad = 1u;
-      if ((int)threadIdx.x < tile) {
-#pragma unroll
-        for (int k = 0; k < kBins; ++k) pre[k] = ld_agent(&slots[threadIdx.x].agg[k]);
+      __syncthreads();
+      if (threadIdx.x == 0) {
+  #pragma unroll
+        for (int k = 0; k < kBins; ++k) st_agent(&me->agg[k], agg[k]);
+        __builtin_amdgcn_s_waitcnt(0);
+        st_agent(&me->status, (epoch << 2) | kStAgg);
       }
-    }
-    if (threadIdx.x == kEncThreads - 1 && tile != 0 && !read_start(slots, epoch, sh)) sh.bad = 1u;
-    block_sum5(pre, sh);
-    const bool ok = sh.bad == 0u;
-    uint64_t my_runs = 0, my_gran = 0, my_raw = 0, my_bad = 0;
-#pragma unroll
-    for (int u = 0; u < kFreePer; ++u) {
-      const int k = key[u];
-      if (k < 0) continue;
-      uint32_t r = 0;
-#pragma unroll
-      for (int j = 0; j < kBins; ++j) {
-        if (j == k) {
-          r = sh.snap[j] + pre[j] + rank0[j];
-          rank0[j] += 1;
+      // every free tile's counts (each published only after its records were read): the runs
+      // freed by the tiles below this one, and leave to clear; then the launch's start counters
+      uint32_t pre[kBins] = {0u, 0u, 0u, 0u, 0u};
+      if ((int)threadIdx.x < Tf && (int)threadIdx.x != tile) {   // (its own records are read)
+        if (wait_state(slots + threadIdx.x, epoch, kStAgg) == 0u) sh.bad = 1u;
+        if ((int)threadIdx.x < tile) {
+  #pragma unroll
+          for (int k = 0; k < kBins; ++k) pre[k] = ld_agent(&slots[threadIdx.x].agg[k]);
         }
       }
-      if (ok && r < s_bcap[k]) {
-        st_agent(bins + s_bbase[k] + r, (uint32_t)rec[u]);
-        my_runs += 1;
-        my_gran += run_granules((uint32_t)k);
-        my_raw += (uint32_t)k;
-      } else {
-        my_bad += 1;
+      if (threadIdx.x == kEncThreads - 1 && tile != 0 && !read_start(slots, epoch, sh)) sh.bad = 1u;
+      block_sum5(pre, sh);
+      const bool ok = sh.bad == 0u;
+      uint64_t my_runs = 0, my_gran = 0, my_raw = 0, my_bad = 0;
+  #pragma unroll
+      for (int u = 0; u < kFreePer; ++u) {
+        const int k = key[u];
+        if (k < 0) continue;
+        uint32_t r = 0;
+  #pragma unroll
+        for (int j = 0; j < kBins; ++j) {
+          if (j == k) {
+            r = sh.snap[j] + pre[j] + rank0[j];
+            rank0[j] += 1;
+          }
+        }
+        if (ok && r < s_bcap[k]) {
+          st_agent(bins + s_bbase[k] + r, (uint32_t)rec[u]);
+          my_runs += 1;
+          my_gran += run_granules((uint32_t)k);
+          my_raw += (uint32_t)k;
+        } else {
+          my_bad += 1;
+        }
       }
-    }
-    if (ok) {
-#pragma unroll
-      for (int u = 0; u < kFreePer; ++u)
-        if (m[u]) st_agent64((uint64_t*)(m[u]), (uint64_t)KVZ_OFF_NONE);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();   // every thread's bin stores and clears are complete
-    if (threadIdx.x == 0) {
-      // a free tile that gave up a wait pushed nothing: the launch's encode tiles then store
-      // nothing and empty the bins (runs leak; no bin entry is ever stale)
-      st_agent(&me->bad, ok ? 0u : 1u);
+      if (ok) {
+  #pragma unroll
+        for (int u = 0; u < kFreePer; ++u)
+          if (m[u]) st_agent64((uint64_t*)(m[u]), (uint64_t)KVZ_OFF_NONE);
+      }
       __builtin_amdgcn_s_waitcnt(0);
-      st_agent(&me->status, (epoch << 2) | kStDone);
-    }
-    // the tile's totals (the counters of a free that cannot happen stay as they were)
-    uint32_t tot[kBins] = {(uint32_t)my_runs, (uint32_t)my_gran, (uint32_t)my_raw, (uint32_t)my_bad, 0u};
-    block_sum5(tot, sh);
-    if (threadIdx.x == 0) {
-      add_agent(&hdr->live_runs, (uint64_t)0 - tot[0]);
-      add_agent(&hdr->live_granules, (uint64_t)0 - tot[1]);
-      add_agent(&hdr->live_raw_blocks, (uint64_t)0 - tot[2]);
-      add_agent(&hdr->bad_frees, tot[3]);
+      __syncthreads();   // every thread's bin stores and clears are complete
+      if (threadIdx.x == 0) {
+        // a free tile that gave up a wait pushed nothing: the launch's encode tiles then store
+        // nothing and empty the bins (runs leak; no bin entry is ever stale)
+        st_agent(&me->bad, ok ? 0u : 1u);
+        __builtin_amdgcn_s_waitcnt(0);
+        st_agent(&me->status, (epoch << 2) | kStDone);
+      }
+      // the tile's totals (the counters of a free that cannot happen stay as they were)
+      uint32_t tot[kBins] = {(uint32_t)my_runs, (uint32_t)my_gran, (uint32_t)my_raw, (uint32_t)my_bad, 0u};
+      block_sum5(tot, sh);
+      if (threadIdx.x == 0) {
+        add_agent(&hdr->live_runs, (uint64_t)0 - tot[0]);
+        add_agent(&hdr->live_granules, (uint64_t)0 - tot[1]);
+        add_agent(&hdr->live_raw_blocks, (uint64_t)0 - tot[2]);
+        add_agent(&hdr->bad_frees, tot[3]);
+      }
     }
   }
 
@@ -445,6 +456,7 @@ __global__ __launch_bounds__(kEncThreads, 4) void encode_onepass_kernel(
 
   for (int tile = t_first; tile < n_tiles; tile += G) {
     const int et = tile - Tf;                 // encode tile index
+    last_tile = tile == n_tiles - 1;
     // load and classify this wave's items
     uint4 w[IPW][4];
     uint32_t tags[IPW];
@@ -482,6 +494,18 @@ __global__ __launch_bounds__(kEncThreads, 4) void encode_onepass_kernel(
     if (!numbered) {
       epoch = s_epoch;
       numbered = true;
+    }
+    if (epoch == 0u) {   // halted: the items are stored nowhere, counted as failed
+      uint32_t failed = 0;
+#pragma unroll
+      for (int u = 0; u < IPW; ++u) {
+        const int item = (et * kEncWaves + wave) * IPW + u;
+        if (item >= n) continue;
+        failed += 1;
+        if (lane == 0) *(global_u64*)(it[u].dst) = (uint64_t)KVZ_OFF_NONE | ((uint64_t)tags[u] << 32);
+      }
+      if (lane == 0) add_agent(&hdr->enospc, failed);
+      continue;
     }
     uint32_t agg[kBins];
 #pragma unroll
@@ -675,12 +699,11 @@ __global__ __launch_bounds__(kEncThreads, 4) void encode_onepass_kernel(
       }
     }
   }
-  if (!numbered) take_number();   // (the host gives every workgroup a tile; kept for safety)
-  // the workgroup that completed the count: every workgroup has read the launch's number
-  if (threadIdx.x == 0 && read_before + 1u == gridDim.x) {
-    st_agent(ctl + kCtlRead, 0u);
-    __hip_atomic_fetch_add(ctl + kCtlLaunches, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  // the last tile's workgroup: the next number, and the halt flag if one of its waits gave up
+  // (every sh.bad write is ordered before this by the tile's last barrier)
+  if (threadIdx.x == 0 && last_tile && epoch != 0u)
+    st_agent64(reinterpret_cast<uint64_t*>(ctl),
+               ((uint64_t)(sh.bad != 0u ? 1u : 0u) << 32) | (uint64_t)(launches + 1u));
 }
 
 // Step 4: natural-order BF16 [16 tokens][32 dims] of each referenced block.
@@ -866,7 +889,8 @@ int check_encode_args(kvz_pool* p, const kvz_encode_item* d_items, int32_t n, ui
     return set_error(KVZ_EINVAL, "pool was made for FP8 tiles (kvz_fp8_pool_init)");
   if (n < 0) return set_error(KVZ_EINVAL, "n < 0");
   if (n > 0 && !d_items) return set_error(KVZ_EINVAL, "items pointer is null");
-  if (flags & ~KVZ_ENC_FORCE_RAW) return set_error(KVZ_EINVAL, "unknown encode flag");
+  if (flags & ~(KVZ_ENC_FORCE_RAW | KVZ_ENC_SIMULATE_GIVE_UP))
+    return set_error(KVZ_EINVAL, "unknown encode flag");
   return KVZ_OK;
 }
 

@@ -827,7 +827,10 @@ extern "C" int kvz_pool_stats(kvz_pool* p, kvz_pool_stats_t* host_out, hipStream
   if (rc != KVZ_OK) return rc;
   if (!host_out) return set_error(KVZ_EINVAL, "host_out is null");
   PoolHdr h;
+  uint32_t ctl[2] = {0u, 0u};   // the one-pass encoder's launch number and halt flag
   rc = check_hip(hipMemcpyAsync(&h, p->state, sizeof(h), hipMemcpyDeviceToHost, s), "stats copy");
+  if (rc != KVZ_OK) return rc;
+  rc = check_hip(hipMemcpyAsync(ctl, p->enc_scratch, sizeof(ctl), hipMemcpyDeviceToHost, s), "stats copy");
   if (rc != KVZ_OK) return rc;
   rc = check_hip(hipStreamSynchronize(s), "stats sync");
   if (rc != KVZ_OK) return rc;
@@ -841,6 +844,7 @@ extern "C" int kvz_pool_stats(kvz_pool* p, kvz_pool_stats_t* host_out, hipStream
   host_out->live_raw_blocks = h.live_raw_blocks;
   host_out->enospc = h.enospc;
   host_out->bad_frees = h.bad_frees;
+  host_out->encoder_halted = ctl[1] ? 1u : 0u;
   return KVZ_OK;
 }
 

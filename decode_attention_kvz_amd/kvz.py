@@ -31,6 +31,7 @@ KVZ_OFF_NONE = 0xFFFFFFFF
 KVZ_KIND_K = 0
 KVZ_KIND_V = 1
 KVZ_ENC_FORCE_RAW = 1
+KVZ_ENC_SIMULATE_GIVE_UP = 2
 KVZ_WS_BAD_COUNTER = 1
 KVZ_PART_ALL, KVZ_PART_LOAD, KVZ_PART_LOAD_RESTORE = 0, 1, 2
 GRANULE = 256
@@ -62,7 +63,8 @@ class PoolStats(ctypes.Structure):
     _fields_ = [("capacity_granules", ctypes.c_uint64), ("frontier_granules", ctypes.c_uint64),
                 ("free_runs", ctypes.c_uint64 * 5), ("live_runs", ctypes.c_uint64),
                 ("live_granules", ctypes.c_uint64), ("live_raw_blocks", ctypes.c_uint64),
-                ("enospc", ctypes.c_uint64), ("bad_frees", ctypes.c_uint64)]
+                ("enospc", ctypes.c_uint64), ("bad_frees", ctypes.c_uint64),
+                ("encoder_halted", ctypes.c_uint64)]
 
 
 class Capacity(ctypes.Structure):
@@ -460,7 +462,7 @@ def kvz_pool_stats(pool, stream=None) -> dict:
     return {"capacity_granules": st.capacity_granules, "frontier_granules": st.frontier_granules,
             "free_runs": list(st.free_runs), "live_runs": st.live_runs,
             "live_granules": st.live_granules, "live_raw_blocks": st.live_raw_blocks,
-            "enospc": st.enospc, "bad_frees": st.bad_frees}
+            "enospc": st.enospc, "bad_frees": st.bad_frees, "encoder_halted": st.encoder_halted}
 
 
 def kvz_decompress_pages(arena, meta, dst, stream=None) -> None:

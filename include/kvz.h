@@ -76,6 +76,10 @@ enum {
 #define KVZ_KIND_K 0u
 #define KVZ_KIND_V 1u
 #define KVZ_ENC_FORCE_RAW 1u    /* kvz_encode_pages flag: store every block raw */
+#define KVZ_ENC_SIMULATE_GIVE_UP 2u  /* kvz_encode_pages / kvz_complete_pages flag, for tests of the
+                                        failure path: a call that takes the one-pass launch acts
+                                        as if one of its waits had given up (see
+                                        kvz_encode_pages); ignored by calls above 16384 items */
 #define KVZ_PART_ALL 0           /* kvz_*_decode_attention_part: the whole call                */
 #define KVZ_PART_LOAD 1          /* only the page loads of the attention kernel                */
 #define KVZ_PART_LOAD_RESTORE 2  /* the page loads and the in-register restore                 */
@@ -126,6 +130,8 @@ typedef struct {
   uint64_t live_raw_blocks;
   uint64_t enospc;             /* groups that found no room (cumulative)                        */
   uint64_t bad_frees;          /* frees dropped because a bin was full (double free)            */
+  uint64_t encoder_halted;     /* 1 once a one-pass encode launch gave up a wait (see
+                                  kvz_encode_pages); 0 after kvz_pool_init                      */
 } kvz_pool_stats_t;
 
 /* Decode-attention arguments, fused compressed path.
@@ -221,7 +227,17 @@ int kvz_slot_free(kvz_pool* p, kvz_group_meta* const* d_metas, int32_t n, hipStr
  * four blocks, allocate a run (same rule and order as kvz_slot_alloc), write the blocks into
  * the arena and the 8-byte metadata to item.dst.  If the pool has no room, dst->off is
  * KVZ_OFF_NONE and nothing is written: the caller keeps that page in BF16.  flags:
- * KVZ_ENC_FORCE_RAW stores every block raw.  d_items: device [n]. */
+ * KVZ_ENC_FORCE_RAW stores every block raw; KVZ_ENC_SIMULATE_GIVE_UP (tests only, see below).
+ * d_items: device [n].
+ * A call of up to 16384 items is one launch whose workgroups wait, each for a bounded time
+ * (about a second), for counts published by lower-numbered workgroups of the same launch; such
+ * waits only run out if a workgroup cannot start while the rest of the launch runs (e.g. the
+ * device is preempted).  A launch whose wait runs out stores nothing (every item KVZ_OFF_NONE,
+ * counted in enospc; the bins are emptied, their runs lost) and halts the pool's one-pass
+ * encoder: from then on every call of up to 16384 items stores nothing, counted in enospc (a
+ * kvz_complete_pages call whose frees share the launch does not free them either), until
+ * kvz_pool_init; kvz_pool_stats reports encoder_halted.  Larger calls, kvz_slot_alloc and
+ * kvz_slot_free are not affected. */
 int kvz_encode_pages(kvz_pool* p, const kvz_encode_item* d_items, int32_t n, uint32_t flags,
                      hipStream_t s);
 

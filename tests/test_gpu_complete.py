@@ -9,6 +9,8 @@
   (up to 1,024 groups each), frees that include the records the encode then rewrites, a call of
   20,000 groups (above the one-pass limit), and an arena that runs out.
 * A captured kvz_complete_pages replayed with new item records each time equals eager calls.
+* A one-pass launch whose wait gives up (forced from the host) stores and frees nothing and
+  halts the one-pass encoder until kvz_pool_init; bulk calls are not affected.
 """
 import numpy as np
 import pytest
@@ -223,3 +225,96 @@ def test_graph_replays_with_new_items_match_eager_calls(n):
         np.testing.assert_array_equal(gtags, tags[src])
         assert pools[0].stats() == pools[1].stats(), rep
         assert pools[0].stats()["enospc"] == 0
+
+
+def test_a_wait_that_gives_up_halts_the_one_pass_encoder():
+    """The failure path of the one-pass launch, forced from the host (KVZ_ENC_SIMULATE_GIVE_UP:
+    every workgroup acts as if a wait had given up; every kernel still runs to its end).  That
+    launch stores and frees nothing and empties the bins; it halts the one-pass encoder, so the
+    next one-pass calls store and free nothing either; a bulk call still allocates as the model
+    says; kvz_pool_init brings the one-pass encoder back."""
+    announce("one-pass encoder: a wait that gives up (forced), then the halted state")
+    rng = np.random.default_rng(13)
+    bank, nat, tags = _bank(seed=13, forced=0.10)
+    arena = paged.SlotArena(256 << 20)
+    model = SlotPoolModel(pool_capacity_granules(arena.arena.numel()))
+    n_slots = 40000
+    meta = torch.empty((n_slots, 8), dtype=torch.uint8, device="cuda")
+    meta[:, :4] = 0xFF
+    meta[:, 4:] = 0
+
+    def ptrs(ids):
+        return torch.from_numpy(meta.data_ptr() + np.asarray(ids, dtype=np.int64) * 8).cuda()
+
+    # a normal call, then a free of part of it (the bins hold runs)
+    src0 = rng.integers(0, nat.shape[0], size=3000)
+    kvz.kvz_encode_pages(arena.pool, _items(bank, src0, meta, np.arange(3000)), 3000)
+    off0 = model.alloc([t.tolist() for t in tags[src0]])
+    kvz.kvz_slot_free(arena.pool, ptrs(np.arange(0, 3000, 3)))
+    model.free([(off0[i], tags[src0[i]].tolist()) for i in range(0, 3000, 3)])
+    _check_stats(arena, model, "before")
+    assert arena.stats()["encoder_halted"] == 0
+    before = meta.cpu().numpy()
+
+    # the forced give-up: frees of 1,000 live groups and 2,000 encodes into fresh slots
+    victims = np.arange(1, 3000, 3)
+    src1 = rng.integers(0, nat.shape[0], size=2000)
+    ids1 = 3000 + np.arange(2000)
+    kvz.kvz_complete_pages(arena.pool, ptrs(victims), _items(bank, src1, meta, ids1), 2000,
+                           flags=kvz.KVZ_ENC_SIMULATE_GIVE_UP)
+    got, gtags = _records(meta, ids1)
+    assert (got == OFF_NONE).all()
+    np.testing.assert_array_equal(gtags, tags[src1])
+    np.testing.assert_array_equal(meta.cpu().numpy()[victims], before[victims])   # not freed
+    st = arena.stats()
+    assert st["encoder_halted"] == 1
+    assert st["free_runs"] == [0] * 5 and st["frontier_granules"] == model.frontier
+    assert st["enospc"] == model.enospc + 2000 and st["bad_frees"] == len(victims)
+    assert st["live_runs"] == model.live_runs and st["live_granules"] == model.live_granules
+    model.bins = [[] for _ in range(5)]            # the launch emptied the bins
+    model.enospc += 2000
+
+    # halted: a one-pass encode and a fused call store and free nothing
+    for what in ("encode", "complete"):
+        src2 = rng.integers(0, nat.shape[0], size=700)
+        ids2 = (5000 if what == "encode" else 6000) + np.arange(700)
+        items = _items(bank, src2, meta, ids2)
+        if what == "encode":
+            kvz.kvz_encode_pages(arena.pool, items, 700)
+        else:
+            kvz.kvz_complete_pages(arena.pool, ptrs(np.arange(2, 3000, 3)), items, 700)
+        got, gtags = _records(meta, ids2)
+        assert (got == OFF_NONE).all(), what
+        np.testing.assert_array_equal(gtags, tags[src2])
+        model.enospc += 700
+        _check_stats(arena, model, f"halted {what}")
+        assert arena.stats()["encoder_halted"] == 1
+        assert arena.stats()["bad_frees"] == len(victims)
+    np.testing.assert_array_equal(meta.cpu().numpy()[2:3000:3], before[2:3000:3])
+
+    # a bulk call is not affected: it allocates from the frontier as the model does
+    src3 = rng.integers(0, nat.shape[0], size=20000)
+    ids3 = 8000 + np.arange(20000)
+    kvz.kvz_encode_pages(arena.pool, _items(bank, src3, meta, ids3), 20000)
+    want3 = np.asarray(model.alloc([t.tolist() for t in tags[src3]]), dtype=np.int64)
+    got, _ = _records(meta, ids3)
+    np.testing.assert_array_equal(got, want3)
+    _check_stats(arena, model, "bulk while halted")
+
+    # kvz_pool_init: empty pool, one-pass encoder working
+    kvz.kvz_pool_destroy(arena.pool)
+    arena.pool = kvz.kvz_pool_init(arena.arena, arena.state)
+    model = SlotPoolModel(pool_capacity_granules(arena.arena.numel()))
+    src4 = rng.integers(0, nat.shape[0], size=3000)
+    ids4 = 30000 + np.arange(3000)
+    kvz.kvz_complete_pages(arena.pool, None, _items(bank, src4, meta, ids4), 3000)
+    want4 = np.asarray(model.alloc([t.tolist() for t in tags[src4]]), dtype=np.int64)
+    got, _ = _records(meta, ids4)
+    np.testing.assert_array_equal(got, want4)
+    _check_stats(arena, model, "after kvz_pool_init")
+    assert arena.stats()["encoder_halted"] == 0
+    arena_h = arena.arena.cpu().numpy()
+    for i in rng.choice(3000, 24, replace=False):
+        g = src4[i]
+        np.testing.assert_array_equal(
+            codec.decode_group(arena_h, int(want4[i]), tags[g].tolist(), int((g // HKV) % 2)), nat[g])
