@@ -172,7 +172,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const kvz_encode_item* items,
 // too - tags its records anew.
 constexpr int kEncWaves = 4;
 constexpr int kEncThreads = kEncWaves * 64;
-constexpr int kFreePer = 4;                                  // listed groups per thread of a free tile
+constexpr int kFreePer = 2;                                  // listed groups per thread of a free tile
 constexpr int kFreeTileItems = kEncThreads * kFreePer;
 constexpr int kMaxFreeTiles = kMaxFreeSlots;
 static_assert(kMaxFreeTiles <= kEncThreads, "one waiting thread per free tile");

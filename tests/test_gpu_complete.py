@@ -5,8 +5,8 @@
   offset and tag equals the oracle pool model and classification, the pool counters equal the
   model's, and a sample of groups decoded by the oracle from the arena bytes equals its source.
 * kvz_complete_pages against kvz_slot_free followed by kvz_encode_pages on a second pool: the
-  same records, arena bytes and counters after every step, for frees of one to six free tiles
-  (up to 1,024 groups each), frees that include the records the encode then rewrites, a call of
+  same records, arena bytes and counters after every step, for frees of one to twelve free tiles
+  (up to 512 groups each), frees that include the records the encode then rewrites, a call of
   20,000 groups (above the one-pass limit), and an arena that runs out.
 * A captured kvz_complete_pages replayed with new item records each time equals eager calls.
 * A one-pass launch whose wait gives up (forced from the host) stores and frees nothing and
@@ -123,7 +123,7 @@ def test_complete_pages_equals_free_then_encode(arena_mb):
     live = {}                                   # slot -> source group
     live_off = {}                               # slot -> offset (the model's)
     free_slots = list(range(n_slots))
-    # (groups freed, groups encoded): one to six free tiles, small and multi-tile encodes, and a
+    # (groups freed, groups encoded): one to twelve free tiles, small and multi-tile encodes, and a
     # call above the one-pass limit (the free, then the bulk path)
     plan = [(0, 3000), (700, 2048), (1024, 1025), (2500, 4096), (6000, 9216), (5000, 100),
             (300, 5000), (4000, 4000), (1, 64), (3000, 20000)]
