@@ -177,7 +177,9 @@ constexpr int kFreeTileItems = kEncThreads * kFreePer;
 constexpr int kMaxFreeTiles = kMaxFreeSlots;
 static_assert(kMaxFreeTiles <= kEncThreads, "one waiting thread per free tile");
 constexpr uint32_t kMaxSpins = 1u << 20;   // a wait that never ends marks its tile's items unstored
-constexpr uint32_t kStAgg = 1, kStDone = 3;                  // free-slot states (low two status bits)
+constexpr uint32_t kStBad = 2, kStDone = 3;                  // free-slot states (low two status bits)
+constexpr int kAggBits = 10;                                 // per class in a free tile's count word
+static_assert(kFreePer * kEncThreads < (1 << kAggBits), "a free tile's counts fit their fields");
 constexpr int kCountBits = 6;                                // per class in an encode record
 constexpr int kPollBatch = 4;                                // record loads in flight per thread
 // the control area's first two words, read and written as one 64-bit word: launches completed,
@@ -219,6 +221,22 @@ __device__ __forceinline__ uint64_t wait_record(const uint64_t* r, uint32_t epoc
   }
 }
 
+// The 14-bit form of an epoch in a free tile's count word (never 0: a zeroed word matches none).
+__device__ __forceinline__ uint32_t epoch14(uint32_t epoch) { return epoch % 16383u + 1u; }
+// A free tile's count word of this launch, or ~0 if the wait gave up.
+__device__ __forceinline__ uint64_t wait_agg(const uint64_t* w, uint32_t epoch) {
+  const uint64_t want = epoch14(epoch);
+  for (uint32_t spins = 0;; ++spins) {
+    const uint64_t v = ld_agent64(w);
+    if ((v >> (kBins * kAggBits)) == want) return v;
+    if (spins > kMaxSpins) return ~0ull;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+__device__ __forceinline__ uint32_t agg_count(uint64_t w, int k) {
+  return (uint32_t)(w >> (kAggBits * k)) & ((1u << kAggBits) - 1u);
+}
+
 struct OnePassShared {
   uint32_t part[kEncWaves][kBins];
   uint32_t bad;
@@ -251,7 +269,10 @@ __device__ __forceinline__ void block_sum5(uint32_t (&v)[kBins], OnePassShared& 
 
 // The launch's starting counters (tile 0's slot), by one thread; false if the wait gave up.
 __device__ __forceinline__ bool read_start(const EncodeSlot* slots, uint32_t epoch, OnePassShared& sh) {
-  if (wait_state(slots, epoch, kStAgg) == 0u) return false;
+  for (uint32_t spins = 0; ld_agent(&slots[0].sstat) != epoch; ++spins) {
+    if (spins > kMaxSpins) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
 #pragma unroll
   for (int k = 0; k < kBins; ++k) sh.snap[k] = ld_agent(&slots[0].snap[k]);
   sh.f0_lo = ld_agent(&slots[0].f0_lo);
@@ -305,9 +326,13 @@ __global__ __launch_bounds__(kEncThreads, 4) void encode_onepass_kernel(
     const uint64_t c = ld_agent64(reinterpret_cast<const uint64_t*>(ctl));
     launches = (uint32_t)c;
     halted = (uint32_t)(c >> 32);
-    if (blockIdx.x == 0) {   // tile 0: the counters the launch starts from
+    // the counters the launch starts from: tile 0 publishes them; a free tile reads the bin
+    // counts itself (only the last tile writes them, after every free tile has published)
+    if (blockIdx.x == 0 || (int)blockIdx.x < Tf) {
 #pragma unroll
       for (int k = 0; k < kBins; ++k) sh.snap[k] = (uint32_t)hdr->bin_cnt[k];
+    }
+    if (blockIdx.x == 0) {
       const uint64_t f0 = hdr->frontier;
       sh.f0_lo = (uint32_t)f0;
       sh.f0_hi = (uint32_t)(f0 >> 32);
@@ -319,15 +344,19 @@ __global__ __launch_bounds__(kEncThreads, 4) void encode_onepass_kernel(
     s_epoch = halted ? 0u : launches % ((1u << 30) - 1u) + 1u;
     if (halted) return;
     if (flags & KVZ_ENC_SIMULATE_GIVE_UP) sh.bad = 1u;   // as if a wait of this workgroup gave up
-    if (blockIdx.x == 0) {   // tile 0 publishes the start counters (its slot's status below)
-#pragma unroll
-      for (int k = 0; k < kBins; ++k) st_agent(&slots[0].snap[k], sh.snap[k]);
-      st_agent(&slots[0].f0_lo, sh.f0_lo);
-      st_agent(&slots[0].f0_hi, sh.f0_hi);
+    if (blockIdx.x == 0 && Tf == 0) {   // tile 0 encodes: its slot only carries the start counters
+      __builtin_amdgcn_s_waitcnt(0);     // (stored with the first loads: complete by now)
+      st_agent(&slots[0].sstat, launches % ((1u << 30) - 1u) + 1u);
     }
-    __builtin_amdgcn_s_waitcnt(0);   // the read has returned (and the counters are out)
-    if (blockIdx.x == 0 && Tf == 0)  // tile 0 encodes: its slot only carries these counters
-      st_agent(&slots[0].status, ((launches % ((1u << 30) - 1u) + 1u) << 2) | kStAgg);
+  };
+  // tile 0's start counters, stored once its first loads are out (thread 0; their status
+  // follows a wait for its stores: in take_number, or after the free tile's scan)
+  auto store_start = [&]() {
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+#pragma unroll
+    for (int k = 0; k < kBins; ++k) st_agent(&slots[0].snap[k], sh.snap[k]);
+    st_agent(&slots[0].f0_lo, sh.f0_lo);
+    st_agent(&slots[0].f0_hi, sh.f0_hi);
   };
   uint32_t epoch = 0;   // from s_epoch after the first barrier past take_number
   bool numbered = false, last_tile = false;
@@ -342,6 +371,7 @@ __global__ __launch_bounds__(kEncThreads, 4) void encode_onepass_kernel(
     uint64_t rec[kFreePer];
 #pragma unroll
     for (int u = 0; u < kFreePer; ++u) m[u] = e0 + u < n_free ? frees[e0 + u] : nullptr;
+    store_start();
 #pragma unroll
     for (int u = 0; u < kFreePer; ++u) rec[u] = m[u] ? *(const global_u64*)(m[u]) : (uint64_t)KVZ_OFF_NONE;
     int key[kFreePer];
@@ -370,10 +400,10 @@ __global__ __launch_bounds__(kEncThreads, 4) void encode_onepass_kernel(
     epoch = s_epoch;
     if (epoch != 0u) {   // (halted: this launch frees nothing)
       uint32_t agg[kBins], rank0[kBins];
-  #pragma unroll
+#pragma unroll
       for (int k = 0; k < kBins; ++k) {
         uint32_t below = 0, tot = 0;
-  #pragma unroll
+#pragma unroll
         for (int w = 0; w < kEncWaves; ++w) {
           below += w < wave ? sh.part[w][k] : 0u;
           tot += sh.part[w][k];
@@ -383,31 +413,36 @@ __global__ __launch_bounds__(kEncThreads, 4) void encode_onepass_kernel(
       }
       __syncthreads();
       if (threadIdx.x == 0) {
-  #pragma unroll
-        for (int k = 0; k < kBins; ++k) st_agent(&me->agg[k], agg[k]);
-        __builtin_amdgcn_s_waitcnt(0);
-        st_agent(&me->status, (epoch << 2) | kStAgg);
+        if (tile == 0) {   // the start counters (stored with the first loads: complete by now)
+          __builtin_amdgcn_s_waitcnt(0);
+          st_agent(&slots[0].sstat, epoch);
+        }
+        uint64_t w = (uint64_t)epoch14(epoch) << (kBins * kAggBits);
+#pragma unroll
+        for (int k = 0; k < kBins; ++k) w |= (uint64_t)agg[k] << (kAggBits * k);
+        st_agent64(&me->aggw, w);   // one word: readers need no status for it
       }
       // every free tile's counts (each published only after its records were read): the runs
-      // freed by the tiles below this one, and leave to clear; then the launch's start counters
+      // freed by the tiles below this one, and leave to clear
       uint32_t pre[kBins] = {0u, 0u, 0u, 0u, 0u};
       if ((int)threadIdx.x < Tf && (int)threadIdx.x != tile) {   // (its own records are read)
-        if (wait_state(slots + threadIdx.x, epoch, kStAgg) == 0u) sh.bad = 1u;
-        if ((int)threadIdx.x < tile) {
-  #pragma unroll
-          for (int k = 0; k < kBins; ++k) pre[k] = ld_agent(&slots[threadIdx.x].agg[k]);
+        const uint64_t w = wait_agg(&slots[threadIdx.x].aggw, epoch);
+        if (w == ~0ull) {
+          sh.bad = 1u;
+        } else if ((int)threadIdx.x < tile) {
+#pragma unroll
+          for (int k = 0; k < kBins; ++k) pre[k] = agg_count(w, k);
         }
       }
-      if (threadIdx.x == kEncThreads - 1 && tile != 0 && !read_start(slots, epoch, sh)) sh.bad = 1u;
       block_sum5(pre, sh);
       const bool ok = sh.bad == 0u;
       uint64_t my_runs = 0, my_gran = 0, my_raw = 0, my_bad = 0;
-  #pragma unroll
+#pragma unroll
       for (int u = 0; u < kFreePer; ++u) {
         const int k = key[u];
         if (k < 0) continue;
         uint32_t r = 0;
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < kBins; ++j) {
           if (j == k) {
             r = sh.snap[j] + pre[j] + rank0[j];
@@ -424,7 +459,7 @@ __global__ __launch_bounds__(kEncThreads, 4) void encode_onepass_kernel(
         }
       }
       if (ok) {
-  #pragma unroll
+#pragma unroll
         for (int u = 0; u < kFreePer; ++u)
           if (m[u]) st_agent64((uint64_t*)(m[u]), (uint64_t)KVZ_OFF_NONE);
       }
@@ -433,9 +468,7 @@ __global__ __launch_bounds__(kEncThreads, 4) void encode_onepass_kernel(
       if (threadIdx.x == 0) {
         // a free tile that gave up a wait pushed nothing: the launch's encode tiles then store
         // nothing and empty the bins (runs leak; no bin entry is ever stale)
-        st_agent(&me->bad, ok ? 0u : 1u);
-        __builtin_amdgcn_s_waitcnt(0);
-        st_agent(&me->status, (epoch << 2) | kStDone);
+        st_agent(&me->status, (epoch << 2) | (ok ? kStDone : kStBad));
       }
       // the tile's totals (the counters of a free that cannot happen stay as they were)
       uint32_t tot[kBins] = {(uint32_t)my_runs, (uint32_t)my_gran, (uint32_t)my_raw, (uint32_t)my_bad, 0u};
@@ -470,6 +503,7 @@ __global__ __launch_bounds__(kEncThreads, 4) void encode_onepass_kernel(
         load_item_chunks<kPolicy>(it[u].src, it[u].src_stride, it[u].kind, lane, w[u]);
       }
     }
+    if (!numbered && Tf == 0) store_start();
 #pragma unroll
     for (int u = 0; u < IPW; ++u) {
       const int item = (et * kEncWaves + wave) * IPW + u;
@@ -560,10 +594,10 @@ __global__ __launch_bounds__(kEncThreads, 4) void encode_onepass_kernel(
       if (threadIdx.x == kEncThreads - 1 && blockIdx.x != 0 && !read_start(slots, epoch, sh))
         sh.bad = 1u;
       if ((int)threadIdx.x < Tf) {
-        if (wait_state(slots + threadIdx.x, epoch, kStDone) == 0u || ld_agent(&slots[threadIdx.x].bad))
-          sh.bad = 1u;
+        if (wait_state(slots + threadIdx.x, epoch, kStBad) != kStDone) sh.bad = 1u;
+        const uint64_t w = ld_agent64(&slots[threadIdx.x].aggw);   // (complete before the status)
 #pragma unroll
-        for (int k = 0; k < kBins; ++k) freed[k] = ld_agent(&slots[threadIdx.x].agg[k]);
+        for (int k = 0; k < kBins; ++k) freed[k] = agg_count(w, k);
       }
       block_sum5(freed, sh);   // (its barriers also order the shared counters above)
     }
@@ -699,8 +733,12 @@ __global__ __launch_bounds__(kEncThreads, 4) void encode_onepass_kernel(
       }
     }
   }
-  // the last tile's workgroup: the next number, and the halt flag if one of its waits gave up
-  // (every sh.bad write is ordered before this by the tile's last barrier)
+  // the last tile's workgroup: the count words of the slots this launch did not use zeroed, the
+  // next number, and the halt flag if one of its waits gave up (every sh.bad write is ordered
+  // before this by the tile's last barrier)
+  if (last_tile && epoch != 0u) {
+    for (int i = Tf + (int)threadIdx.x; i < kMaxFreeSlots; i += kEncThreads) st_agent64(&slots[i].aggw, 0ull);
+  }
   if (threadIdx.x == 0 && last_tile && epoch != 0u)
     st_agent64(reinterpret_cast<uint64_t*>(ctl),
                ((uint64_t)(sh.bad != 0u ? 1u : 0u) << 32) | (uint64_t)(launches + 1u));

@@ -143,22 +143,24 @@ struct kvz_pool {
 
 namespace kvz {
 // The one-pass page-completion encoder's scratch in the pool state: a 256-byte control area
-// (word 0: launches started and numbered, which numbers the next launch's records; word 1:
-// workgroups of the running launch that have read its number, back to zero once all have),
-// then the records of a launch:
-//  * one 128-byte slot per free tile: its counts of freed runs per size class, and status =
-//    epoch << 2 | state (1: counts complete, 3: its bin stores and clears complete); slot 0 also
-//    holds the bin counts and frontier the launch started from (state >= 1 once they are out),
-//    written by tile 0 whether it frees or encodes; bad: a free tile that could not free;
+// (word 0: launches numbered so far, which numbers the next launch's records; word 1: the halt
+// flag), then the records of a launch:
+//  * one 128-byte slot per free tile: its counts of freed runs per size class in one 64-bit
+//    word (a 14-bit form of the epoch, 1..16383, in the top bits, then five 10-bit counts), and
+//    status = epoch << 2 | state (3: its bin stores and clears complete, 2: it could not free);
+//    slot 0 also holds the bin counts and frontier the launch started from, with their own
+//    status word (the epoch once they are out), written by tile 0 whether it frees or encodes.
+//    A launch zeroes the count words of the slots it does not use, so a slot's word is always
+//    the previous launch's or zero;
 //  * one 64-bit word per encode tile: epoch << 32 | its item counts per size class, 6 bits each.
 // A record of another launch has another epoch.
 struct EncodeSlot {
+  uint64_t aggw;
   uint32_t status;
-  uint32_t agg[kBins];
+  uint32_t sstat;
   uint32_t snap[kBins];
   uint32_t f0_lo, f0_hi;
-  uint32_t bad;
-  uint32_t pad[18];
+  uint32_t pad[21];
 };
 static_assert(sizeof(EncodeSlot) == 128, "one record per 128 bytes");
 constexpr int kMaxFreeSlots = 256;        // free tiles per launch (one waiting thread each)
