@@ -344,13 +344,10 @@ __global__ __launch_bounds__(kEncThreads, 4) void encode_onepass_kernel(
     s_epoch = halted ? 0u : launches % ((1u << 30) - 1u) + 1u;
     if (halted) return;
     if (flags & KVZ_ENC_SIMULATE_GIVE_UP) sh.bad = 1u;   // as if a wait of this workgroup gave up
-    if (blockIdx.x == 0 && Tf == 0) {   // tile 0 encodes: its slot only carries the start counters
-      __builtin_amdgcn_s_waitcnt(0);     // (stored with the first loads: complete by now)
-      st_agent(&slots[0].sstat, launches % ((1u << 30) - 1u) + 1u);
-    }
   };
   // tile 0's start counters, stored once its first loads are out (thread 0; their status
-  // follows a wait for its stores: in take_number, or after the free tile's scan)
+  // follows a wait for its stores: after the free tile's scan, or after the encode tile's
+  // record, which every other tile waits for and so goes first)
   auto store_start = [&]() {
     if (threadIdx.x != 0 || blockIdx.x != 0) return;
 #pragma unroll
@@ -554,6 +551,10 @@ __global__ __launch_bounds__(kEncThreads, 4) void encode_onepass_kernel(
 #pragma unroll
       for (int k = 0; k < kBins; ++k) packed |= (uint64_t)agg[k] << (kCountBits * k);
       st_agent64(erec + et, packed);
+      if (blockIdx.x == 0 && Tf == 0 && tile == t_first) {   // tile 0 encodes: the start counters
+        __builtin_amdgcn_s_waitcnt(0);
+        st_agent(&slots[0].sstat, epoch);
+      }
     }
 
     // the counts of the encode tiles between this workgroup's previous tile and this one
