@@ -550,7 +550,8 @@ __global__ __launch_bounds__(kEncThreads, 4) void encode_onepass_kernel(
       uint64_t packed = (uint64_t)epoch << 32;
 #pragma unroll
       for (int k = 0; k < kBins; ++k) packed |= (uint64_t)agg[k] << (kCountBits * k);
-      st_agent64(erec + et, packed);
+#pragma unroll
+      for (int c = 0; c < kRecordCopies; ++c) st_agent64(erec + c * kMaxEncodeTiles + et, packed);
       if (blockIdx.x == 0 && Tf == 0 && tile == t_first) {   // tile 0 encodes: the start counters
         __builtin_amdgcn_s_waitcnt(0);
         st_agent(&slots[0].sstat, epoch);
@@ -562,18 +563,19 @@ __global__ __launch_bounds__(kEncThreads, 4) void encode_onepass_kernel(
     // (every kEncThreads-th record below this tile per thread, kPollBatch loads in flight at
     // once; only a record not yet published is polled again)
     const int lo = et - G + 1 > 0 ? et - G + 1 : 0;
+    const uint64_t* rec_copy = erec + (blockIdx.x % kRecordCopies) * kMaxEncodeTiles;
     bool gave_up = false;
     for (int i0 = et - 1 - (int)threadIdx.x; i0 >= lo && !gave_up; i0 -= kPollBatch * kEncThreads) {
       uint64_t r[kPollBatch];
 #pragma unroll
       for (int u = 0; u < kPollBatch; ++u) {
         const int i = i0 - u * kEncThreads;
-        r[u] = i >= lo ? ld_agent64(erec + i) : (uint64_t)epoch << 32;
+        r[u] = i >= lo ? ld_agent64(rec_copy + i) : (uint64_t)epoch << 32;
       }
 #pragma unroll
       for (int u = 0; u < kPollBatch; ++u) {
         if ((uint32_t)(r[u] >> 32) != epoch && !gave_up) {
-          r[u] = wait_record(erec + (i0 - u * kEncThreads), epoch);
+          r[u] = wait_record(rec_copy + (i0 - u * kEncThreads), epoch);
           gave_up = r[u] == ~0ull;
         }
         if ((uint32_t)(r[u] >> 32) != epoch) continue;

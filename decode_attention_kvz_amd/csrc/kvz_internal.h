@@ -152,7 +152,10 @@ namespace kvz {
 //    status word (the epoch once they are out), written by tile 0 whether it frees or encodes.
 //    A launch zeroes the count words of the slots it does not use, so a slot's word is always
 //    the previous launch's or zero;
-//  * one 64-bit word per encode tile: epoch << 32 | its item counts per size class, 6 bits each.
+//  * one 64-bit word per encode tile: epoch << 32 | its item counts per size class, 6 bits each,
+//    stored kRecordCopies times (arrays of kMaxEncodeTiles words, one after the other): every
+//    tile polls the records of all others, and workgroup b reading copy b % kRecordCopies
+//    spreads those polls over more memory channels (one copy: 13.8 vs 13.0 us per online step).
 // A record of another launch has another epoch.
 struct EncodeSlot {
   uint64_t aggw;
@@ -165,7 +168,8 @@ struct EncodeSlot {
 static_assert(sizeof(EncodeSlot) == 128, "one record per 128 bytes");
 constexpr int kMaxFreeSlots = 256;        // free tiles per launch (one waiting thread each)
 constexpr int kMaxEncodeTiles = 4096;     // encode tiles per launch
+constexpr int kRecordCopies = 8;
 constexpr uint64_t kEncodeCtlBytes = 256;
 constexpr uint64_t kEncodeScratchBytes = kEncodeCtlBytes + (uint64_t)kMaxFreeSlots * sizeof(EncodeSlot) +
-                                         (uint64_t)kMaxEncodeTiles * sizeof(uint64_t);
+                                         (uint64_t)kRecordCopies * kMaxEncodeTiles * sizeof(uint64_t);
 }  // namespace kvz
