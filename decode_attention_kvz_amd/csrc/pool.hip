@@ -14,7 +14,7 @@
 // workgroup, then assign (or push) per tile.  Calls of more than kMaxTiles tiles run as
 // consecutive chunks.  The per-tile counts and bases live in a fixed scratch area of the pool
 // state, so the pool needs no memory beyond the state the caller allocated.
-#include "kvz_internal.h"
+#include "encode_internal.h"
 
 #include <algorithm>
 
