@@ -166,10 +166,11 @@ __global__ __launch_bounds__(256) void pack_kernel(const kvz_encode_item* items,
 // Records, bin entries written in the launch and cleared metadata pass between workgroups with
 // agent-scope (sc1) stores and loads: a record's fields are stored, the thread waits for those
 // stores to complete (s_waitcnt vmcnt(0)), then its status is stored; a reader loads the status
-// and only then the fields.  An encode tile's record is one 64-bit word (epoch and counts).
-// The epoch (the launch's number) is read from the pool state at the start of the launch and
-// advanced once every workgroup has read it, so every execution - a replay of a captured graph
-// too - tags its records anew.
+// and only then the fields.  An encode tile's record, and a free tile's counts, are one 64-bit
+// word each (tag and counts), stored and read with no status.  The tag is the epoch (the
+// launch's number), read from the pool state at the start of the launch and advanced by the
+// last tile's workgroup once every workgroup has read it (see the kernel), so every execution -
+// a replay of a captured graph too - tags its records anew.
 constexpr int kEncWaves = 4;
 constexpr int kEncThreads = kEncWaves * 64;
 constexpr int kFreePer = 2;                                  // listed groups per thread of a free tile
