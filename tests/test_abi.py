@@ -195,3 +195,27 @@ def test_binding_rejects_host_and_misshapen_tensors_before_the_call():
         kvz._dev("ws", FakeDev(ws), min_bytes=(1 << 16) + 1)
     with pytest.raises(ValueError, match="16 bytes"):
         kvz._check_meta(FakeDev(torch.zeros((4, hkv, 8), dtype=torch.uint8)))
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="libkvz.so not built")
+def test_binding_constants_and_stats_layout_match_the_header():
+    """Every KVZ_ constant the binding defines has the header's value, and the binding's pool
+    statistics record has the header's fields (all 64-bit: the header's count of uint64_t
+    fields, arrays counted by length)."""
+    from decode_attention_kvz_amd import kvz
+    text = open(HEADER).read()
+    defines = {m.group(1): int(m.group(2), 0) for m in
+               re.finditer(r"^#define\s+(KVZ_\w+)\s+\(?(-?(?:0x[0-9a-fA-F]+|\d+))u?\)?", text, re.M)}
+    checked = 0
+    for name, value in defines.items():
+        if hasattr(kvz, name):
+            assert getattr(kvz, name) == value, name
+            checked += 1
+    assert checked >= 5
+    body = re.search(r"typedef struct \{(.*?)\} kvz_pool_stats_t;", text, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    n_words = 0
+    for m in re.finditer(r"uint64_t\s+(\w+)(?:\[(\d+)\])?;", body):
+        n_words += int(m.group(2) or 1)
+    assert ctypes.sizeof(kvz.PoolStats) == 8 * n_words
+    assert [f[0] for f in kvz.PoolStats._fields_][-1] == "encoder_halted"
